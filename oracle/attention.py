@@ -1,0 +1,113 @@
+"""The definition of batched paged-KV decode attention, in float64.
+
+What is computed follows "FlashDecoding + FlashInfer — the decode-time
+attention story": one query token per sequence attends over that sequence's
+N keys/values (§"FlashDecoding — the split-KV trick", Q of shape (B, H, 1, D));
+K/V live in fixed-size pages of shape (num_pages, block_size, num_kv_heads,
+head_dim) and a per-request page list with the last page's fill selects them
+(§"Paged attention (vLLM)"); query heads share KV heads when num_kv_heads is
+smaller than num_qo_heads (§"The API you actually use (Python)").
+
+Readings taken where the pages are silent (each listed in the design doc):
+
+* Request r owns pages ``indices[indptr[r]:indptr[r+1]]`` (n_r >= 1 of them)
+  and holds ``L_r = (n_r - 1) * page_size + last_page_len[r]`` tokens; token t
+  sits in page ``indices[indptr[r] + t // page_size]`` at slot
+  ``t % page_size``.
+* Query head h reads KV head ``h // (num_qo_heads // num_kv_heads)``.
+* Scores are ``sm_scale * q . k`` with ``sm_scale = 1/sqrt(head_dim)`` unless
+  given; no position encoding is applied (the wrapper's
+  ``pos_encoding_mode="NONE"``).
+* The output is the max-subtracted softmax average of V, and the optional
+  log-sum-exp is ``m + ln(d)`` in natural log.
+
+The full softmax over each request's gathered tokens is materialised; no
+tiling, splitting or reordering is done here (``oracle.merge`` holds the split
+form, which tests compare with this one).
+
+Test infrastructure: see the package docstring.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+
+from .storage import widen
+
+
+def request_length(indptr, last_page_len, page_size: int, r: int) -> int:
+    n = int(indptr[r + 1]) - int(indptr[r])
+    return (n - 1) * page_size + int(last_page_len[r])
+
+
+def token_locations(indptr, indices, last_page_len, page_size: int, r: int):
+    """(page id, slot) of every token of request r, in logical order."""
+    L = request_length(indptr, last_page_len, page_size, r)
+    t = np.arange(L, dtype=np.int64)
+    pages = np.asarray(indices[int(indptr[r]):int(indptr[r + 1])], dtype=np.int64)
+    return pages[t // page_size], t % page_size
+
+
+def gather_request(kv, indptr, indices, last_page_len, r: int, kv_head: int, kv_dtype: str,
+                   k_scale=None, v_scale=None):
+    """K and V of request r and one KV head as float64 ``[L_r, head_dim]`` each.
+
+    ``kv`` is the combined NHD pool ``[num_pages, 2, page_size, Hkv, D]`` in
+    raw storage; index 0 of axis 1 is K, 1 is V.
+    """
+    page_size = kv.shape[2]
+    page, slot = token_locations(indptr, indices, last_page_len, page_size, r)
+    K = widen(kv[page, 0, slot, kv_head, :], kv_dtype)
+    V = widen(kv[page, 1, slot, kv_head, :], kv_dtype)
+    if kv_dtype == "e4m3":
+        ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
+        vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
+        K = K * ks[page, kv_head][:, None]
+        V = V * vs[page, kv_head][:, None]
+    return K, V
+
+
+def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
+    """Softmax attention of one float64 query row over dense float64 K/V."""
+    s = sm_scale * (K @ qh)
+    m = s.max()
+    p = np.exp(s - m)
+    d = p.sum()
+    return (p @ V) / d, m + math.log(d)
+
+
+def decode(q, kv, indptr, indices, last_page_len, *, num_kv_heads: int, q_dtype: str,
+           kv_dtype: str, sm_scale: Optional[float] = None, k_scale=None, v_scale=None,
+           requests: Optional[Iterable[int]] = None):
+    """Decode attention for every (request, query head).
+
+    Returns ``out`` float64 ``[B, Hq, D]`` and ``lse`` float64 ``[B, Hq]``.
+    With ``requests`` given, only those rows are computed (the rest are NaN).
+    """
+    q64 = widen(q, q_dtype)
+    B, Hq, D = q64.shape
+    if Hq % num_kv_heads:
+        raise ValueError("num_qo_heads must be a multiple of num_kv_heads")
+    g = Hq // num_kv_heads
+    scale = (1.0 / math.sqrt(D)) if sm_scale is None else float(sm_scale)
+    out = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    rows = range(B) if requests is None else requests
+    for r in rows:
+        for kvh in range(num_kv_heads):
+            K, V = gather_request(kv, indptr, indices, last_page_len, r, kvh, kv_dtype,
+                                  k_scale, v_scale)
+            for h in range(kvh * g, (kvh + 1) * g):
+                out[r, h], lse[r, h] = attend(q64[r, h], K, V, scale)
+    return out, lse
+
+
+def decode_case(case: dict, requests=None, sm_scale=None):
+    """``decode`` on a dict produced by ``workloads.host_case``."""
+    w = case["workload"]
+    return decode(case["q"], case["kv"], case["indptr"], case["indices"], case["last_page_len"],
+                  num_kv_heads=w.num_kv_heads, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                  sm_scale=w.scale() if sm_scale is None else sm_scale,
+                  k_scale=case.get("k_scale"), v_scale=case.get("v_scale"), requests=requests)

@@ -1,0 +1,87 @@
+"""Partial softmax states (m, d, o) and the online-softmax merge rule.
+
+"FlashDecoding + FlashInfer — the decode-time attention story", §"FlashDecoding
+— the split-KV trick": each block of the split-KV launch produces a partial
+``(m, d, o)`` for its KV chunk, and two partials combine as
+
+    m = max(m_a, m_b)
+    d = d_a * exp(m_a - m) + d_b * exp(m_b - m)
+    o = o_a * exp(m_a - m) + o_b * exp(m_b - m)
+
+with the same recurrence used per tile inside the main kernel and per split in
+the reduction kernel.
+
+Readings taken (listed in the design doc):
+
+* ``o`` is the unnormalised sum ``sum_t exp(s_t - m) v_t``: the rule rescales
+  ``o`` by ``exp(m_a - m)`` alone, with no ``d`` weight, which is only right
+  for unnormalised sums. The final output is ``o / d``.
+* One token is the state ``(s_t, 1, v_t)``.
+* The empty state ``(-inf, 0, 0)`` is the identity; merging it must return
+  the other operand unchanged (the rule as printed would form
+  ``-inf - (-inf)`` when both are empty).
+
+Test infrastructure: see the package docstring.
+"""
+from __future__ import annotations
+
+import math
+from functools import reduce
+from typing import Iterable, Tuple
+
+import numpy as np
+
+State = Tuple[float, float, np.ndarray]
+
+
+def identity(head_dim: int) -> State:
+    return (-math.inf, 0.0, np.zeros(head_dim))
+
+
+def token_state(s_t: float, v_t: np.ndarray) -> State:
+    return (float(s_t), 1.0, np.asarray(v_t, dtype=np.float64).copy())
+
+
+def chunk_state(s: np.ndarray, V: np.ndarray) -> State:
+    """Partial state of a chunk of scores ``s`` [n] and values ``V`` [n, D]."""
+    if len(s) == 0:
+        return identity(V.shape[1])
+    m = float(np.max(s))
+    p = np.exp(s - m)
+    return (m, float(p.sum()), p @ V)
+
+
+def merge(a: State, b: State) -> State:
+    m_a, d_a, o_a = a
+    m_b, d_b, o_b = b
+    if m_a == -math.inf:
+        return (m_b, d_b, np.array(o_b, dtype=np.float64))
+    if m_b == -math.inf:
+        return (m_a, d_a, np.array(o_a, dtype=np.float64))
+    m = max(m_a, m_b)
+    wa = math.exp(m_a - m)
+    wb = math.exp(m_b - m)
+    return (m, d_a * wa + d_b * wb, o_a * wa + o_b * wb)
+
+
+def fold(states: Iterable[State], head_dim: int) -> State:
+    return reduce(merge, states, identity(head_dim))
+
+
+def finalize(state: State):
+    """Normalised output ``o / d`` and natural-log LSE ``m + ln d``."""
+    m, d, o = state
+    return o / d, m + math.log(d)
+
+
+def split_attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
+                 bounds: Iterable[Tuple[int, int]]):
+    """Attention of one query computed chunk by chunk and merged.
+
+    ``bounds`` lists ``[begin, end)`` token ranges that tile ``[0, L)``.
+    """
+    states = []
+    for b, e in bounds:
+        s = sm_scale * (K[b:e] @ qh)
+        states.append(chunk_state(s, V[b:e]))
+    return finalize(fold(states, K.shape[1]))

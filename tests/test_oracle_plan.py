@@ -1,0 +1,88 @@
+"""Pins for the oracle's partition rule: hand-worked cases and invariants."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import plan as oplan
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_hand_worked_partitions():
+    with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    for c in ex["cases"]:
+        p = oplan.plan(ex["indptr"], ex["last_page_len"], ex["page_size"], ex["num_kv_heads"],
+                       c["slots"], c["balance"], c["min_chunk_pages"])
+        assert p["chunk_pages"] == c["chunk_pages"], c["work"]
+        assert p["items"].tolist() == c["items"], c["work"]
+        assert p["merge_indptr"].tolist() == c["merge_indptr"], c["work"]
+
+
+def _random_table(rng, B, P, max_pages):
+    n = rng.integers(1, max_pages + 1, size=B)
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = rng.integers(1, P + 1, size=B).astype(np.int32)
+    return indptr, last
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_partition_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    P = int(rng.choice([1, 4, 16, 64]))
+    indptr, last = _random_table(rng, B, P, int(rng.integers(1, 300)))
+    hkv = int(rng.choice([1, 2, 8]))
+    slots = int(rng.integers(1, 2048))
+    balance = int(rng.integers(1, 5))
+    cmin = int(rng.integers(1, 40))
+    p = oplan.plan(indptr, last, P, hkv, slots, balance, cmin)
+    C = p["chunk_pages"]
+    n = np.diff(indptr)
+    L = (n - 1) * P + last
+    S, N = int(n.sum()), int(n.max())
+    # chunk length: the closed form, and its bounds
+    assert C == min(N, max(cmin, -(-(S * hkv) // (slots * balance))))
+    assert 1 <= C <= N
+    items = p["items"]
+    # coverage: per request, chunks tile its page range in order, tokens add up
+    for r in range(B):
+        mine = items[items[:, 0] == r]
+        mine = mine[np.argsort(mine[:, 1])]
+        assert mine[0, 1] == indptr[r] and mine[-1, 2] == indptr[r + 1]
+        assert np.all(mine[1:, 1] == mine[:-1, 2])
+        assert np.all(mine[:, 2] - mine[:, 1] <= C) and np.all(mine[:, 2] > mine[:, 1])
+        assert mine[:, 3].sum() == L[r]
+        G = len(mine)
+        assert G == -(-n[r] // C)
+        if G > 1:
+            assert mine[:, 4].tolist() == list(range(p["merge_indptr"][r], p["merge_indptr"][r] + G))
+        else:
+            assert mine[0, 4] == -1 and p["merge_indptr"][r + 1] == p["merge_indptr"][r]
+    # partial slots are a permutation of [0, num_partials)
+    slots_used = np.sort(items[items[:, 4] >= 0, 4])
+    assert np.array_equal(slots_used, np.arange(p["num_partials"]))
+    # longest first, ties by request
+    keys = list(zip(-items[:, 3], items[:, 0], items[:, 1]))
+    assert keys == sorted(keys)
+    assert p["split_requests"].tolist() == [r for r in range(B) if -(-n[r] // C) > 1]
+
+
+def test_uniform_batch_that_fills_the_device_is_not_split():
+    indptr = np.arange(0, 65 * 4, 4, dtype=np.int32)
+    last = np.full(64, 16, np.int32)
+    p = oplan.plan(indptr, last, 16, 8, slots=64, balance=1, min_chunk_pages=1)
+    assert p["chunk_pages"] == 4 and p["num_partials"] == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(indptr=[0, 0], last=[1]),      # empty request
+    dict(indptr=[0, 2], last=[0]),      # last_page_len below 1
+    dict(indptr=[0, 2], last=[17]),     # above page_size
+    dict(indptr=[1, 2], last=[1]),      # indptr[0] != 0
+])
+def test_invalid_tables_rejected(bad):
+    with pytest.raises(ValueError):
+        oplan.plan(bad["indptr"], bad["last"], 16, 1, 8, 1, 1)

@@ -1,0 +1,132 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each test plants one mistake in a copy of an oracle function (on the CPU, via
+monkeypatch) and checks that an independent pin then fails.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import attention, e4m3, merge, storage
+from workloads import custom_workload, host_case
+
+from test_oracle_attention import brute_force
+
+
+def _case():
+    w = custom_workload(3, 4, 2, 8, 4, "f32", "f32", [9, 16, 3], pool_pages=12)
+    return host_case(w, 7, poison=True), w
+
+
+def _matches_brute(case, w):
+    out, lse = attention.decode_case(case)
+    bo, bl = brute_force(case, w.scale())
+    return (np.all(np.isfinite(out)) and np.allclose(out, bo, rtol=1e-12, atol=1e-12)
+            and np.allclose(lse, bl, rtol=1e-12, atol=1e-12))
+
+
+def test_unmodified_oracle_passes():
+    case, w = _case()
+    assert _matches_brute(case, w)
+
+
+def test_wrong_gqa_mapping_is_caught(monkeypatch):
+    case, w = _case()
+    real = attention.gather_request
+
+    def wrong(kv, indptr, indices, last, r, kv_head, *a, **k):
+        return real(kv, indptr, indices, last, r, (kv_head + 1) % kv.shape[3], *a, **k)
+
+    monkeypatch.setattr(attention, "gather_request", wrong)
+    assert not _matches_brute(case, w)
+
+
+def test_wrong_slot_index_is_caught(monkeypatch):
+    case, w = _case()
+
+    def wrong(indptr, indices, last, P, r):
+        L = attention.request_length(indptr, last, P, r)
+        t = np.arange(L)
+        pages = np.asarray(indices[indptr[r]:indptr[r + 1]], dtype=np.int64)
+        return pages[t // P], (t + 1) % P
+
+    monkeypatch.setattr(attention, "token_locations", wrong)
+    assert not _matches_brute(case, w)
+
+
+def test_untruncated_last_page_is_caught(monkeypatch):
+    case, w = _case()
+    monkeypatch.setattr(attention, "request_length",
+                        lambda indptr, last, P, r: (int(indptr[r + 1]) - int(indptr[r])) * P)
+    with np.errstate(invalid="ignore"):
+        assert not _matches_brute(case, w)
+
+
+def test_missing_scale_is_caught(monkeypatch):
+    case, w = _case()
+    real = attention.attend
+    monkeypatch.setattr(attention, "attend", lambda qh, K, V, s: real(qh, K, V, 1.0))
+    assert not _matches_brute(case, w)
+
+
+def test_transposed_kv_halves_are_caught(monkeypatch):
+    case, w = _case()
+    real = attention.gather_request
+
+    def swapped(*a, **k):
+        K, V = real(*a, **k)
+        return V, K
+
+    monkeypatch.setattr(attention, "gather_request", swapped)
+    assert not _matches_brute(case, w)
+
+
+def test_normalised_o_in_merge_is_caught(monkeypatch):
+    """Weighting o by d as well (as if o were normalised) breaks split == unsplit."""
+    def wrong(a, b):
+        m_a, d_a, o_a = a
+        m_b, d_b, o_b = b
+        if m_a == -math.inf:
+            return b
+        if m_b == -math.inf:
+            return a
+        m = max(m_a, m_b)
+        wa, wb = d_a * math.exp(m_a - m), d_b * math.exp(m_b - m)
+        return (m, wa + wb, o_a * wa + o_b * wb)
+
+    monkeypatch.setattr(merge, "merge", wrong)
+    rng = np.random.default_rng(0)
+    s, V = rng.standard_normal(20), rng.standard_normal((20, 4))
+    o, _ = merge.finalize(merge.fold([merge.chunk_state(s[:9], V[:9]),
+                                      merge.chunk_state(s[9:], V[9:])], 4))
+    wts = np.exp(s - s.max())
+    assert not np.allclose(o, (wts @ V) / wts.sum(), rtol=1e-9)
+
+
+def test_wrong_e4m3_bias_is_caught(monkeypatch):
+    monkeypatch.setattr(e4m3, "BIAS", 8)
+    assert e4m3.value(0x38) != 1.0 and e4m3.value(0x7E) != 448.0
+
+
+def test_wrong_bf16_shift_is_caught():
+    bits = np.array([0x3F80], np.uint16)
+    wrong = (bits.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    assert wrong[0] != storage.widen(bits, "bf16")[0] == 1.0
+
+
+@pytest.mark.parametrize("mutant", ["off_by_one_kvlen", "no_last_page_trim"])
+def test_plan_mutants_are_caught(mutant, monkeypatch):
+    from oracle import plan as oplan
+    import json, os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    c = ex["cases"][1]
+    p = oplan.plan(ex["indptr"], ex["last_page_len"], ex["page_size"], 1, c["slots"],
+                   c["balance"], c["min_chunk_pages"])
+    items = p["items"].copy()
+    if mutant == "off_by_one_kvlen":
+        items[:, 3] -= 1
+    else:
+        items[items[:, 0] == 1, 3] = (items[items[:, 0] == 1, 2] - items[items[:, 0] == 1, 1]) * 16
+    assert items.tolist() != c["items"]

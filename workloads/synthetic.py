@@ -1,0 +1,269 @@
+"""Seeded synthetic decode workloads: page tables, paged KV pools and queries.
+
+Storage conventions (shared by every consumer, so each side decodes the raw
+bytes itself):
+
+* ``kv`` is the combined NHD page pool ``[num_pages, 2, page_size,
+  num_kv_heads, head_dim]``; index 0 of the second axis holds K, index 1 holds V.
+* ``"f32"`` storage is ``float32``; ``"bf16"`` storage is the raw 16-bit
+  pattern as ``uint16``; ``"e4m3"`` storage is the raw OCP E4M3FN byte as
+  ``uint8`` with fp32 scales ``k_scale``/``v_scale`` of shape
+  ``[num_pages, num_kv_heads]`` (one per page and KV head).
+* ``q`` is ``[batch, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
+  storage.
+* The page table is ``indptr`` (int32 ``[batch+1]``), ``indices`` (int32 page
+  ids) and ``last_page_len`` (int32 ``[batch]``), as in the paged-KV wrapper
+  of "FlashDecoding + FlashInfer — the decode-time attention story", §"The API
+  you actually use (Python)" and §"Paged attention (vLLM)".
+
+Slots that no request reads (the tail of each last page, and pool pages that
+no request references) can be poisoned with NaN (0x7F for e4m3) so that a
+kernel reading past a request's end cannot go unnoticed.
+
+The module draws random numbers and converts them to storage formats; it does
+no attention arithmetic.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+KV_DTYPES = ("f32", "bf16", "e4m3")
+Q_DTYPES = ("f32", "bf16")
+E4M3_MAX = 448.0
+BF16_NAN_BITS = 0x7FC0
+E4M3_NAN_BYTE = 0x7F
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """Shape and distribution of one synthetic decode batch.
+
+    ``context`` is one of ``("fixed", L)``, ``("loguniform", lo, hi)``,
+    ``("uniform", lo, hi)`` (inclusive) or ``("list", (L0, L1, ...))``.
+    ``pool_pages`` is the size of the page pool; ``None`` means exactly the
+    pages the batch uses. Page ids are a random permutation of the pool.
+    """
+
+    name: str
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    kv_dtype: str
+    q_dtype: str
+    context: tuple
+    pool_pages: Optional[int] = None
+    sm_scale: Optional[float] = None
+
+    @property
+    def group(self) -> int:
+        return self.num_qo_heads // self.num_kv_heads
+
+    def scale(self) -> float:
+        return self.sm_scale if self.sm_scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+
+CONFIGS = {
+    # Single sequence: 32 used pages scattered in a 64-page pool, fp32.
+    "single_seq_fp32": Workload(
+        "single_seq_fp32", 1, 4, 4, 64, 16, "f32", "f32", ("fixed", 512), pool_pages=64),
+    # Llama-3-8B-shaped decode: GQA 4, every context 2048, bf16.
+    "llama3_8b_bf16": Workload(
+        "llama3_8b_bf16", 64, 32, 8, 128, 16, "bf16", "bf16", ("fixed", 2048)),
+    # Heterogeneous ragged batch, contexts log-uniform in [256, 65536].
+    "ragged_loguniform_bf16": Workload(
+        "ragged_loguniform_bf16", 256, 32, 8, 128, 16, "bf16", "bf16",
+        ("loguniform", 256, 65536)),
+    # Long context, small batch, GQA 8, 64-token pages.
+    "long_ctx_gqa8_bf16": Workload(
+        "long_ctx_gqa8_bf16", 2, 64, 8, 128, 64, "bf16", "bf16", ("fixed", 131072)),
+    # fp8 (E4M3) KV with one fp32 scale per (page, KV head); q bf16.
+    "fp8_kv_e4m3": Workload(
+        "fp8_kv_e4m3", 128, 32, 8, 128, 16, "e4m3", "bf16", ("uniform", 1024, 32768)),
+}
+CONFIG_ORDER = list(CONFIGS)
+
+
+def custom_workload(batch, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype,
+                    q_dtype, lens: Sequence[int], pool_pages=None, sm_scale=None,
+                    name="custom") -> Workload:
+    return Workload(name, batch, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype,
+                    q_dtype, ("list", tuple(int(x) for x in lens)), pool_pages, sm_scale)
+
+
+def _context_lengths(w: Workload, rng: np.random.Generator) -> np.ndarray:
+    kind = w.context[0]
+    if kind == "fixed":
+        return np.full(w.batch, int(w.context[1]), dtype=np.int64)
+    if kind == "loguniform":
+        lo, hi = w.context[1], w.context[2]
+        x = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=w.batch)))
+        return np.clip(x, lo, hi).astype(np.int64)
+    if kind == "uniform":
+        return rng.integers(w.context[1], w.context[2], size=w.batch, endpoint=True).astype(np.int64)
+    if kind == "list":
+        lens = np.asarray(w.context[1], dtype=np.int64)
+        assert lens.shape == (w.batch,)
+        return lens
+    raise ValueError(f"unknown context kind {kind!r}")
+
+
+def page_table(w: Workload, seed: int) -> dict:
+    """Draw context lengths and a shuffled page table for ``w``."""
+    rng = np.random.default_rng(seed)
+    lens = _context_lengths(w, rng)
+    if np.any(lens < 1):
+        raise ValueError("every request needs at least one token")
+    P = w.page_size
+    n = (lens + P - 1) // P
+    last = ((lens - 1) % P) + 1
+    used = int(n.sum())
+    pool = max(int(w.pool_pages or used), used)
+    indices = rng.permutation(pool)[:used].astype(np.int32)
+    indptr = np.zeros(w.batch + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(n)
+    return {
+        "indptr": indptr,
+        "indices": indices,
+        "last_page_len": last.astype(np.int32),
+        "kv_lens": lens.astype(np.int64),
+        "num_pages": pool,
+    }
+
+
+def explicit_table(page_lists: Sequence[Sequence[int]], last_page_len: Sequence[int],
+                   page_size: int, num_pages: int) -> dict:
+    """A page table written out by hand (ids may repeat across requests)."""
+    n = np.array([len(p) for p in page_lists], dtype=np.int64)
+    indptr = np.zeros(len(page_lists) + 1, dtype=np.int32)
+    indptr[1:] = np.cumsum(n)
+    indices = np.concatenate([np.asarray(p, dtype=np.int32) for p in page_lists])
+    last = np.asarray(last_page_len, dtype=np.int32)
+    lens = (n - 1) * page_size + last
+    return {"indptr": indptr, "indices": indices, "last_page_len": last,
+            "kv_lens": lens.astype(np.int64), "num_pages": int(num_pages)}
+
+
+def read_mask(table: dict, page_size: int) -> np.ndarray:
+    """Boolean ``[num_pages, page_size]``: True where some request reads the slot."""
+    mask = np.zeros((table["num_pages"], page_size), dtype=bool)
+    indptr, indices, last = table["indptr"], table["indices"], table["last_page_len"]
+    for r in range(len(last)):
+        pages = indices[indptr[r]:indptr[r + 1]]
+        if len(pages) == 0:
+            continue
+        mask[pages[:-1], :] = True
+        mask[pages[-1], : int(last[r])] = True
+    return mask
+
+
+# ---------------------------------------------------------------- host (numpy)
+
+def _to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _to_e4m3_bytes(x: np.ndarray) -> np.ndarray:
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(np.clip(x, -E4M3_MAX, E4M3_MAX), dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _quantize_pool_e4m3(pool32: np.ndarray):
+    """Per (page, K/V, KV head) block: scale = amax / 448, bytes = RNE(x / scale)."""
+    amax = np.abs(pool32).max(axis=(2, 4))  # [pages, 2, Hkv]
+    scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+    y = pool32 / scale[:, :, None, :, None]
+    return _to_e4m3_bytes(y), scale[:, 0, :].copy(), scale[:, 1, :].copy()
+
+
+def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict] = None) -> dict:
+    """Small-case inputs as numpy storage arrays (see module docstring)."""
+    if table is None:
+        table = page_table(w, seed)
+    rng = np.random.default_rng([seed, 1])
+    P, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
+    q32 = rng.standard_normal((w.batch, w.num_qo_heads, D), dtype=np.float32)
+    pool32 = rng.standard_normal((table["num_pages"], 2, P, Hkv, D), dtype=np.float32)
+    k_scale = v_scale = None
+    if w.kv_dtype == "f32":
+        kv = pool32
+    elif w.kv_dtype == "bf16":
+        kv = _to_bf16_bits(pool32)
+    elif w.kv_dtype == "e4m3":
+        kv, k_scale, v_scale = _quantize_pool_e4m3(pool32)
+    else:
+        raise ValueError(w.kv_dtype)
+    q = q32 if w.q_dtype == "f32" else _to_bf16_bits(q32)
+    if poison:
+        unread = ~read_mask(table, P)
+        nan = {"f32": np.float32(np.nan), "bf16": np.uint16(BF16_NAN_BITS),
+               "e4m3": np.uint8(E4M3_NAN_BYTE)}[w.kv_dtype]
+        kv = kv.copy()
+        kv[:, 0][unread] = nan
+        kv[:, 1][unread] = nan
+    out = dict(table)
+    out.update({"q": q, "kv": kv, "k_scale": k_scale, "v_scale": v_scale, "workload": w})
+    return out
+
+
+# ---------------------------------------------------------------- device (torch)
+
+def device_case(w: Workload, seed: int, device, poison: bool = False,
+                table: Optional[dict] = None, chunk_pages: int = 8192) -> dict:
+    """Full-size inputs drawn directly in device memory with a seeded torch generator.
+
+    Returns torch tensors: ``q`` (float32 or bfloat16), ``kv`` (float32,
+    bfloat16 or uint8 bytes for e4m3), ``k_scale``/``v_scale`` (float32, e4m3
+    only), and the numpy page table.
+    """
+    import torch
+
+    if table is None:
+        table = page_table(w, seed)
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 7919 + 17)
+    P, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
+    npg = table["num_pages"]
+    qdt = torch.float32 if w.q_dtype == "f32" else torch.bfloat16
+    q = torch.randn((w.batch, w.num_qo_heads, D), generator=g, device=device,
+                    dtype=torch.float32).to(qdt)
+    k_scale = v_scale = None
+    if w.kv_dtype in ("f32", "bf16"):
+        kdt = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
+        kv = torch.randn((npg, 2, P, Hkv, D), generator=g, device=device, dtype=kdt)
+    elif w.kv_dtype == "e4m3":
+        kv = torch.empty((npg, 2, P, Hkv, D), device=device, dtype=torch.uint8)
+        scale = torch.empty((npg, 2, Hkv), device=device, dtype=torch.float32)
+        for p0 in range(0, npg, chunk_pages):
+            p1 = min(npg, p0 + chunk_pages)
+            x = torch.randn((p1 - p0, 2, P, Hkv, D), generator=g, device=device,
+                            dtype=torch.float32)
+            amax = x.abs().amax(dim=(2, 4))
+            s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+            y = (x / s[:, :, None, :, None]).clamp_(-E4M3_MAX, E4M3_MAX)
+            kv[p0:p1] = y.to(torch.float8_e4m3fn).view(torch.uint8)
+            scale[p0:p1] = s
+            del x, y
+        k_scale = scale[:, 0, :].contiguous()
+        v_scale = scale[:, 1, :].contiguous()
+    else:
+        raise ValueError(w.kv_dtype)
+    if poison:
+        unread = torch.from_numpy(~read_mask(table, P)).to(device)
+        if w.kv_dtype == "e4m3":
+            fill = E4M3_NAN_BYTE
+        else:
+            fill = float("nan")
+        kvv = kv.permute(0, 2, 1, 3, 4)  # [pages, P, 2, Hkv, D] view
+        kvv[unread] = fill
+    out = dict(table)
+    out.update({"q": q, "kv": kv, "k_scale": k_scale, "v_scale": v_scale, "workload": w})
+    return out
