@@ -1,0 +1,202 @@
+/*
+ * pkdecode — batched decode attention over a paged, ragged KV cache on AMD
+ * MI355X (gfx950). C ABI.
+ *
+ * The operation is the paged-KV batch decode of "FlashDecoding + FlashInfer —
+ * the decode-time attention story": one query token per request attends over
+ * that request's KV tokens, which live in fixed-size pages named by a page
+ * table (indptr / indices / last_page_len, §"Paged attention (vLLM) — the
+ * KV-cache layout FlashInfer targets"). Work is split along the KV axis into
+ * partial (m, d, o) softmax states that a second kernel merges with the
+ * online-softmax rule (§"FlashDecoding — the split-KV trick"), and a host-side
+ * plan balances the split so that long requests do not stall short ones
+ * (§"What FlashInfer is", item 3). As in the wrapper of §"The API you actually
+ * use (Python)", plan() is done once per batch shape on the host and run() is
+ * the per-layer hot path.
+ *
+ * Conventions
+ *   - Every function returns PKD_OK (0) or a negative PKD_ERR_* code; the
+ *     message of the calling thread's last failure is pkd_last_error().
+ *     Nothing aborts the process and no C++ exception crosses this boundary.
+ *   - "host" pointers are CPU memory; "device" pointers are HIP device memory
+ *     on the plan's device. The caller owns every buffer passed in; the
+ *     library allocates only the plan handle (host) and a small pinned staging
+ *     copy of the work list.
+ *   - Streams are hipStream_t passed as void*; NULL is the default stream.
+ */
+#ifndef PKDECODE_H
+#define PKDECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define PKD_OK 0
+#define PKD_ERR_INVALID_ARGUMENT (-1)   /* malformed page table, null pointer, bad stride */
+#define PKD_ERR_UNSUPPORTED (-2)        /* head_dim / group / page_size / dtype not built */
+#define PKD_ERR_WORKSPACE_TOO_SMALL (-3)
+#define PKD_ERR_PLAN_MISMATCH (-4)      /* run() arguments disagree with the plan */
+#define PKD_ERR_HIP (-5)                /* a HIP runtime call failed */
+
+/* ---- element types ----------------------------------------------------- */
+#define PKD_DTYPE_F32 0   /* IEEE binary32 */
+#define PKD_DTYPE_BF16 1  /* bfloat16 */
+#define PKD_DTYPE_E4M3 2  /* OCP FP8 E4M3FN byte, with fp32 per-(page, KV head) scales */
+
+/* Columns of one work item as returned by pkd_plan_get_worklist. */
+#define PKD_ITEM_COLS 5   /* request, page_begin, page_end, kv_len, partial_slot */
+
+typedef struct pkd_plan pkd_plan;
+
+/* Arguments of pkd_plan_create.
+ *
+ *  batch            number of requests B (>= 1)
+ *  indptr           host int32[B+1]: request r owns page-table entries
+ *                   [indptr[r], indptr[r+1]); indptr[0] == 0, each request
+ *                   has at least one page
+ *  last_page_len    host int32[B]: tokens in request r's last page, in
+ *                   [1, page_size]; request r holds
+ *                   (n_r - 1) * page_size + last_page_len[r] tokens
+ *  num_qo_heads     query heads Hq; num_kv_heads divides it and query head h
+ *                   reads KV head h / (Hq / Hkv)
+ *  head_dim         64 or 128
+ *  page_size        tokens per page, a power of two in [1, 1024]
+ *  q_dtype          PKD_DTYPE_F32 or PKD_DTYPE_BF16
+ *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_E4M3
+ *  out_dtype        PKD_DTYPE_F32 or PKD_DTYPE_BF16 (bf16 rounds to nearest even)
+ *  sm_scale         logit scale; 0 selects 1/sqrt(head_dim)
+ *  slots            workgroups the device keeps resident at once; 0 queries
+ *                   the device (compute units x resident workgroups per CU
+ *                   for the selected kernel)
+ *  balance          each work unit holds at most 1/balance of a slot's fair
+ *                   share of the batch; 0 selects the default (2)
+ *  min_chunk_pages  shortest chunk a request is split into; 0 selects
+ *                   ceil(256 / page_size)
+ *  device           HIP device ordinal used when slots == 0
+ */
+typedef struct {
+  int32_t batch;
+  const int32_t* indptr;
+  const int32_t* last_page_len;
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t q_dtype;
+  int32_t kv_dtype;
+  int32_t out_dtype;
+  float sm_scale;
+  int32_t slots;
+  int32_t balance;
+  int32_t min_chunk_pages;
+  int32_t device;
+} pkd_plan_args;
+
+/* What a plan decided (pkd_plan_get_info). */
+typedef struct {
+  int32_t batch;
+  int32_t chunk_pages;         /* C: pages per work item (the last chunk may be shorter) */
+  int32_t num_items;           /* work items; the decode grid is num_items x num_kv_heads */
+  int32_t num_partials;        /* partial-state slots (items of split requests) */
+  int32_t num_split_requests;  /* requests with more than one item */
+  int32_t slots;               /* values actually used by the rule */
+  int32_t balance;
+  int32_t min_chunk_pages;
+  int64_t total_kv_tokens;     /* sum over requests of their token counts */
+  size_t workspace_bytes;      /* device workspace run() needs */
+} pkd_plan_info;
+
+/* Arguments of pkd_run. All pointers are device pointers.
+ *
+ *  q            [B, Hq, head_dim] contiguous, q_dtype
+ *  k, v         element (page 0, slot 0, KV head 0, dim 0) of the K and V
+ *               pools; element (page, slot, h, d) of K is at
+ *               k[page*page_stride + slot*token_stride + h*head_stride + d]
+ *               (same for v). The combined NHD pool
+ *               [num_pages, 2, page_size, Hkv, head_dim] is
+ *               k = base, v = base + page_size*Hkv*head_dim,
+ *               page_stride = 2*page_size*Hkv*head_dim,
+ *               token_stride = Hkv*head_dim, head_stride = head_dim.
+ *               Strides are in elements; k, v and every stride must be
+ *               16-byte aligned for f32/bf16 and 8-byte aligned for e4m3.
+ *  indices      int32 page ids of the page table (length indptr[B]); ids may
+ *               repeat across requests (shared prefixes) and are not range
+ *               checked
+ *  k_scale,     float [num_pages, Hkv] contiguous; required for e4m3 KV,
+ *  v_scale      ignored otherwise. Stored K (V) bytes are multiplied by the
+ *               scale of their (page, KV head).
+ *  out          [B, Hq, head_dim] contiguous, out_dtype
+ *  lse          float [B, Hq] or NULL: natural-log log-sum-exp of the scaled
+ *               logits of each (request, query head)
+ *  workspace    the buffer the plan was uploaded to, at least
+ *               info.workspace_bytes long
+ *  stream       hipStream_t; run() only enqueues work and returns
+ */
+typedef struct {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  const int32_t* indices;
+  const float* k_scale;
+  const float* v_scale;
+  void* out;
+  float* lse;
+  void* workspace;
+  size_t workspace_bytes;
+  void* stream;
+} pkd_run_args;
+
+/* Message describing the calling thread's most recent failure ("" if none). */
+const char* pkd_last_error(void);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int pkd_version(void);
+
+/* Validate the page table and build the work partition on the host.
+ * Rejects empty requests, last_page_len outside [1, page_size], a
+ * non-monotone indptr, Hq not a multiple of Hkv (INVALID_ARGUMENT) and
+ * head_dim / group / page_size / dtype combinations with no kernel
+ * (UNSUPPORTED). On success *out owns a new handle. No device work. */
+int pkd_plan_create(const pkd_plan_args* args, pkd_plan** out);
+
+/* Copy out what the plan decided. */
+int pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
+
+/* Copy the work list to host memory: items_out int32[num_items * 5] rows of
+ * (request, page_begin, page_end, kv_len, partial_slot) in launch order
+ * (partial_slot is -1 for a request that is not split); merge_indptr_out
+ * int32[B+1], where the split request r owns partial slots
+ * [merge_indptr[r], merge_indptr[r+1]); split_requests_out (nullable)
+ * int32[num_split_requests], the split requests in ascending order. */
+int pkd_plan_get_worklist(const pkd_plan* plan, int32_t* items_out, int32_t* merge_indptr_out,
+                          int32_t* split_requests_out);
+
+/* Enqueue the copy of the work list into the head of `workspace` on
+ * `stream` (asynchronous; the plan keeps its pinned staging copy alive
+ * until the copy has finished). run() must then be given the same workspace. */
+int pkd_plan_upload(pkd_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Enqueue the decode kernel and, when any request is split, the merge
+ * kernel on args->stream. Allocates nothing and does not synchronise. */
+int pkd_run(const pkd_plan* plan, const pkd_run_args* args);
+
+/* Free the handle (waits for an in-flight upload first). NULL is a no-op. */
+void pkd_plan_destroy(pkd_plan* plan);
+
+/* Workgroups of the decode kernel for (kv_dtype, head_dim, group) that one
+ * compute unit holds at once, and the device's compute-unit count. */
+int pkd_device_slots(int32_t device, int32_t kv_dtype, int32_t head_dim, int32_t group,
+                     int32_t* wgs_per_cu, int32_t* num_cus);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKDECODE_H */

@@ -1,0 +1,22 @@
+"""pkdecode: batched decode attention over a paged, ragged KV cache on MI355X.
+
+The computation runs in libpkdecode.so (hand-written HIP kernels for gfx950
+behind a C ABI, ``include/pkdecode.h``); this package is its Python binding.
+"""
+from ._lib import LIB_PATH, PkdError, load  # noqa: F401
+from .wrapper import (  # noqa: F401
+    DEFAULT_WORKSPACE_BYTES,
+    BatchDecodeWithPagedKVCacheWrapper,
+    Plan,
+    plan_partition,
+)
+
+__all__ = [
+    "BatchDecodeWithPagedKVCacheWrapper",
+    "Plan",
+    "PkdError",
+    "plan_partition",
+    "load",
+    "LIB_PATH",
+    "DEFAULT_WORKSPACE_BYTES",
+]

@@ -1,0 +1,322 @@
+// C-ABI surface of libpkdecode (declared in include/pkdecode.h).
+//
+// plan(): validate the page table, build the work partition on the host and
+// lay out the device workspace; upload(): one asynchronous host-to-device copy
+// of the work list; run(): the decode kernel and, when requests were split,
+// the merge kernel. This mirrors the plan-once / run-per-layer wrapper of
+// "FlashDecoding + FlashInfer — the decode-time attention story", §"The API
+// you actually use (Python)".
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/pkdecode.h"
+#include "launch.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() { return PKD_OK; }
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int elem_bytes(int dtype) { return dtype == PKD_DTYPE_F32 ? 4 : dtype == PKD_DTYPE_BF16 ? 2 : 1; }
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int x) {
+  int r = 0;
+  while ((1 << r) < x) ++r;
+  return r;
+}
+
+}  // namespace
+
+struct pkd_plan {
+  pkd_plan_args args{};
+  float sm_scale = 0.f;
+  pkd::Partition part;
+  pkd_plan_info info{};
+  // Device workspace layout (byte offsets).
+  size_t off_items = 0, off_split = 0, off_merge = 0, header_bytes = 0;
+  size_t off_part_md = 0, off_part_o = 0;
+  std::vector<unsigned char> header;  // host image of [items | split | merge_indptr]
+  void* pinned = nullptr;
+  hipEvent_t upload_done = nullptr;
+  bool upload_pending = false;
+  const void* uploaded_to = nullptr;
+  int device = 0;
+};
+
+extern "C" {
+
+const char* pkd_last_error(void) { return g_last_error.c_str(); }
+
+int pkd_version(void) { return 100; }
+
+int pkd_device_slots(int32_t device, int32_t kv_dtype, int32_t head_dim, int32_t group,
+                     int32_t* wgs_per_cu, int32_t* num_cus) {
+  if (!wgs_per_cu || !num_cus) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
+  if (!pkd::decode_supported(kv_dtype, head_dim, group))
+    return fail(PKD_ERR_UNSUPPORTED, "no kernel for kv_dtype=%d head_dim=%d group=%d", kv_dtype,
+                head_dim, group);
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (prev != device && (e = hipSetDevice(device)) != hipSuccess)
+    return fail(PKD_ERR_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(e));
+  int cus = 0, wgs = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
+  if (e == hipSuccess) e = pkd::decode_occupancy(kv_dtype, head_dim, group, &wgs);
+  if (prev != device) hipSetDevice(prev);
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
+  *wgs_per_cu = wgs;
+  *num_cus = cus;
+  return ok();
+}
+
+int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
+  if (!a || !out) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
+  *out = nullptr;
+  if (a->batch < 1) return fail(PKD_ERR_INVALID_ARGUMENT, "batch must be at least 1");
+  if (!a->indptr || !a->last_page_len)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "indptr and last_page_len must not be NULL");
+  if (a->num_qo_heads < 1 || a->num_kv_heads < 1 || a->num_qo_heads % a->num_kv_heads)
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                a->num_qo_heads, a->num_kv_heads);
+  const int group = a->num_qo_heads / a->num_kv_heads;
+  if (a->q_dtype != PKD_DTYPE_F32 && a->q_dtype != PKD_DTYPE_BF16)
+    return fail(PKD_ERR_UNSUPPORTED, "q_dtype %d not supported", a->q_dtype);
+  if (a->out_dtype != PKD_DTYPE_F32 && a->out_dtype != PKD_DTYPE_BF16)
+    return fail(PKD_ERR_UNSUPPORTED, "out_dtype %d not supported", a->out_dtype);
+  if (a->kv_dtype != PKD_DTYPE_F32 && a->kv_dtype != PKD_DTYPE_BF16 &&
+      a->kv_dtype != PKD_DTYPE_E4M3)
+    return fail(PKD_ERR_UNSUPPORTED, "kv_dtype %d not supported", a->kv_dtype);
+  if (!is_pow2(a->page_size) || a->page_size > 1024)
+    return fail(PKD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]",
+                a->page_size);
+  if (!pkd::decode_supported(a->kv_dtype, a->head_dim, group))
+    return fail(PKD_ERR_UNSUPPORTED, "no kernel for head_dim=%d group=%d kv_dtype=%d",
+                a->head_dim, group, a->kv_dtype);
+  if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "slots, balance and min_chunk_pages must be >= 0");
+  if (!(a->sm_scale >= 0.f) || std::isinf(a->sm_scale))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "sm_scale must be finite and >= 0");
+
+  int slots = a->slots;
+  if (slots == 0) {
+    int32_t wgs = 0, cus = 0;
+    int rc = pkd_device_slots(a->device, a->kv_dtype, a->head_dim, group, &wgs, &cus);
+    if (rc != PKD_OK) return rc;
+    slots = wgs * cus;
+    if (slots < 1) return fail(PKD_ERR_HIP, "device reports no resident workgroups");
+  }
+  pkd::PartitionInput pin;
+  pin.batch = a->batch;
+  pin.indptr = a->indptr;
+  pin.last_page_len = a->last_page_len;
+  pin.page_size = a->page_size;
+  pin.units_per_item = a->num_kv_heads;
+  pin.slots = slots;
+  pin.balance = a->balance ? a->balance : 2;
+  pin.min_chunk_pages = a->min_chunk_pages ? a->min_chunk_pages : (256 + a->page_size - 1) / a->page_size;
+
+  pkd_plan* p = new (std::nothrow) pkd_plan();
+  if (!p) return fail(PKD_ERR_INVALID_ARGUMENT, "out of host memory");
+  std::string err = pkd::build_partition(pin, &p->part);
+  if (!err.empty()) {
+    delete p;
+    return fail(PKD_ERR_INVALID_ARGUMENT, "%s", err.c_str());
+  }
+  p->args = *a;
+  p->args.indptr = nullptr;
+  p->args.last_page_len = nullptr;
+  p->device = a->device;
+  p->sm_scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(float(a->head_dim));
+
+  const auto& part = p->part;
+  const size_t n_items = part.items.size();
+  const size_t n_split = part.split_requests.size();
+  p->off_items = 0;
+  p->off_split = align256(n_items * sizeof(pkd::DeviceItem));
+  p->off_merge = align256(p->off_split + n_split * sizeof(int32_t));
+  p->header_bytes = align256(p->off_merge + (size_t(a->batch) + 1) * sizeof(int32_t));
+  p->off_part_md = p->header_bytes;
+  const size_t rows = size_t(part.num_partials) * size_t(a->num_qo_heads);
+  p->off_part_o = align256(p->off_part_md + rows * 2 * sizeof(float));
+  const size_t ws = align256(p->off_part_o + rows * size_t(a->head_dim) * sizeof(float));
+
+  p->header.assign(p->header_bytes, 0);
+  auto* di = reinterpret_cast<pkd::DeviceItem*>(p->header.data() + p->off_items);
+  for (size_t i = 0; i < n_items; ++i) {
+    const auto& w = part.items[i];
+    di[i] = {w.request, w.page_begin, w.kv_len, w.partial_slot};
+  }
+  if (n_split)
+    std::memcpy(p->header.data() + p->off_split, part.split_requests.data(), n_split * 4);
+  std::memcpy(p->header.data() + p->off_merge, part.merge_indptr.data(),
+              (size_t(a->batch) + 1) * 4);
+
+  pkd_plan_info& inf = p->info;
+  inf.batch = a->batch;
+  inf.chunk_pages = part.chunk_pages;
+  inf.num_items = int32_t(n_items);
+  inf.num_partials = part.num_partials;
+  inf.num_split_requests = int32_t(n_split);
+  inf.slots = pin.slots;
+  inf.balance = pin.balance;
+  inf.min_chunk_pages = pin.min_chunk_pages;
+  inf.total_kv_tokens = part.total_tokens;
+  inf.workspace_bytes = ws;
+  *out = p;
+  return ok();
+}
+
+int pkd_plan_get_info(const pkd_plan* p, pkd_plan_info* info) {
+  if (!p || !info) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
+  *info = p->info;
+  return ok();
+}
+
+int pkd_plan_get_worklist(const pkd_plan* p, int32_t* items_out, int32_t* merge_indptr_out,
+                          int32_t* split_requests_out) {
+  if (!p) return fail(PKD_ERR_INVALID_ARGUMENT, "null plan");
+  if (items_out) {
+    for (size_t i = 0; i < p->part.items.size(); ++i) {
+      const auto& w = p->part.items[i];
+      int32_t* row = items_out + i * PKD_ITEM_COLS;
+      row[0] = w.request;
+      row[1] = w.page_begin;
+      row[2] = w.page_end;
+      row[3] = w.kv_len;
+      row[4] = w.partial_slot;
+    }
+  }
+  if (merge_indptr_out)
+    std::memcpy(merge_indptr_out, p->part.merge_indptr.data(), p->part.merge_indptr.size() * 4);
+  if (split_requests_out && !p->part.split_requests.empty())
+    std::memcpy(split_requests_out, p->part.split_requests.data(),
+                p->part.split_requests.size() * 4);
+  return ok();
+}
+
+int pkd_plan_upload(pkd_plan* p, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!p || !workspace) return fail(PKD_ERR_INVALID_ARGUMENT, "null plan or workspace");
+  if (workspace_bytes < p->info.workspace_bytes)
+    return fail(PKD_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the plan needs %zu",
+                workspace_bytes, p->info.workspace_bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  hipError_t e;
+  if (!p->pinned) {
+    if ((e = hipHostMalloc(&p->pinned, p->header_bytes, hipHostMallocDefault)) != hipSuccess) {
+      p->pinned = nullptr;
+      return fail(PKD_ERR_HIP, "hipHostMalloc(%zu): %s", p->header_bytes, hipGetErrorString(e));
+    }
+    if ((e = hipEventCreateWithFlags(&p->upload_done, hipEventDisableTiming)) != hipSuccess) {
+      p->upload_done = nullptr;
+      return fail(PKD_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+  } else if (p->upload_pending) {
+    if ((e = hipEventSynchronize(p->upload_done)) != hipSuccess)
+      return fail(PKD_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
+  }
+  std::memcpy(p->pinned, p->header.data(), p->header_bytes);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((e = hipMemcpyAsync(workspace, p->pinned, p->header_bytes, hipMemcpyHostToDevice, s)) !=
+      hipSuccess)
+    return fail(PKD_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  if ((e = hipEventRecord(p->upload_done, s)) != hipSuccess)
+    return fail(PKD_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+  p->upload_pending = true;
+  p->uploaded_to = workspace;
+  return ok();
+}
+
+int pkd_run(const pkd_plan* p, const pkd_run_args* r) {
+  if (!p || !r) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
+  const pkd_plan_args& a = p->args;
+  if (!r->q || !r->k || !r->v || !r->indices || !r->out || !r->workspace)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "q, k, v, indices, out and workspace must not be NULL");
+  if (a.kv_dtype == PKD_DTYPE_E4M3 && (!r->k_scale || !r->v_scale))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "e4m3 KV needs k_scale and v_scale");
+  if (r->workspace != p->uploaded_to)
+    return fail(PKD_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
+  if (r->workspace_bytes < p->info.workspace_bytes)
+    return fail(PKD_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the plan needs %zu",
+                r->workspace_bytes, p->info.workspace_bytes);
+  const int eb = elem_bytes(a.kv_dtype);
+  const int vec_bytes = a.kv_dtype == PKD_DTYPE_E4M3 ? 8 : 16;
+  const uintptr_t kp = reinterpret_cast<uintptr_t>(r->k), vp = reinterpret_cast<uintptr_t>(r->v);
+  if (kp % vec_bytes || vp % vec_bytes || (r->page_stride * eb) % vec_bytes ||
+      (r->token_stride * eb) % vec_bytes || (r->head_stride * eb) % vec_bytes)
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "k, v and the strides must be %d-byte aligned for 128-bit row loads", vec_bytes);
+  if (r->page_stride < 0 || r->token_stride < 0 || r->head_stride < 0)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
+
+  pkd::DecodeLaunch L;
+  L.kv_dtype = a.kv_dtype;
+  L.head_dim = a.head_dim;
+  L.group = a.num_qo_heads / a.num_kv_heads;
+  L.num_items = p->info.num_items;
+  L.num_kv_heads = a.num_kv_heads;
+  L.num_qo_heads = a.num_qo_heads;
+  L.page_size_log2 = ilog2(a.page_size);
+  L.sm_scale_log2 = float(double(p->sm_scale) * 1.4426950408889634);
+  L.q_bf16 = a.q_dtype == PKD_DTYPE_BF16;
+  L.out_bf16 = a.out_dtype == PKD_DTYPE_BF16;
+  L.q = r->q;
+  L.k = r->k;
+  L.v = r->v;
+  L.page_stride = r->page_stride;
+  L.token_stride = r->token_stride;
+  L.head_stride = r->head_stride;
+  L.indices = r->indices;
+  L.k_scale = r->k_scale;
+  L.v_scale = r->v_scale;
+  L.out = r->out;
+  L.lse = r->lse;
+  char* ws = static_cast<char*>(r->workspace);
+  L.items = reinterpret_cast<const pkd::DeviceItem*>(ws + p->off_items);
+  L.split_requests = reinterpret_cast<const int32_t*>(ws + p->off_split);
+  L.merge_indptr = reinterpret_cast<const int32_t*>(ws + p->off_merge);
+  L.part_md = reinterpret_cast<float*>(ws + p->off_part_md);
+  L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
+  L.num_split = p->info.num_split_requests;
+  hipStream_t s = static_cast<hipStream_t>(r->stream);
+  hipError_t e = pkd::launch_decode(L, s);
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  e = pkd::launch_merge(L, s);
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+void pkd_plan_destroy(pkd_plan* p) {
+  if (!p) return;
+  if (p->upload_pending && p->upload_done) hipEventSynchronize(p->upload_done);
+  if (p->upload_done) hipEventDestroy(p->upload_done);
+  if (p->pinned) hipHostFree(p->pinned);
+  delete p;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace pkd {
+
+enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
+
+// Device-side layout of one work item (16 bytes).
+struct DeviceItem {
+  int32_t request;
+  int32_t page_begin;
+  int32_t kv_len;
+  int32_t partial_slot;
+};
+
+struct DecodeLaunch {
+  int kv_dtype = 0;
+  int head_dim = 0;
+  int group = 0;
+  int num_items = 0;
+  int num_kv_heads = 0;
+  int num_qo_heads = 0;
+  int page_size_log2 = 0;
+  float sm_scale_log2 = 0.f;  // sm_scale * log2(e)
+  int q_bf16 = 0;
+  int out_bf16 = 0;
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t page_stride = 0;
+  int64_t token_stride = 0;
+  int64_t head_stride = 0;
+  const int32_t* indices = nullptr;
+  const float* k_scale = nullptr;
+  const float* v_scale = nullptr;
+  void* out = nullptr;
+  float* lse = nullptr;
+  const DeviceItem* items = nullptr;
+  float* part_o = nullptr;   // [num_partials, Hq, head_dim]
+  float* part_md = nullptr;  // [num_partials, Hq, 2]: (m in log2 units, d)
+  int num_split = 0;
+  const int32_t* split_requests = nullptr;  // [num_split]
+  const int32_t* merge_indptr = nullptr;    // [batch+1]
+};
+
+bool decode_supported(int kv_dtype, int head_dim, int group);
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int* wgs_per_cu);
+
+}  // namespace pkd

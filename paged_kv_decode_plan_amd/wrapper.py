@@ -1,0 +1,244 @@
+"""Python binding with the plan()/run() shape of the paged-KV decode wrapper.
+
+"FlashDecoding + FlashInfer — the decode-time attention story", §"The API you
+actually use (Python)": a wrapper owns a caller-allocated workspace and a KV
+layout ("NHD"); plan() takes the page table (indptr, indices, last_page_len),
+head counts, head_dim, page_size and dtypes once per batch shape; run(q,
+paged_kv_cache) is the hot path. The quick-start of "GitHub Spotlight:
+FlashInfer" calls the same two steps begin_forward()/forward(); both names
+are accepted.
+
+Everything here is argument marshalling for libpkdecode.so; PyTorch supplies
+device memory and the current stream only.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple, Union
+
+import numpy as np
+
+from . import _lib
+
+DEFAULT_WORKSPACE_BYTES = 128 * 1024 * 1024
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt in (torch.float32, "f32", "float32"):
+        return _lib.DTYPE_F32
+    if dt in (torch.bfloat16, "bf16", "bfloat16"):
+        return _lib.DTYPE_BF16
+    if dt in (torch.float8_e4m3fn, torch.uint8, "e4m3", "float8_e4m3fn"):
+        return _lib.DTYPE_E4M3
+    raise ValueError(f"unsupported dtype {dt}")
+
+
+def _host_i32(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu").numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x), dtype=np.int32)
+
+
+class Plan:
+    """A plan handle (host partition + workspace layout). Host-only until uploaded."""
+
+    def __init__(self, indptr, last_page_len, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, page_size: int, q_dtype: int, kv_dtype: int, out_dtype: int,
+                 sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
+                 min_chunk_pages: int = 0, device: int = 0):
+        lib = _lib.load()
+        self._lib = lib
+        self._handle = ctypes.c_void_p()
+        self.indptr = _host_i32(indptr)
+        self.last_page_len = _host_i32(last_page_len)
+        B = len(self.last_page_len)
+        if len(self.indptr) != B + 1:
+            raise ValueError("indptr must have batch+1 entries")
+        a = _lib.PlanArgs()
+        a.batch = B
+        a.indptr = self.indptr.ctypes.data_as(_lib._c_i32p)
+        a.last_page_len = self.last_page_len.ctypes.data_as(_lib._c_i32p)
+        a.num_qo_heads = num_qo_heads
+        a.num_kv_heads = num_kv_heads
+        a.head_dim = head_dim
+        a.page_size = page_size
+        a.q_dtype = q_dtype
+        a.kv_dtype = kv_dtype
+        a.out_dtype = out_dtype
+        a.sm_scale = 0.0 if sm_scale is None else float(sm_scale)
+        a.slots = slots
+        a.balance = balance
+        a.min_chunk_pages = min_chunk_pages
+        a.device = device
+        _lib.check(lib.pkd_plan_create(ctypes.byref(a), ctypes.byref(self._handle)))
+        info = _lib.PlanInfo()
+        _lib.check(lib.pkd_plan_get_info(self._handle, ctypes.byref(info)))
+        self.info = {f: getattr(info, f) for f, _ in _lib.PlanInfo._fields_}
+        self.batch, self.num_qo_heads, self.num_kv_heads = B, num_qo_heads, num_kv_heads
+        self.head_dim, self.page_size = head_dim, page_size
+        self.q_dtype, self.kv_dtype, self.out_dtype = q_dtype, kv_dtype, out_dtype
+
+    def worklist(self):
+        """(items int32[num_items, 5], merge_indptr int32[B+1], split_requests int32[S])."""
+        n = self.info["num_items"]
+        items = np.zeros((n, _lib.ITEM_COLS), dtype=np.int32)
+        merge = np.zeros(self.batch + 1, dtype=np.int32)
+        split = np.zeros(max(1, self.info["num_split_requests"]), dtype=np.int32)
+        _lib.check(self._lib.pkd_plan_get_worklist(
+            self._handle, items.ctypes.data_as(_lib._c_i32p), merge.ctypes.data_as(_lib._c_i32p),
+            split.ctypes.data_as(_lib._c_i32p)))
+        return items, merge, split[: self.info["num_split_requests"]]
+
+    def upload(self, workspace_ptr: int, workspace_bytes: int, stream_ptr: int) -> None:
+        _lib.check(self._lib.pkd_plan_upload(self._handle, ctypes.c_void_p(workspace_ptr),
+                                             ctypes.c_size_t(workspace_bytes),
+                                             ctypes.c_void_p(stream_ptr)))
+
+    def run_raw(self, args: "_lib.RunArgs") -> None:
+        _lib.check(self._lib.pkd_run(self._handle, ctypes.byref(args)))
+
+    def close(self) -> None:
+        if getattr(self, "_handle", None) and self._handle.value:
+            self._lib.pkd_plan_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
+                   kv_dtype="bf16", q_dtype="bf16", out_dtype="f32", slots=1024, balance=0,
+                   min_chunk_pages=0):
+    """Host-only: build a plan with an explicit slot count and return its decisions."""
+    p = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
+             _dtype_code(q_dtype), _dtype_code(kv_dtype), _dtype_code(out_dtype), None, slots,
+             balance, min_chunk_pages)
+    items, merge, split = p.worklist()
+    info = dict(p.info)
+    p.close()
+    return info, items, merge, split
+
+
+def _split_kv(paged_kv_cache):
+    """(k, v) views from a combined [pages, 2, P, Hkv, D] tensor or a (k, v) pair."""
+    if isinstance(paged_kv_cache, (tuple, list)):
+        k, v = paged_kv_cache
+    else:
+        if paged_kv_cache.dim() != 5 or paged_kv_cache.shape[1] != 2:
+            raise ValueError("combined NHD cache must be [num_pages, 2, page_size, Hkv, head_dim]")
+        k, v = paged_kv_cache[:, 0], paged_kv_cache[:, 1]
+    if k.shape != v.shape or k.stride() != v.stride():
+        raise ValueError("K and V pools must have the same shape and strides")
+    if k.dim() != 4 or k.stride(3) != 1:
+        raise ValueError("K/V pools must be [num_pages, page_size, Hkv, head_dim] with head_dim contiguous")
+    return k, v
+
+
+class BatchDecodeWithPagedKVCacheWrapper:
+    """plan()/run() wrapper over libpkdecode for one device and one workspace."""
+
+    def __init__(self, workspace_buffer, kv_layout: str = "NHD"):
+        if kv_layout != "NHD":
+            raise ValueError("only the NHD layout is supported")
+        if not workspace_buffer.is_cuda:
+            raise ValueError("the workspace must be device memory")
+        self._ws = workspace_buffer
+        self._plan: Optional[Plan] = None
+        self._indices = None
+
+    # -- plan ----------------------------------------------------------------
+    def plan(self, indptr, indices, last_page_len, num_qo_heads: int, num_kv_heads: int,
+             head_dim: int, page_size: int, pos_encoding_mode: str = "NONE",
+             q_data_type=None, kv_data_type=None, out_data_type=None, data_type=None,
+             sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
+             min_chunk_pages: int = 0) -> None:
+        import torch
+        if pos_encoding_mode != "NONE":
+            raise ValueError("only pos_encoding_mode='NONE' is supported")
+        q_dt = q_data_type or data_type or torch.bfloat16
+        kv_dt = kv_data_type or data_type or q_dt
+        out_dt = out_data_type or q_dt
+        if self._plan is not None:
+            self._plan.close()
+        dev = self._ws.device.index or 0
+        self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
+                          _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
+                          slots, balance, min_chunk_pages, dev)
+        self._indices = indices if isinstance(indices, torch.Tensor) else torch.as_tensor(
+            np.asarray(indices, dtype=np.int32))
+        if self._indices.device != self._ws.device or self._indices.dtype != torch.int32:
+            self._indices = self._indices.to(device=self._ws.device, dtype=torch.int32)
+        self._indices = self._indices.contiguous()
+        need = self._plan.info["workspace_bytes"]
+        have = self._ws.numel() * self._ws.element_size()
+        if have < need:
+            raise _lib.PkdError(_lib.PKD_ERR_WORKSPACE_TOO_SMALL,
+                                f"workspace has {have} bytes, the plan needs {need}")
+        stream = torch.cuda.current_stream(self._ws.device).cuda_stream
+        self._plan.upload(self._ws.data_ptr(), have, stream)
+
+    begin_forward = plan
+
+    @property
+    def plan_info(self) -> dict:
+        return dict(self._plan.info)
+
+    # -- run -----------------------------------------------------------------
+    def run(self, q, paged_kv_cache, out=None, lse=None, return_lse: bool = False,
+            k_scale=None, v_scale=None):
+        import torch
+        p = self._plan
+        if p is None:
+            raise RuntimeError("plan() must be called before run()")
+        k, v = _split_kv(paged_kv_cache)
+        if q.shape != (p.batch, p.num_qo_heads, p.head_dim) or not q.is_contiguous():
+            raise ValueError(f"q must be contiguous [{p.batch}, {p.num_qo_heads}, {p.head_dim}]")
+        if _dtype_code(q.dtype) != p.q_dtype or _dtype_code(k.dtype) != p.kv_dtype:
+            raise _lib.PkdError(_lib.PKD_ERR_PLAN_MISMATCH, "q/KV dtypes differ from the plan")
+        if k.shape[1] != p.page_size or k.shape[2] != p.num_kv_heads or k.shape[3] != p.head_dim:
+            raise ValueError("KV pool shape disagrees with the plan")
+        out_dt = torch.float32 if p.out_dtype == _lib.DTYPE_F32 else torch.bfloat16
+        if out is None:
+            out = torch.empty(q.shape, dtype=out_dt, device=q.device)
+        elif out.dtype != out_dt or out.shape != q.shape or not out.is_contiguous():
+            raise ValueError("out has the wrong dtype, shape or layout")
+        if return_lse and lse is None:
+            lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=q.device)
+        if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
+            raise ValueError("lse must be contiguous float32 [batch, num_qo_heads]")
+        a = _lib.RunArgs()
+        a.q = q.data_ptr()
+        a.k = k.data_ptr()
+        a.v = v.data_ptr()
+        a.page_stride, a.token_stride, a.head_stride = k.stride(0), k.stride(1), k.stride(2)
+        a.indices = self._indices.data_ptr()
+        if p.kv_dtype == _lib.DTYPE_E4M3:
+            if k_scale is None or v_scale is None:
+                raise ValueError("e4m3 KV needs k_scale and v_scale [num_pages, num_kv_heads]")
+            for s in (k_scale, v_scale):
+                if (s.dtype != torch.float32 or not s.is_contiguous()
+                        or s.shape != (k.shape[0], p.num_kv_heads)):
+                    raise ValueError("scales must be contiguous float32 [num_pages, num_kv_heads]")
+            a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        a.out = out.data_ptr()
+        a.lse = lse.data_ptr() if lse is not None else None
+        a.workspace = self._ws.data_ptr()
+        a.workspace_bytes = self._ws.numel() * self._ws.element_size()
+        a.stream = torch.cuda.current_stream(q.device).cuda_stream
+        p.run_raw(a)
+        return (out, lse) if (return_lse or lse is not None) else out
+
+    forward = run
+
+    def close(self) -> None:
+        if self._plan is not None:
+            self._plan.close()
+            self._plan = None

@@ -1,0 +1,226 @@
+"""HIP path (through the C ABI) against the float64 oracle on the same seeded inputs.
+
+Tolerances: max-abs 2e-3 for fp32/bf16 KV and 3e-2 for e4m3 KV (against the
+same dequantised values), compared in fp32 output before rounding; bf16
+output adds half an ulp of rounding. Index-exact properties (the gather
+probe, page-permutation invariance, determinism, single key) are bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import (compare, oracle_for, out_to_f64, run_hip, sample_request_case,
+                         to_device)
+from workloads import CONFIGS, custom_workload, device_case, host_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu]", *a, flush=True)
+
+
+# ------------------------------------------------------------------ small cases, every kernel
+
+SMALL = []
+for kv in ("f32", "bf16", "e4m3"):
+    for d in (64, 128):
+        for g in (1, 2, 4, 8):
+            SMALL.append((kv, d, g))
+
+
+@pytest.mark.parametrize("kv,d,g", SMALL)
+@pytest.mark.parametrize("split", ["auto", "forced"])
+def test_small_ragged_matches_oracle(kv, d, g, split):
+    hkv = 2
+    lens = [1, 15, 16, 17, 100, 333, 700, 64, 3]
+    P = 16
+    w = custom_workload(len(lens), hkv * g, hkv, d, P, kv, "bf16" if kv != "f32" else "f32", lens,
+                        pool_pages=sum(-(-x // P) for x in lens) + 7)
+    seed = 100 + 7 * d + g
+    case = host_case(w, seed, poison=True)
+    _say("small", kv, d, g, split, "seed", seed)
+    ref_out, ref_lse = oracle_for(case)
+    dc = to_device(case)
+    kw = dict(slots=4, balance=1, min_chunk_pages=1) if split == "forced" else {}
+    out, lse, info = run_hip(dc, **kw)
+    if split == "forced":
+        assert info["num_split_requests"] > 0
+    compare(out, lse, ref_out, ref_lse, kv)
+
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 32, 64, 128])
+def test_page_sizes(P):
+    lens = [1, P, P + 1, 3 * P + 5, 257]
+    w = custom_workload(len(lens), 8, 2, 128, P, "bf16", "bf16", lens,
+                        pool_pages=sum(-(-x // P) for x in lens) + 3)
+    case = host_case(w, 40 + P, poison=True)
+    _say("page size", P)
+    ref_out, ref_lse = oracle_for(case)
+    dc = to_device(case)
+    for kw in ({}, dict(slots=8, balance=1, min_chunk_pages=1)):
+        out, lse, _ = run_hip(dc, **kw)
+        compare(out, lse, ref_out, ref_lse, "bf16")
+
+
+@pytest.mark.parametrize("kv", ["f32", "bf16", "e4m3"])
+def test_bf16_output_rounding(kv):
+    lens = [5, 200, 31]
+    w = custom_workload(3, 8, 2, 128, 16, kv, "bf16", lens, pool_pages=20)
+    case = host_case(w, 9, poison=True)
+    ref_out, ref_lse = oracle_for(case)
+    out, lse, _ = run_hip(to_device(case), out_dtype="bf16")
+    assert out.dtype == torch.bfloat16
+    compare(out, lse, ref_out, ref_lse, kv, out_dtype="bf16")
+
+
+def test_single_seq_fp32_config_full():
+    """single_seq_fp32: B=1, 4/4 heads, D=64, P=16, 512 tokens in a 64-page pool."""
+    w = CONFIGS["single_seq_fp32"]
+    case = host_case(w, 1, poison=True)
+    ref_out, ref_lse = oracle_for(case)
+    for kw in ({}, dict(slots=64, balance=1, min_chunk_pages=1)):
+        out, lse, _ = run_hip(to_device(case), **kw)
+        compare(out, lse, ref_out, ref_lse, "f32")
+
+
+# ------------------------------------------------------------------ exact properties
+
+def _probe_case(kv_dtype, lens, P, hq, hkv, d, seed):
+    w = custom_workload(len(lens), hq, hkv, d, P, kv_dtype, "f32", lens,
+                        pool_pages=sum(-(-x // P) for x in lens) + 5)
+    case = host_case(w, seed, poison=True)
+    rng = np.random.default_rng(seed)
+    kv = case["kv"]
+    nanmask = np.isnan(kv) if kv_dtype == "f32" else None
+    kv[...] = 0.0
+    pages = np.arange(case["num_pages"], dtype=np.float64)
+    kv[:, 1, :, :, 0] = pages[:, None, None]
+    kv[:, 1, :, :, 1] = np.arange(P)[None, :, None]
+    case["q"][:] = 0.0
+    case["q"][:, :, 0] = 1.0
+    targets = []
+    gap = 200.0 * np.sqrt(d)  # logit of the target exceeds all others by 200
+    for r in range(len(lens)):
+        t = int(rng.integers(0, lens[r]))
+        page = int(case["indices"][case["indptr"][r] + t // P])
+        kv[page, 0, t % P, :, 0] = gap
+        targets.append((page, t % P))
+    kv[nanmask] = np.nan
+    return case, targets
+
+
+@pytest.mark.parametrize("forced_split", [False, True])
+def test_gather_index_probe_bit_exact(forced_split):
+    """One dominant token per request: out must equal that token's V exactly,
+    which reads back (page id, slot) — the gather mapping, bit for bit."""
+    lens = [1, 2, 17, 48, 255, 1000, 4096, 33]
+    P, hq, hkv, d = 16, 8, 4, 64
+    case, targets = _probe_case("f32", lens, P, hq, hkv, d, 77)
+    kw = dict(slots=16, balance=1, min_chunk_pages=1) if forced_split else {}
+    out, _, info = run_hip(to_device(case), **kw)
+    o = out.cpu().numpy()
+    for r, (page, slot) in enumerate(targets):
+        assert np.all(o[r, :, 0] == page) and np.all(o[r, :, 1] == slot), (r, page, slot)
+        assert np.all(o[r, :, 2:] == 0)
+
+
+def test_page_permutation_invariance_bit_exact():
+    lens = [100, 37, 512, 9]
+    w = custom_workload(4, 16, 4, 128, 16, "bf16", "bf16", lens, pool_pages=60)
+    case = host_case(w, 3, poison=True)
+    out1, lse1, _ = run_hip(to_device(case))
+    perm = np.random.default_rng(5).permutation(case["num_pages"])
+    inv = np.empty_like(perm)
+    inv[perm] = np.arange(len(perm))
+    case2 = dict(case)
+    case2["kv"] = case["kv"][inv]
+    case2["indices"] = perm[case["indices"]].astype(np.int32)
+    out2, lse2, _ = run_hip(to_device(case2))
+    assert torch.equal(out1, out2) and torch.equal(lse1, lse2)
+
+
+def test_run_to_run_determinism():
+    w = custom_workload(6, 32, 8, 128, 16, "bf16", "bf16", [3000, 20, 700, 1, 4096, 65], pool_pages=700)
+    case = host_case(w, 12, poison=True)
+    dc = to_device(case)
+    a = run_hip(dc, slots=32, balance=1, min_chunk_pages=1)
+    b = run_hip(dc, slots=32, balance=1, min_chunk_pages=1)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_single_key_returns_v_exactly():
+    w = custom_workload(3, 8, 2, 128, 16, "bf16", "bf16", [1, 1, 1], pool_pages=5)
+    case = host_case(w, 2, poison=True)
+    out, lse, _ = run_hip(to_device(case))
+    ref, _ = oracle_for(case)
+    assert np.array_equal(out_to_f64(out), ref)
+
+
+def test_constant_v_returns_v():
+    w = custom_workload(3, 8, 2, 128, 16, "f32", "f32", [700, 1, 40], pool_pages=50)
+    case = host_case(w, 4, poison=True)
+    c = np.linspace(-3, 3, 128).astype(np.float32)
+    finite = ~np.isnan(case["kv"][:, 1])
+    case["kv"][:, 1] = np.where(finite, c, np.nan)
+    out, _, _ = run_hip(to_device(case), slots=8, balance=1, min_chunk_pages=1)
+    np.testing.assert_allclose(out.cpu().numpy(), np.broadcast_to(c, out.shape), rtol=1e-5, atol=1e-6)
+
+
+def test_split_equals_unsplit_within_tolerance():
+    w = custom_workload(4, 16, 4, 128, 16, "bf16", "bf16", [5000, 300, 64, 1234], pool_pages=500)
+    case = host_case(w, 8, poison=True)
+    dc = to_device(case)
+    a, la, ia = run_hip(dc, slots=1, balance=1, min_chunk_pages=1000)
+    b, lb, ib = run_hip(dc, slots=64, balance=1, min_chunk_pages=1)
+    assert ia["num_partials"] == 0 and ib["num_partials"] > 0
+    assert float((a - b).abs().max()) < 1e-4
+    assert float((la - lb).abs().max()) < 1e-4
+
+
+def test_shared_prefix_pages_are_legal():
+    """The pages' worked example: two requests share their first three pages."""
+    from workloads import explicit_table
+    lists = [[7, 2, 15, 88, 3], [7, 2, 15, 41]]
+    table = explicit_table(lists, [16, 9], 16, num_pages=90)
+    w = custom_workload(2, 8, 2, 128, 16, "bf16", "bf16", [int(x) for x in table["kv_lens"]],
+                        pool_pages=90)
+    case = host_case(w, 6, poison=True, table=table)
+    ref_out, ref_lse = oracle_for(case)
+    for kw in ({}, dict(slots=8, balance=1, min_chunk_pages=1)):
+        out, lse, _ = run_hip(to_device(case), **kw)
+        compare(out, lse, ref_out, ref_lse, "bf16")
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+
+FULL = ["llama3_8b_bf16", "ragged_loguniform_bf16", "long_ctx_gqa8_bf16", "fp8_kv_e4m3"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_workload_sampled_rows(name):
+    """Full-size batch in the bench's launch configuration; the oracle checks
+    sampled requests (shortest, longest and a few random ones), all heads."""
+    w = CONFIGS[name]
+    seed = list(CONFIGS).index(name) + 1
+    _say("full-size", name, "seed", seed)
+    dc = device_case(w, seed, "cuda:0", poison=True)
+    out, lse, info = run_hip(dc)
+    _say("plan", info)
+    lens = dc["kv_lens"]
+    rng = np.random.default_rng(seed)
+    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
+                   *rng.choice(len(lens), size=min(2, len(lens)), replace=False).tolist()})
+    if name == "long_ctx_gqa8_bf16":
+        rows = [1]
+    o = out_to_f64(out)
+    assert np.all(np.isfinite(o))
+    lv = lse.cpu().numpy().astype(np.float64)
+    for r in rows:
+        sub = sample_request_case(dc, r)
+        ref_out, ref_lse = oracle_for(sub)
+        _say("  row", r, "len", int(lens[r]))
+        compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, w.kv_dtype)
+    del dc
+    torch.cuda.empty_cache()
+    assert lv.shape == (w.batch, w.num_qo_heads)

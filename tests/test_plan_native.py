@@ -1,0 +1,82 @@
+"""The C++ planner (through the C ABI, host only) against the oracle's rule, bit for bit."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+import paged_kv_decode_plan_amd as pk
+from oracle import plan as oplan
+from workloads import CONFIGS, page_table
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _both(indptr, last, P, hkv, slots, balance, cmin, hq=None, d=128, kv="bf16"):
+    hq = hq or hkv
+    info, items, merge, split = pk.plan_partition(indptr, last, hq, hkv, d, P, kv_dtype=kv,
+                                                  q_dtype="bf16", slots=slots, balance=balance,
+                                                  min_chunk_pages=cmin)
+    ref = oplan.plan(indptr, last, P, hkv, slots, balance, cmin)
+    return info, items, merge, split, ref
+
+
+def _assert_same(info, items, merge, split, ref):
+    assert info["chunk_pages"] == ref["chunk_pages"]
+    assert np.array_equal(items, ref["items"])
+    assert np.array_equal(merge, ref["merge_indptr"])
+    assert np.array_equal(split, ref["split_requests"])
+    assert info["num_partials"] == ref["num_partials"]
+    assert info["total_kv_tokens"] == int(ref["kv_lens"].sum())
+
+
+def test_golden_partitions_native():
+    with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    for c in ex["cases"]:
+        info, items, merge, split, ref = _both(ex["indptr"], ex["last_page_len"], ex["page_size"],
+                                               1, c["slots"], c["balance"], c["min_chunk_pages"])
+        assert items.tolist() == c["items"]
+        _assert_same(info, items, merge, split, ref)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_tables_bit_exact(seed):
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 300))
+    P = int(rng.choice([1, 2, 16, 64]))
+    n = rng.integers(1, int(rng.integers(2, 500)), size=B)
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = rng.integers(1, P + 1, size=B).astype(np.int32)
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    out = _both(indptr, last, P, hkv, int(rng.integers(1, 4096)), int(rng.integers(1, 6)),
+                int(rng.integers(1, 64)), hq=hkv * int(rng.choice([1, 2, 4, 8])))
+    _assert_same(*out[:4], out[4])
+
+
+@pytest.mark.parametrize("name", list(CONFIGS))
+@pytest.mark.parametrize("slots", [1024, 2048, 768])
+def test_workload_tables_bit_exact(name, slots):
+    w = CONFIGS[name]
+    t = page_table(w, seed=list(CONFIGS).index(name) + 1)
+    cmin = max(1, -(-256 // w.page_size))
+    out = _both(t["indptr"], t["last_page_len"], w.page_size, w.num_kv_heads, slots, 2, cmin,
+                hq=w.num_qo_heads, d=w.head_dim, kv=w.kv_dtype)
+    _assert_same(*out[:4], out[4])
+
+
+def test_default_balance_and_min_chunk():
+    info, *_ = pk.plan_partition([0, 5, 9], [16, 7], 4, 1, 128, 16, slots=8)
+    assert info["balance"] == 2 and info["min_chunk_pages"] == 16
+    info, *_ = pk.plan_partition([0, 5, 9], [16, 7], 4, 1, 128, 64, slots=8)
+    assert info["min_chunk_pages"] == 4
+
+
+def test_workspace_size_formula():
+    info, items, merge, split = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64,
+                                                  balance=1, min_chunk_pages=1)
+    assert info["num_split_requests"] == 2 and info["num_partials"] > 0
+    parts = info["num_partials"] * 32
+    a = lambda x: (x + 255) // 256 * 256
+    header = a(a(a(info["num_items"] * 16) + info["num_split_requests"] * 4) + 3 * 4)
+    assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
