@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark: batched paged-KV decode attention on one MI355X.
+
+One step is one run() over the whole batch: the split-KV decode kernel plus
+the merge kernel when requests are split. The default workload is the
+Llama-3-8B-shaped decode batch (B=64, 32 query / 8 KV heads, head_dim 128,
+16-token pages, every context 2048, bf16). Inputs are synthetic (seeded
+normal values, shuffled page table) and resident in HBM before timing.
+
+Timing: W untimed warmup steps, then K timed steps. Before each timed step a
+1 GiB buffer is read so that neither L2 nor the 256 MB last-level cache holds
+KV; HIP events on the launch stream bracket the decode kernel and the merge
+kernel of every step separately. ``value`` is KV-read GB/s over the whole
+step (algorithmic KV bytes / mean step time). ``roofline`` is for the decode
+kernel alone. ``cpu_baseline`` times the float64 oracle on a bounded sample
+of the same batch on one host core.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "KV-read HBM GB/s (% of peak) + µs per batched decode step"
+CSRC = os.path.join(ROOT, "paged_kv_decode_plan_amd", "csrc")
+
+
+def kv_bytes(w, table) -> int:
+    """Algorithmic bytes the decode kernel must read: every valid K and V element
+    once, plus for e4m3 the fp32 K and V scale of every (page, KV head)."""
+    elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    tokens = int(table["kv_lens"].sum())
+    b = tokens * w.num_kv_heads * w.head_dim * 2 * elem
+    if w.kv_dtype == "e4m3":
+        pages = int(table["indptr"][-1])
+        b += pages * w.num_kv_heads * 2 * 4
+    return b
+
+
+def kernel_source_sha() -> str:
+    """Hash of every device-code source (kernels, their shared header, dispatch)."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith(".hip") or name == "kernel_common.h":
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_decode_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(dcase, w, budget_s: float = 12.0):
+    """The oracle, as it stands, on whole requests of the same batch until about
+    `budget_s` seconds of single-threaded CPU work have been spent."""
+    from threadpoolctl import threadpool_limits
+
+    import numpy as np
+    import torch
+
+    from oracle import attention
+
+    lens = dcase["kv_lens"]
+    order = list(range(len(lens)))
+    done_bytes = 0
+    done = []
+    elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    t_total = 0.0
+    idx = dcase["indices"]
+    with threadpool_limits(limits=1):
+        for r in order:
+            pages = torch.as_tensor(np.asarray(idx[int(dcase["indptr"][r]):int(dcase["indptr"][r + 1])],
+                                               dtype=np.int64), device=dcase["kv"].device)
+            kv = dcase["kv"].index_select(0, pages)
+            if w.kv_dtype == "bf16":
+                kvh = kv.view(torch.int16).cpu().numpy().view(np.uint16)
+            elif w.kv_dtype == "e4m3":
+                kvh = kv.cpu().numpy().view(np.uint8)
+            else:
+                kvh = kv.cpu().numpy()
+            q = dcase["q"][r:r + 1]
+            qh = (q.view(torch.int16).cpu().numpy().view(np.uint16) if w.q_dtype == "bf16"
+                  else q.cpu().numpy())
+            ks = vs = None
+            if w.kv_dtype == "e4m3":
+                ks = dcase["k_scale"].index_select(0, pages).cpu().numpy()
+                vs = dcase["v_scale"].index_select(0, pages).cpu().numpy()
+            n = len(pages)
+            t0 = time.perf_counter()
+            attention.decode(qh, kvh, np.array([0, n], np.int32), np.arange(n, dtype=np.int32),
+                             np.array([dcase["last_page_len"][r]], np.int32),
+                             num_kv_heads=w.num_kv_heads, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                             sm_scale=w.scale(), k_scale=ks, v_scale=vs)
+            t_total += time.perf_counter() - t0
+            done.append(r)
+            done_bytes += int(lens[r]) * w.num_kv_heads * w.head_dim * 2 * elem
+            if t_total >= budget_s:
+                break
+    gbs = done_bytes / t_total / 1e9
+    return {
+        "value": round(gbs, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{len(done)} of {len(lens)} requests ({int(sum(lens[done]))} KV tokens, "
+                   f"all {w.num_qo_heads} query heads), float64 numpy oracle, 1 thread, "
+                   f"{t_total:.1f} s"),
+        "ms_per_full_step_extrapolated": round(t_total / max(1, done_bytes) * kv_bytes_total(dcase, w)
+                                               * 1e3, 1),
+    }
+
+
+def kv_bytes_total(dcase, w):
+    return kv_bytes(w, dcase)
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="llama3_8b_bf16")
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--balance", type=int, default=0)
+    ap.add_argument("--min-chunk-pages", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path here has no multi-GPU "
+              "sharding (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_kv_decode_plan_amd as pk
+    from workloads import CONFIGS, device_case
+
+    if args.config not in CONFIGS:
+        print(f"unknown config {args.config}; choose from {list(CONFIGS)}", file=sys.stderr)
+        return 2
+    w = CONFIGS[args.config]
+    seed = args.seed if args.seed is not None else list(CONFIGS).index(args.config) + 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {w.name} seed {seed}", file=sys.stderr, flush=True)
+    dcase = device_case(w, seed, dev, poison=False)
+    torch.cuda.synchronize()
+    nbytes = kv_bytes(w, dcase)
+
+    ws = torch.empty(pk.DEFAULT_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
+    wrapper = pk.BatchDecodeWithPagedKVCacheWrapper(ws, "NHD")
+    q_dt = dcase["q"].dtype
+    kv_dt = "e4m3" if w.kv_dtype == "e4m3" else dcase["kv"].dtype
+    indices_dev = torch.as_tensor(dcase["indices"], dtype=torch.int32).to(dev)
+    t0 = time.perf_counter()
+    wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
+                 w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt, kv_data_type=kv_dt,
+                 out_data_type=q_dt, sm_scale=w.scale(), balance=args.balance,
+                 min_chunk_pages=args.min_chunk_pages)
+    torch.cuda.synchronize()
+    plan_us = (time.perf_counter() - t0) * 1e6
+    info = wrapper.plan_info
+    out = torch.empty_like(dcase["q"])
+    run_kw = dict(out=out, k_scale=dcase["k_scale"], v_scale=dcase["v_scale"])
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_i64 = flush.view(torch.int64)
+    flush.zero_()
+
+    from paged_kv_decode_plan_amd import _lib
+
+    def step(ev=None):
+        if ev is None:
+            wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+            return
+        ev[0].record()
+        wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_DECODE, **run_kw)
+        ev[1].record()
+        wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_MERGE, **run_kw)
+        ev[2].record()
+
+    print(f"[bench] plan {info}; warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        if not args.warm:
+            flush_i64.max()  # read 1 GiB: evict KV from L2 and the last-level cache
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    mrg_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
+
+    # back-to-back (warm) steps for reference
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / args.steps
+
+    mean_step = statistics.fmean(step_ms)
+    mean_dec = statistics.fmean(dec_ms)
+    q = statistics.quantiles(step_ms, n=10) if len(step_ms) >= 2 else [mean_step] * 9
+    gbs = nbytes / (mean_step * 1e-3) / 1e9
+    dec_gbs = nbytes / (mean_dec * 1e-3) / 1e9
+    traffic = load_traffic(w.name)
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+            "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
+            "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "context": list(w.context),
+            "total_kv_tokens": int(dcase["kv_lens"].sum()), "seed": seed,
+            "cache": "warm" if args.warm else "cold (1 GiB read between steps)",
+        },
+        "us_per_step": round(mean_step * 1e3, 2),
+        "us_per_step_p10_p90": [round(q[0] * 1e3, 2), round(q[-1] * 1e3, 2)],
+        "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
+        "kv_bytes_per_step": nbytes,
+        "warm_us_per_step": round(warm_ms * 1e3, 2),
+        "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
+        "merge_us": round(statistics.fmean(mrg_ms) * 1e3, 2),
+        "plan_us_host": round(plan_us, 1),
+        "plan": {k: info[k] for k in ("chunk_pages", "num_items", "num_partials",
+                                      "num_split_requests", "slots", "balance",
+                                      "min_chunk_pages")},
+        "roofline": {
+            "kernel": "decode_kernel",
+            "bound": "hbm",
+            "achieved": round(dec_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+            "decode_us": round(mean_dec * 1e3, 2),
+            "algorithmic_bytes_per_launch": nbytes,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(dcase, w, args.cpu_budget)
+    wrapper.close()
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

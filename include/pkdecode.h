@@ -63,7 +63,8 @@ typedef struct pkd_plan pkd_plan;
  *                   (n_r - 1) * page_size + last_page_len[r] tokens
  *  num_qo_heads     query heads Hq; num_kv_heads divides it and query head h
  *                   reads KV head h / (Hq / Hkv)
- *  head_dim         64 or 128
+ *  head_dim         64 or 128; query heads per KV head 1, 2, 4 or 8, and also
+ *                   16 for bf16 queries with bf16 or e4m3 KV at head_dim 128
  *  page_size        tokens per page, a power of two in [1, 1024]
  *  q_dtype          PKD_DTYPE_F32 or PKD_DTYPE_BF16
  *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_E4M3
@@ -187,13 +188,24 @@ int pkd_plan_upload(pkd_plan* plan, void* workspace, size_t workspace_bytes, voi
  * kernel on args->stream. Allocates nothing and does not synchronise. */
 int pkd_run(const pkd_plan* plan, const pkd_run_args* args);
 
+/* Stages of run(), for callers that time or interleave them: the split-KV
+ * decode kernel (partial states or final rows) and the merge kernel that
+ * folds the partial states of split requests (a no-op when none is split).
+ * pkd_run(plan, args) == pkd_run_stages(plan, args, PKD_STAGE_ALL). The merge
+ * stage reads what the decode stage of the same plan and workspace wrote. */
+#define PKD_STAGE_DECODE 1
+#define PKD_STAGE_MERGE 2
+#define PKD_STAGE_ALL 3
+int pkd_run_stages(const pkd_plan* plan, const pkd_run_args* args, int32_t stages);
+
 /* Free the handle (waits for an in-flight upload first). NULL is a no-op. */
 void pkd_plan_destroy(pkd_plan* plan);
 
-/* Workgroups of the decode kernel for (kv_dtype, head_dim, group) that one
- * compute unit holds at once, and the device's compute-unit count. */
-int pkd_device_slots(int32_t device, int32_t kv_dtype, int32_t head_dim, int32_t group,
-                     int32_t* wgs_per_cu, int32_t* num_cus);
+/* Workgroups of the decode kernel selected for (q_dtype, kv_dtype, head_dim,
+ * group, page_size) that one compute unit holds at once, and the device's
+ * compute-unit count. */
+int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
+                     int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus);
 
 #ifdef __cplusplus
 }

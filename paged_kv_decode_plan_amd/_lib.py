@@ -22,6 +22,9 @@ DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_E4M3 = 2
 ITEM_COLS = 5
+STAGE_DECODE = 1
+STAGE_MERGE = 2
+STAGE_ALL = 3
 
 _c_i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -113,9 +116,11 @@ def load() -> ctypes.CDLL:
     lib.pkd_plan_upload.restype = ctypes.c_int
     lib.pkd_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs)]
     lib.pkd_run.restype = ctypes.c_int
+    lib.pkd_run_stages.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs), ctypes.c_int32]
+    lib.pkd_run_stages.restype = ctypes.c_int
     lib.pkd_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.pkd_plan_destroy.restype = None
-    lib.pkd_device_slots.argtypes = [ctypes.c_int32] * 4 + [_c_i32p, _c_i32p]
+    lib.pkd_device_slots.argtypes = [ctypes.c_int32] * 6 + [_c_i32p, _c_i32p]
     lib.pkd_device_slots.restype = ctypes.c_int
     _lib = lib
     return lib

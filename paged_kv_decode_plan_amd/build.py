@@ -20,7 +20,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkdecode.so")
 ARCH = "gfx950"
 
-SOURCES = ["planner.cpp", "capi.cpp", "decode.hip"]
+SOURCES = ["planner.cpp", "capi.cpp", "dispatch.hip", "decode_valu.hip", "decode_mfma.hip",
+           "merge.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

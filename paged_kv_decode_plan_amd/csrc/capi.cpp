@@ -72,12 +72,13 @@ const char* pkd_last_error(void) { return g_last_error.c_str(); }
 
 int pkd_version(void) { return 100; }
 
-int pkd_device_slots(int32_t device, int32_t kv_dtype, int32_t head_dim, int32_t group,
-                     int32_t* wgs_per_cu, int32_t* num_cus) {
+int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
+                     int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus) {
   if (!wgs_per_cu || !num_cus) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
-  if (!pkd::decode_supported(kv_dtype, head_dim, group))
-    return fail(PKD_ERR_UNSUPPORTED, "no kernel for kv_dtype=%d head_dim=%d group=%d", kv_dtype,
-                head_dim, group);
+  const int q_bf16 = q_dtype == PKD_DTYPE_BF16;
+  if (!pkd::decode_supported(kv_dtype, head_dim, group, q_bf16, page_size))
+    return fail(PKD_ERR_UNSUPPORTED, "no kernel for kv_dtype=%d head_dim=%d group=%d q_dtype=%d",
+                kv_dtype, head_dim, group, q_dtype);
   int prev = 0;
   hipError_t e = hipGetDevice(&prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -85,7 +86,7 @@ int pkd_device_slots(int32_t device, int32_t kv_dtype, int32_t head_dim, int32_t
     return fail(PKD_ERR_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(e));
   int cus = 0, wgs = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-  if (e == hipSuccess) e = pkd::decode_occupancy(kv_dtype, head_dim, group, &wgs);
+  if (e == hipSuccess) e = pkd::decode_occupancy(kv_dtype, head_dim, group, q_bf16, page_size, &wgs);
   if (prev != device) hipSetDevice(prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
   *wgs_per_cu = wgs;
@@ -114,9 +115,10 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (!is_pow2(a->page_size) || a->page_size > 1024)
     return fail(PKD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]",
                 a->page_size);
-  if (!pkd::decode_supported(a->kv_dtype, a->head_dim, group))
-    return fail(PKD_ERR_UNSUPPORTED, "no kernel for head_dim=%d group=%d kv_dtype=%d",
-                a->head_dim, group, a->kv_dtype);
+  if (!pkd::decode_supported(a->kv_dtype, a->head_dim, group, a->q_dtype == PKD_DTYPE_BF16,
+                             a->page_size))
+    return fail(PKD_ERR_UNSUPPORTED, "no kernel for head_dim=%d group=%d kv_dtype=%d q_dtype=%d",
+                a->head_dim, group, a->kv_dtype, a->q_dtype);
   if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0)
     return fail(PKD_ERR_INVALID_ARGUMENT, "slots, balance and min_chunk_pages must be >= 0");
   if (!(a->sm_scale >= 0.f) || std::isinf(a->sm_scale))
@@ -125,7 +127,8 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   int slots = a->slots;
   if (slots == 0) {
     int32_t wgs = 0, cus = 0;
-    int rc = pkd_device_slots(a->device, a->kv_dtype, a->head_dim, group, &wgs, &cus);
+    int rc = pkd_device_slots(a->device, a->q_dtype, a->kv_dtype, a->head_dim, group,
+                              a->page_size, &wgs, &cus);
     if (rc != PKD_OK) return rc;
     slots = wgs * cus;
     if (slots < 1) return fail(PKD_ERR_HIP, "device reports no resident workgroups");
@@ -252,8 +255,12 @@ int pkd_plan_upload(pkd_plan* p, void* workspace, size_t workspace_bytes, void* 
   return ok();
 }
 
-int pkd_run(const pkd_plan* p, const pkd_run_args* r) {
+int pkd_run(const pkd_plan* p, const pkd_run_args* r) { return pkd_run_stages(p, r, PKD_STAGE_ALL); }
+
+int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   if (!p || !r) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
+  if (stages < 1 || stages > PKD_STAGE_ALL)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of PKD_STAGE_ALL");
   const pkd_plan_args& a = p->args;
   if (!r->q || !r->k || !r->v || !r->indices || !r->out || !r->workspace)
     return fail(PKD_ERR_INVALID_ARGUMENT, "q, k, v, indices, out and workspace must not be NULL");
@@ -271,6 +278,8 @@ int pkd_run(const pkd_plan* p, const pkd_run_args* r) {
       (r->token_stride * eb) % vec_bytes || (r->head_stride * eb) % vec_bytes)
     return fail(PKD_ERR_INVALID_ARGUMENT,
                 "k, v and the strides must be %d-byte aligned for 128-bit row loads", vec_bytes);
+  if (reinterpret_cast<uintptr_t>(r->q) % 16)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
   if (r->page_stride < 0 || r->token_stride < 0 || r->head_stride < 0)
     return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
 
@@ -304,10 +313,15 @@ int pkd_run(const pkd_plan* p, const pkd_run_args* r) {
   L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
   L.num_split = p->info.num_split_requests;
   hipStream_t s = static_cast<hipStream_t>(r->stream);
-  hipError_t e = pkd::launch_decode(L, s);
-  if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  e = pkd::launch_merge(L, s);
-  if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  hipError_t e;
+  if (stages & PKD_STAGE_DECODE) {
+    e = pkd::launch_decode(L, s);
+    if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  }
+  if (stages & PKD_STAGE_MERGE) {
+    e = pkd::launch_merge(L, s);
+    if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 

@@ -1,0 +1,64 @@
+// Kernel choice and launch for the decode stage.
+//
+// The MFMA kernel runs wherever both contractions can take bf16 operands
+// exactly: bf16 or e4m3 KV with bf16 queries and head_dim 128 (group sizes
+// 1..16). fp32 KV or queries, and head_dim 64, use the vector-ALU kernel.
+#include <hip/hip_runtime.h>
+
+#include "kernel_common.h"
+
+namespace pkd {
+
+static DecodeFn choose(int kv_dtype, int head_dim, int group, int q_bf16, int page_size) {
+  if (q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3)) {
+    if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, group, page_size)) return f;
+  }
+  return valu_decode_kernel(kv_dtype, head_dim, group);
+}
+
+bool decode_supported(int kv_dtype, int head_dim, int group, int q_bf16, int page_size) {
+  return choose(kv_dtype, head_dim, group, q_bf16, page_size) != nullptr;
+}
+
+bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int q_bf16, int page_size) {
+  return q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3) &&
+         mfma_decode_kernel(kv_dtype, head_dim, group, page_size) != nullptr;
+}
+
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+  DecodeFn fn = choose(L.kv_dtype, L.head_dim, L.group, L.q_bf16, 1 << L.page_size_log2);
+  if (!fn) return hipErrorInvalidValue;
+  KernelArgs a;
+  a.q = L.q;
+  a.k = L.k;
+  a.v = L.v;
+  a.page_stride = L.page_stride;
+  a.token_stride = L.token_stride;
+  a.head_stride = L.head_stride;
+  a.indices = L.indices;
+  a.k_scale = L.k_scale;
+  a.v_scale = L.v_scale;
+  a.out = L.out;
+  a.lse = L.lse;
+  a.items = L.items;
+  a.part_o = L.part_o;
+  a.part_md = L.part_md;
+  a.num_kv_heads = L.num_kv_heads;
+  a.num_qo_heads = L.num_qo_heads;
+  a.page_size_log2 = L.page_size_log2;
+  a.sm_scale_log2 = L.sm_scale_log2;
+  a.q_bf16 = L.q_bf16;
+  a.out_bf16 = L.out_bf16;
+  const unsigned grid = unsigned(L.num_items) * unsigned(L.num_kv_heads);
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int q_bf16, int page_size,
+                            int* wgs_per_cu) {
+  DecodeFn fn = choose(kv_dtype, head_dim, group, q_bf16, page_size);
+  if (!fn) return hipErrorInvalidValue;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs_per_cu, fn, kThreads, 0);
+}
+
+}  // namespace pkd

@@ -1,0 +1,105 @@
+// Device-side pieces shared by the decode kernels: kernel arguments, bf16
+// rounding, and the end-of-workgroup merge of per-wavefront softmax states.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+
+namespace pkd {
+
+constexpr int kWaves = 4;               // wavefronts per decode workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
+struct KernelArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t page_stride;
+  int64_t token_stride;
+  int64_t head_stride;
+  const int32_t* indices;
+  const float* k_scale;
+  const float* v_scale;
+  void* out;
+  float* lse;
+  const DeviceItem* items;
+  float* part_o;
+  float* part_md;
+  int num_kv_heads;
+  int num_qo_heads;
+  int page_size_log2;
+  float sm_scale_log2;  // logit scale times log2(e): scores are kept in log2 units
+  int q_bf16;
+  int out_bf16;
+};
+
+using DecodeFn = void (*)(KernelArgs);
+
+__device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+__device__ inline uint16_t float_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Shared-memory image of the wavefronts' states for the final merge.
+template <int G, int D>
+struct WaveStates {
+  float o[kWaves][G][D];  // unnormalised sums of p * v, relative to m
+  float m[kWaves][G];     // running max, log2 units (-inf: the wavefront saw no token)
+  float d[kWaves][G];     // sum of p
+};
+
+// Merge the kWaves states of every query head of the group with the
+// online-softmax rule and write either the normalised output row (and its
+// log-sum-exp) or, for a split request, the partial state (m, d, o).
+// Must be called by all threads of the workgroup after a barrier.
+template <int G, int D>
+__device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelArgs& a,
+                                        const DeviceItem& it, int kvh) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = s.m[0][h];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s.m[w][h]);
+    float O = 0.f, Dn = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = exp2f(s.m[w][h] - M);  // 0 for a wavefront without tokens
+      O = fmaf(s.o[w][h][d], sc, O);
+      Dn = fmaf(s.d[w][h], sc, Dn);
+    }
+    const int hq = kvh * G + h;
+    const int64_t row = int64_t(it.request) * a.num_qo_heads + hq;
+    if (it.partial_slot < 0) {
+      const float val = O / Dn;
+      if (a.out_bf16)
+        static_cast<uint16_t*>(a.out)[row * D + d] = float_to_bf16_rne(val);
+      else
+        static_cast<float*>(a.out)[row * D + d] = val;
+      if (a.lse && d == 0) a.lse[row] = (M + log2f(Dn)) * kLn2;
+    } else {
+      const int64_t prow = int64_t(it.partial_slot) * a.num_qo_heads + hq;
+      a.part_o[prow * D + d] = O;
+      if (d == 0) {
+        a.part_md[prow * 2 + 0] = M;
+        a.part_md[prow * 2 + 1] = Dn;
+      }
+    }
+  }
+}
+
+// Kernel selection (each translation unit provides its family).
+DecodeFn valu_decode_kernel(int kv_dtype, int head_dim, int group);
+DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int group, int page_size);
+
+}  // namespace pkd

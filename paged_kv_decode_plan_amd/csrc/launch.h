@@ -47,9 +47,11 @@ struct DecodeLaunch {
   const int32_t* merge_indptr = nullptr;    // [batch+1]
 };
 
-bool decode_supported(int kv_dtype, int head_dim, int group);
+bool decode_supported(int kv_dtype, int head_dim, int group, int q_bf16, int page_size);
+bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int q_bf16, int page_size);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
-hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int* wgs_per_cu);
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int q_bf16, int page_size,
+                            int* wgs_per_cu);
 
 }  // namespace pkd

@@ -99,8 +99,11 @@ class Plan:
                                              ctypes.c_size_t(workspace_bytes),
                                              ctypes.c_void_p(stream_ptr)))
 
-    def run_raw(self, args: "_lib.RunArgs") -> None:
-        _lib.check(self._lib.pkd_run(self._handle, ctypes.byref(args)))
+    def run_raw(self, args: "_lib.RunArgs", stages: int = _lib.STAGE_ALL) -> None:
+        if stages == _lib.STAGE_ALL:
+            _lib.check(self._lib.pkd_run(self._handle, ctypes.byref(args)))
+        else:
+            _lib.check(self._lib.pkd_run_stages(self._handle, ctypes.byref(args), stages))
 
     def close(self) -> None:
         if getattr(self, "_handle", None) and self._handle.value:
@@ -193,7 +196,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
 
     # -- run -----------------------------------------------------------------
     def run(self, q, paged_kv_cache, out=None, lse=None, return_lse: bool = False,
-            k_scale=None, v_scale=None):
+            k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL):
         import torch
         p = self._plan
         if p is None:
@@ -233,7 +236,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         a.workspace = self._ws.data_ptr()
         a.workspace_bytes = self._ws.numel() * self._ws.element_size()
         a.stream = torch.cuda.current_stream(q.device).cuda_stream
-        p.run_raw(a)
+        p.run_raw(a, stages)
         return (out, lse) if (return_lse or lse is not None) else out
 
     forward = run

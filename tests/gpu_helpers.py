@@ -104,7 +104,10 @@ def sample_request_case(dcase: dict, r: int) -> dict:
     w = dcase["workload"]
     indptr, last = dcase["indptr"], dcase["last_page_len"]
     idx = dcase["indices"]
-    pages = idx[int(indptr[r]):int(indptr[r + 1])].long()
+    if isinstance(idx, torch.Tensor):
+        idx = idx.cpu().numpy()
+    pages = torch.as_tensor(np.asarray(idx[int(indptr[r]):int(indptr[r + 1])], dtype=np.int64),
+                            device=dcase["kv"].device)
     kv = dcase["kv"].index_select(0, pages)
     if w.kv_dtype == "bf16":
         kvh = kv.view(torch.int16).cpu().numpy().view(np.uint16)

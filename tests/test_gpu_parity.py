@@ -11,7 +11,7 @@ import torch
 
 from gpu_helpers import (compare, oracle_for, out_to_f64, run_hip, sample_request_case,
                          to_device)
-from workloads import CONFIGS, custom_workload, device_case, host_case
+from workloads import CONFIGS, custom_workload, device_case, host_case, read_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -25,21 +25,25 @@ def _say(*a):
 SMALL = []
 for kv in ("f32", "bf16", "e4m3"):
     for d in (64, 128):
-        for g in (1, 2, 4, 8):
-            SMALL.append((kv, d, g))
+        for g in (1, 2, 4, 8, 16):
+            if g == 16 and (kv == "f32" or d == 64):
+                continue  # group 16 exists only on the MFMA path
+            SMALL.append((kv, d, g, "f32" if kv == "f32" else "bf16"))
+# fp32 queries over bf16 / e4m3 KV take the vector-ALU kernel
+SMALL += [("bf16", 128, 4, "f32"), ("e4m3", 128, 8, "f32"), ("bf16", 128, 1, "f32")]
 
 
-@pytest.mark.parametrize("kv,d,g", SMALL)
+@pytest.mark.parametrize("kv,d,g,qd", SMALL)
 @pytest.mark.parametrize("split", ["auto", "forced"])
-def test_small_ragged_matches_oracle(kv, d, g, split):
+def test_small_ragged_matches_oracle(kv, d, g, qd, split):
     hkv = 2
     lens = [1, 15, 16, 17, 100, 333, 700, 64, 3]
     P = 16
-    w = custom_workload(len(lens), hkv * g, hkv, d, P, kv, "bf16" if kv != "f32" else "f32", lens,
+    w = custom_workload(len(lens), hkv * g, hkv, d, P, kv, qd, lens,
                         pool_pages=sum(-(-x // P) for x in lens) + 7)
     seed = 100 + 7 * d + g
     case = host_case(w, seed, poison=True)
-    _say("small", kv, d, g, split, "seed", seed)
+    _say("small", kv, d, g, qd, split, "seed", seed)
     ref_out, ref_lse = oracle_for(case)
     dc = to_device(case)
     kw = dict(slots=4, balance=1, min_chunk_pages=1) if split == "forced" else {}
@@ -49,18 +53,19 @@ def test_small_ragged_matches_oracle(kv, d, g, split):
     compare(out, lse, ref_out, ref_lse, kv)
 
 
-@pytest.mark.parametrize("P", [1, 2, 4, 8, 32, 64, 128])
-def test_page_sizes(P):
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64, 128])
+def test_page_sizes(P, kv):
     lens = [1, P, P + 1, 3 * P + 5, 257]
-    w = custom_workload(len(lens), 8, 2, 128, P, "bf16", "bf16", lens,
+    w = custom_workload(len(lens), 8, 2, 128, P, kv, "bf16", lens,
                         pool_pages=sum(-(-x // P) for x in lens) + 3)
     case = host_case(w, 40 + P, poison=True)
-    _say("page size", P)
+    _say("page size", P, kv)
     ref_out, ref_lse = oracle_for(case)
     dc = to_device(case)
     for kw in ({}, dict(slots=8, balance=1, min_chunk_pages=1)):
         out, lse, _ = run_hip(dc, **kw)
-        compare(out, lse, ref_out, ref_lse, "bf16")
+        compare(out, lse, ref_out, ref_lse, kv)
 
 
 @pytest.mark.parametrize("kv", ["f32", "bf16", "e4m3"])
@@ -86,43 +91,74 @@ def test_single_seq_fp32_config_full():
 
 # ------------------------------------------------------------------ exact properties
 
-def _probe_case(kv_dtype, lens, P, hq, hkv, d, seed):
-    w = custom_workload(len(lens), hq, hkv, d, P, kv_dtype, "f32", lens,
+def _encode(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if kv_dtype == "f32":
+        return t.numpy()
+    if kv_dtype == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _probe_case(kv_dtype, lens, P, hq, hkv, d, seed, q_dtype="f32"):
+    """V carries the page id in base-16 digits and the slot, all small integers
+    that every KV format stores exactly; one token per request gets a logit 200
+    above all others, so every other weight is exactly 0 in fp32."""
+    w = custom_workload(len(lens), hq, hkv, d, P, kv_dtype, q_dtype, lens,
                         pool_pages=sum(-(-x // P) for x in lens) + 5)
     case = host_case(w, seed, poison=True)
     rng = np.random.default_rng(seed)
-    kv = case["kv"]
-    nanmask = np.isnan(kv) if kv_dtype == "f32" else None
-    kv[...] = 0.0
-    pages = np.arange(case["num_pages"], dtype=np.float64)
-    kv[:, 1, :, :, 0] = pages[:, None, None]
-    kv[:, 1, :, :, 1] = np.arange(P)[None, :, None]
-    case["q"][:] = 0.0
-    case["q"][:, :, 0] = 1.0
+    npg = case["num_pages"]
+    vals = np.zeros((npg, 2, P, hkv, d), np.float32)
+    pages = np.arange(npg)
+    vals[:, 1, :, :, 0] = (pages // 256)[:, None, None]
+    vals[:, 1, :, :, 1] = ((pages // 16) % 16)[:, None, None]
+    vals[:, 1, :, :, 2] = (pages % 16)[:, None, None]
+    vals[:, 1, :, :, 3] = np.arange(P)[None, :, None] % 16
+    vals[:, 1, :, :, 4] = np.arange(P)[None, :, None] // 16
+    kscale = 1.0
+    if kv_dtype == "e4m3":
+        big = 448.0
+        kscale = 200.0 * np.sqrt(d) / big
+        case["k_scale"] = np.full_like(case["k_scale"], kscale)
+        case["v_scale"] = np.ones_like(case["v_scale"])
+    else:
+        big = 200.0 * np.sqrt(d)
     targets = []
-    gap = 200.0 * np.sqrt(d)  # logit of the target exceeds all others by 200
     for r in range(len(lens)):
         t = int(rng.integers(0, lens[r]))
         page = int(case["indices"][case["indptr"][r] + t // P])
-        kv[page, 0, t % P, :, 0] = gap
+        vals[page, 0, t % P, :, 0] = big
         targets.append((page, t % P))
-    kv[nanmask] = np.nan
+    unread = ~read_mask(case, P)
+    enc = _encode(vals, kv_dtype)
+    nan = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0), "e4m3": np.uint8(0x7F)}[kv_dtype]
+    enc[:, 0][unread] = nan
+    enc[:, 1][unread] = nan
+    case["kv"] = enc
+    qv = np.zeros((len(lens), hq, d), np.float32)
+    qv[:, :, 0] = 1.0
+    case["q"] = qv if q_dtype == "f32" else _encode(qv, "bf16")
     return case, targets
 
 
+@pytest.mark.parametrize("kv,d,qd", [("f32", 64, "f32"), ("bf16", 128, "bf16"),
+                                     ("e4m3", 128, "bf16"), ("bf16", 64, "bf16")])
 @pytest.mark.parametrize("forced_split", [False, True])
-def test_gather_index_probe_bit_exact(forced_split):
+def test_gather_index_probe_bit_exact(kv, d, qd, forced_split):
     """One dominant token per request: out must equal that token's V exactly,
     which reads back (page id, slot) — the gather mapping, bit for bit."""
     lens = [1, 2, 17, 48, 255, 1000, 4096, 33]
-    P, hq, hkv, d = 16, 8, 4, 64
-    case, targets = _probe_case("f32", lens, P, hq, hkv, d, 77)
+    P, hq, hkv = 16, 8, 4
+    case, targets = _probe_case(kv, lens, P, hq, hkv, d, 77, qd)
     kw = dict(slots=16, balance=1, min_chunk_pages=1) if forced_split else {}
     out, _, info = run_hip(to_device(case), **kw)
     o = out.cpu().numpy()
     for r, (page, slot) in enumerate(targets):
-        assert np.all(o[r, :, 0] == page) and np.all(o[r, :, 1] == slot), (r, page, slot)
-        assert np.all(o[r, :, 2:] == 0)
+        got_page = o[r, :, 0] * 256 + o[r, :, 1] * 16 + o[r, :, 2]
+        got_slot = o[r, :, 3] + 16 * o[r, :, 4]
+        assert np.all(got_page == page) and np.all(got_slot == slot), (r, page, slot, o[r, 0, :5])
+        assert np.all(o[r, :, 5:] == 0)
 
 
 def test_page_permutation_invariance_bit_exact():
