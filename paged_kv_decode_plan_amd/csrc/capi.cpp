@@ -8,6 +8,7 @@
 // you actually use (Python)".
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -56,9 +57,9 @@ struct pkd_plan {
   pkd::Partition part;
   pkd_plan_info info{};
   // Device workspace layout (byte offsets).
-  size_t off_items = 0, off_split = 0, off_merge = 0, header_bytes = 0;
+  size_t off_items = 0, off_split = 0, header_bytes = 0;
   size_t off_part_md = 0, off_part_o = 0;
-  std::vector<unsigned char> header;  // host image of [items | split | merge_indptr]
+  std::vector<unsigned char> header;  // host image of [items | merge tasks]
   void* pinned = nullptr;
   hipEvent_t upload_done = nullptr;
   bool upload_pending = false;
@@ -161,8 +162,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   const size_t n_split = part.split_requests.size();
   p->off_items = 0;
   p->off_split = align256(n_items * sizeof(pkd::DeviceItem));
-  p->off_merge = align256(p->off_split + n_split * sizeof(int32_t));
-  p->header_bytes = align256(p->off_merge + (size_t(a->batch) + 1) * sizeof(int32_t));
+  p->header_bytes = align256(p->off_split + std::max<size_t>(n_split, 1) * sizeof(pkd::MergeTask));
   p->off_part_md = p->header_bytes;
   const size_t rows = size_t(part.num_partials) * size_t(a->num_qo_heads);
   p->off_part_o = align256(p->off_part_md + rows * 2 * sizeof(float));
@@ -174,10 +174,11 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     const auto& w = part.items[i];
     di[i] = {w.request, w.page_begin, w.kv_len, w.partial_slot};
   }
-  if (n_split)
-    std::memcpy(p->header.data() + p->off_split, part.split_requests.data(), n_split * 4);
-  std::memcpy(p->header.data() + p->off_merge, part.merge_indptr.data(),
-              (size_t(a->batch) + 1) * 4);
+  auto* mt = reinterpret_cast<pkd::MergeTask*>(p->header.data() + p->off_split);
+  for (size_t k = 0; k < n_split; ++k) {
+    const int32_t r = part.split_requests[k];
+    mt[k] = {r, part.merge_indptr[r], part.merge_indptr[r + 1], 0};
+  }
 
   pkd_plan_info& inf = p->info;
   inf.batch = a->batch;
@@ -307,8 +308,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.lse = r->lse;
   char* ws = static_cast<char*>(r->workspace);
   L.items = reinterpret_cast<const pkd::DeviceItem*>(ws + p->off_items);
-  L.split_requests = reinterpret_cast<const int32_t*>(ws + p->off_split);
-  L.merge_indptr = reinterpret_cast<const int32_t*>(ws + p->off_merge);
+  L.merge_tasks = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_split);
   L.part_md = reinterpret_cast<float*>(ws + p->off_part_md);
   L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
   L.num_split = p->info.num_split_requests;

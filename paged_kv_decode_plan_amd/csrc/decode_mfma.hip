@@ -10,26 +10,29 @@
 // (m, d, o) states (§"FlashDecoding — the split-KV trick"); within it the
 // running (m, d, o) is updated tile by tile with the same rule.
 //
-// Both contractions run on v_mfma_f32_16x16x32_bf16 (A: 16 x 32, B: 32 x 16,
-// fp32 C; lane l holds A row l%16 / B column l%16 for the k-slice
-// 8*(l/16)..+8, and C rows 4*(l/16)..+4 of column l%16). The order in which a
-// contraction visits its index is free as long as A and B agree; both
-// products below use that freedom so that every operand comes straight from
-// coalesced loads:
+// Both contractions run on MFMA: S = K.q^T on v_mfma_f32_16x16x32_bf16 and
+// O = P.V on v_mfma_f32_16x16x16_bf16 (lane l holds A row l%16 / B column
+// l%16 for a k-slice chosen by l/16, and C rows 4*(l/16)..+4 of column l%16).
+// The order in which a contraction visits its index is free as long as A and B
+// agree; both products use that freedom so that every operand comes straight
+// from coalesced loads. A wavefront works on 16-token tiles:
 //
-//   S = K . q^T   A = K (rows: 16 tokens), B = q^T (columns: query heads, zero
-//                 beyond G), k = head_dim in four 32-wide steps. Lane l loads
-//                 16 bytes of token l%16; the four lanes of a token read 64
-//                 contiguous bytes per instruction.
-//   O = P . V     A = P (rows: heads, k: 32 tokens), B = V (k: tokens,
+//   S = K . q^T   A = K (rows: the 16 tokens), B = q^T (columns: query heads,
+//                 zero beyond G), k = head_dim in four 32-wide steps. Lane l
+//                 loads 16 bytes of token l%16; the four lanes of a token read
+//                 64 contiguous bytes per instruction.
+//   O = P . V     A = P (rows: heads, k: the 16 tokens), B = V (k: tokens,
 //                 columns: dims). Lane l loads 16-byte chunk l%16 of a V row
 //                 (16 lanes read one whole row), so it holds dims
-//                 8*(l%16)..+8 of eight tokens; MFMA number nc (0..7) takes
+//                 8*(l%16)..+8 of four tokens; MFMA number nc (0..7) takes
 //                 element nc of each, i.e. output column j is dim 8*j + nc.
-//                 The eight tokens of lane l are exactly the eight scores
+//                 The four tokens of lane l (4*(l/16)..+4) are the four scores
 //                 that lane holds in the C layout of S, so P needs no lane
-//                 exchange: k-slot e of quarter q is token 4q+e (e < 4) or
-//                 16+4q+(e-4) (e >= 4) of the 32-token tile.
+//                 exchange.
+//
+// While one tile is computed the next one's loads are in flight (two register
+// buffers), and page ids come from a per-wavefront block of 64 tiles' ids
+// held one per lane and read with readlane, so neither waits inside the loop.
 //
 // P is fed to the bf16 MFMA as a hi + lo pair of bf16 values (two MFMAs),
 // which keeps its 16 significant bits; V is exact in bf16 (e4m3 widens to
@@ -50,12 +53,20 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 constexpr int kD = 128;
-constexpr int kTile = 32;  // tokens per wavefront tile
+constexpr int kTile = 16;       // tokens per wavefront tile
+constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 
 __device__ inline f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// k = 16 variant; operands are four bf16 bit patterns.
+__device__ inline f32x4_t mfma16(uint2 a, uint2 b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
 }
 
 // Pack the low (sel_hi = false) or high 16-bit halves of two words: lo of the
@@ -66,31 +77,52 @@ __device__ inline uint32_t pack_halves(uint32_t a, uint32_t b, bool sel_hi) {
 
 __device__ inline bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Raw buffer loads: a wavefront-uniform descriptor (the tile's first row) plus
+// a 32-bit lane offset and a wavefront-uniform offset, so a tile's loads need
+// no per-lane 64-bit address arithmetic.
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const char* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), short(0), 0x7fffffff, 0x00020000);
+}
+// Cache policy of the K and V loads. V rows are read whole (16 lanes x 16 B)
+// and exactly once, so they are marked non-temporal (NT); K rows arrive in two
+// 64-byte halves of each 128-byte line from consecutive instructions, which
+// the default policy serves from one line fill, so K keeps it. (Measured on
+// MI355X: this pair beat all-default and all-NT for bf16 and e4m3 alike.)
+#ifndef PKD_K_CPOL
+#define PKD_K_CPOL 0
+#endif
+#ifndef PKD_V_CPOL
+#define PKD_V_CPOL 2
+#endif
+template <int CPOL>
+__device__ inline u32x4_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, int(voff), int(soff), CPOL));
+}
+template <int CPOL>
+__device__ inline uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, int(voff), int(soff), CPOL));
+}
+
 // Two e4m3 bytes (half `hi` of a word) -> two bf16 (exact).
 __device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
   return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, true))
             : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, false));
 }
 
-// Token (within a 32-token tile) that k-slot e of lane quarter q stands for in
-// the P.V product; equal to the token of the lane's e-th score in the C layout
-// of S (two 16-token groups, rows 4q..4q+3 of each).
-__device__ inline int pv_token(int q, int e) { return e < 4 ? 4 * q + e : 16 + 4 * q + (e - 4); }
-
 template <int KV>
 struct Loads;
 
 template <>
 struct Loads<kBF16> {
-  u32x4_t k[2][4];  // [token group][dc]: 8 dims of token 16*tg + l%16
-  u32x4_t v[8];     // [e]: dims 8*(l%16)..+8 of token pv_token(q, e)
+  u32x4_t k[4];  // [dc]: 8 dims of token l%16
+  u32x4_t v[4];  // [e]: dims 8*(l%16)..+8 of token 4*(l/16) + e
   static constexpr int kElem = 2;
 };
 
 template <>
 struct Loads<kE4M3> {
-  u32x4_t k[2][2];  // [token group][h]: 16 dims, 64 contiguous bytes per token and instruction
-  uint2 v[8];       // [e]: dims 8*(l%16)..+8 of token pv_token(q, e)
+  u32x4_t k[2];  // [h]: 16 dims of token l%16, 64 contiguous bytes per token and instruction
+  uint2 v[4];    // [e]: dims 8*(l%16)..+8 of token 4*(l/16) + e
   static constexpr int kElem = 1;
 };
 
@@ -105,8 +137,250 @@ __device__ inline int qk_dim(int dc, int q, int e) {
     return 16 * (4 * (dc >> 1) + q) + 8 * (dc & 1) + e;
 }
 
+// Where a tile lives: with pages of at least 16 tokens a 16-token tile lies in
+// one page (tiles start at multiples of 16 and items at page boundaries), so
+// the tile needs one page id (and, for e4m3, one K and one V scale), all
+// wavefront-uniform.
+struct TilePages {
+  int64_t page;
+  float ks;
+  float vs;
+};
+
+struct Ctx {
+  const char* kbase;
+  const char* vbase;
+  const int32_t* page_ids;  // the item's slice of the page table
+  int64_t page_stride, token_stride, head_off;
+  int log2p, pmask, kv_len, q4, j;
+  // Byte offsets of this lane's first K and V load from the tile's first row
+  // (the same for every tile when a tile lies in one page); the other loads
+  // add 64 bytes (K) or one token row (V), both wavefront-uniform.
+  uint32_t koff;
+  uint32_t voff;
+  int64_t vrow_bytes;
+};
+
+// Issue every K and V load of the tile starting at token t0. Every lane
+// issues every load on every path: a token past the end of the item reads the
+// item's last token instead (its score is masked to -inf and its P weight is
+// 0, so it never contributes), which keeps the number of loads in flight the
+// same on all paths and lets the next tile's loads overlap this tile's math.
+template <int KV, bool PAGE16, bool FULL>
+__device__ inline void issue_tile(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
+  constexpr int kElem = Loads<KV>::kElem;
+  const int last = c.kv_len - 1;
+  constexpr int NK = KV == kBF16 ? 4 : 2;
+  if constexpr (PAGE16) {
+    // One page per tile: a wavefront-uniform base plus lane offsets.
+    const int64_t base =
+        (tp.page * c.page_stride + int64_t(t0 & c.pmask) * c.token_stride + c.head_off) * kElem;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase + base);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase + base);
+    uint32_t koff = c.koff;
+    if constexpr (!FULL) {
+      const int tk = min(t0 + c.j, last) - t0;
+      koff = (uint32_t(tk) * uint32_t(c.token_stride) + uint32_t(qk_dim<KV>(0, c.q4, 0))) * kElem;
+    }
+#pragma unroll
+    for (int x = 0; x < NK; ++x) ld.k[x] = bload16<PKD_K_CPOL>(kr, koff + 64 * x, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t voff, soff;
+      if constexpr (FULL) {
+        voff = c.voff;
+        soff = uint32_t(e * c.vrow_bytes);
+      } else {
+        const int tv = min(t0 + 4 * c.q4 + e, last) - t0;
+        voff = (uint32_t(tv) * uint32_t(c.token_stride) + uint32_t(8 * c.j)) * kElem;
+        soff = 0;
+      }
+      if constexpr (KV == kBF16)
+        ld.v[e] = bload16<PKD_V_CPOL>(vr, voff, soff);
+      else
+        ld.v[e] = bload8<PKD_V_CPOL>(vr, voff, soff);
+    }
+  } else {
+    {
+      const int t = FULL ? t0 + c.j : min(t0 + c.j, last);
+      const int64_t page = c.page_ids[t >> c.log2p];
+      const int64_t row = page * c.page_stride + int64_t(t & c.pmask) * c.token_stride + c.head_off;
+#pragma unroll
+      for (int x = 0; x < NK; ++x) {
+        const int dim = KV == kBF16 ? qk_dim<KV>(x, c.q4, 0) : qk_dim<KV>(2 * x, c.q4, 0);
+        ld.k[x] = *reinterpret_cast<const u32x4_t*>(c.kbase + (row + dim) * kElem);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = FULL ? t0 + 4 * c.q4 + e : min(t0 + 4 * c.q4 + e, last);
+      const int64_t page = c.page_ids[t >> c.log2p];
+      const int64_t off =
+          (page * c.page_stride + int64_t(t & c.pmask) * c.token_stride + c.head_off + 8 * c.j) *
+          kElem;
+      if constexpr (KV == kBF16)
+        ld.v[e] = *reinterpret_cast<const u32x4_t*>(c.vbase + off);
+      else
+        ld.v[e] = *reinterpret_cast<const uint2*>(c.vbase + off);
+    }
+  }
+}
+
+template <int KV, bool PAGE16>
+__device__ inline void issue(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
+  if (t0 + kTile <= c.kv_len)
+    issue_tile<KV, PAGE16, true>(ld, c, t0, tp);
+  else
+    issue_tile<KV, PAGE16, false>(ld, c, t0, tp);
+}
+
+// Per-token scale of an e4m3 page (general page sizes); a token past the
+// end reads the last token's scale (its weight is 0).
+__device__ inline float token_scale(const float* sc, const Ctx& c, const KernelArgs& a, int kvh,
+                                    int t) {
+  const int tt = min(t, c.kv_len - 1);
+  return sc[int64_t(c.page_ids[tt >> c.log2p]) * a.num_kv_heads + kvh];
+}
+
+// QK, online softmax and PV for one loaded tile (FULL: all 16 tokens valid).
+template <int KV, bool PAGE16, bool FULL>
+__device__ inline void process_tile(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
+                                    int t0, const TilePages& tp, const bf16x8_t (&qb)[4],
+                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
+  // ---- S = K . q^T: lane l gets tokens 4*q4 + r of head j
+  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (KV == kBF16) {
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) s = mfma(as_bf16x8(ld.k[dc]), qb[dc], s);
+  } else {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4_t w = ld.k[h];
+      u32x4_t lo, hi;  // dims 0..7 and 8..15 of the 16 loaded
+      lo[0] = e4m3x2_to_bf16x2(w[0], false);
+      lo[1] = e4m3x2_to_bf16x2(w[0], true);
+      lo[2] = e4m3x2_to_bf16x2(w[1], false);
+      lo[3] = e4m3x2_to_bf16x2(w[1], true);
+      hi[0] = e4m3x2_to_bf16x2(w[2], false);
+      hi[1] = e4m3x2_to_bf16x2(w[2], true);
+      hi[2] = e4m3x2_to_bf16x2(w[3], false);
+      hi[3] = e4m3x2_to_bf16x2(w[3], true);
+      s = mfma(as_bf16x8(lo), qb[2 * h], s);
+      s = mfma(as_bf16x8(hi), qb[2 * h + 1], s);
+    }
+  }
+
+  // ---- scale and mask
+  float ks = a.sm_scale_log2;
+  if constexpr (KV == kE4M3 && PAGE16) ks *= tp.ks;
+  float sc[4];
+  bool grow = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * c.q4 + r;
+    float kr = ks;
+    if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
+    const float v = (FULL || t < c.kv_len) ? s[r] * kr : -INFINITY;
+    sc[r] = v;
+    grow |= v > m_run + kSlack;
+  }
+
+  // ---- lazy reference max: p = 2^(s - m) may reach 2^kSlack; only when a
+  // score exceeds that does the wavefront move m (to the exact running max of
+  // each head) and rescale d and O by 2^(m_old - m_new). The first tile always
+  // moves it (m starts at -inf). Results do not depend on m beyond rounding.
+  if (__any(grow)) {
+    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+    m_run = m_new;
+    d_run *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float ar = __shfl(alpha, 4 * c.q4 + r, 64);
+#pragma unroll
+      for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= ar;
+    }
+  }
+
+  // ---- P (hi + lo bf16); k-slot e of quarter q4 is token 4*q4 + e
+  float p[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+    d_run += p[e];
+  }
+  if constexpr (KV == kE4M3) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float vs;
+      if constexpr (PAGE16)
+        vs = tp.vs;
+      else
+        vs = token_scale(a.v_scale, c, a, kvh, t0 + 4 * c.q4 + e);
+      p[e] *= vs;
+    }
+  }
+  uint2 p_hi, p_lo;
+  {
+    uint32_t hw[2], lw[2];
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const f32x2_t pp = {p[e], p[e + 1]};
+      const bf16x2_t h = __builtin_convertvector(pp, bf16x2_t);
+      const f32x2_t rest = pp - __builtin_convertvector(h, f32x2_t);
+      const bf16x2_t l = __builtin_convertvector(rest, bf16x2_t);
+      hw[e >> 1] = __builtin_bit_cast(uint32_t, h);
+      lw[e >> 1] = __builtin_bit_cast(uint32_t, l);
+    }
+    p_hi = uint2{hw[0], hw[1]};
+    p_lo = uint2{lw[0], lw[1]};
+  }
+
+  // ---- O += P . V, column j of MFMA nc is dim 8*j + nc
+#pragma unroll
+  for (int nc = 0; nc < 8; ++nc) {
+    uint2 vb;
+    if constexpr (KV == kBF16) {
+      const int w = nc >> 1;
+      const bool hi = nc & 1;
+      vb.x = pack_halves(ld.v[0][w], ld.v[1][w], hi);
+      vb.y = pack_halves(ld.v[2][w], ld.v[3][w], hi);
+    } else {
+      const int w = nc >> 2;           // word of the 8 loaded bytes
+      const bool hiw = (nc >> 1) & 1;  // which byte pair in the word
+      const bool hib = nc & 1;         // which byte of the pair
+      uint32_t x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = e4m3x2_to_bf16x2(w ? ld.v[e].y : ld.v[e].x, hiw);
+      vb.x = pack_halves(x[0], x[1], hib);
+      vb.y = pack_halves(x[2], x[3], hib);
+    }
+    acc[nc] = mfma16(p_hi, vb, acc[nc]);
+    acc[nc] = mfma16(p_lo, vb, acc[nc]);
+  }
+}
+
+// Page ids (and e4m3 scales) of a block of 64 consecutive tiles of one
+// wavefront, one tile per lane; read back with readlane.
+constexpr int kPidBlock = 64;
+
+template <int KV>
+__device__ inline void load_pid_block(const Ctx& c, const KernelArgs& a, int kvh, int wave,
+                                      int first_tile, int lane, int32_t& pid, float& ks,
+                                      float& vs) {
+  const int t = (wave + kWaves * (first_tile + lane)) * kTile;
+  pid = t < c.kv_len ? c.page_ids[t >> c.log2p] : 0;
+  if constexpr (KV == kE4M3) {
+    ks = t < c.kv_len ? a.k_scale[int64_t(pid) * a.num_kv_heads + kvh] : 0.f;
+    vs = t < c.kv_len ? a.v_scale[int64_t(pid) * a.num_kv_heads + kvh] : 0.f;
+  }
+}
+
 template <int KV, int G, bool PAGE16>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAGE16 ? 4 : 3))) void decode_mfma_kernel(KernelArgs a) {
   static_assert(G >= 1 && G <= 16, "at most 16 query heads per KV head");
   __shared__ WaveStates<G, kD> st;
 
@@ -114,22 +388,36 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(KernelArgs a) {
   const DeviceItem it = a.items[blockIdx.x / a.num_kv_heads];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int q4 = lane >> 4;  // lane quarter
-  const int j = lane & 15;   // row/column index inside the 16x16 tiles
-  const int log2p = a.page_size_log2;
-  const int pmask = (1 << log2p) - 1;
+
+  Ctx c;
+  c.kbase = static_cast<const char*>(a.k);
+  c.vbase = static_cast<const char*>(a.v);
+  c.page_ids = a.indices + it.page_begin;
+  c.page_stride = a.page_stride;
+  c.token_stride = a.token_stride;
+  c.head_off = int64_t(kvh) * a.head_stride;
+  c.log2p = a.page_size_log2;
+  c.pmask = (1 << a.page_size_log2) - 1;
+  c.kv_len = it.kv_len;
+  c.q4 = lane >> 4;
+  c.j = lane & 15;
+  {
+    constexpr uint32_t kElem = Loads<KV>::kElem;
+    const uint32_t ts = uint32_t(a.token_stride);
+    c.koff = (uint32_t(c.j) * ts + uint32_t(qk_dim<KV>(0, c.q4, 0))) * kElem;
+    c.voff = (uint32_t(4 * c.q4) * ts + uint32_t(8 * c.j)) * kElem;
+    c.vrow_bytes = a.token_stride * kElem;
+  }
 
   // q^T as the B operand of S = K.q^T: column j = query head kvh*G + j.
   bf16x8_t qb[4];
   {
     const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (int64_t(it.request) * a.num_qo_heads + int64_t(kvh) * G + j) * kD;
+                         (int64_t(it.request) * a.num_qo_heads + int64_t(kvh) * G + c.j) * kD;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       u32x4_t w = {0u, 0u, 0u, 0u};
-      if (j < G) {
-        w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, q4, 0));
-      }
+      if (c.j < G) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
       qb[dc] = as_bf16x8(w);
     }
   }
@@ -137,199 +425,72 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(KernelArgs a) {
   f32x4_t acc[8];
 #pragma unroll
   for (int nc = 0; nc < 8; ++nc) acc[nc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // head j, log2 units, uniform over quarters
-  float d_run = 0.f;        // head j, this lane's tokens
+  float m_run = -INFINITY;  // head j: reference max (log2 units), uniform over quarters
+  float d_run = 0.f;        // head j: sum of p over this lane's tokens
 
-  const char* kbase = static_cast<const char*>(a.k);
-  const char* vbase = static_cast<const char*>(a.v);
-  constexpr int kElem = Loads<KV>::kElem;
-  const int64_t head_off = int64_t(kvh) * a.head_stride;
-  const int32_t* page_ids = a.indices + it.page_begin;
-  const int kv_len = it.kv_len;
-
-  for (int t0 = wave * kTile; t0 < kv_len; t0 += kWaves * kTile) {
-    Loads<KV> ld;
-    float kscale[2] = {1.f, 1.f}, vscale[2] = {1.f, 1.f};
-    // ---- page lookups and loads
-    int64_t gpage[2] = {0, 0};
+  // Tiles of this wavefront: tokens [(wave + 4i) * 16, +16) for i < n.
+  const int first = wave * kTile;
+  const int n = first < c.kv_len ? (c.kv_len - first + kWaves * kTile - 1) / (kWaves * kTile) : 0;
+  if (n > 0) {
+    int32_t pid_cur = 0, pid_next = 0;
+    float ks_cur = 1.f, vs_cur = 1.f, ks_next = 1.f, vs_next = 1.f;
     if constexpr (PAGE16) {
-      // Pages of at least 16 tokens: each 16-token group lies in one page.
-#pragma unroll
-      for (int tg = 0; tg < 2; ++tg) {
-        const int tt = t0 + 16 * tg;
-        if (tt < kv_len) {
-          gpage[tg] = page_ids[tt >> log2p];
-          if constexpr (KV == kE4M3) {
-            kscale[tg] = a.k_scale[gpage[tg] * a.num_kv_heads + kvh];
-            vscale[tg] = a.v_scale[gpage[tg] * a.num_kv_heads + kvh];
-          }
+      load_pid_block<KV>(c, a, kvh, wave, 0, lane, pid_cur, ks_cur, vs_cur);
+      if (n > kPidBlock)
+        load_pid_block<KV>(c, a, kvh, wave, kPidBlock, lane, pid_next, ks_next, vs_next);
+    }
+    // Page of tile i (tiles are issued in order, so the id block only moves forward).
+    auto pages_of = [&](int i) {
+      TilePages tp;
+      tp.page = 0;
+      tp.ks = tp.vs = 1.f;
+      if constexpr (PAGE16) {
+        if (i > 0 && (i % kPidBlock) == 0) {
+          pid_cur = pid_next;
+          ks_cur = ks_next;
+          vs_cur = vs_next;
+          if (i + kPidBlock < n)
+            load_pid_block<KV>(c, a, kvh, wave, i + kPidBlock, lane, pid_next, ks_next, vs_next);
+        }
+        const int slot = i % kPidBlock;
+        tp.page = __builtin_amdgcn_readlane(pid_cur, slot);
+        if constexpr (KV == kE4M3) {
+          tp.ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ks_cur), slot));
+          tp.vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vs_cur), slot));
         }
       }
-    }
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg) {
-      const int t = t0 + 16 * tg + j;
-      const bool ok = t < kv_len;
-      int64_t page = gpage[tg];
-      if constexpr (!PAGE16) page = ok ? page_ids[t >> log2p] : 0;
-      const int64_t row = page * a.page_stride + int64_t(t & pmask) * a.token_stride + head_off;
-      if constexpr (KV == kBF16) {
-#pragma unroll
-        for (int dc = 0; dc < 4; ++dc)
-          ld.k[tg][dc] = ok ? *reinterpret_cast<const u32x4_t*>(
-                                  kbase + (row + qk_dim<KV>(dc, q4, 0)) * kElem)
-                            : u32x4_t{0u, 0u, 0u, 0u};
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-          ld.k[tg][h] = ok ? *reinterpret_cast<const u32x4_t*>(
-                                 kbase + (row + qk_dim<KV>(2 * h, q4, 0)) * kElem)
-                           : u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int tau = pv_token(q4, e);
-      const int t = t0 + tau;
-      const bool ok = t < kv_len;
-      int64_t page = gpage[tau >> 4];
-      if constexpr (!PAGE16) page = ok ? page_ids[t >> log2p] : 0;
-      const int64_t off =
-          (page * a.page_stride + int64_t(t & pmask) * a.token_stride + head_off + 8 * j) * kElem;
-      if constexpr (KV == kBF16)
-        ld.v[e] = ok ? *reinterpret_cast<const u32x4_t*>(vbase + off) : u32x4_t{0u, 0u, 0u, 0u};
-      else
-        ld.v[e] = ok ? *reinterpret_cast<const uint2*>(vbase + off) : uint2{0u, 0u};
-    }
+      return tp;
+    };
+    auto tok = [&](int i) { return first + i * kWaves * kTile; };
 
-    // ---- S = K . q^T for the two 16-token groups
-    f32x4_t s[2];
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg) {
-      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (KV == kBF16) {
-#pragma unroll
-        for (int dc = 0; dc < 4; ++dc) c = mfma(as_bf16x8(ld.k[tg][dc]), qb[dc], c);
-      } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4_t w = ld.k[tg][h];
-          u32x4_t lo, hi;  // dims 0..7 and 8..15 of the 16 loaded
-          lo[0] = e4m3x2_to_bf16x2(w[0], false);
-          lo[1] = e4m3x2_to_bf16x2(w[0], true);
-          lo[2] = e4m3x2_to_bf16x2(w[1], false);
-          lo[3] = e4m3x2_to_bf16x2(w[1], true);
-          hi[0] = e4m3x2_to_bf16x2(w[2], false);
-          hi[1] = e4m3x2_to_bf16x2(w[2], true);
-          hi[2] = e4m3x2_to_bf16x2(w[3], false);
-          hi[3] = e4m3x2_to_bf16x2(w[3], true);
-          c = mfma(as_bf16x8(lo), qb[2 * h], c);
-          c = mfma(as_bf16x8(hi), qb[2 * h + 1], c);
-        }
+    // Two tile buffers: tile i + 1 is in flight while tile i is computed. Inside
+    // the loop the next tile is always issued (full-tile code only) before the
+    // current one is computed, so the wait before each tile's math covers
+    // exactly that tile's loads. Only a wavefront's last tile can be partial;
+    // it is issued and computed after the loop.
+    Loads<KV> cur, nxt;
+    TilePages pc = pages_of(0), pn;
+    if (n == 1) {
+      issue<KV, PAGE16>(cur, c, tok(0), pc);
+      process_tile<KV, PAGE16, false>(cur, c, a, kvh, tok(0), pc, qb, acc, m_run, d_run);
+    } else {
+      issue_tile<KV, PAGE16, true>(cur, c, tok(0), pc);
+      for (int i = 0; i + 2 < n; ++i) {
+        pn = pages_of(i + 1);
+        issue_tile<KV, PAGE16, true>(nxt, c, tok(i + 1), pn);
+        process_tile<KV, PAGE16, true>(cur, c, a, kvh, tok(i), pc, qb, acc, m_run, d_run);
+        cur = nxt;
+        pc = pn;
       }
-      s[tg] = c;
-    }
-
-    // ---- scale, mask and the tile max of head j
-    float sc[8];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int tg = 0; tg < 2; ++tg) {
-      float ks = a.sm_scale_log2;
-      if constexpr (KV == kE4M3 && PAGE16) ks *= kscale[tg];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 16 * tg + 4 * q4 + r;
-        float kr = ks;
-        if constexpr (KV == kE4M3 && !PAGE16) {
-          kr = t < kv_len ? ks * a.k_scale[int64_t(page_ids[t >> log2p]) * a.num_kv_heads + kvh]
-                          : ks;
-        }
-        const float v = t < kv_len ? s[tg][r] * kr : -INFINITY;
-        sc[4 * tg + r] = v;
-        mt = fmaxf(mt, v);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);  // finite: the tile holds a valid token
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-
-    // ---- P (hi + lo bf16) in k-slot order: slot e <-> score sc[e]
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(sc[e] - m_new);
-      psum += p[e];
-    }
-    d_run = d_run * alpha + psum;
-    if constexpr (KV == kE4M3) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float vs;
-        if constexpr (PAGE16) {
-          vs = vscale[e >> 2];
-        } else {
-          const int t = t0 + pv_token(q4, e);
-          vs = t < kv_len ? a.v_scale[int64_t(page_ids[t >> log2p]) * a.num_kv_heads + kvh] : 0.f;
-        }
-        p[e] *= vs;
-      }
-    }
-    bf16x8_t p_hi, p_lo;
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const f32x2_t pp = {p[e], p[e + 1]};
-      const bf16x2_t h = __builtin_convertvector(pp, bf16x2_t);
-      const f32x2_t hf = __builtin_convertvector(h, f32x2_t);
-      const f32x2_t rest = pp - hf;
-      const bf16x2_t l = __builtin_convertvector(rest, bf16x2_t);
-      p_hi[e] = h[0];
-      p_hi[e + 1] = h[1];
-      p_lo[e] = l[0];
-      p_lo[e + 1] = l[1];
-    }
-
-    // ---- rescale O rows (heads 4*q4 + r) when any running max moved
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float ar = __shfl(alpha, 4 * q4 + r, 64);
-#pragma unroll
-        for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= ar;
-      }
-    }
-
-    // ---- O += P . V, column j of MFMA nc is dim 8*j + nc
-#pragma unroll
-    for (int nc = 0; nc < 8; ++nc) {
-      u32x4_t vb;
-      if constexpr (KV == kBF16) {
-        const int w = nc >> 1;
-        const bool hi = nc & 1;
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr)
-          vb[pr] = pack_halves(ld.v[2 * pr][w], ld.v[2 * pr + 1][w], hi);
-      } else {
-        const int w = nc >> 2;          // word of the 8 loaded bytes
-        const bool hiw = (nc >> 1) & 1;  // which byte pair in the word
-        const bool hib = nc & 1;         // which byte of the pair
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-          const uint32_t x0 = e4m3x2_to_bf16x2(w ? ld.v[2 * pr].y : ld.v[2 * pr].x, hiw);
-          const uint32_t x1 = e4m3x2_to_bf16x2(w ? ld.v[2 * pr + 1].y : ld.v[2 * pr + 1].x, hiw);
-          vb[pr] = pack_halves(x0, x1, hib);
-        }
-      }
-      const bf16x8_t vbb = as_bf16x8(vb);
-      acc[nc] = mfma(p_hi, vbb, acc[nc]);
-      acc[nc] = mfma(p_lo, vbb, acc[nc]);
+      pn = pages_of(n - 1);
+      issue<KV, PAGE16>(nxt, c, tok(n - 1), pn);
+      process_tile<KV, PAGE16, true>(cur, c, a, kvh, tok(n - 2), pc, qb, acc, m_run, d_run);
+      process_tile<KV, PAGE16, false>(nxt, c, a, kvh, tok(n - 1), pn, qb, acc, m_run, d_run);
     }
   }
 
   // ---- per-wavefront state -> shared memory
+  const int q4 = c.q4, j = c.j;
   d_run += __shfl_xor(d_run, 16, 64);
   d_run += __shfl_xor(d_run, 32, 64);
 #pragma unroll

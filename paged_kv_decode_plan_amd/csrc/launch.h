@@ -17,6 +17,15 @@ struct DeviceItem {
   int32_t partial_slot;
 };
 
+// Device-side record of one split request for the merge kernel (16 bytes):
+// its partial-state slots are [begin, end).
+struct MergeTask {
+  int32_t request;
+  int32_t begin;
+  int32_t end;
+  int32_t pad;
+};
+
 struct DecodeLaunch {
   int kv_dtype = 0;
   int head_dim = 0;
@@ -43,8 +52,7 @@ struct DecodeLaunch {
   float* part_o = nullptr;   // [num_partials, Hq, head_dim]
   float* part_md = nullptr;  // [num_partials, Hq, 2]: (m in log2 units, d)
   int num_split = 0;
-  const int32_t* split_requests = nullptr;  // [num_split]
-  const int32_t* merge_indptr = nullptr;    // [batch+1]
+  const MergeTask* merge_tasks = nullptr;  // [num_split]
 };
 
 bool decode_supported(int kv_dtype, int head_dim, int group, int q_bf16, int page_size);

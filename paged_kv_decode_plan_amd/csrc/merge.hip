@@ -3,14 +3,16 @@
 // Folds the partial (m, d, o) states that the decode kernel wrote for the
 // chunks of one request with the online-softmax merge rule of "FlashDecoding +
 // FlashInfer — the decode-time attention story", §"FlashDecoding — the
-// split-KV trick", then normalises: out = o / d, lse = m + ln d.
+// split-KV trick": m = max(m_a, m_b), d and o rescaled by exp(m_a - m) and
+// exp(m_b - m) and added; then normalises: out = o / d, lse = m + ln d
+// (partial m is kept in log2 units, so the kernel uses exp2).
 //
-// One workgroup per (split request, query head). All lanes first find the
-// largest m over the request's partials; then each wavefront folds every
-// fourth partial (each lane owning head_dim / 64 output dims, loads unrolled
-// four deep), and the four wavefront sums are added in shared memory. With
-// the common maximum the fold is a plain weighted sum, so its order does not
-// change the result beyond rounding, and the result is the same on every run.
+// One workgroup per (split request, query head). Thread (s, p) owns output
+// dims 2p, 2p+1 and folds the partials whose slot is congruent to s modulo S
+// (S = 256 / (head_dim / 2) subsets), four at a time with all their loads
+// issued first; the S subset states are then merged through shared memory.
+// The (request, first slot, end slot) record comes from the plan in one
+// 16-byte load.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -24,83 +26,81 @@ namespace {
 struct MergeArgs {
   const float* part_o;
   const float* part_md;
-  const int32_t* split_requests;
-  const int32_t* merge_indptr;
+  const MergeTask* tasks;
   void* out;
   float* lse;
   int num_qo_heads;
   int out_bf16;
 };
 
-constexpr int kMergeWaves = 4;
+constexpr int kMergeThreads = 256;
 
 template <int D>
-__global__ __launch_bounds__(kMergeWaves * 64) void merge_kernel(MergeArgs a) {
-  constexpr int PER = D / 64;  // output dims per lane
-  __shared__ float so[kMergeWaves][D];
-  __shared__ float sd[kMergeWaves];
-  const int hq = blockIdx.x % a.num_qo_heads;
-  const int r = a.split_requests[blockIdx.x / a.num_qo_heads];
-  const int b = a.merge_indptr[r];
-  const int e = a.merge_indptr[r + 1];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int64_t H = a.num_qo_heads;
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
+  constexpr int kPairs = D / 2;                  // threads per subset (two dims each)
+  constexpr int kSub = kMergeThreads / kPairs;   // partial subsets
+  __shared__ float sm[kSub], sd[kSub];
+  __shared__ float2 so[kSub][kPairs];
+  const int H = a.num_qo_heads;
+  const MergeTask t = a.tasks[blockIdx.x / H];
+  const int h = blockIdx.x % H;
+  const int sub = threadIdx.x / kPairs;
+  const int pr = threadIdx.x % kPairs;
 
-  float M = -INFINITY;
-  for (int i = b + lane; i < e; i += 64) M = fmaxf(M, a.part_md[(int64_t(i) * H + hq) * 2]);
+  const float2* md = reinterpret_cast<const float2*>(a.part_md);
+  const float2* po = reinterpret_cast<const float2*>(a.part_o);
+  float M = -INFINITY, Dn = 0.f, O0 = 0.f, O1 = 0.f;
+  constexpr int kU = 4;
+  for (int i0 = t.begin + sub; i0 < t.end; i0 += kU * kSub) {
+    float2 mdv[kU], ov[kU];
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) M = fmaxf(M, __shfl_xor(M, s, 64));
-
-  float O[PER];
+    for (int u = 0; u < kU; ++u) {
+      const int i = min(i0 + u * kSub, t.end - 1);  // a clamped repeat is skipped below
+      const int64_t row = int64_t(i) * H + h;
+      mdv[u] = md[row];
+      ov[u] = po[row * kPairs + pr];
+    }
 #pragma unroll
-  for (int k = 0; k < PER; ++k) O[k] = 0.f;
-  float Dn = 0.f;
-  constexpr int kUnroll = 4;
-  for (int i0 = b + wave; i0 < e; i0 += kMergeWaves * kUnroll) {
-    float m[kUnroll], d[kUnroll], o[kUnroll][PER];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int i = i0 + u * kMergeWaves;
-      m[u] = -INFINITY;
-      d[u] = 0.f;
-#pragma unroll
-      for (int k = 0; k < PER; ++k) o[u][k] = 0.f;
-      if (i < e) {
-        const int64_t prow = int64_t(i) * H + hq;
-        m[u] = a.part_md[prow * 2];
-        d[u] = a.part_md[prow * 2 + 1];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) o[u][k] = a.part_o[prow * D + lane * PER + k];
+    for (int u = 0; u < kU; ++u) {
+      if (i0 + u * kSub < t.end) {
+        const float m_new = fmaxf(M, mdv[u].x);
+        const float sa = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first partial
+        const float sb = __builtin_amdgcn_exp2f(mdv[u].x - m_new);
+        Dn = Dn * sa + mdv[u].y * sb;
+        O0 = O0 * sa + ov[u].x * sb;
+        O1 = O1 * sa + ov[u].y * sb;
+        M = m_new;
       }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float sc = exp2f(m[u] - M);
-      Dn = fmaf(d[u], sc, Dn);
-#pragma unroll
-      for (int k = 0; k < PER; ++k) O[k] = fmaf(o[u][k], sc, O[k]);
-    }
   }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) so[wave][lane * PER + k] = O[k];
-  if (lane == 0) sd[wave] = Dn;
+  if (pr == 0) {
+    sm[sub] = M;
+    sd[sub] = Dn;
+  }
+  so[sub][pr] = float2{O0, O1};
   __syncthreads();
-  if (threadIdx.x < D) {
-    const int dd = threadIdx.x;
-    float Ot = 0.f, Dt = 0.f;
+  if (sub == 0) {
+    float Mt = sm[0];
 #pragma unroll
-    for (int w = 0; w < kMergeWaves; ++w) {
-      Ot += so[w][dd];
-      Dt += sd[w];
+    for (int k = 1; k < kSub; ++k) Mt = fmaxf(Mt, sm[k]);
+    float Dt = 0.f, A0 = 0.f, A1 = 0.f;
+#pragma unroll
+    for (int k = 0; k < kSub; ++k) {
+      const float w = __builtin_amdgcn_exp2f(sm[k] - Mt);  // 0 for an empty subset
+      Dt += sd[k] * w;
+      A0 += so[k][pr].x * w;
+      A1 += so[k][pr].y * w;
     }
-    const int64_t row = int64_t(r) * H + hq;
-    const float val = Ot / Dt;
-    if (a.out_bf16)
-      static_cast<uint16_t*>(a.out)[row * D + dd] = float_to_bf16_rne(val);
-    else
-      static_cast<float*>(a.out)[row * D + dd] = val;
-    if (a.lse && dd == 0) a.lse[row] = (M + log2f(Dt)) * kLn2;
+    const int64_t row = int64_t(t.request) * H + h;
+    const float inv = 1.0f / Dt;
+    if (a.out_bf16) {
+      const uint32_t packed = uint32_t(float_to_bf16_rne(A0 * inv)) |
+                              (uint32_t(float_to_bf16_rne(A1 * inv)) << 16);
+      reinterpret_cast<uint32_t*>(a.out)[row * kPairs + pr] = packed;
+    } else {
+      reinterpret_cast<float2*>(a.out)[row * kPairs + pr] = float2{A0 * inv, A1 * inv};
+    }
+    if (a.lse && pr == 0) a.lse[row] = (Mt + log2f(Dt)) * kLn2;
   }
 }
 
@@ -111,18 +111,16 @@ hipError_t launch_merge(const DecodeLaunch& L, hipStream_t stream) {
   MergeArgs a;
   a.part_o = L.part_o;
   a.part_md = L.part_md;
-  a.split_requests = L.split_requests;
-  a.merge_indptr = L.merge_indptr;
+  a.tasks = L.merge_tasks;
   a.out = L.out;
   a.lse = L.lse;
   a.num_qo_heads = L.num_qo_heads;
   a.out_bf16 = L.out_bf16;
   const unsigned grid = unsigned(L.num_split) * unsigned(L.num_qo_heads);
-  const dim3 block(kMergeWaves * 64);
   if (L.head_dim == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), block, 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else if (L.head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), block, 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel<128>, dim3(grid), dim3(kMergeThreads), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -78,5 +78,5 @@ def test_workspace_size_formula():
     assert info["num_split_requests"] == 2 and info["num_partials"] > 0
     parts = info["num_partials"] * 32
     a = lambda x: (x + 255) // 256 * 256
-    header = a(a(a(info["num_items"] * 16) + info["num_split_requests"] * 4) + 3 * 4)
+    header = a(a(info["num_items"] * 16) + max(info["num_split_requests"], 1) * 16)
     assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
