@@ -58,6 +58,58 @@ def kernel_source_sha() -> str:
     return h.hexdigest()
 
 
+def decode_kernel_name(w) -> str:
+    mfma = w.kv_dtype in ("bf16", "e4m3") and w.q_dtype == "bf16" and w.head_dim == 128
+    return "decode_mfma_kernel" if mfma else "decode_kernel"
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
+    """Per-launch HBM bytes of the decode kernel from two rocprofv3 --pmc runs of
+    this bench (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).
+
+    Each counter is scaled by what it reads for kernels of known size in the
+    same run: the 1 GiB read that flushes the caches between timed steps
+    (FETCH_SIZE) and the 1 GiB zero fill of that buffer (WRITE_SIZE).
+    """
+    import csv
+
+    def rows(path, counter):
+        out = []
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    out.append((r["Kernel_Name"], int(r["Grid_Size"]), float(r["Counter_Value"])))
+        return out
+
+    gib_kib = float(1 << 20)
+    fr = rows(fetch_csv, "FETCH_SIZE")
+    wr = rows(write_csv, "WRITE_SIZE")
+    flush_reads = [v for n, g, v in fr if n.startswith("reduce_kernel")]
+    fills = [v for n, g, v in wr if n.startswith("vectorized_elementwise") and v > 0.5 * gib_kib]
+    f_scale = gib_kib / (sum(flush_reads) / len(flush_reads))
+    w_scale = gib_kib / (sum(fills) / len(fills))
+    dec_f = [v for n, g, v in fr if n.startswith("decode_")]
+    dec_w = [v for n, g, v in wr if n.startswith("decode_")]
+    fetch_b = sum(dec_f) / len(dec_f) * 1024 * f_scale
+    write_b = sum(dec_w) / len(dec_w) * 1024 * w_scale
+    return {
+        "workload": workload,
+        "kernel": next(n for n, g, v in fr if n.startswith("decode_")),
+        "dispatches": len(dec_f),
+        "fetch_kib_raw_mean": sum(dec_f) / len(dec_f),
+        "write_kib_raw_mean": sum(dec_w) / len(dec_w),
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "scale_reference": "1 GiB cache-flush read (reduce_kernel) for FETCH_SIZE; 1 GiB zero "
+                           "fill (vectorized_elementwise_kernel) for WRITE_SIZE, same runs",
+        "fetch_bytes_per_launch": fetch_b,
+        "write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "kernel_source_sha256": kernel_source_sha(),
+        "command": command,
+    }
+
+
 def load_traffic(workload: str):
     """HBM bytes per decode launch from committed rocprofv3 counter runs, if they
     were taken on the current kernel source; else None."""
@@ -143,11 +195,28 @@ def main(argv=None) -> int:
     ap.add_argument("--config", default="llama3_8b_bf16")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
+    ap.add_argument("--warm-ref", action="store_true",
+                    help="also time K back-to-back steps without cache flushes (reported "
+                         "as warm_*; off by default so that every decode launch of a run is "
+                         "cold and a profiler's per-kernel average matches the events)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--balance", type=int, default=0)
     ap.add_argument("--min-chunk-pages", type=int, default=0)
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_decode_<config>.json from two rocprofv3 "
+                         "--pmc runs of this bench and exit")
+    ap.add_argument("--counter-command", default="",
+                    help="the rocprofv3 command lines recorded with --summarize-counters")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        t = summarize_counters(*args.summarize_counters, args.config, args.counter_command)
+        path = os.path.join(ROOT, "profiles", f"traffic_decode_{args.config}.json")
+        with open(path, "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path here has no multi-GPU "
@@ -176,13 +245,22 @@ def main(argv=None) -> int:
     q_dt = dcase["q"].dtype
     kv_dt = "e4m3" if w.kv_dtype == "e4m3" else dcase["kv"].dtype
     indices_dev = torch.as_tensor(dcase["indices"], dtype=torch.int32).to(dev)
+    def do_plan():
+        wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
+                     w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
+                     kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
+                     balance=args.balance, min_chunk_pages=args.min_chunk_pages)
+        torch.cuda.synchronize()
+
     t0 = time.perf_counter()
-    wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
-                 w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt, kv_data_type=kv_dt,
-                 out_data_type=q_dt, sm_scale=w.scale(), balance=args.balance,
-                 min_chunk_pages=args.min_chunk_pages)
-    torch.cuda.synchronize()
-    plan_us = (time.perf_counter() - t0) * 1e6
+    do_plan()  # first plan of the process: device query and staging allocation
+    first_plan_us = (time.perf_counter() - t0) * 1e6
+    plan_times = []
+    for _ in range(9):  # steady state: one plan per step, shared by every layer's run()
+        t0 = time.perf_counter()
+        do_plan()
+        plan_times.append((time.perf_counter() - t0) * 1e6)
+    plan_us = statistics.median(plan_times)
     info = wrapper.plan_info
     out = torch.empty_like(dcase["q"])
     run_kw = dict(out=out, k_scale=dcase["k_scale"], v_scale=dcase["v_scale"])
@@ -204,6 +282,8 @@ def main(argv=None) -> int:
 
     print(f"[bench] plan {info}; warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
+        if not args.warm:
+            flush_i64.max()
         step()
     torch.cuda.synchronize()
 
@@ -221,14 +301,15 @@ def main(argv=None) -> int:
     step_ms = [e[0].elapsed_time(e[2]) for e in evs]
     print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
 
-    # back-to-back (warm) steps for reference
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    warm_ms = e0.elapsed_time(e1) / args.steps
+    warm_ms = None
+    if args.warm_ref:  # back-to-back steps, for reference
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        warm_ms = e0.elapsed_time(e1) / args.steps
 
     mean_step = statistics.fmean(step_ms)
     mean_dec = statistics.fmean(dec_ms)
@@ -261,15 +342,16 @@ def main(argv=None) -> int:
         "us_per_step_p10_p90": [round(q[0] * 1e3, 2), round(q[-1] * 1e3, 2)],
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "kv_bytes_per_step": nbytes,
-        "warm_us_per_step": round(warm_ms * 1e3, 2),
-        "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1),
+        "warm_us_per_step": round(warm_ms * 1e3, 2) if warm_ms else None,
+        "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1) if warm_ms else None,
         "merge_us": round(statistics.fmean(mrg_ms) * 1e3, 2),
         "plan_us_host": round(plan_us, 1),
+        "plan_us_host_first": round(first_plan_us, 1),
         "plan": {k: info[k] for k in ("chunk_pages", "num_items", "num_partials",
                                       "num_split_requests", "slots", "balance",
                                       "min_chunk_pages")},
         "roofline": {
-            "kernel": "decode_kernel",
+            "kernel": decode_kernel_name(w),
             "bound": "hbm",
             "achieved": round(dec_gbs, 1),
             "peak": PEAK_HBM_GBS,

@@ -20,8 +20,8 @@
  *     Nothing aborts the process and no C++ exception crosses this boundary.
  *   - "host" pointers are CPU memory; "device" pointers are HIP device memory
  *     on the plan's device. The caller owns every buffer passed in; the
- *     library allocates only the plan handle (host) and a small pinned staging
- *     copy of the work list.
+ *     library allocates only the plan handle (host) and pinned staging blocks
+ *     for the work-list copy, which it pools and reuses across plans.
  *   - Streams are hipStream_t passed as void*; NULL is the default stream.
  */
 #ifndef PKDECODE_H
@@ -74,7 +74,9 @@ typedef struct pkd_plan pkd_plan;
  *                   the device (compute units x resident workgroups per CU
  *                   for the selected kernel)
  *  balance          each work unit holds at most 1/balance of a slot's fair
- *                   share of the batch; 0 selects the default (2)
+ *                   share of the batch; 0 selects the default (1: one
+ *                   round of workgroups; longest-first ordering absorbs the
+ *                   raggedness)
  *  min_chunk_pages  shortest chunk a request is split into; 0 selects
  *                   ceil(256 / page_size)
  *  device           HIP device ordinal used when slots == 0
@@ -198,7 +200,9 @@ int pkd_run(const pkd_plan* plan, const pkd_run_args* args);
 #define PKD_STAGE_ALL 3
 int pkd_run_stages(const pkd_plan* plan, const pkd_run_args* args, int32_t stages);
 
-/* Free the handle (waits for an in-flight upload first). NULL is a no-op. */
+/* Free the handle. Its pinned staging block returns to a process-wide pool
+ * and is handed to another plan only after its last copy has completed, so
+ * destroying a plan never waits. NULL is a no-op. */
 void pkd_plan_destroy(pkd_plan* plan);
 
 /* Workgroups of the decode kernel selected for (q_dtype, kv_dtype, head_dim,

@@ -13,8 +13,11 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/pkdecode.h"
@@ -49,6 +52,72 @@ int ilog2(int x) {
   return r;
 }
 
+// Pinned host staging blocks for plan uploads, shared by all plans of the
+// process. A block goes back to the pool when its plan is destroyed and is
+// handed out again only once the event recorded after its last copy has
+// completed, so plan()/destroy() on the hot path allocate no pinned memory.
+struct PinnedBlock {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;  // recorded after the block's last copy
+};
+
+std::mutex g_pool_mu;
+std::vector<PinnedBlock> g_pool;
+constexpr size_t kPoolMax = 16;
+
+int pinned_acquire(size_t need, PinnedBlock* out) {
+  {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    int best = -1;
+    for (size_t i = 0; i < g_pool.size(); ++i) {
+      if (g_pool[i].bytes < need) continue;
+      if (hipEventQuery(g_pool[i].done) != hipSuccess) continue;  // still copying
+      if (best < 0 || g_pool[i].bytes < g_pool[best].bytes) best = int(i);
+    }
+    if (best >= 0) {
+      *out = g_pool[best];
+      g_pool.erase(g_pool.begin() + best);
+      return PKD_OK;
+    }
+  }
+  size_t bytes = 64 * 1024;
+  while (bytes < need) bytes *= 2;
+  PinnedBlock b;
+  b.bytes = bytes;
+  hipError_t e = hipHostMalloc(&b.ptr, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
+  e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    hipHostFree(b.ptr);
+    return fail(PKD_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+  }
+  *out = b;
+  return PKD_OK;
+}
+
+void pinned_release(PinnedBlock b) {
+  if (!b.ptr) return;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  g_pool.push_back(b);
+  while (g_pool.size() > kPoolMax) {
+    // drop the smallest block whose copy has finished
+    int victim = -1;
+    for (size_t i = 0; i < g_pool.size(); ++i)
+      if (hipEventQuery(g_pool[i].done) == hipSuccess &&
+          (victim < 0 || g_pool[i].bytes < g_pool[victim].bytes))
+        victim = int(i);
+    if (victim < 0) break;
+    hipEventDestroy(g_pool[victim].done);
+    hipHostFree(g_pool[victim].ptr);
+    g_pool.erase(g_pool.begin() + victim);
+  }
+}
+
+// Resident workgroups per CU and CU count, per (device, kernel choice).
+std::mutex g_slots_mu;
+std::map<std::tuple<int, int, int, int, int, int>, std::pair<int, int>> g_slots;
+
 }  // namespace
 
 struct pkd_plan {
@@ -60,9 +129,7 @@ struct pkd_plan {
   size_t off_items = 0, off_split = 0, header_bytes = 0;
   size_t off_part_md = 0, off_part_o = 0;
   std::vector<unsigned char> header;  // host image of [items | merge tasks]
-  void* pinned = nullptr;
-  hipEvent_t upload_done = nullptr;
-  bool upload_pending = false;
+  PinnedBlock staging;                // from the process-wide pool, on first upload
   const void* uploaded_to = nullptr;
   int device = 0;
 };
@@ -80,6 +147,17 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
   if (!pkd::decode_supported(kv_dtype, head_dim, group, q_bf16, page_size))
     return fail(PKD_ERR_UNSUPPORTED, "no kernel for kv_dtype=%d head_dim=%d group=%d q_dtype=%d",
                 kv_dtype, head_dim, group, q_dtype);
+  const auto key = std::make_tuple(int(device), int(kv_dtype), int(head_dim), int(group), q_bf16,
+                                   page_size >= 16 ? 16 : 1);
+  {
+    std::lock_guard<std::mutex> lk(g_slots_mu);
+    auto it = g_slots.find(key);
+    if (it != g_slots.end()) {
+      *wgs_per_cu = it->second.first;
+      *num_cus = it->second.second;
+      return ok();
+    }
+  }
   int prev = 0;
   hipError_t e = hipGetDevice(&prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
@@ -92,6 +170,8 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
   *wgs_per_cu = wgs;
   *num_cus = cus;
+  std::lock_guard<std::mutex> lk(g_slots_mu);
+  g_slots[key] = {wgs, cus};
   return ok();
 }
 
@@ -141,7 +221,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   pin.page_size = a->page_size;
   pin.units_per_item = a->num_kv_heads;
   pin.slots = slots;
-  pin.balance = a->balance ? a->balance : 2;
+  pin.balance = a->balance ? a->balance : 1;
   pin.min_chunk_pages = a->min_chunk_pages ? a->min_chunk_pages : (256 + a->page_size - 1) / a->page_size;
 
   pkd_plan* p = new (std::nothrow) pkd_plan();
@@ -231,27 +311,19 @@ int pkd_plan_upload(pkd_plan* p, void* workspace, size_t workspace_bytes, void* 
   if (reinterpret_cast<uintptr_t>(workspace) % 256)
     return fail(PKD_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   hipError_t e;
-  if (!p->pinned) {
-    if ((e = hipHostMalloc(&p->pinned, p->header_bytes, hipHostMallocDefault)) != hipSuccess) {
-      p->pinned = nullptr;
-      return fail(PKD_ERR_HIP, "hipHostMalloc(%zu): %s", p->header_bytes, hipGetErrorString(e));
-    }
-    if ((e = hipEventCreateWithFlags(&p->upload_done, hipEventDisableTiming)) != hipSuccess) {
-      p->upload_done = nullptr;
-      return fail(PKD_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
-    }
-  } else if (p->upload_pending) {
-    if ((e = hipEventSynchronize(p->upload_done)) != hipSuccess)
-      return fail(PKD_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
+  if (!p->staging.ptr) {
+    const int rc = pinned_acquire(p->header_bytes, &p->staging);
+    if (rc != PKD_OK) return rc;
+  } else if ((e = hipEventSynchronize(p->staging.done)) != hipSuccess) {
+    return fail(PKD_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
   }
-  std::memcpy(p->pinned, p->header.data(), p->header_bytes);
+  std::memcpy(p->staging.ptr, p->header.data(), p->header_bytes);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((e = hipMemcpyAsync(workspace, p->pinned, p->header_bytes, hipMemcpyHostToDevice, s)) !=
+  if ((e = hipMemcpyAsync(workspace, p->staging.ptr, p->header_bytes, hipMemcpyHostToDevice, s)) !=
       hipSuccess)
     return fail(PKD_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
-  if ((e = hipEventRecord(p->upload_done, s)) != hipSuccess)
+  if ((e = hipEventRecord(p->staging.done, s)) != hipSuccess)
     return fail(PKD_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
-  p->upload_pending = true;
   p->uploaded_to = workspace;
   return ok();
 }
@@ -327,9 +399,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
 
 void pkd_plan_destroy(pkd_plan* p) {
   if (!p) return;
-  if (p->upload_pending && p->upload_done) hipEventSynchronize(p->upload_done);
-  if (p->upload_done) hipEventDestroy(p->upload_done);
-  if (p->pinned) hipHostFree(p->pinned);
+  pinned_release(p->staging);  // reused only after its copy has completed
   delete p;
 }
 

@@ -8,8 +8,8 @@
 // (partial m is kept in log2 units, so the kernel uses exp2).
 //
 // One workgroup per (split request, query head). Thread (s, p) owns output
-// dims 2p, 2p+1 and folds the partials whose slot is congruent to s modulo S
-// (S = 256 / (head_dim / 2) subsets), four at a time with all their loads
+// dims 4p..4p+3 and folds the partials whose slot is congruent to s modulo S
+// (S = 512 / (head_dim / 4) subsets), four at a time with all their loads
 // issued first; the S subset states are then merged through shared memory.
 // The (request, first slot, end slot) record comes from the plan in one
 // 16-byte load.
@@ -33,32 +33,34 @@ struct MergeArgs {
   int out_bf16;
 };
 
-constexpr int kMergeThreads = 256;
+constexpr int kMergeThreads = 512;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
-  constexpr int kPairs = D / 2;                  // threads per subset (two dims each)
-  constexpr int kSub = kMergeThreads / kPairs;   // partial subsets
+  constexpr int kQuads = D / 4;                  // threads per subset (four dims each)
+  constexpr int kSub = kMergeThreads / kQuads;   // partial subsets
   __shared__ float sm[kSub], sd[kSub];
-  __shared__ float2 so[kSub][kPairs];
+  __shared__ float4 so[kSub][kQuads];
   const int H = a.num_qo_heads;
   const MergeTask t = a.tasks[blockIdx.x / H];
   const int h = blockIdx.x % H;
-  const int sub = threadIdx.x / kPairs;
-  const int pr = threadIdx.x % kPairs;
+  const int sub = threadIdx.x / kQuads;
+  const int qd = threadIdx.x % kQuads;
 
   const float2* md = reinterpret_cast<const float2*>(a.part_md);
-  const float2* po = reinterpret_cast<const float2*>(a.part_o);
-  float M = -INFINITY, Dn = 0.f, O0 = 0.f, O1 = 0.f;
+  const float4* po = reinterpret_cast<const float4*>(a.part_o);
+  float M = -INFINITY, Dn = 0.f;
+  float4 O = {0.f, 0.f, 0.f, 0.f};
   constexpr int kU = 4;
   for (int i0 = t.begin + sub; i0 < t.end; i0 += kU * kSub) {
-    float2 mdv[kU], ov[kU];
+    float2 mdv[kU];
+    float4 ov[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int i = min(i0 + u * kSub, t.end - 1);  // a clamped repeat is skipped below
       const int64_t row = int64_t(i) * H + h;
       mdv[u] = md[row];
-      ov[u] = po[row * kPairs + pr];
+      ov[u] = po[row * kQuads + qd];
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -67,40 +69,47 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
         const float sa = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first partial
         const float sb = __builtin_amdgcn_exp2f(mdv[u].x - m_new);
         Dn = Dn * sa + mdv[u].y * sb;
-        O0 = O0 * sa + ov[u].x * sb;
-        O1 = O1 * sa + ov[u].y * sb;
+        O.x = O.x * sa + ov[u].x * sb;
+        O.y = O.y * sa + ov[u].y * sb;
+        O.z = O.z * sa + ov[u].z * sb;
+        O.w = O.w * sa + ov[u].w * sb;
         M = m_new;
       }
     }
   }
-  if (pr == 0) {
+  if (qd == 0) {
     sm[sub] = M;
     sd[sub] = Dn;
   }
-  so[sub][pr] = float2{O0, O1};
+  so[sub][qd] = O;
   __syncthreads();
   if (sub == 0) {
     float Mt = sm[0];
 #pragma unroll
     for (int k = 1; k < kSub; ++k) Mt = fmaxf(Mt, sm[k]);
-    float Dt = 0.f, A0 = 0.f, A1 = 0.f;
+    float Dt = 0.f;
+    float4 A = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kSub; ++k) {
       const float w = __builtin_amdgcn_exp2f(sm[k] - Mt);  // 0 for an empty subset
       Dt += sd[k] * w;
-      A0 += so[k][pr].x * w;
-      A1 += so[k][pr].y * w;
+      A.x += so[k][qd].x * w;
+      A.y += so[k][qd].y * w;
+      A.z += so[k][qd].z * w;
+      A.w += so[k][qd].w * w;
     }
     const int64_t row = int64_t(t.request) * H + h;
     const float inv = 1.0f / Dt;
     if (a.out_bf16) {
-      const uint32_t packed = uint32_t(float_to_bf16_rne(A0 * inv)) |
-                              (uint32_t(float_to_bf16_rne(A1 * inv)) << 16);
-      reinterpret_cast<uint32_t*>(a.out)[row * kPairs + pr] = packed;
+      const uint2 packed = {
+          uint32_t(float_to_bf16_rne(A.x * inv)) | (uint32_t(float_to_bf16_rne(A.y * inv)) << 16),
+          uint32_t(float_to_bf16_rne(A.z * inv)) | (uint32_t(float_to_bf16_rne(A.w * inv)) << 16)};
+      reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] = packed;
     } else {
-      reinterpret_cast<float2*>(a.out)[row * kPairs + pr] = float2{A0 * inv, A1 * inv};
+      reinterpret_cast<float4*>(a.out)[row * kQuads + qd] =
+          float4{A.x * inv, A.y * inv, A.z * inv, A.w * inv};
     }
-    if (a.lse && pr == 0) a.lse[row] = (Mt + log2f(Dt)) * kLn2;
+    if (a.lse && qd == 0) a.lse[row] = (Mt + log2f(Dt)) * kLn2;
   }
 }
 

@@ -24,7 +24,7 @@ struct PartitionInput {
   int32_t page_size = 0;
   int32_t units_per_item = 1;  // workgroups launched per item (one per KV head)
   int32_t slots = 1;           // workgroups resident on the device at once
-  int32_t balance = 2;
+  int32_t balance = 1;
   int32_t min_chunk_pages = 1;
 };
 

@@ -67,7 +67,7 @@ def test_workload_tables_bit_exact(name, slots):
 
 def test_default_balance_and_min_chunk():
     info, *_ = pk.plan_partition([0, 5, 9], [16, 7], 4, 1, 128, 16, slots=8)
-    assert info["balance"] == 2 and info["min_chunk_pages"] == 16
+    assert info["balance"] == 1 and info["min_chunk_pages"] == 16
     info, *_ = pk.plan_partition([0, 5, 9], [16, 7], 4, 1, 128, 64, slots=8)
     assert info["min_chunk_pages"] == 4
 
