@@ -270,15 +270,21 @@ def main(argv=None) -> int:
 
     from paged_kv_decode_plan_amd import _lib
 
+    has_merge = info["num_split_requests"] > 0
+
     def step(ev=None):
+        """One run(): the decode kernel, and the merge kernel when the plan split a
+        request. Timed steps bracket the decode launch with events (and the merge
+        launch, only when there is one: an event pair costs a few µs itself)."""
         if ev is None:
             wrapper.run(dcase["q"], dcase["kv"], **run_kw)
             return
         ev[0].record()
         wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_DECODE, **run_kw)
         ev[1].record()
-        wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_MERGE, **run_kw)
-        ev[2].record()
+        if has_merge:
+            wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_MERGE, **run_kw)
+            ev[2].record()
 
     print(f"[bench] plan {info}; warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -297,8 +303,8 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
     dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    mrg_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    step_ms = [e[0].elapsed_time(e[2]) for e in evs]
+    mrg_ms = [e[1].elapsed_time(e[2]) for e in evs] if has_merge else [0.0]
+    step_ms = [e[0].elapsed_time(e[2 if has_merge else 1]) for e in evs]
     print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
 
     warm_ms = None

@@ -13,12 +13,17 @@ The rule adopted (a reading; the design doc lists it):
 1. ``n_r = indptr[r+1] - indptr[r]`` pages and
    ``L_r = (n_r - 1) * P + last_page_len[r]`` tokens per request.
 2. With ``S = sum_r n_r``, ``N = max_r n_r``, ``H`` work units per item (one
-   per KV head) and ``slots`` workgroups resident on the device at once, the
-   chunk length in pages is
-   ``C = min(N, max(C_min, ceil(S * H / (slots * balance))))``:
-   no work unit is longer than ``1/balance`` of a slot's fair share of the
-   batch, nor shorter than ``C_min`` pages (which bounds the partial-state
-   traffic), and nothing is split that fits in one chunk.
+   per KV head) and ``slots`` workgroups resident on the device at once:
+
+   * a batch of near-equal requests (``8 * N * B <= 9 * S``: the longest is
+     within 1/8 of the mean) that already yields at least half the resident
+     slots in work units (``2 * B * H >= slots``) is not split: ``C = N``;
+     splitting it would add partial states and a merge without evening
+     anything out;
+   * otherwise ``C = min(N, max(C_min, ceil(S * H / (slots * balance))))``:
+     no work unit is longer than ``1/balance`` of a slot's fair share of the
+     batch, nor shorter than ``C_min`` pages (which bounds the partial-state
+     traffic), and nothing is split that fits in one chunk.
 3. Request r becomes ``G_r = ceil(n_r / C)`` items; chunk c covers pages
    ``[indptr[r] + c*C, min(indptr[r] + (c+1)*C, indptr[r+1]))``; its token count
    drops ``P - last_page_len[r]`` when it holds the request's last page.
@@ -45,6 +50,8 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
     indptr = [int(x) for x in indptr]
     last = [int(x) for x in last_page_len]
     B = len(last)
+    if B < 1:
+        raise ValueError("the batch needs at least one request")
     if len(indptr) != B + 1 or indptr[0] != 0:
         raise ValueError("indptr must have batch+1 entries starting at 0")
     n = [indptr[r + 1] - indptr[r] for r in range(B)]
@@ -56,9 +63,12 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
         raise ValueError("slots, balance and min_chunk_pages must be positive")
 
     S = sum(n)
-    N = max(n) if B else 0
-    cap = _ceil_div(S * num_kv_heads, slots * balance) if B else 0
-    C = min(N, max(min_chunk_pages, cap)) if B else 0
+    N = max(n)
+    if 8 * N * B <= 9 * S and 2 * B * num_kv_heads >= slots:
+        C = N
+    else:
+        cap = _ceil_div(S * num_kv_heads, slots * balance)
+        C = min(N, max(min_chunk_pages, cap))
 
     G = [_ceil_div(x, C) for x in n]
     merge_indptr = [0]

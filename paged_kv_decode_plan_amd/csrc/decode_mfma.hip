@@ -384,8 +384,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAGE16
   static_assert(G >= 1 && G <= 16, "at most 16 query heads per KV head");
   __shared__ WaveStates<G, kD> st;
 
-  const int kvh = blockIdx.x % a.num_kv_heads;
-  const DeviceItem it = a.items[blockIdx.x / a.num_kv_heads];
+  int item, kvh;
+  decode_block(a.num_kv_heads, a.xcd_group, &item, &kvh);
+  if (item >= a.num_items) return;  // grid padding; no barrier passed yet
+  const DeviceItem it = a.items[item];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 

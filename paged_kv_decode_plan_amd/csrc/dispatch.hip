@@ -43,13 +43,15 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.items = L.items;
   a.part_o = L.part_o;
   a.part_md = L.part_md;
+  a.num_items = L.num_items;
+  a.xcd_group = L.kv_dtype == kE4M3 ? 8 : 1;
   a.num_kv_heads = L.num_kv_heads;
   a.num_qo_heads = L.num_qo_heads;
   a.page_size_log2 = L.page_size_log2;
   a.sm_scale_log2 = L.sm_scale_log2;
   a.q_bf16 = L.q_bf16;
   a.out_bf16 = L.out_bf16;
-  const unsigned grid = unsigned(L.num_items) * unsigned(L.num_kv_heads);
+  const unsigned grid = decode_grid_size(L.num_items, L.num_kv_heads, a.xcd_group);
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

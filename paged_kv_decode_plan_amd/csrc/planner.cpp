@@ -45,8 +45,20 @@ std::string build_partition(const PartitionInput& in, Partition* out) {
   }
   if (total_pages > INT32_MAX) return "page table longer than 2^31 entries";
 
-  const int64_t cap = ceil_div(total_pages * in.units_per_item, int64_t(in.slots) * in.balance);
-  const int64_t C = std::min<int64_t>(max_pages, std::max<int64_t>(in.min_chunk_pages, cap));
+  // A batch of near-equal requests that already yields at least half the
+  // resident slots in work units is left whole: splitting it would only add
+  // partial states and a merge. Otherwise bound every work unit by
+  // 1/balance of a resident slot's fair share (and by min_chunk_pages below).
+  int64_t C;
+  const bool near_equal = 8 * max_pages * B <= 9 * total_pages;
+  const bool enough_units = 2 * int64_t(B) * in.units_per_item >= in.slots;
+  if (near_equal && enough_units) {
+    C = max_pages;
+  } else {
+    const int64_t cap =
+        ceil_div(total_pages * in.units_per_item, int64_t(in.slots) * in.balance);
+    C = std::min<int64_t>(max_pages, std::max<int64_t>(in.min_chunk_pages, cap));
+  }
 
   Partition p;
   p.chunk_pages = int32_t(C);

@@ -38,9 +38,12 @@ struct Partition {
 };
 
 // Returns an empty string on success, else a description of what is wrong
-// with the page table. The rule: chunk length
-//   C = min(max_pages, max(min_chunk_pages, ceil(total_pages * units / (slots * balance))))
-// so that no work unit exceeds 1/balance of one slot's fair share; request r
+// with the page table. The rule: a batch whose longest request is within 1/8
+// of the mean (8 N B <= 9 S) and that gives at least half the resident slots
+// in work units (2 B units >= slots) is not split (C = N); otherwise the chunk
+// length is
+//   C = min(N, max(min_chunk_pages, ceil(S * units / (slots * balance))))
+// so that no work unit exceeds 1/balance of one slot's fair share. Request r
 // becomes ceil(n_r / C) items; items are ordered by descending token count,
 // ties by request then chunk index.
 std::string build_partition(const PartitionInput& in, Partition* out);

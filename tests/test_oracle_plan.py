@@ -14,7 +14,7 @@ def test_hand_worked_partitions():
     with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
         ex = json.load(f)
     for c in ex["cases"]:
-        p = oplan.plan(ex["indptr"], ex["last_page_len"], ex["page_size"], ex["num_kv_heads"],
+        p = oplan.plan(c["indptr"], c["last_page_len"], ex["page_size"], ex["num_kv_heads"],
                        c["slots"], c["balance"], c["min_chunk_pages"])
         assert p["chunk_pages"] == c["chunk_pages"], c["work"]
         assert p["items"].tolist() == c["items"], c["work"]
@@ -44,7 +44,10 @@ def test_partition_invariants(seed):
     L = (n - 1) * P + last
     S, N = int(n.sum()), int(n.max())
     # chunk length: the closed form, and its bounds
-    assert C == min(N, max(cmin, -(-(S * hkv) // (slots * balance))))
+    if 8 * N * B <= 9 * S and 2 * B * hkv >= slots:
+        assert C == N
+    else:
+        assert C == min(N, max(cmin, -(-(S * hkv) // (slots * balance))))
     assert 1 <= C <= N
     items = p["items"]
     # coverage: per request, chunks tile its page range in order, tokens add up
@@ -73,8 +76,19 @@ def test_partition_invariants(seed):
 def test_uniform_batch_that_fills_the_device_is_not_split():
     indptr = np.arange(0, 65 * 4, 4, dtype=np.int32)
     last = np.full(64, 16, np.int32)
-    p = oplan.plan(indptr, last, 16, 8, slots=64, balance=1, min_chunk_pages=1)
+    # 64 requests x 8 heads = 512 units >= half of 1024 slots: left whole
+    p = oplan.plan(indptr, last, 16, 8, slots=1024, balance=1, min_chunk_pages=1)
     assert p["chunk_pages"] == 4 and p["num_partials"] == 0
+    # twice as many slots: not enough units, split to the balance bound
+    p = oplan.plan(indptr, last, 16, 8, slots=2048, balance=1, min_chunk_pages=1)
+    assert p["chunk_pages"] == 1 and p["num_partials"] == 256
+
+
+def test_unequal_batch_is_split_even_with_enough_units():
+    indptr = np.concatenate([[0], np.cumsum([128] * 63 + [300])]).astype(np.int32)
+    last = np.full(64, 16, np.int32)
+    p = oplan.plan(indptr, last, 16, 8, slots=1024, balance=1, min_chunk_pages=16)
+    assert p["chunk_pages"] < 300 and p["num_partials"] > 0
 
 
 @pytest.mark.parametrize("bad", [

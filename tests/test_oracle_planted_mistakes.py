@@ -122,7 +122,7 @@ def test_plan_mutants_are_caught(mutant, monkeypatch):
     with open(os.path.join(os.path.dirname(__file__), "golden", "plan_worked_example.json")) as f:
         ex = json.load(f)
     c = ex["cases"][1]
-    p = oplan.plan(ex["indptr"], ex["last_page_len"], ex["page_size"], 1, c["slots"],
+    p = oplan.plan(c["indptr"], c["last_page_len"], ex["page_size"], 1, c["slots"],
                    c["balance"], c["min_chunk_pages"])
     items = p["items"].copy()
     if mutant == "off_by_one_kvlen":

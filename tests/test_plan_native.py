@@ -34,7 +34,7 @@ def test_golden_partitions_native():
     with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
         ex = json.load(f)
     for c in ex["cases"]:
-        info, items, merge, split, ref = _both(ex["indptr"], ex["last_page_len"], ex["page_size"],
+        info, items, merge, split, ref = _both(c["indptr"], c["last_page_len"], ex["page_size"],
                                                1, c["slots"], c["balance"], c["min_chunk_pages"])
         assert items.tolist() == c["items"]
         _assert_same(info, items, merge, split, ref)
