@@ -56,8 +56,21 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 typedef __attribute__((ext_vector_type(4))) short i16x4_t;
 
 constexpr int kD = 128;
-constexpr int kTile = 16;       // tokens per wavefront tile
+constexpr int kSub = 16;        // tokens per MFMA sub-tile
 constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
+
+// Sub-tiles per wavefront tile: a tile should bring about 8 KiB of K and V
+// per wavefront, so e4m3 (128-byte rows) takes two 16-token sub-tiles.
+#ifndef PKD_E4M3_NSUB
+#define PKD_E4M3_NSUB 2
+#endif
+#ifndef PKD_BF16_NSUB
+#define PKD_BF16_NSUB 1
+#endif
+template <int KV>
+constexpr int nsub() { return KV == kE4M3 ? PKD_E4M3_NSUB : PKD_BF16_NSUB; }
+template <int KV>
+constexpr int tile_tokens() { return kSub * nsub<KV>(); }
 
 __device__ inline f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -137,10 +150,12 @@ __device__ inline int qk_dim(int dc, int q, int e) {
     return 16 * (4 * (dc >> 1) + q) + 8 * (dc & 1) + e;
 }
 
-// Where a tile lives: with pages of at least 16 tokens a 16-token tile lies in
-// one page (tiles start at multiples of 16 and items at page boundaries), so
-// the tile needs one page id (and, for e4m3, one K and one V scale), all
-// wavefront-uniform.
+// Where a sub-tile lives: with pages of at least 16 tokens a 16-token
+// sub-tile lies in one page (sub-tiles start at multiples of 16 and items at
+// page boundaries), so it needs one page id (and, for e4m3, one K and one V
+// scale), all wavefront-uniform. A sub-tile wholly past the item's end is
+// given the page of the item's last sub-tile (its loads repeat valid tokens
+// and its weights are 0).
 struct TilePages {
   int64_t page;
   float ks;
@@ -161,25 +176,29 @@ struct Ctx {
   int64_t vrow_bytes;
 };
 
-// Issue every K and V load of the tile starting at token t0. Every lane
-// issues every load on every path: a token past the end of the item reads the
-// item's last token instead (its score is masked to -inf and its P weight is
-// 0, so it never contributes), which keeps the number of loads in flight the
-// same on all paths and lets the next tile's loads overlap this tile's math.
+// Issue every K and V load of the 16-token sub-tile starting at token t0.
+// Every lane issues every load on every path: a token past the end of the
+// item reads the item's last token instead (its score is masked to -inf and
+// its P weight is 0, so it never contributes), which keeps the number of loads
+// in flight the same on all paths and lets the next tile's loads overlap this
+// tile's math.
 template <int KV, bool PAGE16, bool FULL>
-__device__ inline void issue_tile(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
+__device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
   constexpr int kElem = Loads<KV>::kElem;
   const int last = c.kv_len - 1;
   constexpr int NK = KV == kBF16 ? 4 : 2;
   if constexpr (PAGE16) {
-    // One page per tile: a wavefront-uniform base plus lane offsets.
+    // One page per sub-tile: a wavefront-uniform base plus lane offsets. A
+    // sub-tile past the end loads from the last sub-tile's rows (tp.page is
+    // that sub-tile's page).
+    const int tb = FULL ? t0 : min(t0, last & ~(kSub - 1));
     const int64_t base =
-        (tp.page * c.page_stride + int64_t(t0 & c.pmask) * c.token_stride + c.head_off) * kElem;
+        (tp.page * c.page_stride + int64_t(tb & c.pmask) * c.token_stride + c.head_off) * kElem;
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase + base);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase + base);
     uint32_t koff = c.koff;
     if constexpr (!FULL) {
-      const int tk = min(t0 + c.j, last) - t0;
+      const int tk = min(t0 + c.j, last) - tb;
       koff = (uint32_t(tk) * uint32_t(c.token_stride) + uint32_t(qk_dim<KV>(0, c.q4, 0))) * kElem;
     }
 #pragma unroll
@@ -191,7 +210,7 @@ __device__ inline void issue_tile(Loads<KV>& ld, const Ctx& c, int t0, const Til
         voff = c.voff;
         soff = uint32_t(e * c.vrow_bytes);
       } else {
-        const int tv = min(t0 + 4 * c.q4 + e, last) - t0;
+        const int tv = min(t0 + 4 * c.q4 + e, last) - tb;
         voff = (uint32_t(tv) * uint32_t(c.token_stride) + uint32_t(8 * c.j)) * kElem;
         soff = 0;
       }
@@ -226,12 +245,25 @@ __device__ inline void issue_tile(Loads<KV>& ld, const Ctx& c, int t0, const Til
   }
 }
 
-template <int KV, bool PAGE16>
-__device__ inline void issue(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
-  if (t0 + kTile <= c.kv_len)
-    issue_tile<KV, PAGE16, true>(ld, c, t0, tp);
-  else
-    issue_tile<KV, PAGE16, false>(ld, c, t0, tp);
+// A wavefront tile: nsub<KV>() consecutive sub-tiles, loaded together.
+template <int KV>
+struct Tile {
+  Loads<KV> sub[nsub<KV>()];
+};
+template <int KV>
+struct TileP {
+  TilePages sub[nsub<KV>()];
+};
+
+template <int KV, bool PAGE16, bool FULL>
+__device__ inline void issue_tile(Tile<KV>& T, const Ctx& c, int t0, const TileP<KV>& tp) {
+#pragma unroll
+  for (int s = 0; s < nsub<KV>(); ++s) {
+    if (FULL || t0 + kSub * (s + 1) <= c.kv_len)
+      issue_sub<KV, PAGE16, true>(T.sub[s], c, t0 + kSub * s, tp.sub[s]);
+    else
+      issue_sub<KV, PAGE16, false>(T.sub[s], c, t0 + kSub * s, tp.sub[s]);
+  }
 }
 
 // Per-token scale of an e4m3 page (general page sizes); a token past the
@@ -242,9 +274,9 @@ __device__ inline float token_scale(const float* sc, const Ctx& c, const KernelA
   return sc[int64_t(c.page_ids[tt >> c.log2p]) * a.num_kv_heads + kvh];
 }
 
-// QK, online softmax and PV for one loaded tile (FULL: all 16 tokens valid).
+// QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens valid).
 template <int KV, bool PAGE16, bool FULL>
-__device__ inline void process_tile(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
+__device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
                                     int t0, const TilePages& tp, const bf16x8_t (&qb)[4],
                                     f32x4_t (&acc)[8], float& m_run, float& d_run) {
   // ---- S = K . q^T: lane l gets tokens 4*q4 + r of head j
@@ -363,24 +395,44 @@ __device__ inline void process_tile(const Loads<KV>& ld, const Ctx& c, const Ker
   }
 }
 
-// Page ids (and e4m3 scales) of a block of 64 consecutive tiles of one
-// wavefront, one tile per lane; read back with readlane.
-constexpr int kPidBlock = 64;
+template <int KV, bool PAGE16, bool FULL>
+__device__ inline void process_tile(const Tile<KV>& T, const Ctx& c, const KernelArgs& a, int kvh,
+                                    int t0, const TileP<KV>& tp, const bf16x8_t (&qb)[4],
+                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
+#pragma unroll
+  for (int s = 0; s < nsub<KV>(); ++s)
+    process_sub<KV, PAGE16, FULL>(T.sub[s], c, a, kvh, t0 + kSub * s, tp.sub[s], qb, acc, m_run,
+                                  d_run);
+}
+
+// Page ids (and e4m3 scales) of a block of consecutive tiles of one
+// wavefront, one sub-tile per lane (64 sub-tiles per block); read back with
+// readlane. A sub-tile past the item's end takes the last sub-tile's page.
+template <int KV>
+constexpr int pid_block_tiles() { return 64 / nsub<KV>(); }
 
 template <int KV>
 __device__ inline void load_pid_block(const Ctx& c, const KernelArgs& a, int kvh, int wave,
                                       int first_tile, int lane, int32_t& pid, float& ks,
                                       float& vs) {
-  const int t = (wave + kWaves * (first_tile + lane)) * kTile;
-  pid = t < c.kv_len ? c.page_ids[t >> c.log2p] : 0;
+  const int tile = first_tile + lane / nsub<KV>();
+  const int t = (wave + kWaves * tile) * tile_tokens<KV>() + kSub * (lane % nsub<KV>());
+  const int tt = min(t, (c.kv_len - 1) & ~(kSub - 1));
+  pid = c.page_ids[tt >> c.log2p];
   if constexpr (KV == kE4M3) {
-    ks = t < c.kv_len ? a.k_scale[int64_t(pid) * a.num_kv_heads + kvh] : 0.f;
-    vs = t < c.kv_len ? a.v_scale[int64_t(pid) * a.num_kv_heads + kvh] : 0.f;
+    ks = a.k_scale[int64_t(pid) * a.num_kv_heads + kvh];
+    vs = a.v_scale[int64_t(pid) * a.num_kv_heads + kvh];
   }
 }
 
+// Register budget: 128 VGPRs (4 wavefronts per SIMD) when a tile is one
+// 16-token sub-tile of pages >= 16; larger tiles and per-lane page lookups need
+// up to 168 (3 wavefronts per SIMD).
+template <int KV, bool PAGE16>
+constexpr int waves_per_simd() { return PAGE16 && nsub<KV>() == 1 ? 4 : 3; }
+
 template <int KV, int G, bool PAGE16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAGE16 ? 4 : 3))) void decode_mfma_kernel(KernelArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16>()))) void decode_mfma_kernel(KernelArgs a) {
   static_assert(G >= 1 && G <= 16, "at most 16 query heads per KV head");
   __shared__ WaveStates<G, kD> st;
 
@@ -430,50 +482,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAGE16
   float m_run = -INFINITY;  // head j: reference max (log2 units), uniform over quarters
   float d_run = 0.f;        // head j: sum of p over this lane's tokens
 
-  // Tiles of this wavefront: tokens [(wave + 4i) * 16, +16) for i < n.
-  const int first = wave * kTile;
-  const int n = first < c.kv_len ? (c.kv_len - first + kWaves * kTile - 1) / (kWaves * kTile) : 0;
+  // Tiles of this wavefront: tokens [(wave + 4i) * TT, +TT) for i < n, with
+  // TT = tile_tokens<KV>().
+  constexpr int TT = tile_tokens<KV>();
+  constexpr int NS = nsub<KV>();
+  constexpr int kBlk = pid_block_tiles<KV>();
+  const int first = wave * TT;
+  const int n = first < c.kv_len ? (c.kv_len - first + kWaves * TT - 1) / (kWaves * TT) : 0;
   if (n > 0) {
     int32_t pid_cur = 0, pid_next = 0;
     float ks_cur = 1.f, vs_cur = 1.f, ks_next = 1.f, vs_next = 1.f;
     if constexpr (PAGE16) {
       load_pid_block<KV>(c, a, kvh, wave, 0, lane, pid_cur, ks_cur, vs_cur);
-      if (n > kPidBlock)
-        load_pid_block<KV>(c, a, kvh, wave, kPidBlock, lane, pid_next, ks_next, vs_next);
+      if (n > kBlk) load_pid_block<KV>(c, a, kvh, wave, kBlk, lane, pid_next, ks_next, vs_next);
     }
-    // Page of tile i (tiles are issued in order, so the id block only moves forward).
+    // Pages of tile i (tiles are issued in order, so the id block only moves forward).
     auto pages_of = [&](int i) {
-      TilePages tp;
-      tp.page = 0;
-      tp.ks = tp.vs = 1.f;
+      TileP<KV> tp;
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        tp.sub[s2].page = 0;
+        tp.sub[s2].ks = tp.sub[s2].vs = 1.f;
+      }
       if constexpr (PAGE16) {
-        if (i > 0 && (i % kPidBlock) == 0) {
+        if (i > 0 && (i % kBlk) == 0) {
           pid_cur = pid_next;
           ks_cur = ks_next;
           vs_cur = vs_next;
-          if (i + kPidBlock < n)
-            load_pid_block<KV>(c, a, kvh, wave, i + kPidBlock, lane, pid_next, ks_next, vs_next);
+          if (i + kBlk < n)
+            load_pid_block<KV>(c, a, kvh, wave, i + kBlk, lane, pid_next, ks_next, vs_next);
         }
-        const int slot = i % kPidBlock;
-        tp.page = __builtin_amdgcn_readlane(pid_cur, slot);
-        if constexpr (KV == kE4M3) {
-          tp.ks = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ks_cur), slot));
-          tp.vs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vs_cur), slot));
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) {
+          const int slot = (i % kBlk) * NS + s2;
+          tp.sub[s2].page = __builtin_amdgcn_readlane(pid_cur, slot);
+          if constexpr (KV == kE4M3) {
+            tp.sub[s2].ks = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ks_cur), slot));
+            tp.sub[s2].vs = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vs_cur), slot));
+          }
         }
       }
       return tp;
     };
-    auto tok = [&](int i) { return first + i * kWaves * kTile; };
+    auto tok = [&](int i) { return first + i * kWaves * TT; };
 
     // Two tile buffers: tile i + 1 is in flight while tile i is computed. Inside
     // the loop the next tile is always issued (full-tile code only) before the
     // current one is computed, so the wait before each tile's math covers
     // exactly that tile's loads. Only a wavefront's last tile can be partial;
     // it is issued and computed after the loop.
-    Loads<KV> cur, nxt;
-    TilePages pc = pages_of(0), pn;
+    Tile<KV> cur, nxt;
+    TileP<KV> pc = pages_of(0), pn;
     if (n == 1) {
-      issue<KV, PAGE16>(cur, c, tok(0), pc);
+      issue_tile<KV, PAGE16, false>(cur, c, tok(0), pc);
       process_tile<KV, PAGE16, false>(cur, c, a, kvh, tok(0), pc, qb, acc, m_run, d_run);
     } else {
       issue_tile<KV, PAGE16, true>(cur, c, tok(0), pc);
@@ -485,7 +548,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(PAGE16
         pc = pn;
       }
       pn = pages_of(n - 1);
-      issue<KV, PAGE16>(nxt, c, tok(n - 1), pn);
+      issue_tile<KV, PAGE16, false>(nxt, c, tok(n - 1), pn);
       process_tile<KV, PAGE16, true>(cur, c, a, kvh, tok(n - 2), pc, qb, acc, m_run, d_run);
       process_tile<KV, PAGE16, false>(nxt, c, a, kvh, tok(n - 1), pn, qb, acc, m_run, d_run);
     }
