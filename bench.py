@@ -13,7 +13,9 @@ KV; HIP events on the launch stream bracket the decode kernel and the merge
 kernel of every step separately. ``value`` is KV-read GB/s over the whole
 step (algorithmic KV bytes / mean step time). ``roofline`` is for the decode
 kernel alone. ``cpu_baseline`` times the float64 oracle on a bounded sample
-of the same batch on one host core.
+of the same batch on one host core (and its ``parallel`` entry, the same
+sample on a thread pool over the host cores); ``calibration`` is a plain
+1 GiB streaming read timed on the same device.
 
 Prints one JSON line.
 """
@@ -123,25 +125,98 @@ def load_traffic(workload: str):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(dcase, w, budget_s: float = 12.0):
-    """The oracle, as it stands, on whole requests of the same batch until about
-    `budget_s` seconds of single-threaded CPU work have been spent."""
+def _oracle_request(w, item):
+    """The oracle on one request already copied to host memory (one sample task)."""
+    import numpy as np
+
+    from oracle import attention
+
+    qh, kvh, n, last, ks, vs = item
+    return attention.decode(qh, kvh, np.array([0, n], np.int32), np.arange(n, dtype=np.int32),
+                            np.array([last], np.int32), num_kv_heads=w.num_kv_heads,
+                            q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, sm_scale=w.scale(),
+                            k_scale=ks, v_scale=vs)
+
+
+def _pool_worker(conn):
+    """A single-threaded oracle worker: receive its requests, wait for the start
+    signal, compute them, report the time taken."""
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[var] = "1"
+    w, items = conn.recv()
+    _oracle_request(w, items[0]) if items else None  # imports and first-touch outside timing
+    conn.send("ready")
+    conn.recv()
+    t0 = time.perf_counter()
+    for it in items:
+        _oracle_request(w, it)
+    conn.send(time.perf_counter() - t0)
+    conn.close()
+
+
+def _oracle_pool(w, items, workers: int) -> float:
+    """Wall seconds for `workers` processes to run the oracle on `items`, which
+    are assigned longest first to the least-loaded worker before timing."""
+    import multiprocessing as mp
+
+    ctx = mp.get_context("spawn")  # fresh interpreters: no device state is inherited
+    shares = [[] for _ in range(workers)]
+    load = [0] * workers
+    for it in sorted(items, key=lambda it: -it[1].nbytes):
+        k = load.index(min(load))
+        shares[k].append(it)
+        load[k] += it[1].nbytes
+    procs, conns = [], []
+    try:
+        for k in range(workers):
+            parent, child = ctx.Pipe()
+            p = ctx.Process(target=_pool_worker, args=(child,), daemon=True)
+            p.start()
+            procs.append(p)
+            conns.append(parent)
+        for c, share in zip(conns, shares):
+            c.send((w, share))
+        for c in conns:
+            if c.recv() != "ready":
+                raise RuntimeError("oracle worker failed to start")
+        t0 = time.perf_counter()
+        for c in conns:
+            c.send("go")
+        for c in conns:
+            c.recv()
+        return time.perf_counter() - t0
+    finally:
+        for p in procs:
+            p.join(timeout=60)
+            if p.is_alive():
+                p.terminate()
+
+
+def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
+    """The oracle, as it stands, on whole requests of the same batch.
+
+    Single thread: requests in batch order until about `budget_s` seconds of
+    CPU work have been spent. Parallel: the same requests (up to `keep_bytes`
+    of host KV) again, spread by KV bytes over worker processes, one per host
+    core this process may use (at most 16), each single-threaded. Copying KV to
+    the host and handing it to the workers is outside both timings.
+    """
     from threadpoolctl import threadpool_limits
 
     import numpy as np
     import torch
 
-    from oracle import attention
-
     lens = dcase["kv_lens"]
-    order = list(range(len(lens)))
     done_bytes = 0
     done = []
+    kept = []
+    kept_bytes = 0
+    kept_kv = 0
     elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
     t_total = 0.0
     idx = dcase["indices"]
     with threadpool_limits(limits=1):
-        for r in order:
+        for r in range(len(lens)):
             pages = torch.as_tensor(np.asarray(idx[int(dcase["indptr"][r]):int(dcase["indptr"][r + 1])],
                                                dtype=np.int64), device=dcase["kv"].device)
             kv = dcase["kv"].index_select(0, pages)
@@ -158,18 +233,23 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0):
             if w.kv_dtype == "e4m3":
                 ks = dcase["k_scale"].index_select(0, pages).cpu().numpy()
                 vs = dcase["v_scale"].index_select(0, pages).cpu().numpy()
-            n = len(pages)
+            item = (qh, kvh, len(pages), int(dcase["last_page_len"][r]), ks, vs)
             t0 = time.perf_counter()
-            attention.decode(qh, kvh, np.array([0, n], np.int32), np.arange(n, dtype=np.int32),
-                             np.array([dcase["last_page_len"][r]], np.int32),
-                             num_kv_heads=w.num_kv_heads, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                             sm_scale=w.scale(), k_scale=ks, v_scale=vs)
+            _oracle_request(w, item)
             t_total += time.perf_counter() - t0
             done.append(r)
-            done_bytes += int(lens[r]) * w.num_kv_heads * w.head_dim * 2 * elem
+            req_bytes = int(lens[r]) * w.num_kv_heads * w.head_dim * 2 * elem
+            done_bytes += req_bytes
+            if kept_bytes + kvh.nbytes <= keep_bytes:
+                kept.append(item)
+                kept_bytes += kvh.nbytes
+                kept_kv += req_bytes
             if t_total >= budget_s:
                 break
     gbs = done_bytes / t_total / 1e9
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(kept)))
+    t_par = _oracle_pool(w, kept, workers)
     return {
         "value": round(gbs, 4),
         "unit": "GB/s",
@@ -180,6 +260,13 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0):
                    f"{t_total:.1f} s"),
         "ms_per_full_step_extrapolated": round(t_total / max(1, done_bytes) * kv_bytes_total(dcase, w)
                                                * 1e3, 1),
+        "parallel": {
+            "value": round(kept_kv / t_par / 1e9, 4),
+            "unit": "GB/s",
+            "cores": workers,
+            "sample": (f"the first {len(kept)} of those requests over {workers} single-threaded "
+                       f"worker processes, {t_par:.2f} s"),
+        },
     }
 
 
@@ -307,6 +394,17 @@ def main(argv=None) -> int:
     step_ms = [e[0].elapsed_time(e[2 if has_merge else 1]) for e in evs]
     print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
 
+    # Calibration: the plain 1 GiB read used as the cache flush, timed alone.
+    cal_ms = []
+    for _ in range(10):
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        flush_i64.max()
+        c1.record()
+        torch.cuda.synchronize()
+        cal_ms.append(c0.elapsed_time(c1))
+    cal_gbs = flush.numel() / (statistics.median(cal_ms) * 1e-3) / 1e9
+
     warm_ms = None
     if args.warm_ref:  # back-to-back steps, for reference
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -351,6 +449,11 @@ def main(argv=None) -> int:
         "warm_us_per_step": round(warm_ms * 1e3, 2) if warm_ms else None,
         "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1) if warm_ms else None,
         "merge_us": round(statistics.fmean(mrg_ms) * 1e3, 2),
+        "calibration": {
+            "kernel": "torch int64 max over a 1 GiB buffer (plain streaming read)",
+            "read_gbs": round(cal_gbs, 1),
+            "pct_of_peak_hbm": round(100.0 * cal_gbs / PEAK_HBM_GBS, 2),
+        },
         "plan_us_host": round(plan_us, 1),
         "plan_us_host_first": round(first_plan_us, 1),
         "plan": {k: info[k] for k in ("chunk_pages", "num_items", "num_partials",
