@@ -135,7 +135,8 @@ def _oracle_request(w, item):
     return attention.decode(qh, kvh, np.array([0, n], np.int32), np.arange(n, dtype=np.int32),
                             np.array([last], np.int32), num_kv_heads=w.num_kv_heads,
                             q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, sm_scale=w.scale(),
-                            k_scale=ks, v_scale=vs)
+                            k_scale=ks, v_scale=vs,
+                            qo_indptr=np.array([0, qh.shape[0]], np.int32))
 
 
 def _pool_worker(conn):
@@ -226,7 +227,8 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
                 kvh = kv.cpu().numpy().view(np.uint8)
             else:
                 kvh = kv.cpu().numpy()
-            q = dcase["q"][r:r + 1]
+            qo = dcase["qo_indptr"]
+            q = dcase["q"][r:r + 1] if qo is None else dcase["q"][int(qo[r]):int(qo[r + 1])]
             qh = (q.view(torch.int16).cpu().numpy().view(np.uint16) if w.q_dtype == "bf16"
                   else q.cpu().numpy())
             ks = vs = None
@@ -336,7 +338,8 @@ def main(argv=None) -> int:
         wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
                      w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
                      kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
-                     balance=args.balance, min_chunk_pages=args.min_chunk_pages)
+                     balance=args.balance, min_chunk_pages=args.min_chunk_pages,
+                     qo_indptr=dcase["qo_indptr"])
         torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -437,6 +440,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,
+            "query_tokens": int(info["query_rows"]),
             "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim, "page_size": w.page_size,
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "context": list(w.context),
             "total_kv_tokens": int(dcase["kv_lens"].sum()), "seed": seed,
@@ -458,7 +462,7 @@ def main(argv=None) -> int:
         "plan_us_host_first": round(first_plan_us, 1),
         "plan": {k: info[k] for k in ("chunk_pages", "num_items", "num_partials",
                                       "num_split_requests", "slots", "balance",
-                                      "min_chunk_pages")},
+                                      "min_chunk_pages", "queries_per_item")},
         "roofline": {
             "kernel": decode_kernel_name(w),
             "bound": "hbm",

@@ -6,7 +6,11 @@
  * the decode-time attention story": one query token per request attends over
  * that request's KV tokens, which live in fixed-size pages named by a page
  * table (indptr / indices / last_page_len, §"Paged attention (vLLM) — the
- * KV-cache layout FlashInfer targets"). Work is split along the KV axis into
+ * KV-cache layout FlashInfer targets"). A request may instead bring a handful
+ * of new tokens (speculative or parallel decoding, the page's opening), laid
+ * out as ragged q rows by qo_indptr (§"Ragged attention — variable-length
+ * batching"); they are the request's last KV tokens and each attends causally
+ * (up to and including its own position). Work is split along the KV axis into
  * partial (m, d, o) softmax states that a second kernel merges with the
  * online-softmax rule (§"FlashDecoding — the split-KV trick"), and a host-side
  * plan balances the split so that long requests do not stall short ones
@@ -47,8 +51,10 @@ extern "C" {
 #define PKD_DTYPE_BF16 1  /* bfloat16 */
 #define PKD_DTYPE_E4M3 2  /* OCP FP8 E4M3FN byte, with fp32 per-(page, KV head) scales */
 
-/* Columns of one work item as returned by pkd_plan_get_worklist. */
-#define PKD_ITEM_COLS 5   /* request, page_begin, page_end, kv_len, partial_slot */
+/* Columns of one work item as returned by pkd_plan_get_worklist:
+ * request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible
+ * (see pkd_plan_get_worklist). */
+#define PKD_ITEM_COLS 8
 
 typedef struct pkd_plan pkd_plan;
 
@@ -80,6 +86,15 @@ typedef struct pkd_plan pkd_plan;
  *  min_chunk_pages  shortest chunk a request is split into; 0 selects
  *                   ceil(256 / page_size)
  *  device           HIP device ordinal used when slots == 0
+ *  qo_indptr        host int32[B+1] or NULL. NULL: one query token per
+ *                   request (q row r). Otherwise request r owns the q rows
+ *                   [qo_indptr[r], qo_indptr[r+1]): q_r >= 1 new tokens, at
+ *                   most its KV token count, which are its last q_r KV
+ *                   tokens in order; new token i attends to the first
+ *                   L_r - q_r + 1 + i KV tokens. More than one token per
+ *                   request needs bf16 q, bf16 or e4m3 KV and head_dim 128
+ *                   (else UNSUPPORTED); a work item then carries up to
+ *                   16 / group of a request's tokens.
  */
 typedef struct {
   int32_t batch;
@@ -97,6 +112,7 @@ typedef struct {
   int32_t balance;
   int32_t min_chunk_pages;
   int32_t device;
+  const int32_t* qo_indptr;
 } pkd_plan_args;
 
 /* What a plan decided (pkd_plan_get_info). */
@@ -104,18 +120,23 @@ typedef struct {
   int32_t batch;
   int32_t chunk_pages;         /* C: pages per work item (the last chunk may be shorter) */
   int32_t num_items;           /* work items; the decode grid is num_items x num_kv_heads */
-  int32_t num_partials;        /* partial-state slots (items of split requests) */
+  int32_t num_partials;        /* partial-state rows (per q row of each chunk of split requests) */
   int32_t num_split_requests;  /* requests with more than one item */
   int32_t slots;               /* values actually used by the rule */
   int32_t balance;
   int32_t min_chunk_pages;
   int64_t total_kv_tokens;     /* sum over requests of their token counts */
   size_t workspace_bytes;      /* device workspace run() needs */
+  int32_t query_rows;          /* rows of q, out and lse (B with one token per request) */
+  int32_t queries_per_item;    /* new tokens of one request a work item carries at most */
+  int32_t max_qo_len;          /* most new tokens of one request */
+  int32_t num_merge_tasks;     /* q rows of split requests (merge grid / num_qo_heads) */
 } pkd_plan_info;
 
 /* Arguments of pkd_run. All pointers are device pointers.
  *
- *  q            [B, Hq, head_dim] contiguous, q_dtype
+ *  q            [rows, Hq, head_dim] contiguous, q_dtype (rows =
+ *               info.query_rows: B, or qo_indptr[B])
  *  k, v         element (page 0, slot 0, KV head 0, dim 0) of the K and V
  *               pools; element (page, slot, h, d) of K is at
  *               k[page*page_stride + slot*token_stride + h*head_stride + d]
@@ -132,9 +153,9 @@ typedef struct {
  *  k_scale,     float [num_pages, Hkv] contiguous; required for e4m3 KV,
  *  v_scale      ignored otherwise. Stored K (V) bytes are multiplied by the
  *               scale of their (page, KV head).
- *  out          [B, Hq, head_dim] contiguous, out_dtype
- *  lse          float [B, Hq] or NULL: natural-log log-sum-exp of the scaled
- *               logits of each (request, query head)
+ *  out          [rows, Hq, head_dim] contiguous, out_dtype
+ *  lse          float [rows, Hq] or NULL: natural-log log-sum-exp of the
+ *               scaled logits of each (q row, query head)
  *  workspace    the buffer the plan was uploaded to, at least
  *               info.workspace_bytes long
  *  stream       hipStream_t; run() only enqueues work and returns
@@ -172,11 +193,17 @@ int pkd_plan_create(const pkd_plan_args* args, pkd_plan** out);
 /* Copy out what the plan decided. */
 int pkd_plan_get_info(const pkd_plan* plan, pkd_plan_info* info);
 
-/* Copy the work list to host memory: items_out int32[num_items * 5] rows of
- * (request, page_begin, page_end, kv_len, partial_slot) in launch order
- * (partial_slot is -1 for a request that is not split); merge_indptr_out
- * int32[B+1], where the split request r owns partial slots
- * [merge_indptr[r], merge_indptr[r+1]); split_requests_out (nullable)
+/* Copy the work list to host memory: items_out int32[num_items * 8] rows of
+ * (request, page_begin, page_end, kv_len, partial_slot, q_row, q_len,
+ * visible) in launch order. An item covers page-table entries
+ * [page_begin, page_end) (kv_len tokens) for the q_len q rows from q_row;
+ * the first of those rows sees min(kv_len, visible) of the item's tokens and
+ * row i sees min(kv_len, visible + i) (kv_len itself with one token per
+ * request). partial_slot is -1 for a request that is not split, else the
+ * partial-state row of q row q_row (row i uses partial_slot + i).
+ * merge_indptr_out int32[B+1]: the split request r owns partial-state rows
+ * [merge_indptr[r], merge_indptr[r+1]), chunk c's row for its token i being
+ * merge_indptr[r] + c * q_r + i; split_requests_out (nullable)
  * int32[num_split_requests], the split requests in ascending order. */
 int pkd_plan_get_worklist(const pkd_plan* plan, int32_t* items_out, int32_t* merge_indptr_out,
                           int32_t* split_requests_out);

@@ -20,6 +20,12 @@ Readings taken where the pages are silent (each listed in the design doc):
   ``pos_encoding_mode="NONE"``).
 * The output is the max-subtracted softmax average of V, and the optional
   log-sum-exp is ``m + ln(d)`` in natural log.
+* Several query tokens per request (the "handful with speculative decoding"
+  of the page's opening, laid out as the ragged ``qo_indptr`` rows of
+  §"Ragged attention — variable-length batching"): the n new tokens of a
+  request are its last n KV tokens, in order, and new token i (0-based) sees
+  the KV tokens up to and including its own position, i.e. the first
+  ``L_r - n + 1 + i`` of them (causal within the new tokens).
 
 The full softmax over each request's gathered tokens is materialised; no
 tiling, splitting or reordering is done here (``oracle.merge`` holds the split
@@ -78,29 +84,50 @@ def attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float):
     return (p @ V) / d, m + math.log(d)
 
 
+def visible_tokens(L: int, n_new: int, i: int) -> int:
+    """KV tokens seen by new token i of a request of L tokens whose last n_new
+    tokens are new: all tokens up to and including its own position."""
+    return L - n_new + 1 + i
+
+
 def decode(q, kv, indptr, indices, last_page_len, *, num_kv_heads: int, q_dtype: str,
            kv_dtype: str, sm_scale: Optional[float] = None, k_scale=None, v_scale=None,
-           requests: Optional[Iterable[int]] = None):
-    """Decode attention for every (request, query head).
+           requests: Optional[Iterable[int]] = None, qo_indptr=None):
+    """Decode attention for every (query token, query head).
 
-    Returns ``out`` float64 ``[B, Hq, D]`` and ``lse`` float64 ``[B, Hq]``.
-    With ``requests`` given, only those rows are computed (the rest are NaN).
+    Without ``qo_indptr`` q holds one token per request (``[B, Hq, D]``). With
+    it, request r owns q rows ``qo_indptr[r]:qo_indptr[r+1]`` (at least one, at
+    most ``L_r``), attended causally as described in the module docstring.
+    Returns ``out`` float64 ``[rows, Hq, D]`` and ``lse`` float64 ``[rows, Hq]``.
+    With ``requests`` given, only those requests' rows are computed (the rest
+    are NaN).
     """
     q64 = widen(q, q_dtype)
-    B, Hq, D = q64.shape
+    R, Hq, D = q64.shape
+    B = len(last_page_len)
+    qo = np.arange(B + 1) if qo_indptr is None else np.asarray(qo_indptr, dtype=np.int64)
+    if len(qo) != B + 1 or qo[0] != 0 or qo[-1] != R or np.any(np.diff(qo) < 1):
+        raise ValueError("qo_indptr must start at 0, give every request a query row and "
+                         "end at the number of q rows")
     if Hq % num_kv_heads:
         raise ValueError("num_qo_heads must be a multiple of num_kv_heads")
     g = Hq // num_kv_heads
     scale = (1.0 / math.sqrt(D)) if sm_scale is None else float(sm_scale)
-    out = np.full((B, Hq, D), np.nan)
-    lse = np.full((B, Hq), np.nan)
-    rows = range(B) if requests is None else requests
-    for r in rows:
+    out = np.full((R, Hq, D), np.nan)
+    lse = np.full((R, Hq), np.nan)
+    for r in (range(B) if requests is None else requests):
+        L = request_length(indptr, last_page_len, kv.shape[2], r)
+        n_new = int(qo[r + 1] - qo[r])
+        if n_new > L:
+            raise ValueError("a request has more query tokens than KV tokens")
         for kvh in range(num_kv_heads):
             K, V = gather_request(kv, indptr, indices, last_page_len, r, kvh, kv_dtype,
                                   k_scale, v_scale)
-            for h in range(kvh * g, (kvh + 1) * g):
-                out[r, h], lse[r, h] = attend(q64[r, h], K, V, scale)
+            for i in range(n_new):
+                vis = visible_tokens(L, n_new, i)
+                row = int(qo[r]) + i
+                for h in range(kvh * g, (kvh + 1) * g):
+                    out[row, h], lse[row, h] = attend(q64[row, h], K[:vis], V[:vis], scale)
     return out, lse
 
 
@@ -110,4 +137,5 @@ def decode_case(case: dict, requests=None, sm_scale=None):
     return decode(case["q"], case["kv"], case["indptr"], case["indices"], case["last_page_len"],
                   num_kv_heads=w.num_kv_heads, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
                   sm_scale=w.scale() if sm_scale is None else sm_scale,
-                  k_scale=case.get("k_scale"), v_scale=case.get("v_scale"), requests=requests)
+                  k_scale=case.get("k_scale"), v_scale=case.get("v_scale"), requests=requests,
+                  qo_indptr=case.get("qo_indptr"))

@@ -34,6 +34,22 @@ The rule adopted (a reading; the design doc lists it):
    then chunk index, so the hardware's in-order dispatch starts the long
    work units first and the short ones fill in behind them.
 
+Several new tokens per request (``qo_indptr``, ``q_r`` tokens for request r;
+the causal reading is stated in ``oracle.attention``): a work item carries at
+most ``queries_per_item`` (``Q``) of a request's new tokens, so request r
+counts as ``U_r = ceil(q_r / Q)`` units of ``n_r`` pages each. Steps 2-5 run
+over units instead of requests (``B`` = number of units, ``S`` = sum of their
+pages; with one token per request nothing changes), every chunk of a request
+is repeated for each of its query blocks (block b holds tokens
+``[b*Q, min((b+1)*Q, q_r))``), and partial states are kept per query token:
+``merge_indptr[r+1] = merge_indptr[r] + (G_r * q_r if G_r > 1 else 0)``, item
+(r, c, b) writes rows ``merge_indptr[r] + c*q_r + b*Q + i`` for its block's
+token i. Each item also records its first q row ``qo_indptr[r] + b*Q``, its
+token count, and how many of its KV tokens the block's first token sees,
+``min(kv_len, L_r - q_r + 1 + b*Q - c*C*P)`` (token i of the block sees
+``min(kv_len, that + i)``; a value <= 0 means it sees none). Ties in step 5
+go by request, chunk, then query block.
+
 Test infrastructure: see the package docstring.
 """
 from __future__ import annotations
@@ -45,8 +61,12 @@ def _ceil_div(a: int, b: int) -> int:
     return -(-a // b)
 
 
+ITEM_COLUMNS = ("request", "page_begin", "page_end", "kv_len", "partial_slot", "q_row",
+                "q_len", "visible")
+
+
 def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
-         balance: int, min_chunk_pages: int) -> dict:
+         balance: int, min_chunk_pages: int, qo_indptr=None, queries_per_item: int = 1) -> dict:
     indptr = [int(x) for x in indptr]
     last = [int(x) for x in last_page_len]
     B = len(last)
@@ -59,12 +79,22 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
         raise ValueError("every request needs at least one page")
     if any(not (1 <= lp <= page_size) for lp in last):
         raise ValueError("last_page_len must lie in [1, page_size]")
-    if slots < 1 or balance < 1 or min_chunk_pages < 1:
-        raise ValueError("slots, balance and min_chunk_pages must be positive")
+    if slots < 1 or balance < 1 or min_chunk_pages < 1 or queries_per_item < 1:
+        raise ValueError("slots, balance, min_chunk_pages and queries_per_item must be positive")
+    L = [(n[r] - 1) * page_size + last[r] for r in range(B)]
+    qo = list(range(B + 1)) if qo_indptr is None else [int(x) for x in qo_indptr]
+    if len(qo) != B + 1 or qo[0] != 0:
+        raise ValueError("qo_indptr must have batch+1 entries starting at 0")
+    nq = [qo[r + 1] - qo[r] for r in range(B)]
+    if any(not (1 <= nq[r] <= L[r]) for r in range(B)):
+        raise ValueError("every request needs between 1 and L_r query tokens")
+    Q = queries_per_item
+    U = [_ceil_div(x, Q) for x in nq]  # query blocks (units) per request
 
-    S = sum(n)
+    units = sum(U)
+    S = sum(n[r] * U[r] for r in range(B))
     N = max(n)
-    if 8 * N * B <= 9 * S and 2 * B * num_kv_heads >= slots:
+    if 8 * N * units <= 9 * S and 2 * units * num_kv_heads >= slots:
         C = N
     else:
         cap = _ceil_div(S * num_kv_heads, slots * balance)
@@ -73,7 +103,7 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
     G = [_ceil_div(x, C) for x in n]
     merge_indptr = [0]
     for r in range(B):
-        merge_indptr.append(merge_indptr[-1] + (G[r] if G[r] > 1 else 0))
+        merge_indptr.append(merge_indptr[-1] + (G[r] * nq[r] if G[r] > 1 else 0))
 
     rows = []
     for r in range(B):
@@ -83,10 +113,13 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
             kv_len = (pe - pb) * page_size
             if pe == indptr[r + 1]:
                 kv_len -= page_size - last[r]
-            slot = merge_indptr[r] + c if G[r] > 1 else -1
-            rows.append((r, pb, pe, kv_len, slot, c))
-    rows.sort(key=lambda t: (-t[3], t[0], t[5]))
-    items = np.array([t[:5] for t in rows], dtype=np.int32).reshape(-1, 5)
+            for b in range(U[r]):
+                q_len = min(Q, nq[r] - b * Q)
+                visible = min(kv_len, L[r] - nq[r] + 1 + b * Q - c * C * page_size)
+                slot = merge_indptr[r] + c * nq[r] + b * Q if G[r] > 1 else -1
+                rows.append((r, pb, pe, kv_len, slot, qo[r] + b * Q, q_len, visible, c, b))
+    rows.sort(key=lambda t: (-t[3], t[0], t[8], t[9]))
+    items = np.array([t[:8] for t in rows], dtype=np.int32).reshape(-1, len(ITEM_COLUMNS))
     split = np.array([r for r in range(B) if G[r] > 1], dtype=np.int32)
     return {
         "chunk_pages": C,
@@ -94,5 +127,5 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
         "merge_indptr": np.array(merge_indptr, dtype=np.int32),
         "split_requests": split,
         "num_partials": merge_indptr[-1],
-        "kv_lens": np.array([(n[r] - 1) * page_size + last[r] for r in range(B)], dtype=np.int64),
+        "kv_lens": np.array(L, dtype=np.int64),
     }

@@ -21,7 +21,7 @@ PKD_ERR_HIP = -5
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_E4M3 = 2
-ITEM_COLS = 5
+ITEM_COLS = 8  # request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible
 STAGE_DECODE = 1
 STAGE_MERGE = 2
 STAGE_ALL = 3
@@ -46,6 +46,7 @@ class PlanArgs(ctypes.Structure):
         ("balance", ctypes.c_int32),
         ("min_chunk_pages", ctypes.c_int32),
         ("device", ctypes.c_int32),
+        ("qo_indptr", _c_i32p),
     ]
 
 
@@ -61,6 +62,10 @@ class PlanInfo(ctypes.Structure):
         ("min_chunk_pages", ctypes.c_int32),
         ("total_kv_tokens", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_size_t),
+        ("query_rows", ctypes.c_int32),
+        ("queries_per_item", ctypes.c_int32),
+        ("max_qo_len", ctypes.c_int32),
+        ("num_merge_tasks", ctypes.c_int32),
     ]
 
 

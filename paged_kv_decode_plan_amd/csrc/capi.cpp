@@ -116,39 +116,18 @@ void pinned_release(PinnedBlock b) {
 
 // Resident workgroups per CU and CU count, per (device, kernel choice).
 std::mutex g_slots_mu;
-std::map<std::tuple<int, int, int, int, int, int>, std::pair<int, int>> g_slots;
+std::map<std::tuple<int, int, int, int, int, int, int>, std::pair<int, int>> g_slots;
 
-}  // namespace
-
-struct pkd_plan {
-  pkd_plan_args args{};
-  float sm_scale = 0.f;
-  pkd::Partition part;
-  pkd_plan_info info{};
-  // Device workspace layout (byte offsets).
-  size_t off_items = 0, off_split = 0, header_bytes = 0;
-  size_t off_part_md = 0, off_part_o = 0;
-  std::vector<unsigned char> header;  // host image of [items | merge tasks]
-  PinnedBlock staging;                // from the process-wide pool, on first upload
-  const void* uploaded_to = nullptr;
-  int device = 0;
-};
-
-extern "C" {
-
-const char* pkd_last_error(void) { return g_last_error.c_str(); }
-
-int pkd_version(void) { return 100; }
-
-int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
-                     int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus) {
-  if (!wgs_per_cu || !num_cus) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
+int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
+                 int32_t group, int32_t rows, int32_t page_size, int32_t* wgs_per_cu,
+                 int32_t* num_cus) {
   const int q_bf16 = q_dtype == PKD_DTYPE_BF16;
-  if (!pkd::decode_supported(kv_dtype, head_dim, group, q_bf16, page_size))
-    return fail(PKD_ERR_UNSUPPORTED, "no kernel for kv_dtype=%d head_dim=%d group=%d q_dtype=%d",
-                kv_dtype, head_dim, group, q_dtype);
-  const auto key = std::make_tuple(int(device), int(kv_dtype), int(head_dim), int(group), q_bf16,
-                                   page_size >= 16 ? 16 : 1);
+  if (!pkd::decode_supported(kv_dtype, head_dim, group, rows, q_bf16, page_size))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "no kernel for kv_dtype=%d head_dim=%d group=%d rows=%d q_dtype=%d", kv_dtype,
+                head_dim, group, rows, q_dtype);
+  const auto key = std::make_tuple(int(device), int(kv_dtype), int(head_dim), int(group),
+                                   int(rows), q_bf16, page_size >= 16 ? 16 : 1);
   {
     std::lock_guard<std::mutex> lk(g_slots_mu);
     auto it = g_slots.find(key);
@@ -165,7 +144,8 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
     return fail(PKD_ERR_HIP, "hipSetDevice(%d): %s", device, hipGetErrorString(e));
   int cus = 0, wgs = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
-  if (e == hipSuccess) e = pkd::decode_occupancy(kv_dtype, head_dim, group, q_bf16, page_size, &wgs);
+  if (e == hipSuccess)
+    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_bf16, page_size, &wgs);
   if (prev != device) hipSetDevice(prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
   *wgs_per_cu = wgs;
@@ -173,6 +153,36 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
   std::lock_guard<std::mutex> lk(g_slots_mu);
   g_slots[key] = {wgs, cus};
   return ok();
+}
+
+}  // namespace
+
+struct pkd_plan {
+  pkd_plan_args args{};
+  float sm_scale = 0.f;
+  pkd::Partition part;
+  pkd_plan_info info{};
+  int rows = 0;  // query rows per work item and KV head (kernel choice)
+  // Device workspace layout (byte offsets).
+  size_t off_items = 0, off_split = 0, header_bytes = 0;
+  size_t off_part_md = 0, off_part_o = 0;
+  std::vector<unsigned char> header;  // host image of [items | merge tasks]
+  PinnedBlock staging;                // from the process-wide pool, on first upload
+  const void* uploaded_to = nullptr;
+  int device = 0;
+};
+
+extern "C" {
+
+const char* pkd_last_error(void) { return g_last_error.c_str(); }
+
+int pkd_version(void) { return 200; }
+
+int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
+                     int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus) {
+  if (!wgs_per_cu || !num_cus) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
+  return device_slots(device, q_dtype, kv_dtype, head_dim, group, group, page_size, wgs_per_cu,
+                      num_cus);
 }
 
 int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
@@ -196,10 +206,31 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (!is_pow2(a->page_size) || a->page_size > 1024)
     return fail(PKD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]",
                 a->page_size);
-  if (!pkd::decode_supported(a->kv_dtype, a->head_dim, group, a->q_dtype == PKD_DTYPE_BF16,
-                             a->page_size))
+  if (!pkd::decode_supported(a->kv_dtype, a->head_dim, group, group,
+                             a->q_dtype == PKD_DTYPE_BF16, a->page_size))
     return fail(PKD_ERR_UNSUPPORTED, "no kernel for head_dim=%d group=%d kv_dtype=%d q_dtype=%d",
                 a->head_dim, group, a->kv_dtype, a->q_dtype);
+  // Several new tokens per request: a work item carries up to 16 / group of
+  // one request's tokens, so that its group x tokens rows fill the columns of
+  // one MFMA tile.
+  int32_t max_q = 1;
+  if (a->qo_indptr) {
+    if (a->qo_indptr[0] != 0) return fail(PKD_ERR_INVALID_ARGUMENT, "qo_indptr[0] must be 0");
+    for (int32_t r = 0; r < a->batch; ++r) {
+      const int64_t q = int64_t(a->qo_indptr[r + 1]) - a->qo_indptr[r];
+      if (q < 1)
+        return fail(PKD_ERR_INVALID_ARGUMENT, "request %d has %lld query tokens", r, (long long)q);
+      max_q = int32_t(std::min<int64_t>(std::max<int64_t>(max_q, q), INT32_MAX));
+    }
+  }
+  const int32_t queries_per_item = max_q > 1 ? std::max(1, 16 / group) : 1;
+  const int32_t rows = group * std::min(queries_per_item, max_q);
+  if (max_q > 1 && !pkd::decode_uses_mfma(a->kv_dtype, a->head_dim, group, rows,
+                                          a->q_dtype == PKD_DTYPE_BF16, a->page_size))
+    return fail(PKD_ERR_UNSUPPORTED,
+                "several query tokens per request need bf16 q, bf16 or e4m3 KV and head_dim 128 "
+                "(group %d, head_dim %d, kv_dtype %d, q_dtype %d)",
+                group, a->head_dim, a->kv_dtype, a->q_dtype);
   if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0)
     return fail(PKD_ERR_INVALID_ARGUMENT, "slots, balance and min_chunk_pages must be >= 0");
   if (!(a->sm_scale >= 0.f) || std::isinf(a->sm_scale))
@@ -208,8 +239,8 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   int slots = a->slots;
   if (slots == 0) {
     int32_t wgs = 0, cus = 0;
-    int rc = pkd_device_slots(a->device, a->q_dtype, a->kv_dtype, a->head_dim, group,
-                              a->page_size, &wgs, &cus);
+    int rc = device_slots(a->device, a->q_dtype, a->kv_dtype, a->head_dim, group, rows,
+                          a->page_size, &wgs, &cus);
     if (rc != PKD_OK) return rc;
     slots = wgs * cus;
     if (slots < 1) return fail(PKD_ERR_HIP, "device reports no resident workgroups");
@@ -218,6 +249,8 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   pin.batch = a->batch;
   pin.indptr = a->indptr;
   pin.last_page_len = a->last_page_len;
+  pin.qo_indptr = max_q > 1 ? a->qo_indptr : nullptr;
+  pin.queries_per_item = queries_per_item;
   pin.page_size = a->page_size;
   pin.units_per_item = a->num_kv_heads;
   pin.slots = slots;
@@ -234,31 +267,42 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   p->args = *a;
   p->args.indptr = nullptr;
   p->args.last_page_len = nullptr;
+  p->args.qo_indptr = nullptr;
+  p->rows = rows;
   p->device = a->device;
   p->sm_scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(float(a->head_dim));
 
   const auto& part = p->part;
   const size_t n_items = part.items.size();
   const size_t n_split = part.split_requests.size();
+  // One merge task per q row of a split request.
+  std::vector<pkd::MergeTask> tasks;
+  for (const int32_t r : part.split_requests) {
+    const int32_t q0 = max_q > 1 ? a->qo_indptr[r] : r;
+    const int32_t nq = max_q > 1 ? a->qo_indptr[r + 1] - a->qo_indptr[r] : 1;
+    const int32_t chunks = (part.merge_indptr[r + 1] - part.merge_indptr[r]) / nq;
+    for (int32_t i = 0; i < nq; ++i) tasks.push_back({q0 + i, part.merge_indptr[r] + i, chunks, nq});
+  }
+  const size_t n_tasks = tasks.size();
   p->off_items = 0;
   p->off_split = align256(n_items * sizeof(pkd::DeviceItem));
-  p->header_bytes = align256(p->off_split + std::max<size_t>(n_split, 1) * sizeof(pkd::MergeTask));
+  p->header_bytes = align256(p->off_split + std::max<size_t>(n_tasks, 1) * sizeof(pkd::MergeTask));
   p->off_part_md = p->header_bytes;
-  const size_t rows = size_t(part.num_partials) * size_t(a->num_qo_heads);
-  p->off_part_o = align256(p->off_part_md + rows * 2 * sizeof(float));
-  const size_t ws = align256(p->off_part_o + rows * size_t(a->head_dim) * sizeof(float));
+  const size_t prows = size_t(part.num_partials) * size_t(a->num_qo_heads);
+  p->off_part_o = align256(p->off_part_md + prows * 2 * sizeof(float));
+  const size_t ws = align256(p->off_part_o + prows * size_t(a->head_dim) * sizeof(float));
 
   p->header.assign(p->header_bytes, 0);
   auto* di = reinterpret_cast<pkd::DeviceItem*>(p->header.data() + p->off_items);
   for (size_t i = 0; i < n_items; ++i) {
     const auto& w = part.items[i];
-    di[i] = {w.request, w.page_begin, w.kv_len, w.partial_slot};
+    // The kernel reads only the tokens some row of the block sees.
+    const int64_t seen = std::max<int64_t>(
+        0, std::min<int64_t>(w.kv_len, int64_t(w.visible) + w.q_len - 1));
+    di[i] = {w.page_begin, int32_t(seen), w.partial_slot, w.q_row, w.q_len, w.visible, {0, 0}};
   }
-  auto* mt = reinterpret_cast<pkd::MergeTask*>(p->header.data() + p->off_split);
-  for (size_t k = 0; k < n_split; ++k) {
-    const int32_t r = part.split_requests[k];
-    mt[k] = {r, part.merge_indptr[r], part.merge_indptr[r + 1], 0};
-  }
+  if (n_tasks)
+    std::memcpy(p->header.data() + p->off_split, tasks.data(), n_tasks * sizeof(pkd::MergeTask));
 
   pkd_plan_info& inf = p->info;
   inf.batch = a->batch;
@@ -271,6 +315,10 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   inf.min_chunk_pages = pin.min_chunk_pages;
   inf.total_kv_tokens = part.total_tokens;
   inf.workspace_bytes = ws;
+  inf.query_rows = part.query_rows;
+  inf.queries_per_item = queries_per_item;
+  inf.max_qo_len = max_q;
+  inf.num_merge_tasks = int32_t(n_tasks);
   *out = p;
   return ok();
 }
@@ -293,6 +341,9 @@ int pkd_plan_get_worklist(const pkd_plan* p, int32_t* items_out, int32_t* merge_
       row[2] = w.page_end;
       row[3] = w.kv_len;
       row[4] = w.partial_slot;
+      row[5] = w.q_row;
+      row[6] = w.q_len;
+      row[7] = w.visible;
     }
   }
   if (merge_indptr_out)
@@ -360,6 +411,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.kv_dtype = a.kv_dtype;
   L.head_dim = a.head_dim;
   L.group = a.num_qo_heads / a.num_kv_heads;
+  L.rows = p->rows;
   L.num_items = p->info.num_items;
   L.num_kv_heads = a.num_kv_heads;
   L.num_qo_heads = a.num_qo_heads;
@@ -383,7 +435,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.merge_tasks = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_split);
   L.part_md = reinterpret_cast<float*>(ws + p->off_part_md);
   L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
-  L.num_split = p->info.num_split_requests;
+  L.num_split = p->info.num_merge_tasks;
   hipStream_t s = static_cast<hipStream_t>(r->stream);
   hipError_t e;
   if (stages & PKD_STAGE_DECODE) {

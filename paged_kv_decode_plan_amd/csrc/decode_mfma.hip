@@ -1,14 +1,19 @@
 // MFMA split-KV paged decode kernel, for gfx950 (bf16 or e4m3 KV, bf16 q,
-// head_dim 128, up to 16 query heads per KV head).
+// head_dim 128, up to 16 query rows per KV head).
 //
 // What is computed ("FlashDecoding + FlashInfer — the decode-time attention
-// story"): for one query token per request and each query head h, the softmax
-// of scale * q.K over the request's KV tokens, applied to V; K/V rows are
-// gathered through the page table (§"Paged attention (vLLM)"). A workgroup
-// handles one work item (a run of one request's pages) for one KV head and the
-// G query heads that share it and ends with either the output rows or partial
-// (m, d, o) states (§"FlashDecoding — the split-KV trick"); within it the
-// running (m, d, o) is updated tile by tile with the same rule.
+// story"): for each query token of a request and each query head h, the
+// softmax of scale * q.K over the request's KV tokens, applied to V; K/V rows
+// are gathered through the page table (§"Paged attention (vLLM)"). A
+// workgroup handles one work item (a run of one request's pages, for a block
+// of that request's query tokens) for one KV head and ends with either the
+// output rows or partial (m, d, o) states (§"FlashDecoding — the split-KV
+// trick"); within it the running (m, d, o) is updated tile by tile with the
+// same rule. Its G rows are (query token i, query head hh of the group) with
+// row = i * group + hh: the group's heads for one token per request, or, with
+// several new tokens per request (the ragged q rows of §"Ragged attention"),
+// up to 16 / group tokens, token i seeing the first min(kv_len, visible + i)
+// tokens of the item (causal within the new tokens).
 //
 // Both contractions run on MFMA: S = K.q^T on v_mfma_f32_16x16x32_bf16 and
 // O = P.V on v_mfma_f32_16x16x16_bf16 (lane l holds A row l%16 / B column
@@ -168,6 +173,7 @@ struct Ctx {
   const int32_t* page_ids;  // the item's slice of the page table
   int64_t page_stride, token_stride, head_off;
   int log2p, pmask, kv_len, q4, j;
+  int lim;  // tokens of the item seen by this lane's row (column j of S)
   // Byte offsets of this lane's first K and V load from the tile's first row
   // (the same for every tile when a tile lies in one page); the other loads
   // add 64 bytes (K) or one token row (V), both wavefront-uniform.
@@ -312,7 +318,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     const int t = t0 + 4 * c.q4 + r;
     float kr = ks;
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
-    const float v = (FULL || t < c.kv_len) ? s[r] * kr : -INFINITY;
+    const float v = (FULL || t < c.lim) ? s[r] * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
   }
@@ -326,7 +332,10 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+    // 0 while m_run = -inf; a masked tile can leave a row without any token
+    // yet (m_new = -inf), whose d and O are still 0: no rescale.
+    float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    if constexpr (!FULL) alpha = m_new == -INFINITY ? 1.f : alpha;
     m_run = m_new;
     d_run *= alpha;
 #pragma unroll
@@ -342,6 +351,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+    if constexpr (!FULL) p[e] = sc[e] == -INFINITY ? 0.f : p[e];  // also when m_run = -inf
     d_run += p[e];
   }
   if constexpr (KV == kE4M3) {
@@ -433,7 +443,7 @@ constexpr int waves_per_simd() { return PAGE16 && nsub<KV>() == 1 ? 4 : 3; }
 
 template <int KV, int G, bool PAGE16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16>()))) void decode_mfma_kernel(KernelArgs a) {
-  static_assert(G >= 1 && G <= 16, "at most 16 query heads per KV head");
+  static_assert(G >= 1 && G <= 16, "at most 16 query rows per KV head");
   __shared__ WaveStates<G, kD> st;
 
   int item, kvh;
@@ -455,6 +465,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   c.kv_len = it.kv_len;
   c.q4 = lane >> 4;
   c.j = lane & 15;
+  // Row j of S: query token qi of the item's block, query head kvh*group + hh.
+  const int qi = c.j >> a.group_log2;
+  const int hh = c.j & ((1 << a.group_log2) - 1);
+  const bool row_ok = c.j < G && qi < it.q_len;
+  c.lim = row_ok ? min(it.kv_len, it.visible + qi) : it.kv_len;
   {
     constexpr uint32_t kElem = Loads<KV>::kElem;
     const uint32_t ts = uint32_t(a.token_stride);
@@ -463,15 +478,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     c.vrow_bytes = a.token_stride * kElem;
   }
 
-  // q^T as the B operand of S = K.q^T: column j = query head kvh*G + j.
+  // q^T as the B operand of S = K.q^T: column j = row j (zero beyond the block).
   bf16x8_t qb[4];
   {
-    const uint16_t* qp = static_cast<const uint16_t*>(a.q) +
-                         (int64_t(it.request) * a.num_qo_heads + int64_t(kvh) * G + c.j) * kD;
+    const uint16_t* qp =
+        static_cast<const uint16_t*>(a.q) +
+        (int64_t(it.q_row + qi) * a.num_qo_heads + (int64_t(kvh) << a.group_log2) + hh) * kD;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       u32x4_t w = {0u, 0u, 0u, 0u};
-      if (c.j < G) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
+      if (row_ok) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
       qb[dc] = as_bf16x8(w);
     }
   }
@@ -588,12 +604,12 @@ DecodeFn pick_group(int g) {
 
 }  // namespace
 
-DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int group, int page_size) {
+DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size) {
   if (head_dim != kD) return nullptr;
   const bool p16 = page_size >= 16;
   switch (kv_dtype) {
-    case kBF16: return p16 ? pick_group<kBF16, true>(group) : pick_group<kBF16, false>(group);
-    case kE4M3: return p16 ? pick_group<kE4M3, true>(group) : pick_group<kE4M3, false>(group);
+    case kBF16: return p16 ? pick_group<kBF16, true>(rows) : pick_group<kBF16, false>(rows);
+    case kE4M3: return p16 ? pick_group<kE4M3, true>(rows) : pick_group<kE4M3, false>(rows);
     default: return nullptr;
   }
 }

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
   // q for this lane's VEC dims, head order permuted per lane (see row_reduce_scatter).
   float qr[G][VEC];
   {
-    const int64_t qbase = (int64_t(it.request) * a.num_qo_heads + int64_t(kvh) * G) * D + j * VEC;
+    const int64_t qbase = (int64_t(it.q_row) * a.num_qo_heads + int64_t(kvh) * G) * D + j * VEC;
 #pragma unroll
     for (int p = 0; p < G; ++p) {
       const int h = p ^ own;

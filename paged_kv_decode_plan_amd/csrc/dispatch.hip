@@ -2,31 +2,44 @@
 //
 // The MFMA kernel runs wherever both contractions can take bf16 operands
 // exactly: bf16 or e4m3 KV with bf16 queries and head_dim 128 (group sizes
-// 1..16). fp32 KV or queries, and head_dim 64, use the vector-ALU kernel.
+// 1..16). fp32 KV or queries, and head_dim 64, use the vector-ALU kernel,
+// which handles one query token per request only. A work item of several new
+// tokens of a request puts group x tokens rows (at most 16) on the MFMA
+// columns; the kernel instance is the one for that row count rounded up to a
+// power of two.
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
 
 namespace pkd {
 
-static DecodeFn choose(int kv_dtype, int head_dim, int group, int q_bf16, int page_size) {
+static int pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
+                       int page_size) {
+  if ((group & (group - 1)) || rows < group || rows % group) return nullptr;
   if (q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3)) {
-    if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, group, page_size)) return f;
+    if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size)) return f;
   }
+  if (rows != group) return nullptr;
   return valu_decode_kernel(kv_dtype, head_dim, group);
 }
 
-bool decode_supported(int kv_dtype, int head_dim, int group, int q_bf16, int page_size) {
-  return choose(kv_dtype, head_dim, group, q_bf16, page_size) != nullptr;
+bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size) {
+  return choose(kv_dtype, head_dim, group, rows, q_bf16, page_size) != nullptr;
 }
 
-bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int q_bf16, int page_size) {
-  return q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3) &&
-         mfma_decode_kernel(kv_dtype, head_dim, group, page_size) != nullptr;
+bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size) {
+  return q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3) && rows >= group &&
+         mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size) != nullptr;
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
-  DecodeFn fn = choose(L.kv_dtype, L.head_dim, L.group, L.q_bf16, 1 << L.page_size_log2);
+  DecodeFn fn = choose(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_bf16, 1 << L.page_size_log2);
   if (!fn) return hipErrorInvalidValue;
   KernelArgs a;
   a.q = L.q;
@@ -47,6 +60,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.xcd_group = L.kv_dtype == kE4M3 ? 8 : 1;
   a.num_kv_heads = L.num_kv_heads;
   a.num_qo_heads = L.num_qo_heads;
+  a.group_log2 = ilog2(L.group);
   a.page_size_log2 = L.page_size_log2;
   a.sm_scale_log2 = L.sm_scale_log2;
   a.q_bf16 = L.q_bf16;
@@ -56,9 +70,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int q_bf16, int page_size,
-                            int* wgs_per_cu) {
-  DecodeFn fn = choose(kv_dtype, head_dim, group, q_bf16, page_size);
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
+                            int page_size, int* wgs_per_cu) {
+  DecodeFn fn = choose(kv_dtype, head_dim, group, rows, q_bf16, page_size);
   if (!fn) return hipErrorInvalidValue;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs_per_cu, fn, kThreads, 0);
 }

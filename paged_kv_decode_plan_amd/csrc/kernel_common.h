@@ -35,6 +35,7 @@ struct KernelArgs {
   int xcd_group;  // workgroup-id grouping g (see decode_block)
   int num_kv_heads;
   int num_qo_heads;
+  int group_log2;  // query heads per KV head (a power of two), as log2
   int page_size_log2;
   float sm_scale_log2;  // logit scale times log2(e): scores are kept in log2 units
   int q_bf16;
@@ -80,28 +81,34 @@ struct WaveStates {
   float d[kWaves][G];     // sum of p
 };
 
-// Merge the kWaves states of every query head of the group with the
-// online-softmax rule and write either the normalised output row (and its
-// log-sum-exp) or, for a split request, the partial state (m, d, o).
+// Merge the kWaves states of every row (query token i, query head hh of the
+// group; row = i * group + hh) with the online-softmax rule and write either
+// the normalised output row (and its log-sum-exp) or, for a split request,
+// the partial state (m, d, o). A row none of whose tokens were seen here (a
+// chunk past a new token's causal limit) gives the empty state (-inf, 0, 0).
 // Must be called by all threads of the workgroup after a barrier.
 template <int G, int D>
 __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelArgs& a,
                                         const DeviceItem& it, int kvh) {
+  const int gmask = (1 << a.group_log2) - 1;
   for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx % D;
+    const int i = h >> a.group_log2;
+    if (i >= it.q_len) break;  // rows are in order: every later one is padding too
     float M = s.m[0][h];
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s.m[w][h]);
     float O = 0.f, Dn = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float sc = exp2f(s.m[w][h] - M);  // 0 for a wavefront without tokens
+      const float mw = s.m[w][h];
+      const float sc = mw == -INFINITY ? 0.f : exp2f(mw - M);  // a wavefront without tokens
       O = fmaf(s.o[w][h][d], sc, O);
       Dn = fmaf(s.d[w][h], sc, Dn);
     }
-    const int hq = kvh * G + h;
-    const int64_t row = int64_t(it.request) * a.num_qo_heads + hq;
+    const int hq = (kvh << a.group_log2) + (h & gmask);
+    const int64_t row = int64_t(it.q_row + i) * a.num_qo_heads + hq;
     if (it.partial_slot < 0) {
       const float val = O / Dn;
       if (a.out_bf16)
@@ -110,7 +117,7 @@ __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelA
         static_cast<float*>(a.out)[row * D + d] = val;
       if (a.lse && d == 0) a.lse[row] = (M + log2f(Dn)) * kLn2;
     } else {
-      const int64_t prow = int64_t(it.partial_slot) * a.num_qo_heads + hq;
+      const int64_t prow = int64_t(it.partial_slot + i) * a.num_qo_heads + hq;
       a.part_o[prow * D + d] = O;
       if (d == 0) {
         a.part_md[prow * 2 + 0] = M;
@@ -120,8 +127,9 @@ __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelA
   }
 }
 
-// Kernel selection (each translation unit provides its family).
+// Kernel selection (each translation unit provides its family). `rows` is the
+// number of (query token, query head) rows one workgroup handles.
 DecodeFn valu_decode_kernel(int kv_dtype, int head_dim, int group);
-DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int group, int page_size);
+DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size);
 
 }  // namespace pkd

@@ -9,27 +9,35 @@ namespace pkd {
 
 enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
 
-// Device-side layout of one work item (16 bytes).
+// Device-side layout of one work item (32 bytes): pages
+// [page_begin, page_begin + ceil(kv_len / page_size)) of the page table for
+// the q rows [q_row, q_row + q_len). kv_len counts only tokens some row of
+// the block sees; row i sees min(kv_len, visible + i) of them (the causal
+// limit of several new tokens per request; one token sees them all).
 struct DeviceItem {
-  int32_t request;
   int32_t page_begin;
   int32_t kv_len;
-  int32_t partial_slot;
+  int32_t partial_slot;  // partial-state row of q row q_row; -1: write the output
+  int32_t q_row;
+  int32_t q_len;
+  int32_t visible;
+  int32_t pad[2];
 };
 
-// Device-side record of one split request for the merge kernel (16 bytes):
-// its partial-state slots are [begin, end).
+// Device-side record of one merge (16 bytes): output row out_row folds the
+// partial-state rows first + c * stride for c in [0, count).
 struct MergeTask {
-  int32_t request;
-  int32_t begin;
-  int32_t end;
-  int32_t pad;
+  int32_t out_row;
+  int32_t first;
+  int32_t count;
+  int32_t stride;
 };
 
 struct DecodeLaunch {
   int kv_dtype = 0;
   int head_dim = 0;
   int group = 0;
+  int rows = 0;  // query rows per work item and KV head: group x query tokens per item
   int num_items = 0;
   int num_kv_heads = 0;
   int num_qo_heads = 0;
@@ -51,15 +59,17 @@ struct DecodeLaunch {
   const DeviceItem* items = nullptr;
   float* part_o = nullptr;   // [num_partials, Hq, head_dim]
   float* part_md = nullptr;  // [num_partials, Hq, 2]: (m in log2 units, d)
-  int num_split = 0;
+  int num_split = 0;                       // merge tasks
   const MergeTask* merge_tasks = nullptr;  // [num_split]
 };
 
-bool decode_supported(int kv_dtype, int head_dim, int group, int q_bf16, int page_size);
-bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int q_bf16, int page_size);
+// `rows` is group x (query tokens per work item); rows > group (several new
+// tokens per request) is served by the MFMA kernel only.
+bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size);
+bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
-hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int q_bf16, int page_size,
-                            int* wgs_per_cu);
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
+                            int page_size, int* wgs_per_cu);
 
 }  // namespace pkd

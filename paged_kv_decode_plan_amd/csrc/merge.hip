@@ -7,12 +7,16 @@
 // exp(m_b - m) and added; then normalises: out = o / d, lse = m + ln d
 // (partial m is kept in log2 units, so the kernel uses exp2).
 //
-// One workgroup per (split request, query head). Thread (s, p) owns output
-// dims 4p..4p+3 and folds the partials whose slot is congruent to s modulo S
+// One workgroup per (merge task, query head): a task is one q row of a split
+// request, whose partial states are the rows first + c * stride, c < count
+// (stride 1 with one query token per request; with several new tokens the
+// chunks' rows of one token are that many apart). Thread (s, p) owns output
+// dims 4p..4p+3 and folds the partials c congruent to s modulo S
 // (S = 512 / (head_dim / 4) subsets), four at a time with all their loads
 // issued first; the S subset states are then merged through shared memory.
-// The (request, first slot, end slot) record comes from the plan in one
-// 16-byte load.
+// The empty state (m = -inf, d = 0: a chunk wholly past a new token's causal
+// limit) is the identity of the fold. The task record comes from the plan in
+// one 16-byte load.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -52,22 +56,23 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   float M = -INFINITY, Dn = 0.f;
   float4 O = {0.f, 0.f, 0.f, 0.f};
   constexpr int kU = 4;
-  for (int i0 = t.begin + sub; i0 < t.end; i0 += kU * kSub) {
+  for (int c0 = sub; c0 < t.count; c0 += kU * kSub) {
     float2 mdv[kU];
     float4 ov[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int i = min(i0 + u * kSub, t.end - 1);  // a clamped repeat is skipped below
-      const int64_t row = int64_t(i) * H + h;
+      const int c = min(c0 + u * kSub, t.count - 1);  // a clamped repeat is skipped below
+      const int64_t row = (int64_t(t.first) + int64_t(c) * t.stride) * H + h;
       mdv[u] = md[row];
       ov[u] = po[row * kQuads + qd];
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      if (i0 + u * kSub < t.end) {
+      if (c0 + u * kSub < t.count) {
         const float m_new = fmaxf(M, mdv[u].x);
-        const float sa = __builtin_amdgcn_exp2f(M - m_new);  // 0 on the first partial
-        const float sb = __builtin_amdgcn_exp2f(mdv[u].x - m_new);
+        // 0 on the first partial (M = -inf), and for an empty partial
+        const float sa = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - m_new);
+        const float sb = mdv[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mdv[u].x - m_new);
         Dn = Dn * sa + mdv[u].y * sb;
         O.x = O.x * sa + ov[u].x * sb;
         O.y = O.y * sa + ov[u].y * sb;
@@ -91,14 +96,14 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     float4 A = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < kSub; ++k) {
-      const float w = __builtin_amdgcn_exp2f(sm[k] - Mt);  // 0 for an empty subset
+      const float w = sm[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[k] - Mt);  // empty subset
       Dt += sd[k] * w;
       A.x += so[k][qd].x * w;
       A.y += so[k][qd].y * w;
       A.z += so[k][qd].z * w;
       A.w += so[k][qd].w * w;
     }
-    const int64_t row = int64_t(t.request) * H + h;
+    const int64_t row = int64_t(t.out_row) * H + h;
     const float inv = 1.0f / Dt;
     if (a.out_bf16) {
       const uint2 packed = {

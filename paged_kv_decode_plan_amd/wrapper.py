@@ -50,7 +50,7 @@ class Plan:
     def __init__(self, indptr, last_page_len, num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int, q_dtype: int, kv_dtype: int, out_dtype: int,
                  sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
-                 min_chunk_pages: int = 0, device: int = 0):
+                 min_chunk_pages: int = 0, device: int = 0, qo_indptr=None):
         lib = _lib.load()
         self._lib = lib
         self._handle = ctypes.c_void_p()
@@ -59,6 +59,9 @@ class Plan:
         B = len(self.last_page_len)
         if len(self.indptr) != B + 1:
             raise ValueError("indptr must have batch+1 entries")
+        self.qo_indptr = None if qo_indptr is None else _host_i32(qo_indptr)
+        if self.qo_indptr is not None and len(self.qo_indptr) != B + 1:
+            raise ValueError("qo_indptr must have batch+1 entries")
         a = _lib.PlanArgs()
         a.batch = B
         a.indptr = self.indptr.ctypes.data_as(_lib._c_i32p)
@@ -75,16 +78,19 @@ class Plan:
         a.balance = balance
         a.min_chunk_pages = min_chunk_pages
         a.device = device
+        if self.qo_indptr is not None:
+            a.qo_indptr = self.qo_indptr.ctypes.data_as(_lib._c_i32p)
         _lib.check(lib.pkd_plan_create(ctypes.byref(a), ctypes.byref(self._handle)))
         info = _lib.PlanInfo()
         _lib.check(lib.pkd_plan_get_info(self._handle, ctypes.byref(info)))
         self.info = {f: getattr(info, f) for f, _ in _lib.PlanInfo._fields_}
         self.batch, self.num_qo_heads, self.num_kv_heads = B, num_qo_heads, num_kv_heads
+        self.query_rows = self.info["query_rows"]
         self.head_dim, self.page_size = head_dim, page_size
         self.q_dtype, self.kv_dtype, self.out_dtype = q_dtype, kv_dtype, out_dtype
 
     def worklist(self):
-        """(items int32[num_items, 5], merge_indptr int32[B+1], split_requests int32[S])."""
+        """(items int32[num_items, 8], merge_indptr int32[B+1], split_requests int32[S])."""
         n = self.info["num_items"]
         items = np.zeros((n, _lib.ITEM_COLS), dtype=np.int32)
         merge = np.zeros(self.batch + 1, dtype=np.int32)
@@ -119,11 +125,11 @@ class Plan:
 
 def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                    kv_dtype="bf16", q_dtype="bf16", out_dtype="f32", slots=1024, balance=0,
-                   min_chunk_pages=0):
+                   min_chunk_pages=0, qo_indptr=None):
     """Host-only: build a plan with an explicit slot count and return its decisions."""
     p = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
              _dtype_code(q_dtype), _dtype_code(kv_dtype), _dtype_code(out_dtype), None, slots,
-             balance, min_chunk_pages)
+             balance, min_chunk_pages, qo_indptr=qo_indptr)
     items, merge, split = p.worklist()
     info = dict(p.info)
     p.close()
@@ -162,7 +168,10 @@ class BatchDecodeWithPagedKVCacheWrapper:
              head_dim: int, page_size: int, pos_encoding_mode: str = "NONE",
              q_data_type=None, kv_data_type=None, out_data_type=None, data_type=None,
              sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
-             min_chunk_pages: int = 0) -> None:
+             min_chunk_pages: int = 0, qo_indptr=None) -> None:
+        """Plan one batch. ``qo_indptr`` (host, [batch+1]) gives request r the q
+        rows ``qo_indptr[r]:qo_indptr[r+1]``: its newest tokens, attended
+        causally; omitted, every request has one query token (q row r)."""
         import torch
         if pos_encoding_mode != "NONE":
             raise ValueError("only pos_encoding_mode='NONE' is supported")
@@ -174,7 +183,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         dev = self._ws.device.index or 0
         self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                           _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
-                          slots, balance, min_chunk_pages, dev)
+                          slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr)
         self._indices = indices if isinstance(indices, torch.Tensor) else torch.as_tensor(
             np.asarray(indices, dtype=np.int32))
         if self._indices.device != self._ws.device or self._indices.dtype != torch.int32:
@@ -202,8 +211,9 @@ class BatchDecodeWithPagedKVCacheWrapper:
         if p is None:
             raise RuntimeError("plan() must be called before run()")
         k, v = _split_kv(paged_kv_cache)
-        if q.shape != (p.batch, p.num_qo_heads, p.head_dim) or not q.is_contiguous():
-            raise ValueError(f"q must be contiguous [{p.batch}, {p.num_qo_heads}, {p.head_dim}]")
+        if q.shape != (p.query_rows, p.num_qo_heads, p.head_dim) or not q.is_contiguous():
+            raise ValueError(
+                f"q must be contiguous [{p.query_rows}, {p.num_qo_heads}, {p.head_dim}]")
         if _dtype_code(q.dtype) != p.q_dtype or _dtype_code(k.dtype) != p.kv_dtype:
             raise _lib.PkdError(_lib.PKD_ERR_PLAN_MISMATCH, "q/KV dtypes differ from the plan")
         if k.shape[1] != p.page_size or k.shape[2] != p.num_kv_heads or k.shape[3] != p.head_dim:
@@ -214,7 +224,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         elif out.dtype != out_dt or out.shape != q.shape or not out.is_contiguous():
             raise ValueError("out has the wrong dtype, shape or layout")
         if return_lse and lse is None:
-            lse = torch.empty((p.batch, p.num_qo_heads), dtype=torch.float32, device=q.device)
+            lse = torch.empty((p.query_rows, p.num_qo_heads), dtype=torch.float32, device=q.device)
         if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()):
             raise ValueError("lse must be contiguous float32 [batch, num_qo_heads]")
         a = _lib.RunArgs()

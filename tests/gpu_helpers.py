@@ -32,6 +32,7 @@ def to_device(case: dict, device=DEV) -> dict:
         "k_scale": None,
         "v_scale": None,
         "workload": w,
+        "qo_indptr": case.get("qo_indptr"),
     }
     if w.kv_dtype == "e4m3":
         d["k_scale"] = torch.from_numpy(case["k_scale"]).to(device).contiguous()
@@ -59,7 +60,7 @@ def run_hip(dcase: dict, out_dtype="f32", slots=0, balance=0, min_chunk_pages=0,
                  w.page_size, q_data_type=dcase["q"].dtype,
                  kv_data_type=("e4m3" if w.kv_dtype == "e4m3" else dcase["kv"].dtype),
                  out_data_type=odt, sm_scale=w.scale(), slots=slots, balance=balance,
-                 min_chunk_pages=min_chunk_pages)
+                 min_chunk_pages=min_chunk_pages, qo_indptr=dcase.get("qo_indptr"))
     out, l = wrapper.run(dcase["q"], dcase["kv"] if kv is None else kv, return_lse=lse,
                          k_scale=dcase["k_scale"], v_scale=dcase["v_scale"])
     torch.cuda.synchronize()
@@ -115,7 +116,9 @@ def sample_request_case(dcase: dict, r: int) -> dict:
         kvh = kv.cpu().numpy()
     else:
         kvh = kv.cpu().numpy().view(np.uint8)
-    q = dcase["q"][r:r + 1]
+    qo = dcase.get("qo_indptr")
+    q0, q1 = (r, r + 1) if qo is None else (int(qo[r]), int(qo[r + 1]))
+    q = dcase["q"][q0:q1]
     qh = q.view(torch.int16).cpu().numpy().view(np.uint16) if w.q_dtype == "bf16" else q.cpu().numpy()
     n = len(pages)
     sub = {
@@ -126,6 +129,7 @@ def sample_request_case(dcase: dict, r: int) -> dict:
         "num_pages": n,
         "workload": w,
         "k_scale": None, "v_scale": None,
+        "qo_indptr": None if qo is None else np.array([0, q1 - q0], np.int32),
     }
     if w.kv_dtype == "e4m3":
         sub["k_scale"] = dcase["k_scale"].index_select(0, pages).cpu().numpy()

@@ -17,8 +17,25 @@ def test_hand_worked_partitions():
         p = oplan.plan(c["indptr"], c["last_page_len"], ex["page_size"], ex["num_kv_heads"],
                        c["slots"], c["balance"], c["min_chunk_pages"])
         assert p["chunk_pages"] == c["chunk_pages"], c["work"]
+        assert p["items"][:, :5].tolist() == c["items"], c["work"]
+        assert p["merge_indptr"].tolist() == c["merge_indptr"], c["work"]
+        # one query token per request: its own row, and it sees the whole item
+        items = p["items"]
+        assert np.array_equal(items[:, 5], items[:, 0])
+        assert np.all(items[:, 6] == 1) and np.array_equal(items[:, 7], items[:, 3])
+
+
+def test_hand_worked_multi_query_partitions():
+    with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    for c in ex["multi_query_cases"]:
+        p = oplan.plan(c["indptr"], c["last_page_len"], ex["page_size"], ex["num_kv_heads"],
+                       c["slots"], c["balance"], c["min_chunk_pages"], c["qo_indptr"],
+                       c["queries_per_item"])
+        assert p["chunk_pages"] == c["chunk_pages"], c["work"]
         assert p["items"].tolist() == c["items"], c["work"]
         assert p["merge_indptr"].tolist() == c["merge_indptr"], c["work"]
+        assert p["num_partials"] == c["num_partials"], c["work"]
 
 
 def _random_table(rng, B, P, max_pages):
@@ -71,6 +88,51 @@ def test_partition_invariants(seed):
     keys = list(zip(-items[:, 3], items[:, 0], items[:, 1]))
     assert keys == sorted(keys)
     assert p["split_requests"].tolist() == [r for r in range(B) if -(-n[r] // C) > 1]
+
+
+@pytest.mark.parametrize("seed", range(25))
+def test_multi_query_partition_invariants(seed):
+    """Every new token of every request sees each of its pages through exactly one
+    item, with the causal token count; partial rows are a permutation."""
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 20))
+    P = int(rng.choice([1, 4, 16]))
+    indptr, last = _random_table(rng, B, P, int(rng.integers(1, 60)))
+    n = np.diff(indptr)
+    L = (n - 1) * P + last
+    nq = np.minimum(rng.integers(1, 12, size=B), L)
+    qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    Q = int(rng.integers(1, 9))
+    hkv = int(rng.choice([1, 2, 8]))
+    p = oplan.plan(indptr, last, P, hkv, int(rng.integers(1, 512)), int(rng.integers(1, 4)),
+                   int(rng.integers(1, 10)), qo, Q)
+    C = p["chunk_pages"]
+    items = p["items"]
+    U = -(-nq // Q)
+    units, S = int(U.sum()), int((n * U).sum())
+    assert len(items) == int((-(-n // C) * U).sum())
+    rows_written = []
+    for r in range(B):
+        for j in range(int(nq[r])):
+            row = int(qo[r]) + j
+            mine = items[(items[:, 0] == r) & (items[:, 5] <= row) & (row < items[:, 5] + items[:, 6])]
+            mine = mine[np.argsort(mine[:, 1])]
+            assert mine[0, 1] == indptr[r] and mine[-1, 2] == indptr[r + 1]
+            assert np.all(mine[1:, 1] == mine[:-1, 2])
+            own = int(L[r] - nq[r] + j)  # position of this token in its request
+            for it in mine:
+                i = row - it[5]
+                first_tok = (it[1] - indptr[r]) * P
+                seen = sum(1 for t in range(first_tok, first_tok + it[3]) if t <= own)
+                assert max(0, min(it[3], it[7] + i)) == seen
+                if it[4] >= 0:
+                    rows_written.append(int(it[4]) + i)
+    assert sorted(rows_written) == list(range(p["num_partials"]))
+    G = -(-n // C)
+    assert p["merge_indptr"].tolist() == np.concatenate(
+        [[0], np.cumsum(np.where(G > 1, G * nq, 0))]).tolist()
+    keys = [(-it[3], it[0], it[1], it[5]) for it in items]
+    assert keys == sorted(keys)
 
 
 def test_uniform_batch_that_fills_the_device_is_not_split():

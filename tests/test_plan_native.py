@@ -12,12 +12,14 @@ from workloads import CONFIGS, page_table
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
-def _both(indptr, last, P, hkv, slots, balance, cmin, hq=None, d=128, kv="bf16"):
+def _both(indptr, last, P, hkv, slots, balance, cmin, hq=None, d=128, kv="bf16",
+          qo_indptr=None):
     hq = hq or hkv
     info, items, merge, split = pk.plan_partition(indptr, last, hq, hkv, d, P, kv_dtype=kv,
                                                   q_dtype="bf16", slots=slots, balance=balance,
-                                                  min_chunk_pages=cmin)
-    ref = oplan.plan(indptr, last, P, hkv, slots, balance, cmin)
+                                                  min_chunk_pages=cmin, qo_indptr=qo_indptr)
+    ref = oplan.plan(indptr, last, P, hkv, slots, balance, cmin, qo_indptr,
+                     info["queries_per_item"])
     return info, items, merge, split, ref
 
 
@@ -36,9 +38,65 @@ def test_golden_partitions_native():
     for c in ex["cases"]:
         info, items, merge, split, ref = _both(c["indptr"], c["last_page_len"], ex["page_size"],
                                                1, c["slots"], c["balance"], c["min_chunk_pages"])
-        assert items.tolist() == c["items"]
+        assert items[:, :5].tolist() == c["items"]
         _assert_same(info, items, merge, split, ref)
 
+
+def test_golden_multi_query_partitions_native():
+    """Eight query heads per KV head: a work item carries 16 / 8 = 2 new tokens."""
+    with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
+        ex = json.load(f)
+    for c in ex["multi_query_cases"]:
+        info, items, merge, split, ref = _both(
+            c["indptr"], c["last_page_len"], ex["page_size"], 1, c["slots"], c["balance"],
+            c["min_chunk_pages"], hq=8, qo_indptr=c["qo_indptr"])
+        assert info["queries_per_item"] == c["queries_per_item"]
+        assert items.tolist() == c["items"]
+        assert info["num_partials"] == c["num_partials"]
+        assert info["query_rows"] == c["qo_indptr"][-1]
+        _assert_same(info, items, merge, split, ref)
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_multi_query_tables_bit_exact(seed):
+    rng = np.random.default_rng(5000 + seed)
+    B = int(rng.integers(1, 120))
+    P = int(rng.choice([1, 16, 64]))
+    n = rng.integers(1, int(rng.integers(2, 200)), size=B)
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = rng.integers(1, P + 1, size=B).astype(np.int32)
+    L = (n - 1) * P + last
+    nq = np.minimum(rng.integers(1, int(rng.integers(2, 40)), size=B), L)
+    qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    hkv = int(rng.choice([1, 2, 8]))
+    g = int(rng.choice([1, 2, 4, 8, 16]))
+    out = _both(indptr, last, P, hkv, int(rng.integers(1, 4096)), int(rng.integers(1, 4)),
+                int(rng.integers(1, 32)), hq=hkv * g, kv=str(rng.choice(["bf16", "e4m3"])),
+                qo_indptr=qo)
+    info = out[0]
+    assert info["queries_per_item"] == (max(1, 16 // g) if nq.max() > 1 else 1)
+    assert info["max_qo_len"] == nq.max() and info["query_rows"] == qo[-1]
+    _assert_same(*out[:4], out[4])
+
+
+def test_multi_query_needs_the_mfma_path():
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 2], [5], 4, 4, 64, 16, q_dtype="bf16", qo_indptr=[0, 2])
+    assert e.value.code == pk._lib.PKD_ERR_UNSUPPORTED
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 2], [5], 4, 4, 128, 16, kv_dtype="f32", qo_indptr=[0, 2])
+    assert e.value.code == pk._lib.PKD_ERR_UNSUPPORTED
+    # one token per request through qo_indptr is plain decode: any kernel
+    info, items, *_ = pk.plan_partition([0, 2], [5], 4, 4, 64, 16, kv_dtype="f32",
+                                        qo_indptr=[0, 1])
+    assert info["queries_per_item"] == 1 and items[0, 6] == 1
+
+
+@pytest.mark.parametrize("qo", [[0, 0, 2], [0, 2, 1], [1, 2, 3], [0, 30, 31]])
+def test_invalid_query_layouts_rejected_natively(qo):
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 2, 3], [5, 3], 8, 2, 128, 16, qo_indptr=qo)
+    assert e.value.code == pk._lib.PKD_ERR_INVALID_ARGUMENT
 
 @pytest.mark.parametrize("seed", range(40))
 def test_random_tables_bit_exact(seed):
@@ -61,7 +119,7 @@ def test_workload_tables_bit_exact(name, slots):
     t = page_table(w, seed=list(CONFIGS).index(name) + 1)
     cmin = max(1, -(-256 // w.page_size))
     out = _both(t["indptr"], t["last_page_len"], w.page_size, w.num_kv_heads, slots, 2, cmin,
-                hq=w.num_qo_heads, d=w.head_dim, kv=w.kv_dtype)
+                hq=w.num_qo_heads, d=w.head_dim, kv=w.kv_dtype, qo_indptr=t["qo_indptr"])
     _assert_same(*out[:4], out[4])
 
 
@@ -78,5 +136,14 @@ def test_workspace_size_formula():
     assert info["num_split_requests"] == 2 and info["num_partials"] > 0
     parts = info["num_partials"] * 32
     a = lambda x: (x + 255) // 256 * 256
-    header = a(a(info["num_items"] * 16) + max(info["num_split_requests"], 1) * 16)
+    assert info["num_merge_tasks"] == info["num_split_requests"]
+    header = a(a(info["num_items"] * 32) + max(info["num_merge_tasks"], 1) * 16)
+    assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+    # several new tokens: one merge task and one partial row per token of a split request
+    info, items, merge, split = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64,
+                                                  balance=1, min_chunk_pages=1,
+                                                  qo_indptr=[0, 3, 5])
+    assert info["num_merge_tasks"] == 5 and info["queries_per_item"] == 4
+    parts = info["num_partials"] * 32
+    header = a(a(info["num_items"] * 32) + info["num_merge_tasks"] * 16)
     assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)

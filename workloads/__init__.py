@@ -13,5 +13,6 @@ from .synthetic import (  # noqa: F401
     explicit_table,
     host_case,
     page_table,
+    query_rows,
     read_mask,
 )

@@ -9,8 +9,10 @@ bytes itself):
   pattern as ``uint16``; ``"e4m3"`` storage is the raw OCP E4M3FN byte as
   ``uint8`` with fp32 scales ``k_scale``/``v_scale`` of shape
   ``[num_pages, num_kv_heads]`` (one per page and KV head).
-* ``q`` is ``[batch, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
-  storage.
+* ``q`` is ``[rows, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
+  storage: one row per request, or, for a workload with several new tokens
+  per request, the ragged rows ``qo_indptr[r]:qo_indptr[r+1]`` of request r
+  (``qo_indptr`` int32 ``[batch+1]``; ``None`` for one token per request).
 * The page table is ``indptr`` (int32 ``[batch+1]``), ``indices`` (int32 page
   ids) and ``last_page_len`` (int32 ``[batch]``), as in the paged-KV wrapper
   of "FlashDecoding + FlashInfer — the decode-time attention story", §"The API
@@ -46,6 +48,9 @@ class Workload:
     ``("uniform", lo, hi)`` (inclusive) or ``("list", (L0, L1, ...))``.
     ``pool_pages`` is the size of the page pool; ``None`` means exactly the
     pages the batch uses. Page ids are a random permutation of the pool.
+    ``queries`` is ``None`` (one query token per request) or a spec of the
+    same kinds as ``context`` for the number of new tokens per request,
+    clipped to ``[1, L_r]``.
     """
 
     name: str
@@ -59,6 +64,7 @@ class Workload:
     context: tuple
     pool_pages: Optional[int] = None
     sm_scale: Optional[float] = None
+    queries: Optional[tuple] = None
 
     @property
     def group(self) -> int:
@@ -85,32 +91,49 @@ CONFIGS = {
     # fp8 (E4M3) KV with one fp32 scale per (page, KV head); q bf16.
     "fp8_kv_e4m3": Workload(
         "fp8_kv_e4m3", 128, 32, 8, 128, 16, "e4m3", "bf16", ("uniform", 1024, 32768)),
+    # Speculative-style multi-token decode: the Llama-3-8B-shaped batch with 4
+    # new tokens per request (16 query rows per KV head).
+    "spec4_llama3_8b_bf16": Workload(
+        "spec4_llama3_8b_bf16", 64, 32, 8, 128, 16, "bf16", "bf16", ("fixed", 2048),
+        queries=("fixed", 4)),
 }
 CONFIG_ORDER = list(CONFIGS)
 
 
 def custom_workload(batch, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype,
                     q_dtype, lens: Sequence[int], pool_pages=None, sm_scale=None,
-                    name="custom") -> Workload:
+                    name="custom", qo_lens: Optional[Sequence[int]] = None) -> Workload:
+    queries = None if qo_lens is None else ("list", tuple(int(x) for x in qo_lens))
     return Workload(name, batch, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype,
-                    q_dtype, ("list", tuple(int(x) for x in lens)), pool_pages, sm_scale)
+                    q_dtype, ("list", tuple(int(x) for x in lens)), pool_pages, sm_scale,
+                    queries)
+
+
+def _draw_lengths(spec: tuple, batch: int, rng: np.random.Generator) -> np.ndarray:
+    kind = spec[0]
+    if kind == "fixed":
+        return np.full(batch, int(spec[1]), dtype=np.int64)
+    if kind == "loguniform":
+        lo, hi = spec[1], spec[2]
+        x = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=batch)))
+        return np.clip(x, lo, hi).astype(np.int64)
+    if kind == "uniform":
+        return rng.integers(spec[1], spec[2], size=batch, endpoint=True).astype(np.int64)
+    if kind == "list":
+        lens = np.asarray(spec[1], dtype=np.int64)
+        assert lens.shape == (batch,)
+        return lens
+    raise ValueError(f"unknown length kind {kind!r}")
 
 
 def _context_lengths(w: Workload, rng: np.random.Generator) -> np.ndarray:
-    kind = w.context[0]
-    if kind == "fixed":
-        return np.full(w.batch, int(w.context[1]), dtype=np.int64)
-    if kind == "loguniform":
-        lo, hi = w.context[1], w.context[2]
-        x = np.floor(np.exp(rng.uniform(math.log(lo), math.log(hi), size=w.batch)))
-        return np.clip(x, lo, hi).astype(np.int64)
-    if kind == "uniform":
-        return rng.integers(w.context[1], w.context[2], size=w.batch, endpoint=True).astype(np.int64)
-    if kind == "list":
-        lens = np.asarray(w.context[1], dtype=np.int64)
-        assert lens.shape == (w.batch,)
-        return lens
-    raise ValueError(f"unknown context kind {kind!r}")
+    return _draw_lengths(w.context, w.batch, rng)
+
+
+def query_rows(table: dict) -> int:
+    """Number of q rows of a page table (one per request unless ``qo_indptr``)."""
+    qo = table.get("qo_indptr")
+    return len(table["last_page_len"]) if qo is None else int(qo[-1])
 
 
 def page_table(w: Workload, seed: int) -> dict:
@@ -127,12 +150,18 @@ def page_table(w: Workload, seed: int) -> dict:
     indices = rng.permutation(pool)[:used].astype(np.int32)
     indptr = np.zeros(w.batch + 1, dtype=np.int32)
     indptr[1:] = np.cumsum(n)
+    qo_indptr = None
+    if w.queries is not None:
+        nq = np.clip(_draw_lengths(w.queries, w.batch, np.random.default_rng([seed, 2])), 1, lens)
+        qo_indptr = np.zeros(w.batch + 1, dtype=np.int32)
+        qo_indptr[1:] = np.cumsum(nq)
     return {
         "indptr": indptr,
         "indices": indices,
         "last_page_len": last.astype(np.int32),
         "kv_lens": lens.astype(np.int64),
         "num_pages": pool,
+        "qo_indptr": qo_indptr,
     }
 
 
@@ -146,7 +175,7 @@ def explicit_table(page_lists: Sequence[Sequence[int]], last_page_len: Sequence[
     last = np.asarray(last_page_len, dtype=np.int32)
     lens = (n - 1) * page_size + last
     return {"indptr": indptr, "indices": indices, "last_page_len": last,
-            "kv_lens": lens.astype(np.int64), "num_pages": int(num_pages)}
+            "kv_lens": lens.astype(np.int64), "num_pages": int(num_pages), "qo_indptr": None}
 
 
 def read_mask(table: dict, page_size: int) -> np.ndarray:
@@ -190,7 +219,7 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
         table = page_table(w, seed)
     rng = np.random.default_rng([seed, 1])
     P, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
-    q32 = rng.standard_normal((w.batch, w.num_qo_heads, D), dtype=np.float32)
+    q32 = rng.standard_normal((query_rows(table), w.num_qo_heads, D), dtype=np.float32)
     pool32 = rng.standard_normal((table["num_pages"], 2, P, Hkv, D), dtype=np.float32)
     k_scale = v_scale = None
     if w.kv_dtype == "f32":
@@ -233,7 +262,7 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
     P, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
     npg = table["num_pages"]
     qdt = torch.float32 if w.q_dtype == "f32" else torch.bfloat16
-    q = torch.randn((w.batch, w.num_qo_heads, D), generator=g, device=device,
+    q = torch.randn((query_rows(table), w.num_qo_heads, D), generator=g, device=device,
                     dtype=torch.float32).to(qdt)
     k_scale = v_scale = None
     if w.kv_dtype in ("f32", "bf16"):
