@@ -95,6 +95,14 @@ typedef struct pkd_plan pkd_plan;
  *                   request needs bf16 q, bf16 or e4m3 KV and head_dim 128
  *                   (else UNSUPPORTED); a work item then carries up to
  *                   16 / group of a request's tokens.
+ *  non_causal       0: the causal rule above. 1: every q row of request r
+ *                   sees all of its KV tokens and q_r may exceed them: the
+ *                   shared-prefix level of cascade attention, where the
+ *                   queries of all requests sharing a prefix attend to it as
+ *                   one request ("Cascade Attention" of "FlashInfer vs
+ *                   FlashAttention-3: GPU Kernel Optimization & FP8 Serving
+ *                   Latency", §"Key Features"); combine its output with the
+ *                   per-request suffix level through pkd_merge_states.
  */
 typedef struct {
   int32_t batch;
@@ -113,6 +121,7 @@ typedef struct {
   int32_t min_chunk_pages;
   int32_t device;
   const int32_t* qo_indptr;
+  int32_t non_causal;
 } pkd_plan_args;
 
 /* What a plan decided (pkd_plan_get_info). */
@@ -231,6 +240,46 @@ int pkd_run_stages(const pkd_plan* plan, const pkd_run_args* args, int32_t stage
  * and is handed to another plan only after its last copy has completed, so
  * destroying a plan never waits. NULL is a no-op. */
 void pkd_plan_destroy(pkd_plan* plan);
+
+/* Arguments of pkd_merge_states. Device pointers.
+ *
+ *  rows, num_heads, head_dim   shape [rows, num_heads, head_dim] of v_a, v_b
+ *                              and v_out; head_dim a multiple of 4
+ *  in_dtype                    PKD_DTYPE_F32 or PKD_DTYPE_BF16 (v_a, v_b)
+ *  out_dtype                   PKD_DTYPE_F32 or PKD_DTYPE_BF16 (v_out)
+ *  v_a, s_a, v_b, s_b          two normalised attention results over disjoint
+ *                              token sets: output rows and their natural-log
+ *                              log-sum-exp, float [rows, num_heads];
+ *                              s = -inf marks a result over no tokens
+ *  v_out, s_out                merged result; s_out may be NULL; v_out may
+ *                              alias v_a or v_b when the dtypes agree, s_out
+ *                              may alias s_a or s_b
+ *  stream                      hipStream_t
+ *
+ * Pointers to f32 rows must be 16-byte aligned, to bf16 rows 8-byte aligned. */
+typedef struct {
+  int64_t rows;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t in_dtype;
+  int32_t out_dtype;
+  const void* v_a;
+  const float* s_a;
+  const void* v_b;
+  const float* s_b;
+  void* v_out;
+  float* s_out;
+  void* stream;
+} pkd_merge_states_args;
+
+/* Merge two normalised results of the same queries over disjoint token sets
+ * with the online-softmax rule of "FlashDecoding + FlashInfer — the
+ * decode-time attention story", §"FlashDecoding — the split-KV trick": a
+ * result (v, s) is the state (m = s, d = 1, o = v), so
+ *   s_out = max(s_a, s_b) + ln(w_a + w_b),  w_x = exp(s_x - max(s_a, s_b)),
+ *   v_out = (w_a v_a + w_b v_b) / (w_a + w_b).
+ * Both sides empty gives v_out = 0, s_out = -inf. Enqueues one kernel. */
+int pkd_merge_states(const pkd_merge_states_args* args);
 
 /* Workgroups of the decode kernel selected for (q_dtype, kv_dtype, head_dim,
  * group, page_size) that one compute unit holds at once, and the device's

@@ -26,6 +26,13 @@ Readings taken where the pages are silent (each listed in the design doc):
   request are its last n KV tokens, in order, and new token i (0-based) sees
   the KV tokens up to and including its own position, i.e. the first
   ``L_r - n + 1 + i`` of them (causal within the new tokens).
+* Cascade attention over a shared prefix (the "Cascade Attention" of
+  "FlashInfer vs FlashAttention-3: GPU Kernel Optimization & FP8 Serving
+  Latency", §"Key Features"): the queries of every request that shares a
+  prefix attend to it as one batch, so there the rows are not causal
+  (``causal=False``: every row sees all of its request's tokens). The
+  cascade's result is plain decode over prefix + suffix, which
+  ``merge.merge_normalized`` reaches from the two levels.
 
 The full softmax over each request's gathered tokens is materialised; no
 tiling, splitting or reordering is done here (``oracle.merge`` holds the split
@@ -92,7 +99,7 @@ def visible_tokens(L: int, n_new: int, i: int) -> int:
 
 def decode(q, kv, indptr, indices, last_page_len, *, num_kv_heads: int, q_dtype: str,
            kv_dtype: str, sm_scale: Optional[float] = None, k_scale=None, v_scale=None,
-           requests: Optional[Iterable[int]] = None, qo_indptr=None):
+           requests: Optional[Iterable[int]] = None, qo_indptr=None, causal: bool = True):
     """Decode attention for every (query token, query head).
 
     Without ``qo_indptr`` q holds one token per request (``[B, Hq, D]``). With
@@ -118,13 +125,13 @@ def decode(q, kv, indptr, indices, last_page_len, *, num_kv_heads: int, q_dtype:
     for r in (range(B) if requests is None else requests):
         L = request_length(indptr, last_page_len, kv.shape[2], r)
         n_new = int(qo[r + 1] - qo[r])
-        if n_new > L:
+        if causal and n_new > L:
             raise ValueError("a request has more query tokens than KV tokens")
         for kvh in range(num_kv_heads):
             K, V = gather_request(kv, indptr, indices, last_page_len, r, kvh, kv_dtype,
                                   k_scale, v_scale)
             for i in range(n_new):
-                vis = visible_tokens(L, n_new, i)
+                vis = visible_tokens(L, n_new, i) if causal else L
                 row = int(qo[r]) + i
                 for h in range(kvh * g, (kvh + 1) * g):
                     out[row, h], lse[row, h] = attend(q64[row, h], K[:vis], V[:vis], scale)

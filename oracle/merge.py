@@ -74,6 +74,26 @@ def finalize(state: State):
     return o / d, m + math.log(d)
 
 
+def merge_normalized(v_a, lse_a, v_b, lse_b):
+    """Merge two normalised attention results over disjoint token sets.
+
+    A result ``(v, lse)`` (output row and natural-log log-sum-exp) is the state
+    ``(lse, 1, v)``: ``o / d = v`` and ``m + ln d = lse``. Arrays ``v_*``
+    ``[..., D]`` and ``lse_*`` ``[...]``; each row is merged with ``merge`` and
+    finalised. This is how the levels of cascade attention combine.
+    """
+    v_a = np.asarray(v_a, dtype=np.float64)
+    v_b = np.asarray(v_b, dtype=np.float64)
+    lse_a = np.asarray(lse_a, dtype=np.float64)
+    lse_b = np.asarray(lse_b, dtype=np.float64)
+    out = np.empty(np.broadcast_shapes(v_a.shape, v_b.shape))
+    lse = np.empty(out.shape[:-1])
+    for idx in np.ndindex(*lse.shape):
+        st = merge((float(lse_a[idx]), 1.0, v_a[idx]), (float(lse_b[idx]), 1.0, v_b[idx]))
+        out[idx], lse[idx] = finalize(st)
+    return out, lse
+
+
 def split_attend(qh: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float,
                  bounds: Iterable[Tuple[int, int]]):
     """Attention of one query computed chunk by chunk and merged.

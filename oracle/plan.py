@@ -48,7 +48,9 @@ token i. Each item also records its first q row ``qo_indptr[r] + b*Q``, its
 token count, and how many of its KV tokens the block's first token sees,
 ``min(kv_len, L_r - q_r + 1 + b*Q - c*C*P)`` (token i of the block sees
 ``min(kv_len, that + i)``; a value <= 0 means it sees none). Ties in step 5
-go by request, chunk, then query block.
+go by request, chunk, then query block. With ``causal=False`` (the shared
+prefix of cascade attention) every row sees the whole item (``visible =
+kv_len``) and a request may have more query rows than KV tokens.
 
 Test infrastructure: see the package docstring.
 """
@@ -66,7 +68,8 @@ ITEM_COLUMNS = ("request", "page_begin", "page_end", "kv_len", "partial_slot", "
 
 
 def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
-         balance: int, min_chunk_pages: int, qo_indptr=None, queries_per_item: int = 1) -> dict:
+         balance: int, min_chunk_pages: int, qo_indptr=None, queries_per_item: int = 1,
+         causal: bool = True) -> dict:
     indptr = [int(x) for x in indptr]
     last = [int(x) for x in last_page_len]
     B = len(last)
@@ -86,8 +89,8 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
     if len(qo) != B + 1 or qo[0] != 0:
         raise ValueError("qo_indptr must have batch+1 entries starting at 0")
     nq = [qo[r + 1] - qo[r] for r in range(B)]
-    if any(not (1 <= nq[r] <= L[r]) for r in range(B)):
-        raise ValueError("every request needs between 1 and L_r query tokens")
+    if any(nq[r] < 1 or (causal and nq[r] > L[r]) for r in range(B)):
+        raise ValueError("every request needs at least 1 (causal: at most L_r) query tokens")
     Q = queries_per_item
     U = [_ceil_div(x, Q) for x in nq]  # query blocks (units) per request
 
@@ -116,6 +119,8 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
             for b in range(U[r]):
                 q_len = min(Q, nq[r] - b * Q)
                 visible = min(kv_len, L[r] - nq[r] + 1 + b * Q - c * C * page_size)
+                if not causal:
+                    visible = kv_len
                 slot = merge_indptr[r] + c * nq[r] + b * Q if G[r] > 1 else -1
                 rows.append((r, pb, pe, kv_len, slot, qo[r] + b * Q, q_len, visible, c, b))
     rows.sort(key=lambda t: (-t[3], t[0], t[8], t[9]))

@@ -7,12 +7,16 @@ from ._lib import LIB_PATH, PkdError, load  # noqa: F401
 from .wrapper import (  # noqa: F401
     DEFAULT_WORKSPACE_BYTES,
     BatchDecodeWithPagedKVCacheWrapper,
+    CascadeBatchDecodeWrapper,
     Plan,
+    merge_state,
     plan_partition,
 )
 
 __all__ = [
     "BatchDecodeWithPagedKVCacheWrapper",
+    "CascadeBatchDecodeWrapper",
+    "merge_state",
     "Plan",
     "PkdError",
     "plan_partition",

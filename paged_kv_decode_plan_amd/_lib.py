@@ -47,6 +47,7 @@ class PlanArgs(ctypes.Structure):
         ("min_chunk_pages", ctypes.c_int32),
         ("device", ctypes.c_int32),
         ("qo_indptr", _c_i32p),
+        ("non_causal", ctypes.c_int32),
     ]
 
 
@@ -88,6 +89,23 @@ class RunArgs(ctypes.Structure):
     ]
 
 
+class MergeStatesArgs(ctypes.Structure):
+    _fields_ = [
+        ("rows", ctypes.c_int64),
+        ("num_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("in_dtype", ctypes.c_int32),
+        ("out_dtype", ctypes.c_int32),
+        ("v_a", ctypes.c_void_p),
+        ("s_a", ctypes.c_void_p),
+        ("v_b", ctypes.c_void_p),
+        ("s_b", ctypes.c_void_p),
+        ("v_out", ctypes.c_void_p),
+        ("s_out", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
 class PkdError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"pkdecode error {code}: {msg}")
@@ -125,6 +143,8 @@ def load() -> ctypes.CDLL:
     lib.pkd_run_stages.restype = ctypes.c_int
     lib.pkd_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.pkd_plan_destroy.restype = None
+    lib.pkd_merge_states.argtypes = [ctypes.POINTER(MergeStatesArgs)]
+    lib.pkd_merge_states.restype = ctypes.c_int
     lib.pkd_device_slots.argtypes = [ctypes.c_int32] * 6 + [_c_i32p, _c_i32p]
     lib.pkd_device_slots.restype = ctypes.c_int
     _lib = lib

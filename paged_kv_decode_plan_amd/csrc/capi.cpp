@@ -214,6 +214,8 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   // one request's tokens, so that its group x tokens rows fill the columns of
   // one MFMA tile.
   int32_t max_q = 1;
+  if (a->non_causal != 0 && a->non_causal != 1)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "non_causal must be 0 or 1");
   if (a->qo_indptr) {
     if (a->qo_indptr[0] != 0) return fail(PKD_ERR_INVALID_ARGUMENT, "qo_indptr[0] must be 0");
     for (int32_t r = 0; r < a->batch; ++r) {
@@ -251,6 +253,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   pin.last_page_len = a->last_page_len;
   pin.qo_indptr = max_q > 1 ? a->qo_indptr : nullptr;
   pin.queries_per_item = queries_per_item;
+  pin.causal = a->non_causal == 0;
   pin.page_size = a->page_size;
   pin.units_per_item = a->num_kv_heads;
   pin.slots = slots;
@@ -446,6 +449,41 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
     e = pkd::launch_merge(L, s);
     if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   }
+  return ok();
+}
+
+int pkd_merge_states(const pkd_merge_states_args* m) {
+  if (!m) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
+  if (m->rows < 0 || m->num_heads < 1 || m->head_dim < 4 || m->head_dim % 4)
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "rows must be >= 0, num_heads >= 1 and head_dim a positive multiple of 4");
+  for (int dt : {m->in_dtype, m->out_dtype})
+    if (dt != PKD_DTYPE_F32 && dt != PKD_DTYPE_BF16)
+      return fail(PKD_ERR_UNSUPPORTED, "merge_states takes f32 or bf16 rows (dtype %d)", dt);
+  if (m->rows == 0) return ok();
+  if (!m->v_a || !m->s_a || !m->v_b || !m->s_b || !m->v_out)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "v_a, s_a, v_b, s_b and v_out must not be NULL");
+  const uintptr_t in_align = m->in_dtype == PKD_DTYPE_F32 ? 16 : 8;
+  const uintptr_t out_align = m->out_dtype == PKD_DTYPE_F32 ? 16 : 8;
+  if (reinterpret_cast<uintptr_t>(m->v_a) % in_align ||
+      reinterpret_cast<uintptr_t>(m->v_b) % in_align ||
+      reinterpret_cast<uintptr_t>(m->v_out) % out_align)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "row pointers must be 16-byte (f32) or 8-byte (bf16) "
+                                          "aligned");
+  pkd::MergeStatesLaunch L;
+  L.rows = m->rows;
+  L.num_heads = m->num_heads;
+  L.head_dim = m->head_dim;
+  L.in_bf16 = m->in_dtype == PKD_DTYPE_BF16;
+  L.out_bf16 = m->out_dtype == PKD_DTYPE_BF16;
+  L.v_a = m->v_a;
+  L.s_a = m->s_a;
+  L.v_b = m->v_b;
+  L.s_b = m->s_b;
+  L.v_out = m->v_out;
+  L.s_out = m->s_out;
+  const hipError_t e = pkd::launch_merge_states(L, static_cast<hipStream_t>(m->stream));
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge_states launch: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -72,4 +72,19 @@ hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
 hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
                             int page_size, int* wgs_per_cu);
 
+struct MergeStatesLaunch {
+  int64_t rows = 0;
+  int num_heads = 0;
+  int head_dim = 0;
+  int in_bf16 = 0;
+  int out_bf16 = 0;
+  const void* v_a = nullptr;
+  const float* s_a = nullptr;
+  const void* v_b = nullptr;
+  const float* s_b = nullptr;
+  void* v_out = nullptr;
+  float* s_out = nullptr;
+};
+hipError_t launch_merge_states(const MergeStatesLaunch& a, hipStream_t stream);
+
 }  // namespace pkd

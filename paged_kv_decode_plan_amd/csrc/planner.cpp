@@ -47,7 +47,7 @@ std::string build_partition(const PartitionInput& in, Partition* out) {
     const int64_t L = (n - 1) * in.page_size + lp;
     if (in.qo_indptr) {
       const int64_t q = int64_t(in.qo_indptr[r + 1]) - in.qo_indptr[r];
-      if (q < 1 || q > L) {
+      if (q < 1 || (in.causal && q > L)) {
         snprintf(msg, sizeof msg,
                  "request %d has %lld query tokens; it needs between 1 and its %lld KV tokens", r,
                  (long long)q, (long long)L);
@@ -125,8 +125,9 @@ std::string build_partition(const PartitionInput& in, Partition* out) {
         w.q_len = int32_t(std::min<int64_t>(Q, nq[r] - b * Q));
         // Tokens of this chunk the block's first token sees: everything up to its
         // own position L - q_r + b*Q, counted from the chunk's first token.
-        w.visible = int32_t(std::min<int64_t>(
-            w.kv_len, L - nq[r] + 1 + b * Q - int64_t(c) * C * in.page_size));
+        w.visible = in.causal ? int32_t(std::min<int64_t>(
+                                    w.kv_len, L - nq[r] + 1 + b * Q - int64_t(c) * C * in.page_size))
+                              : w.kv_len;
         w.partial_slot =
             chunks[r] > 1 ? int32_t(p.merge_indptr[r] + int64_t(c) * nq[r] + b * Q) : -1;
         rows.push_back({w, c, b});

@@ -28,6 +28,7 @@ struct PartitionInput {
   const int32_t* last_page_len = nullptr;  // [batch]
   const int32_t* qo_indptr = nullptr;      // [batch+1] or NULL: one query token per request
   int32_t queries_per_item = 1;            // query tokens per work item
+  bool causal = true;  // false: every q row sees all of its request's tokens
   int32_t page_size = 0;
   int32_t units_per_item = 1;  // workgroups launched per item (one per KV head)
   int32_t slots = 1;           // workgroups resident on the device at once
@@ -60,7 +61,9 @@ struct Partition {
 // ceil(q_r / queries_per_item) query blocks of n_r pages each: B and S above
 // count blocks and their pages, every chunk is repeated per block, partial
 // states are kept per query token (merge_indptr[r+1] - merge_indptr[r] =
-// G_r * q_r when split), and ties go by request, chunk, then block.
+// G_r * q_r when split), and ties go by request, chunk, then block. Without
+// causality (the shared prefix of cascade attention) every row sees the whole
+// item and q_r is not bounded by the request's token count.
 std::string build_partition(const PartitionInput& in, Partition* out);
 
 }  // namespace pkd

@@ -50,7 +50,8 @@ class Plan:
     def __init__(self, indptr, last_page_len, num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int, q_dtype: int, kv_dtype: int, out_dtype: int,
                  sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
-                 min_chunk_pages: int = 0, device: int = 0, qo_indptr=None):
+                 min_chunk_pages: int = 0, device: int = 0, qo_indptr=None,
+                 causal: bool = True):
         lib = _lib.load()
         self._lib = lib
         self._handle = ctypes.c_void_p()
@@ -80,6 +81,7 @@ class Plan:
         a.device = device
         if self.qo_indptr is not None:
             a.qo_indptr = self.qo_indptr.ctypes.data_as(_lib._c_i32p)
+        a.non_causal = 0 if causal else 1
         _lib.check(lib.pkd_plan_create(ctypes.byref(a), ctypes.byref(self._handle)))
         info = _lib.PlanInfo()
         _lib.check(lib.pkd_plan_get_info(self._handle, ctypes.byref(info)))
@@ -125,11 +127,11 @@ class Plan:
 
 def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                    kv_dtype="bf16", q_dtype="bf16", out_dtype="f32", slots=1024, balance=0,
-                   min_chunk_pages=0, qo_indptr=None):
+                   min_chunk_pages=0, qo_indptr=None, causal=True):
     """Host-only: build a plan with an explicit slot count and return its decisions."""
     p = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
              _dtype_code(q_dtype), _dtype_code(kv_dtype), _dtype_code(out_dtype), None, slots,
-             balance, min_chunk_pages, qo_indptr=qo_indptr)
+             balance, min_chunk_pages, qo_indptr=qo_indptr, causal=causal)
     items, merge, split = p.worklist()
     info = dict(p.info)
     p.close()
@@ -168,10 +170,12 @@ class BatchDecodeWithPagedKVCacheWrapper:
              head_dim: int, page_size: int, pos_encoding_mode: str = "NONE",
              q_data_type=None, kv_data_type=None, out_data_type=None, data_type=None,
              sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
-             min_chunk_pages: int = 0, qo_indptr=None) -> None:
+             min_chunk_pages: int = 0, qo_indptr=None, causal: bool = True) -> None:
         """Plan one batch. ``qo_indptr`` (host, [batch+1]) gives request r the q
         rows ``qo_indptr[r]:qo_indptr[r+1]``: its newest tokens, attended
-        causally; omitted, every request has one query token (q row r)."""
+        causally; omitted, every request has one query token (q row r). With
+        ``causal=False`` every row sees all of its request's tokens (the
+        shared-prefix level of cascade attention)."""
         import torch
         if pos_encoding_mode != "NONE":
             raise ValueError("only pos_encoding_mode='NONE' is supported")
@@ -183,7 +187,8 @@ class BatchDecodeWithPagedKVCacheWrapper:
         dev = self._ws.device.index or 0
         self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                           _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
-                          slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr)
+                          slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr,
+                          causal=causal)
         self._indices = indices if isinstance(indices, torch.Tensor) else torch.as_tensor(
             np.asarray(indices, dtype=np.int32))
         if self._indices.device != self._ws.device or self._indices.dtype != torch.int32:
@@ -255,3 +260,89 @@ class BatchDecodeWithPagedKVCacheWrapper:
         if self._plan is not None:
             self._plan.close()
             self._plan = None
+
+
+def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, out_dtype=None):
+    """Merge two normalised attention results of the same rows over disjoint
+    token sets (``v`` [rows, heads, head_dim] float32/bfloat16, ``s`` float32
+    [rows, heads] natural-log LSE; -inf marks an empty side). Returns
+    ``(v_out, s_out)``; runs ``pkd_merge_states`` on the current stream."""
+    import torch
+    if v_a.shape != v_b.shape or v_a.dtype != v_b.dtype or v_a.dim() != 3:
+        raise ValueError("v_a and v_b must be [rows, heads, head_dim] of one dtype")
+    for s in (s_a, s_b):
+        if s.shape != v_a.shape[:2] or s.dtype != torch.float32 or not s.is_contiguous():
+            raise ValueError("s_a and s_b must be contiguous float32 [rows, heads]")
+    if not (v_a.is_contiguous() and v_b.is_contiguous()):
+        raise ValueError("v_a and v_b must be contiguous")
+    odt = out_dtype or (v_out.dtype if v_out is not None else v_a.dtype)
+    if v_out is None:
+        v_out = torch.empty(v_a.shape, dtype=odt, device=v_a.device)
+    elif v_out.shape != v_a.shape or v_out.dtype != odt or not v_out.is_contiguous():
+        raise ValueError("v_out has the wrong shape, dtype or layout")
+    if s_out is None:
+        s_out = torch.empty(v_a.shape[:2], dtype=torch.float32, device=v_a.device)
+    a = _lib.MergeStatesArgs()
+    a.rows, a.num_heads, a.head_dim = v_a.shape
+    a.in_dtype = _dtype_code(v_a.dtype)
+    a.out_dtype = _dtype_code(odt)
+    a.v_a, a.s_a, a.v_b, a.s_b = v_a.data_ptr(), s_a.data_ptr(), v_b.data_ptr(), s_b.data_ptr()
+    a.v_out, a.s_out = v_out.data_ptr(), s_out.data_ptr()
+    a.stream = torch.cuda.current_stream(v_a.device).cuda_stream
+    _lib.check(_lib.load().pkd_merge_states(ctypes.byref(a)))
+    return v_out, s_out
+
+
+class CascadeBatchDecodeWrapper:
+    """Two-level cascade decode: the queries of all requests that share a
+    prefix attend to it once, as one non-causal request of the plan (level
+    0); each request attends to its own suffix pages (level 1); the two
+    normalised results merge with ``merge_state``.
+
+    Requests must be ordered by prefix group: group p owns the q rows
+    ``shared_qo_indptr[p]:shared_qo_indptr[p+1]`` (one per request). The
+    caller's workspace is split in two halves, one per level.
+    """
+
+    def __init__(self, workspace_buffer, kv_layout: str = "NHD"):
+        half = (workspace_buffer.numel() * workspace_buffer.element_size() // 2) // 256 * 256
+        raw = workspace_buffer.view(-1).view(__import__("torch").uint8)
+        self._levels = (BatchDecodeWithPagedKVCacheWrapper(raw[:half], kv_layout),
+                        BatchDecodeWithPagedKVCacheWrapper(raw[half:2 * half], kv_layout))
+        self._rows = 0
+
+    def plan(self, shared_indptr, shared_indices, shared_last_page_len, shared_qo_indptr,
+             unique_indptr, unique_indices, unique_last_page_len, num_qo_heads: int,
+             num_kv_heads: int, head_dim: int, page_size: int, q_data_type=None,
+             kv_data_type=None, out_data_type=None, sm_scale: Optional[float] = None,
+             slots: int = 0, balance: int = 0, min_chunk_pages: int = 0) -> None:
+        import torch
+        qo = _host_i32(shared_qo_indptr)
+        rows = len(_host_i32(unique_last_page_len))
+        if int(qo[-1]) != rows:
+            raise ValueError("the prefix groups must cover every request exactly once")
+        kw = dict(q_data_type=q_data_type, kv_data_type=kv_data_type,
+                  out_data_type=torch.float32, sm_scale=sm_scale, slots=slots,
+                  balance=balance, min_chunk_pages=min_chunk_pages)
+        self._levels[0].plan(shared_indptr, shared_indices, shared_last_page_len, num_qo_heads,
+                             num_kv_heads, head_dim, page_size, qo_indptr=qo, causal=False, **kw)
+        self._levels[1].plan(unique_indptr, unique_indices, unique_last_page_len, num_qo_heads,
+                             num_kv_heads, head_dim, page_size, **kw)
+        self._rows, self._heads, self._dim = rows, num_qo_heads, head_dim
+        self._out_dtype = out_data_type or q_data_type or torch.bfloat16
+
+    def run(self, q, paged_kv_cache, out=None, return_lse: bool = False, k_scale=None,
+            v_scale=None):
+        import torch
+        shape = (self._rows, self._heads, self._dim)
+        o = torch.empty((2,) + shape, dtype=torch.float32, device=q.device)
+        s = torch.empty((2,) + shape[:2], dtype=torch.float32, device=q.device)
+        for lvl in range(2):
+            self._levels[lvl].run(q, paged_kv_cache, out=o[lvl], lse=s[lvl], k_scale=k_scale,
+                                  v_scale=v_scale)
+        out, lse = merge_state(o[0], s[0], o[1], s[1], v_out=out, out_dtype=self._out_dtype)
+        return (out, lse) if return_lse else out
+
+    def close(self) -> None:
+        for w in self._levels:
+            w.close()

@@ -162,3 +162,20 @@ def test_unequal_batch_is_split_even_with_enough_units():
 def test_invalid_tables_rejected(bad):
     with pytest.raises(ValueError):
         oplan.plan(bad["indptr"], bad["last"], 16, 1, 8, 1, 1)
+
+
+def test_non_causal_rows_see_every_item_token():
+    """The shared-prefix level of cascade attention: rows are not causal, and a
+    request may carry more query rows than it has KV tokens."""
+    indptr, last = [0, 3, 4], [3, 2]
+    p = oplan.plan(indptr, last, 4, 1, 8, 1, 1, qo_indptr=[0, 20, 23], queries_per_item=4,
+                   causal=False)
+    items = p["items"]
+    assert np.array_equal(items[:, 7], items[:, 3])
+    with pytest.raises(ValueError):  # 3 rows over 2 tokens is only legal without causality
+        oplan.plan(indptr, last, 4, 1, 8, 1, 1, qo_indptr=[0, 20, 23], queries_per_item=4)
+    for r, (q0, q1) in enumerate([(0, 20), (20, 23)]):
+        for row in range(q0, q1):
+            mine = items[(items[:, 0] == r) & (items[:, 5] <= row) & (row < items[:, 5] + items[:, 6])]
+            assert sorted(mine[:, 1].tolist()) == sorted(set(mine[:, 1].tolist()))
+            assert mine[:, 3].sum() == (indptr[r + 1] - indptr[r] - 1) * 4 + last[r]

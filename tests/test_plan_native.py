@@ -147,3 +147,24 @@ def test_workspace_size_formula():
     parts = info["num_partials"] * 32
     header = a(a(info["num_items"] * 32) + info["num_merge_tasks"] * 16)
     assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_non_causal_tables_bit_exact(seed):
+    """The shared-prefix level of cascade attention: many q rows per request,
+    more than its tokens allowed, every row sees the whole item."""
+    rng = np.random.default_rng(7000 + seed)
+    B = int(rng.integers(1, 6))
+    P = 16
+    n = rng.integers(1, 300, size=B)
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = rng.integers(1, P + 1, size=B).astype(np.int32)
+    nq = rng.integers(1, 200, size=B)
+    qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    g = int(rng.choice([1, 4, 8]))
+    info, items, merge, split = pk.plan_partition(indptr, last, 8 * g, 8, 128, P, slots=1024,
+                                                  balance=1, min_chunk_pages=16, qo_indptr=qo,
+                                                  causal=False)
+    ref = oplan.plan(indptr, last, P, 8, 1024, 1, 16, qo, info["queries_per_item"], causal=False)
+    _assert_same(info, items, merge, split, ref)
+    assert np.array_equal(items[:, 7], items[:, 3])
