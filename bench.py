@@ -34,15 +34,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PLAN_KEYS = ("chunk_pages", "num_items", "num_partials", "num_split_requests", "slots",
+             "balance", "min_chunk_pages", "queries_per_item")
 METRIC = "KV-read HBM GB/s (% of peak) + µs per batched decode step"
 CSRC = os.path.join(ROOT, "paged_kv_decode_plan_amd", "csrc")
 
 
-def kv_bytes(w, table) -> int:
+def kv_bytes(w, table, logical: bool = False) -> int:
     """Algorithmic bytes the decode kernel must read: every valid K and V element
-    once, plus for e4m3 the fp32 K and V scale of every (page, KV head)."""
+    once, plus for e4m3 the fp32 K and V scale of every (page, KV head). With a
+    shared prefix (cascade) each group's prefix counts once, unless `logical`
+    (every request's full context, as plain decode would read it)."""
     elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
     tokens = int(table["kv_lens"].sum())
+    if w.shared_prefix is not None and not logical:
+        groups, prefix = w.shared_prefix
+        tokens = tokens - len(table["kv_lens"]) * prefix + groups * prefix
     b = tokens * w.num_kv_heads * w.head_dim * 2 * elem
     if w.kv_dtype == "e4m3":
         pages = int(table["indptr"][-1])
@@ -288,6 +295,9 @@ def main(argv=None) -> int:
                     help="also time K back-to-back steps without cache flushes (reported "
                          "as warm_*; off by default so that every decode launch of a run is "
                          "cold and a profiler's per-kernel average matches the events)")
+    ap.add_argument("--flat", action="store_true",
+                    help="for a shared-prefix workload, run plain decode over every request's "
+                         "full page list instead of the cascade (for comparison)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--balance", type=int, default=0)
@@ -327,20 +337,41 @@ def main(argv=None) -> int:
     print(f"[bench] generating {w.name} seed {seed}", file=sys.stderr, flush=True)
     dcase = device_case(w, seed, dev, poison=False)
     torch.cuda.synchronize()
+    if args.flat and w.shared_prefix is not None:
+        import dataclasses
+        w = dataclasses.replace(w, shared_prefix=None)  # same tables, read in full
     nbytes = kv_bytes(w, dcase)
 
     ws = torch.empty(pk.DEFAULT_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
-    wrapper = pk.BatchDecodeWithPagedKVCacheWrapper(ws, "NHD")
     q_dt = dcase["q"].dtype
     kv_dt = "e4m3" if w.kv_dtype == "e4m3" else dcase["kv"].dtype
-    indices_dev = torch.as_tensor(dcase["indices"], dtype=torch.int32).to(dev)
-    def do_plan():
-        wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
-                     w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
-                     kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
-                     balance=args.balance, min_chunk_pages=args.min_chunk_pages,
-                     qo_indptr=dcase["qo_indptr"])
-        torch.cuda.synchronize()
+    cascade = w.shared_prefix is not None
+    if cascade:
+        # Two levels (shared prefixes once for all their requests' queries,
+        # then each request's own pages) and the merge of their results.
+        wrapper = pk.CascadeBatchDecodeWrapper(ws, "NHD")
+        sh, un = dcase["shared"], dcase["unique"]
+        sh_idx = torch.as_tensor(sh["indices"], dtype=torch.int32).to(dev)
+        un_idx = torch.as_tensor(un["indices"], dtype=torch.int32).to(dev)
+
+        def do_plan():
+            wrapper.plan(sh["indptr"], sh_idx, sh["last_page_len"], dcase["group_qo_indptr"],
+                         un["indptr"], un_idx, un["last_page_len"], w.num_qo_heads,
+                         w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
+                         kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
+                         balance=args.balance, min_chunk_pages=args.min_chunk_pages)
+            torch.cuda.synchronize()
+    else:
+        wrapper = pk.BatchDecodeWithPagedKVCacheWrapper(ws, "NHD")
+        indices_dev = torch.as_tensor(dcase["indices"], dtype=torch.int32).to(dev)
+
+        def do_plan():
+            wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
+                         w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
+                         kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
+                         balance=args.balance, min_chunk_pages=args.min_chunk_pages,
+                         qo_indptr=dcase["qo_indptr"])
+            torch.cuda.synchronize()
 
     t0 = time.perf_counter()
     do_plan()  # first plan of the process: device query and staging allocation
@@ -351,7 +382,12 @@ def main(argv=None) -> int:
         do_plan()
         plan_times.append((time.perf_counter() - t0) * 1e6)
     plan_us = statistics.median(plan_times)
-    info = wrapper.plan_info
+    if cascade:
+        levels = [lv.plan_info for lv in wrapper._levels]
+        info = dict(levels[1])
+        info["levels"] = levels
+    else:
+        info = wrapper.plan_info
     out = torch.empty_like(dcase["q"])
     run_kw = dict(out=out, k_scale=dcase["k_scale"], v_scale=dcase["v_scale"])
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -360,7 +396,7 @@ def main(argv=None) -> int:
 
     from paged_kv_decode_plan_amd import _lib
 
-    has_merge = info["num_split_requests"] > 0
+    has_merge = not cascade and info["num_split_requests"] > 0
 
     def step(ev=None):
         """One run(): the decode kernel, and the merge kernel when the plan split a
@@ -368,6 +404,11 @@ def main(argv=None) -> int:
         launch, only when there is one: an event pair costs a few µs itself)."""
         if ev is None:
             wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+            return
+        if cascade:  # one bracket around both levels and the merges
+            ev[0].record()
+            wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+            ev[1].record()
             return
         ev[0].record()
         wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_DECODE, **run_kw)
@@ -460,11 +501,12 @@ def main(argv=None) -> int:
         },
         "plan_us_host": round(plan_us, 1),
         "plan_us_host_first": round(first_plan_us, 1),
-        "plan": {k: info[k] for k in ("chunk_pages", "num_items", "num_partials",
-                                      "num_split_requests", "slots", "balance",
-                                      "min_chunk_pages", "queries_per_item")},
+        "plan": ({"levels": [{k: lv[k] for k in PLAN_KEYS} for lv in info["levels"]]}
+                 if cascade else {k: info[k] for k in PLAN_KEYS}),
         "roofline": {
-            "kernel": decode_kernel_name(w),
+            "kernel": ("cascade step: prefix-level and suffix-level " + decode_kernel_name(w)
+                       + " with their merges and merge_states" if cascade
+                       else decode_kernel_name(w)),
             "bound": "hbm",
             "achieved": round(dec_gbs, 1),
             "peak": PEAK_HBM_GBS,
@@ -475,6 +517,13 @@ def main(argv=None) -> int:
             "algorithmic_bytes_per_launch": nbytes,
         },
     }
+    if cascade:
+        logical = kv_bytes(w, dcase, logical=True)
+        result["cascade"] = {
+            "shared_prefix": list(w.shared_prefix),
+            "logical_kv_bytes_per_step": logical,
+            "logical_kv_gbs": round(logical / (mean_step * 1e-3) / 1e9, 1),
+        }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(dcase, w, args.cpu_budget)

@@ -51,6 +51,10 @@ class Workload:
     ``queries`` is ``None`` (one query token per request) or a spec of the
     same kinds as ``context`` for the number of new tokens per request,
     clipped to ``[1, L_r]``.
+    ``shared_prefix`` is ``None`` or ``(groups, prefix_tokens)``: the requests
+    fall into ``groups`` contiguous, near-equal groups, each sharing one prefix
+    of ``prefix_tokens`` tokens (whole pages) ahead of its requests' own
+    ``context`` tokens.
     """
 
     name: str
@@ -65,6 +69,7 @@ class Workload:
     pool_pages: Optional[int] = None
     sm_scale: Optional[float] = None
     queries: Optional[tuple] = None
+    shared_prefix: Optional[tuple] = None
 
     @property
     def group(self) -> int:
@@ -96,6 +101,11 @@ CONFIGS = {
     "spec4_llama3_8b_bf16": Workload(
         "spec4_llama3_8b_bf16", 64, 32, 8, 128, 16, "bf16", "bf16", ("fixed", 2048),
         queries=("fixed", 4)),
+    # Cascade: 64 requests share one 8192-token prefix (a long system prompt or
+    # document) and each has 512 tokens of its own.
+    "cascade_prefix8k_bf16": Workload(
+        "cascade_prefix8k_bf16", 64, 32, 8, 128, 16, "bf16", "bf16", ("fixed", 512),
+        shared_prefix=(1, 8192)),
 }
 CONFIG_ORDER = list(CONFIGS)
 
@@ -136,8 +146,53 @@ def query_rows(table: dict) -> int:
     return len(table["last_page_len"]) if qo is None else int(qo[-1])
 
 
+def _shared_prefix_table(w: Workload, seed: int) -> dict:
+    """Page tables of a shared-prefix workload: the full per-request lists
+    (prefix pages, then the request's own), the prefix level (one request per
+    group) and the suffix level (each request's own pages)."""
+    rng = np.random.default_rng(seed)
+    lens = _context_lengths(w, rng)
+    if np.any(lens < 1):
+        raise ValueError("every request needs at least one token of its own")
+    groups, prefix_tokens = w.shared_prefix
+    P = w.page_size
+    if prefix_tokens % P or prefix_tokens < P or not 1 <= groups <= w.batch:
+        raise ValueError("the shared prefix must be whole pages and groups in [1, batch]")
+    npre = prefix_tokens // P
+    n = (lens + P - 1) // P
+    last = (((lens - 1) % P) + 1).astype(np.int32)
+    used = groups * npre + int(n.sum())
+    pool = max(int(w.pool_pages or used), used)
+    perm = rng.permutation(pool)[:used].astype(np.int32)
+    prefixes = [perm[g * npre:(g + 1) * npre] for g in range(groups)]
+    at = groups * npre
+    own = []
+    for r in range(w.batch):
+        own.append(perm[at:at + int(n[r])])
+        at += int(n[r])
+    bounds = np.linspace(0, w.batch, groups + 1).round().astype(np.int32)
+    owner = np.searchsorted(bounds, np.arange(w.batch), side="right") - 1
+
+    def table(lists, last_page_len):
+        cnt = np.array([len(x) for x in lists], dtype=np.int64)
+        indptr = np.zeros(len(lists) + 1, dtype=np.int32)
+        indptr[1:] = np.cumsum(cnt)
+        return {"indptr": indptr, "indices": np.concatenate(lists).astype(np.int32),
+                "last_page_len": np.asarray(last_page_len, dtype=np.int32)}
+
+    full = table([np.concatenate([prefixes[owner[r]], own[r]]) for r in range(w.batch)], last)
+    full.update({"kv_lens": (lens + prefix_tokens).astype(np.int64), "num_pages": pool,
+                 "qo_indptr": None,
+                 "shared": table(prefixes, np.full(groups, P)),
+                 "unique": table(own, last),
+                 "group_qo_indptr": bounds.astype(np.int32)})
+    return full
+
+
 def page_table(w: Workload, seed: int) -> dict:
     """Draw context lengths and a shuffled page table for ``w``."""
+    if w.shared_prefix is not None:
+        return _shared_prefix_table(w, seed)
     rng = np.random.default_rng(seed)
     lens = _context_lengths(w, rng)
     if np.any(lens < 1):
