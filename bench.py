@@ -298,6 +298,11 @@ def main(argv=None) -> int:
     ap.add_argument("--flat", action="store_true",
                     help="for a shared-prefix workload, run plain decode over every request's "
                          "full page list instead of the cascade (for comparison)")
+    ap.add_argument("--fixed-capacity", action="store_true",
+                    help="plan with fixed capacities (the graph-capturable launch shape)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays "
+                         "(implies --fixed-capacity)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--balance", type=int, default=0)
@@ -322,6 +327,7 @@ def main(argv=None) -> int:
               "sharding (run with --gpus 1)", file=sys.stderr)
         return 2
 
+    import numpy as np
     import torch
 
     import paged_kv_decode_plan_amd as pk
@@ -364,13 +370,28 @@ def main(argv=None) -> int:
     else:
         wrapper = pk.BatchDecodeWithPagedKVCacheWrapper(ws, "NHD")
         indices_dev = torch.as_tensor(dcase["indices"], dtype=torch.int32).to(dev)
+        capacity = None
+        if args.fixed_capacity or args.graph:
+            # Capacities from the bounds of the plan rule: items <= query blocks +
+            # slots * balance / Hkv; merge tasks <= q rows; partial rows <= items
+            # times tokens per item.
+            qo = dcase["qo_indptr"]
+            rows = w.batch if qo is None else int(qo[-1])
+            max_q = 1 if qo is None else int(np.diff(qo).max())
+            probe = pk.plan_partition(dcase["indptr"], dcase["last_page_len"], w.num_qo_heads,
+                                      w.num_kv_heads, w.head_dim, w.page_size,
+                                      kv_dtype=w.kv_dtype, q_dtype=w.q_dtype, slots=1,
+                                      qo_indptr=qo)[0]
+            items = rows + 4096 * max(1, args.balance) // w.num_kv_heads
+            capacity = dict(items=items, merge_tasks=rows,
+                            partials=items * probe["queries_per_item"], qo_len=max_q)
 
         def do_plan():
             wrapper.plan(dcase["indptr"], indices_dev, dcase["last_page_len"], w.num_qo_heads,
                          w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
                          kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
                          balance=args.balance, min_chunk_pages=args.min_chunk_pages,
-                         qo_indptr=dcase["qo_indptr"])
+                         qo_indptr=dcase["qo_indptr"], capacity=capacity)
             torch.cuda.synchronize()
 
     t0 = time.perf_counter()
@@ -397,11 +418,30 @@ def main(argv=None) -> int:
     from paged_kv_decode_plan_amd import _lib
 
     has_merge = not cascade and info["num_split_requests"] > 0
+    graph = None
+    if args.graph:
+        if cascade:
+            print("--graph covers single-plan workloads only", file=sys.stderr)
+            return 2
+        wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+        torch.cuda.synchronize()
+        has_merge = False
 
     def step(ev=None):
         """One run(): the decode kernel, and the merge kernel when the plan split a
         request. Timed steps bracket the decode launch with events (and the merge
         launch, only when there is one: an event pair costs a few µs itself)."""
+        if graph is not None:  # decode and merge kernels replayed from the graph
+            if ev is not None:
+                ev[0].record()
+            graph.replay()
+            if ev is not None:
+                ev[1].record()
+            return
         if ev is None:
             wrapper.run(dcase["q"], dcase["kv"], **run_kw)
             return
@@ -486,6 +526,8 @@ def main(argv=None) -> int:
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "context": list(w.context),
             "total_kv_tokens": int(dcase["kv_lens"].sum()), "seed": seed,
             "cache": "warm" if args.warm else "cold (1 GiB read between steps)",
+            "launch": ("hip graph replay, fixed-capacity plan" if args.graph else
+                       "fixed-capacity plan" if args.fixed_capacity else "exact plan"),
         },
         "us_per_step": round(mean_step * 1e3, 2),
         "us_per_step_p10_p90": [round(q[0] * 1e3, 2), round(q[-1] * 1e3, 2)],

@@ -103,6 +103,26 @@ typedef struct pkd_plan pkd_plan;
  *                   FlashAttention-3: GPU Kernel Optimization & FP8 Serving
  *                   Latency", §"Key Features"); combine its output with the
  *                   per-request suffix level through pkd_merge_states.
+ *  capacity_items,  all 0: the plan is laid out and launched for exactly its
+ *  capacity_merge_tasks,  own work list. All > 0: a fixed-capacity plan for
+ *  capacity_partials,     HIP graphs. Its workspace layout, launch grids,
+ *  capacity_qo_len        kernel choice and kernel arguments depend only on
+ *                   these capacities and on the other scalar arguments, not
+ *                   on the page table: the kernels read the current counts
+ *                   from the workspace and idle workgroups past them return
+ *                   at once. A graph that captured pkd_run of one such plan
+ *                   therefore computes any other plan with the same scalar
+ *                   arguments and capacities once that plan has been
+ *                   uploaded to the same workspace (pkd_plan_upload is not
+ *                   part of the graph; q, k, v, indices, scales, out and lse
+ *                   must be the same buffers, large enough for every plan).
+ *                   The plan fails (INVALID_ARGUMENT) if its work items,
+ *                   merge tasks (q rows of split requests), partial-state
+ *                   rows or most new tokens of one request exceed them.
+ *                   Work items never exceed query blocks + slots * balance /
+ *                   num_kv_heads (query blocks = B with one token per
+ *                   request), and merge tasks and partial rows never exceed
+ *                   the q rows and the work items times the tokens per item.
  */
 typedef struct {
   int32_t batch;
@@ -122,6 +142,10 @@ typedef struct {
   int32_t device;
   const int32_t* qo_indptr;
   int32_t non_causal;
+  int32_t capacity_items;
+  int32_t capacity_merge_tasks;
+  int32_t capacity_partials;
+  int32_t capacity_qo_len;
 } pkd_plan_args;
 
 /* What a plan decided (pkd_plan_get_info). */

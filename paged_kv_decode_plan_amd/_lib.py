@@ -48,6 +48,10 @@ class PlanArgs(ctypes.Structure):
         ("device", ctypes.c_int32),
         ("qo_indptr", _c_i32p),
         ("non_causal", ctypes.c_int32),
+        ("capacity_items", ctypes.c_int32),
+        ("capacity_merge_tasks", ctypes.c_int32),
+        ("capacity_partials", ctypes.c_int32),
+        ("capacity_qo_len", ctypes.c_int32),
     ]
 
 

@@ -163,6 +163,8 @@ struct pkd_plan {
   pkd::Partition part;
   pkd_plan_info info{};
   int rows = 0;  // query rows per work item and KV head (kernel choice)
+  bool fixed = false;    // fixed-capacity plan: grids from capacities, counts read on device
+  int32_t launch_items = 0, launch_tasks = 0;
   // Device workspace layout (byte offsets).
   size_t off_items = 0, off_split = 0, header_bytes = 0;
   size_t off_part_md = 0, off_part_o = 0;
@@ -225,8 +227,21 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
       max_q = int32_t(std::min<int64_t>(std::max<int64_t>(max_q, q), INT32_MAX));
     }
   }
-  const int32_t queries_per_item = max_q > 1 ? std::max(1, 16 / group) : 1;
-  const int32_t rows = group * std::min(queries_per_item, max_q);
+  // Fixed-capacity plans: everything the launch depends on comes from the
+  // capacities (see the header), so the kernel choice uses capacity_qo_len.
+  const int32_t caps[4] = {a->capacity_items, a->capacity_merge_tasks, a->capacity_partials,
+                           a->capacity_qo_len};
+  const bool fixed = caps[0] || caps[1] || caps[2] || caps[3];
+  if (fixed && (caps[0] < 1 || caps[1] < 1 || caps[2] < 1 || caps[3] < 1))
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "a fixed-capacity plan needs all four capacities positive (%d, %d, %d, %d)",
+                caps[0], caps[1], caps[2], caps[3]);
+  if (fixed && max_q > caps[3])
+    return fail(PKD_ERR_INVALID_ARGUMENT, "a request has %d new tokens; capacity_qo_len is %d",
+                max_q, caps[3]);
+  const int32_t qo_shape = fixed ? caps[3] : max_q;
+  const int32_t queries_per_item = qo_shape > 1 ? std::max(1, 16 / group) : 1;
+  const int32_t rows = group * std::min(queries_per_item, qo_shape);
   if (max_q > 1 && !pkd::decode_uses_mfma(a->kv_dtype, a->head_dim, group, rows,
                                           a->q_dtype == PKD_DTYPE_BF16, a->page_size))
     return fail(PKD_ERR_UNSUPPORTED,
@@ -287,15 +302,35 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     for (int32_t i = 0; i < nq; ++i) tasks.push_back({q0 + i, part.merge_indptr[r] + i, chunks, nq});
   }
   const size_t n_tasks = tasks.size();
-  p->off_items = 0;
-  p->off_split = align256(n_items * sizeof(pkd::DeviceItem));
-  p->header_bytes = align256(p->off_split + std::max<size_t>(n_tasks, 1) * sizeof(pkd::MergeTask));
-  p->off_part_md = p->header_bytes;
-  const size_t prows = size_t(part.num_partials) * size_t(a->num_qo_heads);
+  if (fixed && (n_items > size_t(caps[0]) || n_tasks > size_t(caps[1]) ||
+                size_t(part.num_partials) > size_t(caps[2]))) {
+    const size_t np = size_t(part.num_partials);
+    delete p;
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "the plan needs %zu work items, %zu merge tasks and %zu partial rows; the "
+                "capacities are %d, %d and %d",
+                n_items, n_tasks, np, caps[0], caps[1], caps[2]);
+  }
+  // Workspace: [counts (256 B) | items | merge tasks | partial (m, d) | partial o],
+  // sized by the plan itself or, for a fixed-capacity plan, by its capacities.
+  const size_t lay_items = fixed ? size_t(caps[0]) : n_items;
+  const size_t lay_tasks = fixed ? size_t(caps[1]) : std::max<size_t>(n_tasks, 1);
+  const size_t lay_parts = fixed ? size_t(caps[2]) : size_t(part.num_partials);
+  p->fixed = fixed;
+  p->launch_items = int32_t(lay_items);
+  p->launch_tasks = fixed ? caps[1] : int32_t(n_tasks);
+  p->off_items = 256;
+  p->off_split = align256(p->off_items + lay_items * sizeof(pkd::DeviceItem));
+  const size_t end_split = align256(p->off_split + lay_tasks * sizeof(pkd::MergeTask));
+  p->header_bytes = p->off_split + std::max<size_t>(n_tasks, 1) * sizeof(pkd::MergeTask);
+  p->off_part_md = end_split;
+  const size_t prows = lay_parts * size_t(a->num_qo_heads);
   p->off_part_o = align256(p->off_part_md + prows * 2 * sizeof(float));
   const size_t ws = align256(p->off_part_o + prows * size_t(a->head_dim) * sizeof(float));
 
   p->header.assign(p->header_bytes, 0);
+  reinterpret_cast<int32_t*>(p->header.data())[0] = int32_t(n_items);
+  reinterpret_cast<int32_t*>(p->header.data())[1] = int32_t(n_tasks);
   auto* di = reinterpret_cast<pkd::DeviceItem*>(p->header.data() + p->off_items);
   for (size_t i = 0; i < n_items; ++i) {
     const auto& w = part.items[i];
@@ -415,7 +450,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.head_dim = a.head_dim;
   L.group = a.num_qo_heads / a.num_kv_heads;
   L.rows = p->rows;
-  L.num_items = p->info.num_items;
+  L.num_items = p->launch_items;
   L.num_kv_heads = a.num_kv_heads;
   L.num_qo_heads = a.num_qo_heads;
   L.page_size_log2 = ilog2(a.page_size);
@@ -438,7 +473,8 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.merge_tasks = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_split);
   L.part_md = reinterpret_cast<float*>(ws + p->off_part_md);
   L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
-  L.num_split = p->info.num_merge_tasks;
+  L.num_split = p->launch_tasks;
+  L.counts = p->fixed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
   hipStream_t s = static_cast<hipStream_t>(r->stream);
   hipError_t e;
   if (stages & PKD_STAGE_DECODE) {

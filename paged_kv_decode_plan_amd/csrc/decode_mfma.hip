@@ -448,7 +448,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 
   int item, kvh;
   decode_block(a.num_kv_heads, a.xcd_group, &item, &kvh);
-  if (item >= a.num_items) return;  // grid padding; no barrier passed yet
+  if (item >= launch_items(a)) return;  // grid padding; no barrier passed yet
   const DeviceItem it = a.items[item];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
 
   int item_idx, kvh;
   decode_block(a.num_kv_heads, a.xcd_group, &item_idx, &kvh);
-  if (item_idx >= a.num_items) return;  // grid padding; no barrier passed yet
+  if (item_idx >= launch_items(a)) return;  // grid padding; no barrier passed yet
   const DeviceItem it = a.items[item_idx];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;

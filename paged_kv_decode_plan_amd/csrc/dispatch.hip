@@ -54,6 +54,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.out = L.out;
   a.lse = L.lse;
   a.items = L.items;
+  a.counts = L.counts;
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.num_items = L.num_items;

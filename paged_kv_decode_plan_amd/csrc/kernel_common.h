@@ -29,6 +29,7 @@ struct KernelArgs {
   void* out;
   float* lse;
   const DeviceItem* items;
+  const int32_t* counts;  // nullptr, or {work items, merge tasks} of the uploaded plan
   float* part_o;
   float* part_md;
   int num_items;
@@ -62,6 +63,12 @@ __device__ inline void decode_block(int num_kv_heads, int g, int* item, int* kvh
   const int id = int(blockIdx.x);
   *item = g * (id / (g * num_kv_heads)) + id % g;
   *kvh = (id / g) % num_kv_heads;
+}
+
+// Work items of this launch: the grid's count, or, for a fixed-capacity plan
+// (grid sized by its capacity), the count its upload wrote to the workspace.
+__device__ inline int launch_items(const KernelArgs& a) {
+  return a.counts ? a.counts[0] : a.num_items;
 }
 
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }

@@ -61,6 +61,10 @@ struct DecodeLaunch {
   float* part_md = nullptr;  // [num_partials, Hq, 2]: (m in log2 units, d)
   int num_split = 0;                       // merge tasks
   const MergeTask* merge_tasks = nullptr;  // [num_split]
+  // Fixed-capacity plans: {work items, merge tasks} of the uploaded plan, read
+  // by the kernels (num_items / num_split are then the capacities). nullptr:
+  // the launch is sized exactly.
+  const int32_t* counts = nullptr;
 };
 
 // `rows` is group x (query tokens per work item); rows > group (several new

@@ -31,6 +31,7 @@ struct MergeArgs {
   const float* part_o;
   const float* part_md;
   const MergeTask* tasks;
+  const int32_t* counts;  // fixed-capacity plan: counts[1] merge tasks are live
   void* out;
   float* lse;
   int num_qo_heads;
@@ -46,6 +47,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   __shared__ float sm[kSub], sd[kSub];
   __shared__ float4 so[kSub][kQuads];
   const int H = a.num_qo_heads;
+  if (a.counts && int(blockIdx.x / H) >= a.counts[1]) return;  // past the plan's tasks
   const MergeTask t = a.tasks[blockIdx.x / H];
   const int h = blockIdx.x % H;
   const int sub = threadIdx.x / kQuads;
@@ -126,6 +128,7 @@ hipError_t launch_merge(const DecodeLaunch& L, hipStream_t stream) {
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.tasks = L.merge_tasks;
+  a.counts = L.counts;
   a.out = L.out;
   a.lse = L.lse;
   a.num_qo_heads = L.num_qo_heads;

@@ -51,7 +51,7 @@ class Plan:
                  head_dim: int, page_size: int, q_dtype: int, kv_dtype: int, out_dtype: int,
                  sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
                  min_chunk_pages: int = 0, device: int = 0, qo_indptr=None,
-                 causal: bool = True):
+                 causal: bool = True, capacity=None):
         lib = _lib.load()
         self._lib = lib
         self._handle = ctypes.c_void_p()
@@ -82,6 +82,10 @@ class Plan:
         if self.qo_indptr is not None:
             a.qo_indptr = self.qo_indptr.ctypes.data_as(_lib._c_i32p)
         a.non_causal = 0 if causal else 1
+        if capacity is not None:
+            c = _capacity(capacity)
+            (a.capacity_items, a.capacity_merge_tasks, a.capacity_partials,
+             a.capacity_qo_len) = c
         _lib.check(lib.pkd_plan_create(ctypes.byref(a), ctypes.byref(self._handle)))
         info = _lib.PlanInfo()
         _lib.check(lib.pkd_plan_get_info(self._handle, ctypes.byref(info)))
@@ -125,13 +129,22 @@ class Plan:
             pass
 
 
+def _capacity(capacity) -> Tuple[int, int, int, int]:
+    """(items, merge_tasks, partials, qo_len) from a dict with those keys or a tuple."""
+    if isinstance(capacity, dict):
+        return (int(capacity["items"]), int(capacity["merge_tasks"]),
+                int(capacity["partials"]), int(capacity.get("qo_len", 1)))
+    items, tasks, parts, *rest = capacity
+    return int(items), int(tasks), int(parts), int(rest[0]) if rest else 1
+
+
 def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                    kv_dtype="bf16", q_dtype="bf16", out_dtype="f32", slots=1024, balance=0,
-                   min_chunk_pages=0, qo_indptr=None, causal=True):
+                   min_chunk_pages=0, qo_indptr=None, causal=True, capacity=None):
     """Host-only: build a plan with an explicit slot count and return its decisions."""
     p = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
              _dtype_code(q_dtype), _dtype_code(kv_dtype), _dtype_code(out_dtype), None, slots,
-             balance, min_chunk_pages, qo_indptr=qo_indptr, causal=causal)
+             balance, min_chunk_pages, qo_indptr=qo_indptr, causal=causal, capacity=capacity)
     items, merge, split = p.worklist()
     info = dict(p.info)
     p.close()
@@ -170,12 +183,17 @@ class BatchDecodeWithPagedKVCacheWrapper:
              head_dim: int, page_size: int, pos_encoding_mode: str = "NONE",
              q_data_type=None, kv_data_type=None, out_data_type=None, data_type=None,
              sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
-             min_chunk_pages: int = 0, qo_indptr=None, causal: bool = True) -> None:
+             min_chunk_pages: int = 0, qo_indptr=None, causal: bool = True,
+             capacity=None) -> None:
         """Plan one batch. ``qo_indptr`` (host, [batch+1]) gives request r the q
         rows ``qo_indptr[r]:qo_indptr[r+1]``: its newest tokens, attended
         causally; omitted, every request has one query token (q row r). With
         ``causal=False`` every row sees all of its request's tokens (the
-        shared-prefix level of cascade attention)."""
+        shared-prefix level of cascade attention). ``capacity`` (dict with
+        ``items``, ``merge_tasks``, ``partials``, ``qo_len``) makes a
+        fixed-capacity plan: run() then launches the same grids with the same
+        arguments for every such plan, so a captured HIP graph of run() stays
+        valid across plan()/upload of new batches."""
         import torch
         if pos_encoding_mode != "NONE":
             raise ValueError("only pos_encoding_mode='NONE' is supported")
@@ -188,7 +206,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                           _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
                           slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr,
-                          causal=causal)
+                          causal=causal, capacity=capacity)
         self._indices = indices if isinstance(indices, torch.Tensor) else torch.as_tensor(
             np.asarray(indices, dtype=np.int32))
         if self._indices.device != self._ws.device or self._indices.dtype != torch.int32:

@@ -137,7 +137,7 @@ def test_workspace_size_formula():
     parts = info["num_partials"] * 32
     a = lambda x: (x + 255) // 256 * 256
     assert info["num_merge_tasks"] == info["num_split_requests"]
-    header = a(a(info["num_items"] * 32) + max(info["num_merge_tasks"], 1) * 16)
+    header = a(a(256 + info["num_items"] * 32) + max(info["num_merge_tasks"], 1) * 16)
     assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
     # several new tokens: one merge task and one partial row per token of a split request
     info, items, merge, split = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64,
@@ -145,8 +145,43 @@ def test_workspace_size_formula():
                                                   qo_indptr=[0, 3, 5])
     assert info["num_merge_tasks"] == 5 and info["queries_per_item"] == 4
     parts = info["num_partials"] * 32
-    header = a(a(info["num_items"] * 32) + info["num_merge_tasks"] * 16)
+    header = a(a(256 + info["num_items"] * 32) + info["num_merge_tasks"] * 16)
     assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+    # fixed capacity: the layout follows the capacities, not the plan
+    cap = dict(items=100, merge_tasks=40, partials=300, qo_len=4)
+    info2, *_ = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64, balance=1,
+                                  min_chunk_pages=1, qo_indptr=[0, 3, 5], capacity=cap)
+    parts = 300 * 32
+    header = a(a(256 + 100 * 32) + 40 * 16)
+    assert info2["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+
+
+def test_capacity_limits_are_enforced():
+    cap = dict(items=4, merge_tasks=40, partials=300, qo_len=1)
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64, balance=1,
+                          min_chunk_pages=1, capacity=cap)
+    assert "capacities" in str(e.value)
+    with pytest.raises(pk.PkdError):  # more new tokens than capacity_qo_len
+        pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, qo_indptr=[0, 3, 5],
+                          capacity=dict(items=100, merge_tasks=40, partials=300, qo_len=2))
+    with pytest.raises(pk.PkdError):  # all four or none
+        pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, capacity=(100, 0, 300, 1))
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_item_count_bound_for_capacities(seed):
+    """The bound the header gives for capacity_items: query blocks + slots *
+    balance / num_kv_heads."""
+    rng = np.random.default_rng(9000 + seed)
+    B = int(rng.integers(1, 200))
+    n = rng.integers(1, int(rng.integers(2, 400)), size=B)
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = rng.integers(1, 17, size=B).astype(np.int32)
+    hkv, slots, bal = int(rng.choice([1, 2, 8])), int(rng.integers(1, 3000)), int(rng.integers(1, 4))
+    info, items, *_ = pk.plan_partition(indptr, last, 4 * hkv, hkv, 128, 16, slots=slots,
+                                        balance=bal, min_chunk_pages=int(rng.integers(1, 20)))
+    assert info["num_items"] <= B + slots * bal // hkv
 
 
 @pytest.mark.parametrize("seed", range(10))
