@@ -303,6 +303,8 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays "
                          "(implies --fixed-capacity)")
+    ap.add_argument("--wgs-per-cu", type=int, default=0,
+                    help="cap on decode workgroups per compute unit (0: library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--balance", type=int, default=0)
@@ -391,7 +393,8 @@ def main(argv=None) -> int:
                          w.num_kv_heads, w.head_dim, w.page_size, q_data_type=q_dt,
                          kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
                          balance=args.balance, min_chunk_pages=args.min_chunk_pages,
-                         qo_indptr=dcase["qo_indptr"], capacity=capacity)
+                         qo_indptr=dcase["qo_indptr"], capacity=capacity,
+                         max_wgs_per_cu=args.wgs_per_cu)
             torch.cuda.synchronize()
 
     t0 = time.perf_counter()

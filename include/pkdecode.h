@@ -123,6 +123,10 @@ typedef struct pkd_plan pkd_plan;
  *                   num_kv_heads (query blocks = B with one token per
  *                   request), and merge tasks and partial rows never exceed
  *                   the q rows and the work items times the tokens per item.
+ *  max_wgs_per_cu   0: the library's default residency for the KV dtype.
+ *                   1..4: run() reserves LDS so that at most this many decode
+ *                   workgroups share a compute unit (and slots == 0 counts
+ *                   them); larger values add no reservation.
  */
 typedef struct {
   int32_t batch;
@@ -146,6 +150,7 @@ typedef struct {
   int32_t capacity_merge_tasks;
   int32_t capacity_partials;
   int32_t capacity_qo_len;
+  int32_t max_wgs_per_cu;
 } pkd_plan_args;
 
 /* What a plan decided (pkd_plan_get_info). */

@@ -52,6 +52,7 @@ class PlanArgs(ctypes.Structure):
         ("capacity_merge_tasks", ctypes.c_int32),
         ("capacity_partials", ctypes.c_int32),
         ("capacity_qo_len", ctypes.c_int32),
+        ("max_wgs_per_cu", ctypes.c_int32),
     ]
 
 

@@ -116,18 +116,26 @@ void pinned_release(PinnedBlock b) {
 
 // Resident workgroups per CU and CU count, per (device, kernel choice).
 std::mutex g_slots_mu;
-std::map<std::tuple<int, int, int, int, int, int, int>, std::pair<int, int>> g_slots;
+std::map<std::tuple<int, int, int, int, int, int, int, int>, std::pair<int, int>> g_slots;
+
+// Decode workgroups per compute unit the library allows by default. One
+// workgroup per CU (four wavefronts) is the fastest residency measured on
+// MI355X for the one-token MFMA kernel on every bf16 and e4m3 workload (the
+// eight KV heads of a work item are then read at the same time, and far
+// fewer pages are open at once); several new tokens per item carry more math
+// per byte and keep the occupancy registers allow. 0: no cap.
+int32_t default_wgs_cap(bool mfma, bool one_token) { return mfma && one_token ? 1 : 0; }
 
 int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
-                 int32_t group, int32_t rows, int32_t page_size, int32_t* wgs_per_cu,
-                 int32_t* num_cus) {
+                 int32_t group, int32_t rows, int32_t page_size, int32_t wgs_cap,
+                 int32_t* wgs_per_cu, int32_t* num_cus) {
   const int q_bf16 = q_dtype == PKD_DTYPE_BF16;
   if (!pkd::decode_supported(kv_dtype, head_dim, group, rows, q_bf16, page_size))
     return fail(PKD_ERR_UNSUPPORTED,
                 "no kernel for kv_dtype=%d head_dim=%d group=%d rows=%d q_dtype=%d", kv_dtype,
                 head_dim, group, rows, q_dtype);
   const auto key = std::make_tuple(int(device), int(kv_dtype), int(head_dim), int(group),
-                                   int(rows), q_bf16, page_size >= 16 ? 16 : 1);
+                                   int(rows), q_bf16, page_size >= 16 ? 16 : 1, int(wgs_cap));
   {
     std::lock_guard<std::mutex> lk(g_slots_mu);
     auto it = g_slots.find(key);
@@ -145,7 +153,8 @@ int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head
   int cus = 0, wgs = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e == hipSuccess)
-    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_bf16, page_size, &wgs);
+    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_bf16, page_size, wgs_cap,
+                              &wgs);
   if (prev != device) hipSetDevice(prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
   *wgs_per_cu = wgs;
@@ -163,6 +172,7 @@ struct pkd_plan {
   pkd::Partition part;
   pkd_plan_info info{};
   int rows = 0;  // query rows per work item and KV head (kernel choice)
+  int wgs_cap = 0;  // decode workgroups per compute unit at most (0: no cap)
   bool fixed = false;    // fixed-capacity plan: grids from capacities, counts read on device
   int32_t launch_items = 0, launch_tasks = 0;
   // Device workspace layout (byte offsets).
@@ -183,8 +193,10 @@ int pkd_version(void) { return 200; }
 int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
                      int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus) {
   if (!wgs_per_cu || !num_cus) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
-  return device_slots(device, q_dtype, kv_dtype, head_dim, group, group, page_size, wgs_per_cu,
-                      num_cus);
+  const bool mfma = pkd::decode_uses_mfma(kv_dtype, head_dim, group, group,
+                                          q_dtype == PKD_DTYPE_BF16, page_size);
+  return device_slots(device, q_dtype, kv_dtype, head_dim, group, group, page_size,
+                      default_wgs_cap(mfma, true), wgs_per_cu, num_cus);
 }
 
 int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
@@ -248,8 +260,13 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                 "several query tokens per request need bf16 q, bf16 or e4m3 KV and head_dim 128 "
                 "(group %d, head_dim %d, kv_dtype %d, q_dtype %d)",
                 group, a->head_dim, a->kv_dtype, a->q_dtype);
-  if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0)
-    return fail(PKD_ERR_INVALID_ARGUMENT, "slots, balance and min_chunk_pages must be >= 0");
+  if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0 || a->max_wgs_per_cu < 0)
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "slots, balance, min_chunk_pages and max_wgs_per_cu must be >= 0");
+  const bool mfma = pkd::decode_uses_mfma(a->kv_dtype, a->head_dim, group, rows,
+                                          a->q_dtype == PKD_DTYPE_BF16, a->page_size);
+  const int32_t wgs_cap =
+      a->max_wgs_per_cu ? a->max_wgs_per_cu : default_wgs_cap(mfma, rows == group);
   if (!(a->sm_scale >= 0.f) || std::isinf(a->sm_scale))
     return fail(PKD_ERR_INVALID_ARGUMENT, "sm_scale must be finite and >= 0");
 
@@ -257,7 +274,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (slots == 0) {
     int32_t wgs = 0, cus = 0;
     int rc = device_slots(a->device, a->q_dtype, a->kv_dtype, a->head_dim, group, rows,
-                          a->page_size, &wgs, &cus);
+                          a->page_size, wgs_cap, &wgs, &cus);
     if (rc != PKD_OK) return rc;
     slots = wgs * cus;
     if (slots < 1) return fail(PKD_ERR_HIP, "device reports no resident workgroups");
@@ -287,6 +304,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   p->args.last_page_len = nullptr;
   p->args.qo_indptr = nullptr;
   p->rows = rows;
+  p->wgs_cap = wgs_cap;
   p->device = a->device;
   p->sm_scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(float(a->head_dim));
 
@@ -450,6 +468,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.head_dim = a.head_dim;
   L.group = a.num_qo_heads / a.num_kv_heads;
   L.rows = p->rows;
+  L.wgs_cap = p->wgs_cap;
   L.num_items = p->launch_items;
   L.num_kv_heads = a.num_kv_heads;
   L.num_qo_heads = a.num_qo_heads;

@@ -29,6 +29,22 @@ static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_bf
   return valu_decode_kernel(kv_dtype, head_dim, group);
 }
 
+// Dynamic LDS that caps the decode workgroups one compute unit holds at once
+// at `cap` (gfx950: 160 KiB of LDS per CU): each workgroup then holds a total
+// inside (160 KiB / (cap + 1), 160 KiB / cap], with margin on both sides. No
+// cap (0) or a cap the other resources already impose: nothing added.
+static hipError_t cap_lds(DecodeFn fn, int cap, size_t* bytes) {
+  *bytes = 0;
+  if (cap <= 0 || cap > 4) return hipSuccess;
+  static constexpr size_t kTotal[5] = {0, 96u << 10, 72u << 10, 48u << 10, 36u << 10};
+  hipFuncAttributes attr;
+  if (hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
+      e != hipSuccess)
+    return e;
+  if (attr.sharedSizeBytes < kTotal[cap]) *bytes = kTotal[cap] - attr.sharedSizeBytes;
+  return hipSuccess;
+}
+
 bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size) {
   return choose(kv_dtype, head_dim, group, rows, q_bf16, page_size) != nullptr;
 }
@@ -67,15 +83,19 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.q_bf16 = L.q_bf16;
   a.out_bf16 = L.out_bf16;
   const unsigned grid = decode_grid_size(L.num_items, L.num_kv_heads, a.xcd_group);
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), 0, stream, a);
+  size_t lds = 0;
+  if (hipError_t e = cap_lds(fn, L.wgs_cap, &lds); e != hipSuccess) return e;
+  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
 hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
-                            int page_size, int* wgs_per_cu) {
+                            int page_size, int wgs_cap, int* wgs_per_cu) {
   DecodeFn fn = choose(kv_dtype, head_dim, group, rows, q_bf16, page_size);
   if (!fn) return hipErrorInvalidValue;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs_per_cu, fn, kThreads, 0);
+  size_t lds = 0;
+  if (hipError_t e = cap_lds(fn, wgs_cap, &lds); e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(wgs_per_cu, fn, kThreads, lds);
 }
 
 }  // namespace pkd

@@ -38,6 +38,7 @@ struct DecodeLaunch {
   int head_dim = 0;
   int group = 0;
   int rows = 0;  // query rows per work item and KV head: group x query tokens per item
+  int wgs_cap = 0;  // at most this many decode workgroups per compute unit (0: no cap)
   int num_items = 0;
   int num_kv_heads = 0;
   int num_qo_heads = 0;
@@ -74,7 +75,7 @@ bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_bf1
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
 hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
-                            int page_size, int* wgs_per_cu);
+                            int page_size, int wgs_cap, int* wgs_per_cu);
 
 struct MergeStatesLaunch {
   int64_t rows = 0;

@@ -51,7 +51,7 @@ class Plan:
                  head_dim: int, page_size: int, q_dtype: int, kv_dtype: int, out_dtype: int,
                  sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
                  min_chunk_pages: int = 0, device: int = 0, qo_indptr=None,
-                 causal: bool = True, capacity=None):
+                 causal: bool = True, capacity=None, max_wgs_per_cu: int = 0):
         lib = _lib.load()
         self._lib = lib
         self._handle = ctypes.c_void_p()
@@ -82,6 +82,7 @@ class Plan:
         if self.qo_indptr is not None:
             a.qo_indptr = self.qo_indptr.ctypes.data_as(_lib._c_i32p)
         a.non_causal = 0 if causal else 1
+        a.max_wgs_per_cu = max_wgs_per_cu
         if capacity is not None:
             c = _capacity(capacity)
             (a.capacity_items, a.capacity_merge_tasks, a.capacity_partials,
@@ -184,7 +185,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
              q_data_type=None, kv_data_type=None, out_data_type=None, data_type=None,
              sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
              min_chunk_pages: int = 0, qo_indptr=None, causal: bool = True,
-             capacity=None) -> None:
+             capacity=None, max_wgs_per_cu: int = 0) -> None:
         """Plan one batch. ``qo_indptr`` (host, [batch+1]) gives request r the q
         rows ``qo_indptr[r]:qo_indptr[r+1]``: its newest tokens, attended
         causally; omitted, every request has one query token (q row r). With
@@ -206,7 +207,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                           _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
                           slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr,
-                          causal=causal, capacity=capacity)
+                          causal=causal, capacity=capacity, max_wgs_per_cu=max_wgs_per_cu)
         self._indices = indices if isinstance(indices, torch.Tensor) else torch.as_tensor(
             np.asarray(indices, dtype=np.int32))
         if self._indices.device != self._ws.device or self._indices.dtype != torch.int32:
