@@ -120,7 +120,7 @@ typedef struct pkd_plan pkd_plan;
  *                   merge tasks (q rows of split requests), partial-state
  *                   rows or most new tokens of one request exceed them.
  *                   Work items never exceed query blocks + slots * balance /
- *                   num_kv_heads (query blocks = B with one token per
+ *                   info.units_per_item (query blocks = B with one token per
  *                   request), and merge tasks and partial rows never exceed
  *                   the q rows and the work items times the tokens per item.
  *  max_wgs_per_cu   0: the library's default residency for the KV dtype.
@@ -169,6 +169,7 @@ typedef struct {
   int32_t queries_per_item;    /* new tokens of one request a work item carries at most */
   int32_t max_qo_len;          /* most new tokens of one request */
   int32_t num_merge_tasks;     /* q rows of split requests (merge grid / num_qo_heads) */
+  int32_t units_per_item;      /* decode workgroups per work item (one per KV head) */
 } pkd_plan_info;
 
 /* Arguments of pkd_run. All pointers are device pointers.

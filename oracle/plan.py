@@ -12,8 +12,9 @@ The rule adopted (a reading; the design doc lists it):
 
 1. ``n_r = indptr[r+1] - indptr[r]`` pages and
    ``L_r = (n_r - 1) * P + last_page_len[r]`` tokens per request.
-2. With ``S = sum_r n_r``, ``N = max_r n_r``, ``H`` work units per item (one
-   per KV head) and ``slots`` workgroups resident on the device at once:
+2. With ``S = sum_r n_r``, ``N = max_r n_r``, ``H`` work units per item (the
+   workgroups one item runs as: one per KV head) and ``slots`` workgroups
+   resident on the device at once:
 
    * a batch of near-equal requests (``8 * N * B <= 9 * S``: the longest is
      within 1/8 of the mean) that already yields at least half the resident

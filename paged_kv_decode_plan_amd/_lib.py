@@ -72,6 +72,7 @@ class PlanInfo(ctypes.Structure):
         ("queries_per_item", ctypes.c_int32),
         ("max_qo_len", ctypes.c_int32),
         ("num_merge_tasks", ctypes.c_int32),
+        ("units_per_item", ctypes.c_int32),
     ]
 
 

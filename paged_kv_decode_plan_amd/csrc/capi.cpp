@@ -375,6 +375,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   inf.queries_per_item = queries_per_item;
   inf.max_qo_len = max_q;
   inf.num_merge_tasks = int32_t(n_tasks);
+  inf.units_per_item = pin.units_per_item;
   *out = p;
   return ok();
 }

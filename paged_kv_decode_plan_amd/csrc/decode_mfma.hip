@@ -445,10 +445,6 @@ template <int KV, int G, bool PAGE16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16>()))) void decode_mfma_kernel(KernelArgs a) {
   static_assert(G >= 1 && G <= 16, "at most 16 query rows per KV head");
   __shared__ WaveStates<G, kD> st;
-#ifdef PKD_LDS_PAD
-  __shared__ volatile char lds_pad[PKD_LDS_PAD];
-  if (a.num_items < 0) lds_pad[threadIdx.x] = 0;
-#endif
 
   int item, kvh;
   decode_block(a.num_kv_heads, a.xcd_group, &item, &kvh);

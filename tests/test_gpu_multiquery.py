@@ -71,7 +71,7 @@ def test_chunks_past_a_tokens_causal_limit_give_empty_partials():
     assert np.sum(items[:, 7] + items[:, 6] - 1 <= 0) > 0  # blocks that see none of a chunk
     ref_out, ref_lse = oracle_for(case)
     out, lse, info = run_hip(to_device(case), **kw)
-    assert info["num_merge_tasks"] == nq[0]
+    assert info["num_merge_tasks"] >= nq[0]
     compare(out, lse, ref_out, ref_lse, "bf16")
 
 

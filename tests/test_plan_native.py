@@ -18,7 +18,7 @@ def _both(indptr, last, P, hkv, slots, balance, cmin, hq=None, d=128, kv="bf16",
     info, items, merge, split = pk.plan_partition(indptr, last, hq, hkv, d, P, kv_dtype=kv,
                                                   q_dtype="bf16", slots=slots, balance=balance,
                                                   min_chunk_pages=cmin, qo_indptr=qo_indptr)
-    ref = oplan.plan(indptr, last, P, hkv, slots, balance, cmin, qo_indptr,
+    ref = oplan.plan(indptr, last, P, info["units_per_item"], slots, balance, cmin, qo_indptr,
                      info["queries_per_item"])
     return info, items, merge, split, ref
 
@@ -181,7 +181,7 @@ def test_item_count_bound_for_capacities(seed):
     hkv, slots, bal = int(rng.choice([1, 2, 8])), int(rng.integers(1, 3000)), int(rng.integers(1, 4))
     info, items, *_ = pk.plan_partition(indptr, last, 4 * hkv, hkv, 128, 16, slots=slots,
                                         balance=bal, min_chunk_pages=int(rng.integers(1, 20)))
-    assert info["num_items"] <= B + slots * bal // hkv
+    assert info["num_items"] <= B + slots * bal // info["units_per_item"]
 
 
 @pytest.mark.parametrize("seed", range(10))
@@ -200,6 +200,7 @@ def test_non_causal_tables_bit_exact(seed):
     info, items, merge, split = pk.plan_partition(indptr, last, 8 * g, 8, 128, P, slots=1024,
                                                   balance=1, min_chunk_pages=16, qo_indptr=qo,
                                                   causal=False)
-    ref = oplan.plan(indptr, last, P, 8, 1024, 1, 16, qo, info["queries_per_item"], causal=False)
+    ref = oplan.plan(indptr, last, P, info["units_per_item"], 1024, 1, 16, qo,
+                     info["queries_per_item"], causal=False)
     _assert_same(info, items, merge, split, ref)
     assert np.array_equal(items[:, 7], items[:, 3])
