@@ -7,10 +7,11 @@ Every stored format here is a subset of float64, so widening is exact:
   ``uint16 -> uint32 << 16 -> float32 -> float64``.
 * ``"e4m3"`` — the OCP E4M3FN table of ``oracle.e4m3``, then multiplied by the
   fp32 scale of its (page, KV head); the product of an 4-bit-mantissa value and
-  a 24-bit-mantissa scale is exact in float64. The scale granularity (one per
-  page and KV head, separately for K and V) is the reading taken for the fp8
-  KV cache with scaling factors of "FlashInfer vs FlashAttention-3: GPU Kernel
-  Optimization & FP8 Serving Latency", §"Production War Story".
+  a 24-bit-mantissa scale is exact in float64. The scale granularity — one per
+  page and KV head, or one per token and KV head (the page's "per-token"
+  row-wise scaling), separately for K and V — is the reading taken for the
+  fp8 KV cache with scaling factors of "FlashInfer vs FlashAttention-3: GPU
+  Kernel Optimization & FP8 Serving Latency", §"Production War Story".
 
 Test infrastructure: see the package docstring.
 """

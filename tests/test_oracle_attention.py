@@ -57,7 +57,10 @@ def brute_force(case, sm_scale):
             scores, vals = [], []
             for page, slot in toks:
                 ks = vs = 1.0
-                if w.kv_dtype == "e4m3":
+                if w.kv_dtype == "e4m3" and case["k_scale"].ndim == 3:  # per token
+                    ks = float(case["k_scale"][page, slot, kvh])
+                    vs = float(case["v_scale"][page, slot, kvh])
+                elif w.kv_dtype == "e4m3":
                     ks = float(case["k_scale"][page, kvh])
                     vs = float(case["v_scale"][page, kvh])
                 kvec = [_scalar(kv[page, 0, slot, kvh, d], w.kv_dtype) * ks for d in range(D)]
@@ -251,3 +254,34 @@ def test_worked_page_table_gather_probe():
     # The shared prefix: both requests read identical tokens for the shared pages.
     shared = ex["shared_prefix_pages"]
     assert lists[0][:shared] == lists[1][:shared]
+
+
+@pytest.mark.parametrize("seed,qd,hq,hkv,p,lens", [
+    (11, "bf16", 4, 1, 4, [13, 2, 40]),
+    (12, "f32", 8, 2, 8, [17, 8, 1, 33]),
+])
+def test_rowwise_e4m3_scales_match_brute_force(seed, qd, hq, hkv, p, lens):
+    """One scale per (page, slot, KV head): the brute force indexes it by the
+    slot it walks to; the oracle by its vectorised gather."""
+    w = custom_workload(len(lens), hq, hkv, 8, p, "e4m3", qd, lens,
+                        pool_pages=sum(-(-x // p) for x in lens) + 3, kv_scale="token")
+    case = host_case(w, seed, poison=True)
+    assert case["k_scale"].shape == (case["kv"].shape[0], p, hkv)
+    out, lse = attention.decode_case(case)
+    bo, bl = brute_force(case, w.scale())
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-12)
+
+
+def test_rowwise_scales_equal_to_page_scales_give_page_results():
+    """Per-token scales that repeat each page's scale reproduce the per-page path."""
+    w = custom_workload(3, 8, 2, 16, 4, "e4m3", "bf16", [13, 2, 40], pool_pages=20)
+    case = host_case(w, 13, poison=True)
+    out0, lse0 = attention.decode_case(case)
+    P = case["kv"].shape[2]
+    tok = dict(case)
+    tok["k_scale"] = np.repeat(case["k_scale"][:, None, :], P, axis=1)
+    tok["v_scale"] = np.repeat(case["v_scale"][:, None, :], P, axis=1)
+    out1, lse1 = attention.decode_case(tok)
+    np.testing.assert_array_equal(out0, out1)
+    np.testing.assert_array_equal(lse0, lse1)

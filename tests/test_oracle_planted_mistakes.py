@@ -130,3 +130,16 @@ def test_plan_mutants_are_caught(mutant, monkeypatch):
     else:
         items[items[:, 0] == 1, 3] = (items[items[:, 0] == 1, 2] - items[items[:, 0] == 1, 1]) * 16
     assert items.tolist() != c["items"]
+
+
+def test_rowwise_scale_slot_mixup_is_caught():
+    """Indexing a row-wise scale by the wrong slot must break the brute-force match."""
+    w = custom_workload(3, 4, 2, 8, 4, "e4m3", "bf16", [9, 16, 3], pool_pages=12,
+                        kv_scale="token")
+    case = host_case(w, 7, poison=True)
+    assert _matches_brute(case, w)
+    wrong = dict(case)
+    wrong["k_scale"] = np.roll(case["k_scale"], 1, axis=1)  # scale of the neighbouring slot
+    out, _ = attention.decode_case(wrong)
+    bo, _ = brute_force(case, w.scale())
+    assert not np.allclose(out, bo, rtol=1e-9, atol=1e-9)

@@ -8,7 +8,9 @@ bytes itself):
 * ``"f32"`` storage is ``float32``; ``"bf16"`` storage is the raw 16-bit
   pattern as ``uint16``; ``"e4m3"`` storage is the raw OCP E4M3FN byte as
   ``uint8`` with fp32 scales ``k_scale``/``v_scale`` of shape
-  ``[num_pages, num_kv_heads]`` (one per page and KV head).
+  ``[num_pages, num_kv_heads]`` (one per page and KV head) or, for a
+  workload with ``kv_scale="token"``, ``[num_pages, page_size,
+  num_kv_heads]`` (one per token and KV head).
 * ``q`` is ``[rows, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
   storage: one row per request, or, for a workload with several new tokens
   per request, the ragged rows ``qo_indptr[r]:qo_indptr[r+1]`` of request r
@@ -70,6 +72,7 @@ class Workload:
     sm_scale: Optional[float] = None
     queries: Optional[tuple] = None
     shared_prefix: Optional[tuple] = None
+    kv_scale: str = "page"  # e4m3 scale granularity: "page" (page, head) or "token"
 
     @property
     def group(self) -> int:
@@ -101,6 +104,10 @@ CONFIGS = {
     "spec4_llama3_8b_bf16": Workload(
         "spec4_llama3_8b_bf16", 64, 32, 8, 128, 16, "bf16", "bf16", ("fixed", 2048),
         queries=("fixed", 4)),
+    # fp8 KV with row-wise scales: one fp32 scale per (token, KV head).
+    "fp8_rowwise_e4m3": Workload(
+        "fp8_rowwise_e4m3", 128, 32, 8, 128, 16, "e4m3", "bf16", ("uniform", 1024, 32768),
+        kv_scale="token"),
     # Cascade: 64 requests share one 8192-token prefix (a long system prompt or
     # document) and each has 512 tokens of its own.
     "cascade_prefix8k_bf16": Workload(
@@ -112,11 +119,12 @@ CONFIG_ORDER = list(CONFIGS)
 
 def custom_workload(batch, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype,
                     q_dtype, lens: Sequence[int], pool_pages=None, sm_scale=None,
-                    name="custom", qo_lens: Optional[Sequence[int]] = None) -> Workload:
+                    name="custom", qo_lens: Optional[Sequence[int]] = None,
+                    kv_scale: str = "page") -> Workload:
     queries = None if qo_lens is None else ("list", tuple(int(x) for x in qo_lens))
     return Workload(name, batch, num_qo_heads, num_kv_heads, head_dim, page_size, kv_dtype,
                     q_dtype, ("list", tuple(int(x) for x in lens)), pool_pages, sm_scale,
-                    queries)
+                    queries, kv_scale=kv_scale)
 
 
 def _draw_lengths(spec: tuple, batch: int, rng: np.random.Generator) -> np.ndarray:
@@ -260,8 +268,14 @@ def _to_e4m3_bytes(x: np.ndarray) -> np.ndarray:
     return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
-def _quantize_pool_e4m3(pool32: np.ndarray):
-    """Per (page, K/V, KV head) block: scale = amax / 448, bytes = RNE(x / scale)."""
+def _quantize_pool_e4m3(pool32: np.ndarray, per_token: bool = False):
+    """Per (page, K/V, KV head) block — or per (page, K/V, token, KV head) row —
+    scale = amax / 448, bytes = RNE(x / scale)."""
+    if per_token:
+        amax = np.abs(pool32).max(axis=4)  # [pages, 2, P, Hkv]
+        scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
+        y = pool32 / scale[..., None]
+        return _to_e4m3_bytes(y), scale[:, 0].copy(), scale[:, 1].copy()
     amax = np.abs(pool32).max(axis=(2, 4))  # [pages, 2, Hkv]
     scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
     y = pool32 / scale[:, :, None, :, None]
@@ -282,7 +296,7 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
     elif w.kv_dtype == "bf16":
         kv = _to_bf16_bits(pool32)
     elif w.kv_dtype == "e4m3":
-        kv, k_scale, v_scale = _quantize_pool_e4m3(pool32)
+        kv, k_scale, v_scale = _quantize_pool_e4m3(pool32, w.kv_scale == "token")
     else:
         raise ValueError(w.kv_dtype)
     q = q32 if w.q_dtype == "f32" else _to_bf16_bits(q32)
@@ -325,19 +339,26 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
         kv = torch.randn((npg, 2, P, Hkv, D), generator=g, device=device, dtype=kdt)
     elif w.kv_dtype == "e4m3":
         kv = torch.empty((npg, 2, P, Hkv, D), device=device, dtype=torch.uint8)
-        scale = torch.empty((npg, 2, Hkv), device=device, dtype=torch.float32)
+        per_token = w.kv_scale == "token"
+        sshape = (npg, 2, P, Hkv) if per_token else (npg, 2, Hkv)
+        scale = torch.empty(sshape, device=device, dtype=torch.float32)
         for p0 in range(0, npg, chunk_pages):
             p1 = min(npg, p0 + chunk_pages)
             x = torch.randn((p1 - p0, 2, P, Hkv, D), generator=g, device=device,
                             dtype=torch.float32)
-            amax = x.abs().amax(dim=(2, 4))
-            s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
-            y = (x / s[:, :, None, :, None]).clamp_(-E4M3_MAX, E4M3_MAX)
+            if per_token:
+                amax = x.abs().amax(dim=4)
+                s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+                y = (x / s[..., None]).clamp_(-E4M3_MAX, E4M3_MAX)
+            else:
+                amax = x.abs().amax(dim=(2, 4))
+                s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+                y = (x / s[:, :, None, :, None]).clamp_(-E4M3_MAX, E4M3_MAX)
             kv[p0:p1] = y.to(torch.float8_e4m3fn).view(torch.uint8)
             scale[p0:p1] = s
             del x, y
-        k_scale = scale[:, 0, :].contiguous()
-        v_scale = scale[:, 1, :].contiguous()
+        k_scale = scale[:, 0].contiguous()
+        v_scale = scale[:, 1].contiguous()
     else:
         raise ValueError(w.kv_dtype)
     if poison:
