@@ -51,7 +51,9 @@ def kv_bytes(w, table, logical: bool = False) -> int:
         groups, prefix = w.shared_prefix
         tokens = tokens - len(table["kv_lens"]) * prefix + groups * prefix
     b = tokens * w.num_kv_heads * w.head_dim * 2 * elem
-    if w.kv_dtype == "e4m3":
+    if w.kv_dtype == "e4m3" and w.kv_scale == "token":
+        b += tokens * w.num_kv_heads * 2 * 4
+    elif w.kv_dtype == "e4m3":
         pages = int(table["indptr"][-1])
         b += pages * w.num_kv_heads * 2 * 4
     return b
@@ -394,7 +396,7 @@ def main(argv=None) -> int:
                          kv_data_type=kv_dt, out_data_type=q_dt, sm_scale=w.scale(),
                          balance=args.balance, min_chunk_pages=args.min_chunk_pages,
                          qo_indptr=dcase["qo_indptr"], capacity=capacity,
-                         max_wgs_per_cu=args.wgs_per_cu)
+                         max_wgs_per_cu=args.wgs_per_cu, kv_scale=w.kv_scale)
             torch.cuda.synchronize()
 
     t0 = time.perf_counter()

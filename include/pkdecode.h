@@ -123,6 +123,13 @@ typedef struct pkd_plan pkd_plan;
  *                   info.units_per_item (query blocks = B with one token per
  *                   request), and merge tasks and partial rows never exceed
  *                   the q rows and the work items times the tokens per item.
+ *  kv_scale_per_token  e4m3 KV only. 0: k_scale/v_scale hold one fp32 scale
+ *                   per (page, KV head), [num_pages, Hkv]. 1: one per (token,
+ *                   KV head), [num_pages, Hkv, page_size] (a head's scales of a
+ *                   page contiguous, 16-byte aligned arrays) — the per-token
+ *                   row-wise fp8 scaling of "FlashInfer vs FlashAttention-3:
+ *                   GPU Kernel Optimization & FP8 Serving Latency",
+ *                   §"Production War Story" (bf16 q and head_dim 128 only).
  *  max_wgs_per_cu   0: the library's default residency for the KV dtype.
  *                   1..4: run() reserves LDS so that at most this many decode
  *                   workgroups share a compute unit (and slots == 0 counts
@@ -151,6 +158,7 @@ typedef struct {
   int32_t capacity_partials;
   int32_t capacity_qo_len;
   int32_t max_wgs_per_cu;
+  int32_t kv_scale_per_token;
 } pkd_plan_args;
 
 /* What a plan decided (pkd_plan_get_info). */
@@ -189,9 +197,10 @@ typedef struct {
  *  indices      int32 page ids of the page table (length indptr[B]); ids may
  *               repeat across requests (shared prefixes) and are not range
  *               checked
- *  k_scale,     float [num_pages, Hkv] contiguous; required for e4m3 KV,
- *  v_scale      ignored otherwise. Stored K (V) bytes are multiplied by the
- *               scale of their (page, KV head).
+ *  k_scale,     float [num_pages, Hkv] contiguous (or, with
+ *  v_scale      kv_scale_per_token, [num_pages, Hkv, page_size]); required for
+ *               e4m3 KV, ignored otherwise. Stored K (V) bytes are multiplied
+ *               by the scale of their (page, KV head) or (token, KV head).
  *  out          [rows, Hq, head_dim] contiguous, out_dtype
  *  lse          float [rows, Hq] or NULL: natural-log log-sum-exp of the
  *               scaled logits of each (q row, query head)

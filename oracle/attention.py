@@ -69,8 +69,8 @@ def gather_request(kv, indptr, indices, last_page_len, r: int, kv_head: int, kv_
 
     ``kv`` is the combined NHD pool ``[num_pages, 2, page_size, Hkv, D]`` in
     raw storage; index 0 of axis 1 is K, 1 is V. e4m3 scales are
-    ``[num_pages, Hkv]`` (one per page and KV head) or ``[num_pages,
-    page_size, Hkv]`` (one per token and KV head: the row-wise scaling of
+    ``[num_pages, Hkv]`` (one per page and KV head) or ``[num_pages, Hkv,
+    page_size]`` (one per token and KV head: the row-wise scaling of
     "FlashInfer vs FlashAttention-3: GPU Kernel Optimization & FP8 Serving
     Latency", §"Production War Story").
     """
@@ -81,9 +81,9 @@ def gather_request(kv, indptr, indices, last_page_len, r: int, kv_head: int, kv_
     if kv_dtype == "e4m3":
         ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
         vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
-        if ks.ndim == 3:  # one scale per (page, slot, KV head): row-wise
-            K = K * ks[page, slot, kv_head][:, None]
-            V = V * vs[page, slot, kv_head][:, None]
+        if ks.ndim == 3:  # one scale per (page, KV head, slot): row-wise
+            K = K * ks[page, kv_head, slot][:, None]
+            V = V * vs[page, kv_head, slot][:, None]
         else:  # one scale per (page, KV head)
             K = K * ks[page, kv_head][:, None]
             V = V * vs[page, kv_head][:, None]

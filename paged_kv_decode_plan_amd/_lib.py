@@ -53,6 +53,7 @@ class PlanArgs(ctypes.Structure):
         ("capacity_partials", ctypes.c_int32),
         ("capacity_qo_len", ctypes.c_int32),
         ("max_wgs_per_cu", ctypes.c_int32),
+        ("kv_scale_per_token", ctypes.c_int32),
     ]
 
 

@@ -172,6 +172,7 @@ struct pkd_plan {
   pkd::Partition part;
   pkd_plan_info info{};
   int rows = 0;  // query rows per work item and KV head (kernel choice)
+  int kv_impl = 0;  // KV format as the kernels see it (pkd::kF32 .. kE4M3T)
   int wgs_cap = 0;  // decode workgroups per compute unit at most (0: no cap)
   bool fixed = false;    // fixed-capacity plan: grids from capacities, counts read on device
   int32_t launch_items = 0, launch_tasks = 0;
@@ -217,13 +218,21 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (a->kv_dtype != PKD_DTYPE_F32 && a->kv_dtype != PKD_DTYPE_BF16 &&
       a->kv_dtype != PKD_DTYPE_E4M3)
     return fail(PKD_ERR_UNSUPPORTED, "kv_dtype %d not supported", a->kv_dtype);
+  if (a->kv_scale_per_token != 0 && a->kv_scale_per_token != 1)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "kv_scale_per_token must be 0 or 1");
+  if (a->kv_scale_per_token && a->kv_dtype != PKD_DTYPE_E4M3)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "kv_scale_per_token applies to e4m3 KV only");
+  // The kernels' view of the KV format: row-wise e4m3 scales are their own form.
+  const int32_t kv_impl = a->kv_scale_per_token ? pkd::kE4M3T : a->kv_dtype;
   if (!is_pow2(a->page_size) || a->page_size > 1024)
     return fail(PKD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]",
                 a->page_size);
-  if (!pkd::decode_supported(a->kv_dtype, a->head_dim, group, group,
+  if (!pkd::decode_supported(kv_impl, a->head_dim, group, group,
                              a->q_dtype == PKD_DTYPE_BF16, a->page_size))
-    return fail(PKD_ERR_UNSUPPORTED, "no kernel for head_dim=%d group=%d kv_dtype=%d q_dtype=%d",
-                a->head_dim, group, a->kv_dtype, a->q_dtype);
+    return fail(PKD_ERR_UNSUPPORTED,
+                "no kernel for head_dim=%d group=%d kv_dtype=%d q_dtype=%d%s", a->head_dim, group,
+                a->kv_dtype, a->q_dtype,
+                a->kv_scale_per_token ? " with row-wise scales (needs bf16 q, head_dim 128)" : "");
   // Several new tokens per request: a work item carries up to 16 / group of
   // one request's tokens, so that its group x tokens rows fill the columns of
   // one MFMA tile.
@@ -254,7 +263,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   const int32_t qo_shape = fixed ? caps[3] : max_q;
   const int32_t queries_per_item = qo_shape > 1 ? std::max(1, 16 / group) : 1;
   const int32_t rows = group * std::min(queries_per_item, qo_shape);
-  if (max_q > 1 && !pkd::decode_uses_mfma(a->kv_dtype, a->head_dim, group, rows,
+  if (max_q > 1 && !pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
                                           a->q_dtype == PKD_DTYPE_BF16, a->page_size))
     return fail(PKD_ERR_UNSUPPORTED,
                 "several query tokens per request need bf16 q, bf16 or e4m3 KV and head_dim 128 "
@@ -263,7 +272,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0 || a->max_wgs_per_cu < 0)
     return fail(PKD_ERR_INVALID_ARGUMENT,
                 "slots, balance, min_chunk_pages and max_wgs_per_cu must be >= 0");
-  const bool mfma = pkd::decode_uses_mfma(a->kv_dtype, a->head_dim, group, rows,
+  const bool mfma = pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
                                           a->q_dtype == PKD_DTYPE_BF16, a->page_size);
   const int32_t wgs_cap =
       a->max_wgs_per_cu ? a->max_wgs_per_cu : default_wgs_cap(mfma, rows == group);
@@ -273,7 +282,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   int slots = a->slots;
   if (slots == 0) {
     int32_t wgs = 0, cus = 0;
-    int rc = device_slots(a->device, a->q_dtype, a->kv_dtype, a->head_dim, group, rows,
+    int rc = device_slots(a->device, a->q_dtype, kv_impl, a->head_dim, group, rows,
                           a->page_size, wgs_cap, &wgs, &cus);
     if (rc != PKD_OK) return rc;
     slots = wgs * cus;
@@ -304,6 +313,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   p->args.last_page_len = nullptr;
   p->args.qo_indptr = nullptr;
   p->rows = rows;
+  p->kv_impl = kv_impl;
   p->wgs_cap = wgs_cap;
   p->device = a->device;
   p->sm_scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(float(a->head_dim));
@@ -447,6 +457,9 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
     return fail(PKD_ERR_INVALID_ARGUMENT, "q, k, v, indices, out and workspace must not be NULL");
   if (a.kv_dtype == PKD_DTYPE_E4M3 && (!r->k_scale || !r->v_scale))
     return fail(PKD_ERR_INVALID_ARGUMENT, "e4m3 KV needs k_scale and v_scale");
+  if (a.kv_scale_per_token && (reinterpret_cast<uintptr_t>(r->k_scale) % 16 ||
+                               reinterpret_cast<uintptr_t>(r->v_scale) % 16))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "row-wise scale arrays must be 16-byte aligned");
   if (r->workspace != p->uploaded_to)
     return fail(PKD_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
   if (r->workspace_bytes < p->info.workspace_bytes)
@@ -465,7 +478,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
     return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
 
   pkd::DecodeLaunch L;
-  L.kv_dtype = a.kv_dtype;
+  L.kv_dtype = p->kv_impl;
   L.head_dim = a.head_dim;
   L.group = a.num_qo_heads / a.num_kv_heads;
   L.rows = p->rows;

@@ -73,7 +73,9 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 #define PKD_BF16_NSUB 1
 #endif
 template <int KV>
-constexpr int nsub() { return KV == kE4M3 ? PKD_E4M3_NSUB : PKD_BF16_NSUB; }
+constexpr bool fp8() { return KV == kE4M3 || KV == kE4M3T; }
+template <int KV>
+constexpr int nsub() { return fp8<KV>() ? PKD_E4M3_NSUB : PKD_BF16_NSUB; }
 template <int KV>
 constexpr int tile_tokens() { return kSub * nsub<KV>(); }
 
@@ -144,6 +146,17 @@ struct Loads<kE4M3> {
   static constexpr int kElem = 1;
 };
 
+// e4m3 with row-wise scales: the same bytes, plus the K and V scales of the
+// four tokens 4*(l/16) + e whose scores (and P weights) this lane holds.
+template <>
+struct Loads<kE4M3T> {
+  u32x4_t k[2];
+  uint2 v[4];
+  float ks[4];
+  float vs[4];
+  static constexpr int kElem = 1;
+};
+
 // The head_dim index visited by QK k-slot (dc, q, e): bf16 lanes load 8 dims at
 // chunk 4*dc + q; e4m3 lanes load 16 dims at chunk 4*h + q and split them
 // into dc = 2h (first 8) and dc = 2h + 1 (last 8).
@@ -171,6 +184,9 @@ struct Ctx {
   const char* kbase;
   const char* vbase;
   const int32_t* page_ids;  // the item's slice of the page table
+  const float* k_scale;     // row-wise e4m3 scales (kE4M3T only)
+  const float* v_scale;
+  int num_kv_heads, kvh;
   int64_t page_stride, token_stride, head_off;
   int log2p, pmask, kv_len, q4, j;
   int lim;  // tokens of the item seen by this lane's row (column j of S)
@@ -249,6 +265,28 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
         ld.v[e] = *reinterpret_cast<const uint2*>(c.vbase + off);
     }
   }
+  if constexpr (KV == kE4M3T) {
+    // Row-wise scales [pages, Hkv, page_size] of this lane's four tokens
+    // 4*(l/16)..+4: with 16-token sub-tiles in one page they are four
+    // consecutive floats (one 16-byte load each for K and V); otherwise one
+    // lookup per token, clamped like the rows themselves.
+    if constexpr (PAGE16 && FULL) {
+      const int64_t idx = ((tp.page * c.num_kv_heads + c.kvh) << c.log2p) + (t0 & c.pmask) + 4 * c.q4;
+      const float4 k4 = *reinterpret_cast<const float4*>(c.k_scale + idx);
+      const float4 v4 = *reinterpret_cast<const float4*>(c.v_scale + idx);
+      ld.ks[0] = k4.x, ld.ks[1] = k4.y, ld.ks[2] = k4.z, ld.ks[3] = k4.w;
+      ld.vs[0] = v4.x, ld.vs[1] = v4.y, ld.vs[2] = v4.z, ld.vs[3] = v4.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = min(t0 + 4 * c.q4 + e, last);
+        const int64_t page = PAGE16 ? tp.page : int64_t(c.page_ids[t >> c.log2p]);
+        const int64_t idx = ((page * c.num_kv_heads + c.kvh) << c.log2p) + (t & c.pmask);
+        ld.ks[e] = c.k_scale[idx];
+        ld.vs[e] = c.v_scale[idx];
+      }
+    }
+  }
 }
 
 // A wavefront tile: nsub<KV>() consecutive sub-tiles, loaded together.
@@ -318,6 +356,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     const int t = t0 + 4 * c.q4 + r;
     float kr = ks;
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
+    if constexpr (KV == kE4M3T) kr = ks * ld.ks[r];
     const float v = (FULL || t < c.lim) ? s[r] * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
@@ -364,6 +403,10 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
         vs = token_scale(a.v_scale, c, a, kvh, t0 + 4 * c.q4 + e);
       p[e] *= vs;
     }
+  }
+  if constexpr (KV == kE4M3T) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) p[e] *= ld.vs[e];
   }
   uint2 p_hi, p_lo;
   {
@@ -437,9 +480,13 @@ __device__ inline void load_pid_block(const Ctx& c, const KernelArgs& a, int kvh
 
 // Register budget: 128 VGPRs (4 wavefronts per SIMD) when a tile is one
 // 16-token sub-tile of pages >= 16; larger tiles and per-lane page lookups need
-// up to 168 (3 wavefronts per SIMD).
+// up to 168 (3 wavefronts per SIMD); row-wise e4m3 scales ride along with the
+// loads and get up to 256 (2 per SIMD, still twice what one workgroup per CU
+// uses).
 template <int KV, bool PAGE16>
-constexpr int waves_per_simd() { return PAGE16 && nsub<KV>() == 1 ? 4 : 3; }
+constexpr int waves_per_simd() {
+  return KV == kE4M3T ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
+}
 
 template <int KV, int G, bool PAGE16>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16>()))) void decode_mfma_kernel(KernelArgs a) {
@@ -457,6 +504,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   c.kbase = static_cast<const char*>(a.k);
   c.vbase = static_cast<const char*>(a.v);
   c.page_ids = a.indices + it.page_begin;
+  c.k_scale = a.k_scale;
+  c.v_scale = a.v_scale;
+  c.num_kv_heads = a.num_kv_heads;
+  c.kvh = kvh;
   c.page_stride = a.page_stride;
   c.token_stride = a.token_stride;
   c.head_off = int64_t(kvh) * a.head_stride;
@@ -610,6 +661,7 @@ DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size)
   switch (kv_dtype) {
     case kBF16: return p16 ? pick_group<kBF16, true>(rows) : pick_group<kBF16, false>(rows);
     case kE4M3: return p16 ? pick_group<kE4M3, true>(rows) : pick_group<kE4M3, false>(rows);
+    case kE4M3T: return p16 ? pick_group<kE4M3T, true>(rows) : pick_group<kE4M3T, false>(rows);
     default: return nullptr;
   }
 }

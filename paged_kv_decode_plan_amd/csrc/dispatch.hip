@@ -22,10 +22,10 @@ static int pow2_ceil(int x) {
 static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
                        int page_size) {
   if ((group & (group - 1)) || rows < group || rows % group) return nullptr;
-  if (q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3)) {
+  if (q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T)) {
     if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size)) return f;
   }
-  if (rows != group) return nullptr;
+  if (rows != group || kv_dtype == kE4M3T) return nullptr;  // MFMA-only forms
   return valu_decode_kernel(kv_dtype, head_dim, group);
 }
 
@@ -50,7 +50,8 @@ bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_bf1
 }
 
 bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size) {
-  return q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3) && rows >= group &&
+  return q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T) &&
+         rows >= group &&
          mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size) != nullptr;
 }
 
@@ -74,7 +75,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.num_items = L.num_items;
-  a.xcd_group = L.kv_dtype == kE4M3 ? 8 : 1;
+  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T) ? 8 : 1;
   a.num_kv_heads = L.num_kv_heads;
   a.num_qo_heads = L.num_qo_heads;
   a.group_log2 = ilog2(L.group);

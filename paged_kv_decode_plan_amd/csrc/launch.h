@@ -7,7 +7,9 @@
 
 namespace pkd {
 
-enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2 };
+// KV element formats as the kernels see them: kE4M3T is e4m3 with one scale
+// per (token, KV head) instead of one per (page, KV head).
+enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE4M3T = 3 };
 
 // Device-side layout of one work item (32 bytes): pages
 // [page_begin, page_begin + ceil(kv_len / page_size)) of the page table for

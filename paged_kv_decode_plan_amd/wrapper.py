@@ -51,7 +51,8 @@ class Plan:
                  head_dim: int, page_size: int, q_dtype: int, kv_dtype: int, out_dtype: int,
                  sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
                  min_chunk_pages: int = 0, device: int = 0, qo_indptr=None,
-                 causal: bool = True, capacity=None, max_wgs_per_cu: int = 0):
+                 causal: bool = True, capacity=None, max_wgs_per_cu: int = 0,
+                 kv_scale: str = "page"):
         lib = _lib.load()
         self._lib = lib
         self._handle = ctypes.c_void_p()
@@ -83,6 +84,10 @@ class Plan:
             a.qo_indptr = self.qo_indptr.ctypes.data_as(_lib._c_i32p)
         a.non_causal = 0 if causal else 1
         a.max_wgs_per_cu = max_wgs_per_cu
+        if kv_scale not in ("page", "token"):
+            raise ValueError("kv_scale must be 'page' or 'token'")
+        a.kv_scale_per_token = 1 if kv_scale == "token" else 0
+        self.kv_scale = kv_scale
         if capacity is not None:
             c = _capacity(capacity)
             (a.capacity_items, a.capacity_merge_tasks, a.capacity_partials,
@@ -185,7 +190,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
              q_data_type=None, kv_data_type=None, out_data_type=None, data_type=None,
              sm_scale: Optional[float] = None, slots: int = 0, balance: int = 0,
              min_chunk_pages: int = 0, qo_indptr=None, causal: bool = True,
-             capacity=None, max_wgs_per_cu: int = 0) -> None:
+             capacity=None, max_wgs_per_cu: int = 0, kv_scale: str = "page") -> None:
         """Plan one batch. ``qo_indptr`` (host, [batch+1]) gives request r the q
         rows ``qo_indptr[r]:qo_indptr[r+1]``: its newest tokens, attended
         causally; omitted, every request has one query token (q row r). With
@@ -194,7 +199,9 @@ class BatchDecodeWithPagedKVCacheWrapper:
         ``items``, ``merge_tasks``, ``partials``, ``qo_len``) makes a
         fixed-capacity plan: run() then launches the same grids with the same
         arguments for every such plan, so a captured HIP graph of run() stays
-        valid across plan()/upload of new batches."""
+        valid across plan()/upload of new batches. ``kv_scale`` (e4m3 KV):
+        ``"page"`` for one scale per (page, KV head), ``"token"`` for one per
+        (token, KV head)."""
         import torch
         if pos_encoding_mode != "NONE":
             raise ValueError("only pos_encoding_mode='NONE' is supported")
@@ -207,7 +214,8 @@ class BatchDecodeWithPagedKVCacheWrapper:
         self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                           _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
                           slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr,
-                          causal=causal, capacity=capacity, max_wgs_per_cu=max_wgs_per_cu)
+                          causal=causal, capacity=capacity, max_wgs_per_cu=max_wgs_per_cu,
+                          kv_scale=kv_scale)
         self._indices = indices if isinstance(indices, torch.Tensor) else torch.as_tensor(
             np.asarray(indices, dtype=np.int32))
         if self._indices.device != self._ws.device or self._indices.dtype != torch.int32:
@@ -260,10 +268,11 @@ class BatchDecodeWithPagedKVCacheWrapper:
         if p.kv_dtype == _lib.DTYPE_E4M3:
             if k_scale is None or v_scale is None:
                 raise ValueError("e4m3 KV needs k_scale and v_scale [num_pages, num_kv_heads]")
+            want = ((k.shape[0], p.num_kv_heads, p.page_size) if p.kv_scale == "token"
+                    else (k.shape[0], p.num_kv_heads))
             for s in (k_scale, v_scale):
-                if (s.dtype != torch.float32 or not s.is_contiguous()
-                        or s.shape != (k.shape[0], p.num_kv_heads)):
-                    raise ValueError("scales must be contiguous float32 [num_pages, num_kv_heads]")
+                if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != want:
+                    raise ValueError(f"scales must be contiguous float32 {list(want)}")
             a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
         a.out = out.data_ptr()
         a.lse = lse.data_ptr() if lse is not None else None

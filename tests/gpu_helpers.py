@@ -60,7 +60,8 @@ def run_hip(dcase: dict, out_dtype="f32", slots=0, balance=0, min_chunk_pages=0,
                  w.page_size, q_data_type=dcase["q"].dtype,
                  kv_data_type=("e4m3" if w.kv_dtype == "e4m3" else dcase["kv"].dtype),
                  out_data_type=odt, sm_scale=w.scale(), slots=slots, balance=balance,
-                 min_chunk_pages=min_chunk_pages, qo_indptr=dcase.get("qo_indptr"))
+                 min_chunk_pages=min_chunk_pages, qo_indptr=dcase.get("qo_indptr"),
+                 kv_scale=w.kv_scale)
     out, l = wrapper.run(dcase["q"], dcase["kv"] if kv is None else kv, return_lse=lse,
                          k_scale=dcase["k_scale"], v_scale=dcase["v_scale"])
     torch.cuda.synchronize()

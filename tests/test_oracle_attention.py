@@ -58,8 +58,8 @@ def brute_force(case, sm_scale):
             for page, slot in toks:
                 ks = vs = 1.0
                 if w.kv_dtype == "e4m3" and case["k_scale"].ndim == 3:  # per token
-                    ks = float(case["k_scale"][page, slot, kvh])
-                    vs = float(case["v_scale"][page, slot, kvh])
+                    ks = float(case["k_scale"][page, kvh, slot])
+                    vs = float(case["v_scale"][page, kvh, slot])
                 elif w.kv_dtype == "e4m3":
                     ks = float(case["k_scale"][page, kvh])
                     vs = float(case["v_scale"][page, kvh])
@@ -266,7 +266,7 @@ def test_rowwise_e4m3_scales_match_brute_force(seed, qd, hq, hkv, p, lens):
     w = custom_workload(len(lens), hq, hkv, 8, p, "e4m3", qd, lens,
                         pool_pages=sum(-(-x // p) for x in lens) + 3, kv_scale="token")
     case = host_case(w, seed, poison=True)
-    assert case["k_scale"].shape == (case["kv"].shape[0], p, hkv)
+    assert case["k_scale"].shape == (case["kv"].shape[0], hkv, p)
     out, lse = attention.decode_case(case)
     bo, bl = brute_force(case, w.scale())
     np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-12)
@@ -280,8 +280,8 @@ def test_rowwise_scales_equal_to_page_scales_give_page_results():
     out0, lse0 = attention.decode_case(case)
     P = case["kv"].shape[2]
     tok = dict(case)
-    tok["k_scale"] = np.repeat(case["k_scale"][:, None, :], P, axis=1)
-    tok["v_scale"] = np.repeat(case["v_scale"][:, None, :], P, axis=1)
+    tok["k_scale"] = np.repeat(case["k_scale"][:, :, None], P, axis=2)
+    tok["v_scale"] = np.repeat(case["v_scale"][:, :, None], P, axis=2)
     out1, lse1 = attention.decode_case(tok)
     np.testing.assert_array_equal(out0, out1)
     np.testing.assert_array_equal(lse0, lse1)

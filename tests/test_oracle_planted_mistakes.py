@@ -139,7 +139,7 @@ def test_rowwise_scale_slot_mixup_is_caught():
     case = host_case(w, 7, poison=True)
     assert _matches_brute(case, w)
     wrong = dict(case)
-    wrong["k_scale"] = np.roll(case["k_scale"], 1, axis=1)  # scale of the neighbouring slot
+    wrong["k_scale"] = np.roll(case["k_scale"], 1, axis=2)  # scale of the neighbouring slot
     out, _ = attention.decode_case(wrong)
     bo, _ = brute_force(case, w.scale())
     assert not np.allclose(out, bo, rtol=1e-9, atol=1e-9)

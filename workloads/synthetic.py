@@ -9,8 +9,9 @@ bytes itself):
   pattern as ``uint16``; ``"e4m3"`` storage is the raw OCP E4M3FN byte as
   ``uint8`` with fp32 scales ``k_scale``/``v_scale`` of shape
   ``[num_pages, num_kv_heads]`` (one per page and KV head) or, for a
-  workload with ``kv_scale="token"``, ``[num_pages, page_size,
-  num_kv_heads]`` (one per token and KV head).
+  workload with ``kv_scale="token"``, ``[num_pages, num_kv_heads,
+  page_size]`` (one per token and KV head; a head's scales of a page are
+  contiguous).
 * ``q`` is ``[rows, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
   storage: one row per request, or, for a workload with several new tokens
   per request, the ragged rows ``qo_indptr[r]:qo_indptr[r+1]`` of request r
@@ -275,7 +276,8 @@ def _quantize_pool_e4m3(pool32: np.ndarray, per_token: bool = False):
         amax = np.abs(pool32).max(axis=4)  # [pages, 2, P, Hkv]
         scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
         y = pool32 / scale[..., None]
-        return _to_e4m3_bytes(y), scale[:, 0].copy(), scale[:, 1].copy()
+        st = np.ascontiguousarray(scale.transpose(0, 1, 3, 2))  # [pages, 2, Hkv, P]
+        return _to_e4m3_bytes(y), st[:, 0].copy(), st[:, 1].copy()
     amax = np.abs(pool32).max(axis=(2, 4))  # [pages, 2, Hkv]
     scale = np.where(amax > 0, amax / E4M3_MAX, 1.0).astype(np.float32)
     y = pool32 / scale[:, :, None, :, None]
@@ -340,16 +342,17 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
     elif w.kv_dtype == "e4m3":
         kv = torch.empty((npg, 2, P, Hkv, D), device=device, dtype=torch.uint8)
         per_token = w.kv_scale == "token"
-        sshape = (npg, 2, P, Hkv) if per_token else (npg, 2, Hkv)
+        sshape = (npg, 2, Hkv, P) if per_token else (npg, 2, Hkv)
         scale = torch.empty(sshape, device=device, dtype=torch.float32)
         for p0 in range(0, npg, chunk_pages):
             p1 = min(npg, p0 + chunk_pages)
             x = torch.randn((p1 - p0, 2, P, Hkv, D), generator=g, device=device,
                             dtype=torch.float32)
             if per_token:
-                amax = x.abs().amax(dim=4)
+                amax = x.abs().amax(dim=4)  # [pages, 2, P, Hkv]
                 s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
                 y = (x / s[..., None]).clamp_(-E4M3_MAX, E4M3_MAX)
+                s = s.transpose(2, 3)  # [pages, 2, Hkv, P]
             else:
                 amax = x.abs().amax(dim=(2, 4))
                 s = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
