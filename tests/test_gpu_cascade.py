@@ -129,3 +129,33 @@ def test_cascade_matches_decode_over_prefix_plus_suffix(kv, g, out_dt):
     cw.close()
     assert out.dtype == out_dt
     compare(out, lse, ref_out, ref_lse, kv, out_dtype="bf16" if out_dt == torch.bfloat16 else "f32")
+
+
+def test_full_size_cascade_sampled_requests():
+    """The 64-request, 8192-token shared-prefix workload at full size in the
+    bench's configuration; sampled requests against decode over their full
+    page lists."""
+    from gpu_helpers import sample_request_case
+    from workloads import CONFIGS, device_case
+    name = "cascade_prefix8k_bf16"
+    w = CONFIGS[name]
+    seed = list(CONFIGS).index(name) + 1
+    _say("full-size", name, "seed", seed)
+    dc = device_case(w, seed, DEV, poison=True)
+    sh, un = dc["shared"], dc["unique"]
+    cw = pk.CascadeBatchDecodeWrapper(workspace(), "NHD")
+    cw.plan(sh["indptr"], torch.from_numpy(sh["indices"]).to(DEV), sh["last_page_len"],
+            dc["group_qo_indptr"], un["indptr"], torch.from_numpy(un["indices"]).to(DEV),
+            un["last_page_len"], w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+            q_data_type=torch.bfloat16, kv_data_type=torch.bfloat16,
+            out_data_type=torch.float32, sm_scale=w.scale())
+    out, lse = cw.run(dc["q"], dc["kv"], return_lse=True)
+    torch.cuda.synchronize()
+    cw.close()
+    assert torch.isfinite(out).all()
+    for r in (0, 31, w.batch - 1):
+        sub = sample_request_case(dc, r)
+        ref_out, ref_lse = attention.decode_case(sub)
+        compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, "bf16")
+    del dc
+    torch.cuda.empty_cache()
