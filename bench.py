@@ -1,21 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark: batched paged-KV decode attention on one MI355X.
 
-One step is one run() over the whole batch: the split-KV decode kernel plus
-the merge kernel when requests are split. The default workload is the
+One step is one run() over the whole batch: the split-KV decode kernel, whose
+last workgroup of each split request also merges its partial states. The
+default workload is the
 Llama-3-8B-shaped decode batch (B=64, 32 query / 8 KV heads, head_dim 128,
 16-token pages, every context 2048, bf16). Inputs are synthetic (seeded
 normal values, shuffled page table) and resident in HBM before timing.
 
 Timing: W untimed warmup steps, then K timed steps. Before each timed step a
 1 GiB buffer is read so that neither L2 nor the 256 MB last-level cache holds
-KV; HIP events on the launch stream bracket the decode kernel and the merge
-kernel of every step separately. ``value`` is KV-read GB/s over the whole
-step (algorithmic KV bytes / mean step time). ``roofline`` is for the decode
-kernel alone. ``cpu_baseline`` times the float64 oracle on a bounded sample
-of the same batch on one host core (and its ``parallel`` entry, the same
-sample on a thread pool over the host cores); ``calibration`` is a plain
-1 GiB streaming read timed on the same device.
+KV; HIP events on the launch stream bracket every step (with
+``--separate-merge``, the decode and merge stages apart). ``value`` is KV-read
+GB/s over the whole step (algorithmic KV bytes / mean step time).
+``roofline`` is for the decode kernel. ``cpu_baseline`` times the float64
+oracle on a bounded sample of the same batch on one host core (and its
+``parallel`` entry, the same sample over single-threaded worker processes);
+``calibration`` is a plain 1 GiB streaming read timed on the same device.
 
 Prints one JSON line.
 """
@@ -307,6 +308,9 @@ def main(argv=None) -> int:
                          "(implies --fixed-capacity)")
     ap.add_argument("--wgs-per-cu", type=int, default=0,
                     help="cap on decode workgroups per compute unit (0: library default)")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="launch and time the decode and merge stages apart instead of one "
+                         "run() with the merge folded into the decode kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--balance", type=int, default=0)
@@ -422,7 +426,9 @@ def main(argv=None) -> int:
 
     from paged_kv_decode_plan_amd import _lib
 
-    has_merge = not cascade and info["num_split_requests"] > 0
+    # By default a step is one run(): the decode kernel with the merge of split
+    # requests folded in. --separate-merge times the two stages apart instead.
+    has_merge = args.separate_merge and not cascade and info["num_split_requests"] > 0
     graph = None
     if args.graph:
         if cascade:
@@ -437,9 +443,9 @@ def main(argv=None) -> int:
         has_merge = False
 
     def step(ev=None):
-        """One run(): the decode kernel, and the merge kernel when the plan split a
-        request. Timed steps bracket the decode launch with events (and the merge
-        launch, only when there is one: an event pair costs a few µs itself)."""
+        """One run(). Timed steps bracket it with events; with --separate-merge
+        the decode and merge stages are launched and bracketed apart (an event
+        pair costs a few µs itself)."""
         if graph is not None:  # decode and merge kernels replayed from the graph
             if ev is not None:
                 ev[0].record()
@@ -450,7 +456,7 @@ def main(argv=None) -> int:
         if ev is None:
             wrapper.run(dcase["q"], dcase["kv"], **run_kw)
             return
-        if cascade:  # one bracket around both levels and the merges
+        if not has_merge:  # one bracket around the whole run
             ev[0].record()
             wrapper.run(dcase["q"], dcase["kv"], **run_kw)
             ev[1].record()
@@ -541,6 +547,10 @@ def main(argv=None) -> int:
         "warm_us_per_step": round(warm_ms * 1e3, 2) if warm_ms else None,
         "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1) if warm_ms else None,
         "merge_us": round(statistics.fmean(mrg_ms) * 1e3, 2),
+        "merge": ("none (no request split)" if info["num_split_requests"] == 0 else
+                  "separate stages (timed apart)" if has_merge else
+                  "folded into the decode kernel" if info.get("merge_folded") else
+                  "separate merge kernel inside the step"),
         "calibration": {
             "kernel": "torch int64 max over a 1 GiB buffer (plain streaming read)",
             "read_gbs": round(cal_gbs, 1),

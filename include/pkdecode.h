@@ -178,6 +178,7 @@ typedef struct {
   int32_t max_qo_len;          /* most new tokens of one request */
   int32_t num_merge_tasks;     /* q rows of split requests (merge grid / num_qo_heads) */
   int32_t units_per_item;      /* decode workgroups per work item (one per KV head) */
+  int32_t merge_folded;        /* 1: pkd_run folds the merge into the decode kernel */
 } pkd_plan_info;
 
 /* Arguments of pkd_run. All pointers are device pointers.
@@ -261,15 +262,22 @@ int pkd_plan_get_worklist(const pkd_plan* plan, int32_t* items_out, int32_t* mer
  * until the copy has finished). run() must then be given the same workspace. */
 int pkd_plan_upload(pkd_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Enqueue the decode kernel and, when any request is split, the merge
- * kernel on args->stream. Allocates nothing and does not synchronise. */
+/* Enqueue the run on args->stream: the decode kernel and, when a request was
+ * split, the merge. For an exact plan whose split requests have at most four
+ * chunks the merge is folded into the decode kernel (one launch): the last
+ * workgroup of each split request (per query block and KV head) folds its
+ * partial states into the output rows, counting chunk arrivals with an
+ * atomic counter kept in the workspace, which it leaves at zero. Otherwise
+ * (longer folds, fixed-capacity plans) the separate merge kernel follows.
+ * Allocates nothing and does not synchronise. */
 int pkd_run(const pkd_plan* plan, const pkd_run_args* args);
 
-/* Stages of run(), for callers that time or interleave them: the split-KV
- * decode kernel (partial states or final rows) and the merge kernel that
- * folds the partial states of split requests (a no-op when none is split).
- * pkd_run(plan, args) == pkd_run_stages(plan, args, PKD_STAGE_ALL). The merge
- * stage reads what the decode stage of the same plan and workspace wrote. */
+/* Stages of run(), kept apart, for callers that time or interleave them or
+ * combine partial states themselves: the split-KV decode kernel alone
+ * (partial states of split requests, final rows of the others) and the
+ * separate merge kernel that folds the partial states (a no-op when none is
+ * split). PKD_STAGE_ALL is pkd_run. The merge stage reads what the decode
+ * stage of the same plan and workspace wrote. */
 #define PKD_STAGE_DECODE 1
 #define PKD_STAGE_MERGE 2
 #define PKD_STAGE_ALL 3

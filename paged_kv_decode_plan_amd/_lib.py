@@ -74,6 +74,7 @@ class PlanInfo(ctypes.Structure):
         ("max_qo_len", ctypes.c_int32),
         ("num_merge_tasks", ctypes.c_int32),
         ("units_per_item", ctypes.c_int32),
+        ("merge_folded", ctypes.c_int32),
     ]
 
 

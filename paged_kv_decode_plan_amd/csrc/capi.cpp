@@ -177,7 +177,9 @@ struct pkd_plan {
   bool fixed = false;    // fixed-capacity plan: grids from capacities, counts read on device
   int32_t launch_items = 0, launch_tasks = 0;
   // Device workspace layout (byte offsets).
-  size_t off_items = 0, off_split = 0, header_bytes = 0;
+  size_t off_items = 0, off_split = 0, off_blocks = 0, off_counters = 0, header_bytes = 0;
+  int32_t num_blocks = 0;  // fused-merge records (split request, query block)
+  bool fuse_ok = false;    // run() may fold the merge into the decode kernel
   size_t off_part_md = 0, off_part_o = 0;
   std::vector<unsigned char> header;  // host image of [items | merge tasks]
   PinnedBlock staging;                // from the process-wide pool, on first upload
@@ -330,6 +332,24 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     for (int32_t i = 0; i < nq; ++i) tasks.push_back({q0 + i, part.merge_indptr[r] + i, chunks, nq});
   }
   const size_t n_tasks = tasks.size();
+  // One fused-merge record per (split request, query block); the item's
+  // record index is found from its first q row.
+  std::vector<pkd::MergeTask> blocks;
+  std::map<int32_t, int32_t> block_of_row;
+  for (const int32_t r : part.split_requests) {
+    const int32_t q0 = max_q > 1 ? a->qo_indptr[r] : r;
+    const int32_t nq = max_q > 1 ? a->qo_indptr[r + 1] - a->qo_indptr[r] : 1;
+    const int32_t chunks = (part.merge_indptr[r + 1] - part.merge_indptr[r]) / nq;
+    for (int32_t b = 0; b * queries_per_item < nq; ++b) {
+      block_of_row[q0 + b * queries_per_item] = int32_t(blocks.size());
+      blocks.push_back({q0 + b * queries_per_item, part.merge_indptr[r] + b * queries_per_item,
+                        chunks, nq});
+    }
+  }
+  const size_t n_blocks = blocks.size();
+  constexpr int32_t kFuseChunks = 4;
+  int32_t max_chunks = 0;
+  for (const auto& b : blocks) max_chunks = std::max(max_chunks, b.count);
   if (fixed && (n_items > size_t(caps[0]) || n_tasks > size_t(caps[1]) ||
                 size_t(part.num_partials) > size_t(caps[2]))) {
     const size_t np = size_t(part.num_partials);
@@ -339,19 +359,28 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                 "capacities are %d, %d and %d",
                 n_items, n_tasks, np, caps[0], caps[1], caps[2]);
   }
-  // Workspace: [counts (256 B) | items | merge tasks | partial (m, d) | partial o],
-  // sized by the plan itself or, for a fixed-capacity plan, by its capacities.
+  // Workspace: [counts (256 B) | items | merge tasks | fused-merge records |
+  // fused-merge counters | partial (m, d) | partial o], sized by the plan
+  // itself or, for a fixed-capacity plan, by its capacities (records never
+  // outnumber merge tasks). The uploaded header runs through the counters,
+  // so every upload starts them at zero; the kernel leaves them at zero.
   const size_t lay_items = fixed ? size_t(caps[0]) : n_items;
   const size_t lay_tasks = fixed ? size_t(caps[1]) : std::max<size_t>(n_tasks, 1);
   const size_t lay_parts = fixed ? size_t(caps[2]) : size_t(part.num_partials);
   p->fixed = fixed;
   p->launch_items = int32_t(lay_items);
   p->launch_tasks = fixed ? caps[1] : int32_t(n_tasks);
+  p->num_blocks = int32_t(n_blocks);
+  p->fuse_ok = !fixed && max_chunks <= kFuseChunks;
   p->off_items = 256;
   p->off_split = align256(p->off_items + lay_items * sizeof(pkd::DeviceItem));
-  const size_t end_split = align256(p->off_split + lay_tasks * sizeof(pkd::MergeTask));
-  p->header_bytes = p->off_split + std::max<size_t>(n_tasks, 1) * sizeof(pkd::MergeTask);
-  p->off_part_md = end_split;
+  p->off_blocks = align256(p->off_split + lay_tasks * sizeof(pkd::MergeTask));
+  p->off_counters = align256(p->off_blocks + lay_tasks * sizeof(pkd::MergeTask));
+  const size_t end_counters =
+      align256(p->off_counters + lay_tasks * size_t(a->num_kv_heads) * sizeof(int32_t));
+  p->header_bytes = p->off_counters + std::max<size_t>(n_blocks, 1) *
+                                          size_t(a->num_kv_heads) * sizeof(int32_t);
+  p->off_part_md = end_counters;
   const size_t prows = lay_parts * size_t(a->num_qo_heads);
   p->off_part_o = align256(p->off_part_md + prows * 2 * sizeof(float));
   const size_t ws = align256(p->off_part_o + prows * size_t(a->head_dim) * sizeof(float));
@@ -365,10 +394,14 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     // The kernel reads only the tokens some row of the block sees.
     const int64_t seen = std::max<int64_t>(
         0, std::min<int64_t>(w.kv_len, int64_t(w.visible) + w.q_len - 1));
-    di[i] = {w.page_begin, int32_t(seen), w.partial_slot, w.q_row, w.q_len, w.visible, {0, 0}};
+    const int32_t blk = w.partial_slot >= 0 ? block_of_row.at(w.q_row) : -1;
+    di[i] = {w.page_begin, int32_t(seen), w.partial_slot, w.q_row, w.q_len, w.visible, blk, 0};
   }
   if (n_tasks)
     std::memcpy(p->header.data() + p->off_split, tasks.data(), n_tasks * sizeof(pkd::MergeTask));
+  if (n_blocks)
+    std::memcpy(p->header.data() + p->off_blocks, blocks.data(),
+                n_blocks * sizeof(pkd::MergeTask));
 
   pkd_plan_info& inf = p->info;
   inf.batch = a->batch;
@@ -386,6 +419,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   inf.max_qo_len = max_q;
   inf.num_merge_tasks = int32_t(n_tasks);
   inf.units_per_item = pin.units_per_item;
+  inf.merge_folded = p->fuse_ok && n_split > 0 ? 1 : 0;
   *out = p;
   return ok();
 }
@@ -508,13 +542,22 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
   L.num_split = p->launch_tasks;
   L.counts = p->fixed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+  L.block_merges = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_blocks);
+  L.counters = reinterpret_cast<int32_t*>(ws + p->off_counters);
+  // A whole run of an exact plan whose split requests have at most
+  // kFuseChunks chunks folds the merge into the decode kernel (one launch
+  // instead of two: what matters when the batch is small). Longer folds run
+  // faster in the separate merge kernel, which spreads them over many more
+  // workgroups; fixed-capacity plans keep both launches so that one captured
+  // graph fits every plan; the stages alone always keep them apart.
+  L.fuse_merge = stages == PKD_STAGE_ALL && p->fuse_ok ? 1 : 0;
   hipStream_t s = static_cast<hipStream_t>(r->stream);
   hipError_t e;
   if (stages & PKD_STAGE_DECODE) {
     e = pkd::launch_decode(L, s);
     if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
-  if (stages & PKD_STAGE_MERGE) {
+  if ((stages & PKD_STAGE_MERGE) && !L.fuse_merge) {
     e = pkd::launch_merge(L, s);
     if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
   }

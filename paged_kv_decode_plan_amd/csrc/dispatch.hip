@@ -72,6 +72,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.lse = L.lse;
   a.items = L.items;
   a.counts = L.counts;
+  a.block_merges = L.block_merges;
+  a.counters = L.counters;
+  a.fuse_merge = L.fuse_merge;
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.num_items = L.num_items;

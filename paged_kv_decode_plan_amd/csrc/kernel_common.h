@@ -30,6 +30,9 @@ struct KernelArgs {
   float* lse;
   const DeviceItem* items;
   const int32_t* counts;  // nullptr, or {work items, merge tasks} of the uploaded plan
+  const MergeTask* block_merges;  // fused merge records (fuse_merge only)
+  int32_t* counters;              // fused merge arrival counters, [record][KV head]
+  int fuse_merge;
   float* part_o;
   float* part_md;
   int num_items;
@@ -78,6 +81,80 @@ __device__ inline uint16_t float_to_bf16_rne(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
   u += 0x7fffu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
+}
+
+// The merge of a split request, folded into the decode kernel: every
+// workgroup of a chunk publishes its partial states (release fence), then
+// counts itself in with one atomic add on the (request, query block, KV head)
+// counter; the one that completes the count is the last, and after an acquire
+// fence it folds the chunks' partial states of its rows with the
+// online-softmax rule (chunks in order, so the result does not depend on
+// which workgroup finishes last), writes the output rows and LSE, and resets
+// the counter for the next run. Called by every thread of the workgroup.
+template <int D>
+__device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, int kvh,
+                                     int nthreads) {
+  __shared__ int s_last;
+  const MergeTask mt = a.block_merges[it.block_merge];
+  int32_t* counter = a.counters + int64_t(it.block_merge) * a.num_kv_heads + kvh;
+  __threadfence();  // this workgroup's partial states before its arrival
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1) == mt.count - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();  // every other chunk's partial states after the count
+  const int gmask = (1 << a.group_log2) - 1;
+  const int rows = it.q_len << a.group_log2;
+  constexpr int kQuads = D / 4;
+  constexpr int kU = 8;  // chunks whose loads are in flight together
+  const float2* md = reinterpret_cast<const float2*>(a.part_md);
+  const float4* po = reinterpret_cast<const float4*>(a.part_o);
+  for (int idx = threadIdx.x; idx < rows * kQuads; idx += nthreads) {
+    const int h = idx / kQuads;
+    const int qd = idx % kQuads;
+    const int i = h >> a.group_log2;
+    const int hq = (kvh << a.group_log2) + (h & gmask);
+    float M = -INFINITY, Dn = 0.f;
+    float4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < mt.count; c0 += kU) {
+      float2 st[kU];
+      float4 ov[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int c = min(c0 + u, mt.count - 1);  // a clamped repeat is skipped below
+        const int64_t prow =
+            (int64_t(mt.first) + int64_t(c) * mt.stride + i) * a.num_qo_heads + hq;
+        st[u] = md[prow];
+        ov[u] = po[prow * kQuads + qd];
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        if (c0 + u < mt.count) {
+          const float m_new = fmaxf(M, st[u].x);
+          const float sa = M == -INFINITY ? 0.f : exp2f(M - m_new);
+          const float sb = st[u].x == -INFINITY ? 0.f : exp2f(st[u].x - m_new);
+          Dn = Dn * sa + st[u].y * sb;
+          O.x = O.x * sa + ov[u].x * sb;
+          O.y = O.y * sa + ov[u].y * sb;
+          O.z = O.z * sa + ov[u].z * sb;
+          O.w = O.w * sa + ov[u].w * sb;
+          M = m_new;
+        }
+      }
+    }
+    const int64_t row = int64_t(mt.out_row + i) * a.num_qo_heads + hq;
+    const float inv = 1.0f / Dn;
+    if (a.out_bf16) {
+      reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] =
+          uint2{uint32_t(float_to_bf16_rne(O.x * inv)) | (uint32_t(float_to_bf16_rne(O.y * inv)) << 16),
+                uint32_t(float_to_bf16_rne(O.z * inv)) | (uint32_t(float_to_bf16_rne(O.w * inv)) << 16)};
+    } else {
+      reinterpret_cast<float4*>(a.out)[row * kQuads + qd] =
+          float4{O.x * inv, O.y * inv, O.z * inv, O.w * inv};
+    }
+    if (a.lse && qd == 0) a.lse[row] = (M + log2f(Dn)) * kLn2;
+  }
+  if (threadIdx.x == 0) *counter = 0;
 }
 
 // Shared-memory image of the wavefronts' states for the final merge.
@@ -132,6 +209,7 @@ __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelA
       }
     }
   }
+  if (it.partial_slot >= 0 && a.fuse_merge) merge_if_last<D>(a, it, kvh, blockDim.x);
 }
 
 // Kernel selection (each translation unit provides its family). `rows` is the

@@ -23,7 +23,8 @@ struct DeviceItem {
   int32_t q_row;
   int32_t q_len;
   int32_t visible;
-  int32_t pad[2];
+  int32_t block_merge;  // split item: its (request, query block)'s merge record; else -1
+  int32_t pad;
 };
 
 // Device-side record of one merge (16 bytes): output row out_row folds the
@@ -68,6 +69,12 @@ struct DecodeLaunch {
   // by the kernels (num_items / num_split are then the capacities). nullptr:
   // the launch is sized exactly.
   const int32_t* counts = nullptr;
+  // Merge folded into the decode kernel: one record per (split request, query
+  // block) (out_row = its first q row, count = chunks, stride = q_r) and one
+  // arrival counter per (record, KV head), zero between runs.
+  int fuse_merge = 0;
+  const MergeTask* block_merges = nullptr;
+  int32_t* counters = nullptr;
 };
 
 // `rows` is group x (query tokens per work item); rows > group (several new

@@ -260,3 +260,55 @@ def test_full_size_workload_sampled_rows(name):
     del dc
     torch.cuda.empty_cache()
     assert lv.shape == (w.batch, w.num_qo_heads)
+
+
+# ------------------------------------------------------------------ merge paths
+
+def _merge_case(lens, seed, kv="bf16"):
+    w = custom_workload(len(lens), 16, 4, 128, 16, kv, "bf16", lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 4)
+    return w, host_case(w, seed, poison=True)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_folded_merge_matches_oracle_and_resets(kv):
+    """Short splits (at most four chunks per request): run() folds the merge
+    into the decode kernel; the result matches the oracle and repeating the
+    run (arrival counters back at zero) gives the same bits."""
+    import paged_kv_decode_plan_amd as pk
+    from gpu_helpers import workspace
+    w, case = _merge_case([300, 64, 900, 17], 31, kv)
+    ref_out, ref_lse = oracle_for(case)
+    dc = to_device(case)
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+    wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], 16, 4, 128, 16,
+            q_data_type=torch.bfloat16, kv_data_type="e4m3" if kv == "e4m3" else torch.bfloat16,
+            out_data_type=torch.float32, sm_scale=w.scale(), slots=32, balance=1,
+            min_chunk_pages=16)
+    info = wr.plan_info
+    assert info["num_split_requests"] > 0 and info["merge_folded"] == 1
+    outs = []
+    for _ in range(3):
+        out, lse = wr.run(dc["q"], dc["kv"], return_lse=True, k_scale=dc["k_scale"],
+                          v_scale=dc["v_scale"])
+        torch.cuda.synchronize()
+        compare(out, lse, ref_out, ref_lse, kv)
+        outs.append((out.clone(), lse.clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    # the stages kept apart (decode writes partial states, the merge kernel folds)
+    o2, l2 = torch.empty_like(outs[0][0]), torch.empty_like(outs[0][1])
+    for st in (pk._lib.STAGE_DECODE, pk._lib.STAGE_MERGE):
+        wr.run(dc["q"], dc["kv"], out=o2, lse=l2, k_scale=dc["k_scale"], v_scale=dc["v_scale"],
+               stages=st)
+    torch.cuda.synchronize()
+    compare(o2, l2, ref_out, ref_lse, kv)
+    wr.close()
+
+
+def test_long_splits_use_the_merge_kernel():
+    w, case = _merge_case([3000, 64, 2000], 32)
+    ref_out, ref_lse = oracle_for(case)
+    out, lse, info = run_hip(to_device(case), slots=256, balance=1, min_chunk_pages=1)
+    assert info["num_split_requests"] > 0 and info["merge_folded"] == 0
+    compare(out, lse, ref_out, ref_lse, "bf16")

@@ -130,30 +130,38 @@ def test_default_balance_and_min_chunk():
     assert info["min_chunk_pages"] == 4
 
 
+def _layout_bytes(items, tasks, parts_rows, hkv, d=128):
+    """[counts 256 | items 32 B | merge tasks 16 B | fused-merge records 16 B |
+    counters 4 B per KV head | partial (m, d) 8 B | partial o 4*D B], each
+    region 256-byte aligned."""
+    a = lambda x: (x + 255) // 256 * 256
+    end = a(256 + items * 32)
+    end = a(end + tasks * 16)
+    end = a(end + tasks * 16)
+    end = a(end + tasks * hkv * 4)
+    end = a(end + parts_rows * 8)
+    return a(end + parts_rows * d * 4)
+
+
 def test_workspace_size_formula():
     info, items, merge, split = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64,
                                                   balance=1, min_chunk_pages=1)
     assert info["num_split_requests"] == 2 and info["num_partials"] > 0
-    parts = info["num_partials"] * 32
-    a = lambda x: (x + 255) // 256 * 256
     assert info["num_merge_tasks"] == info["num_split_requests"]
-    header = a(a(256 + info["num_items"] * 32) + max(info["num_merge_tasks"], 1) * 16)
-    assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+    assert info["workspace_bytes"] == _layout_bytes(info["num_items"], info["num_merge_tasks"],
+                                                    info["num_partials"] * 32, 8)
     # several new tokens: one merge task and one partial row per token of a split request
     info, items, merge, split = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64,
                                                   balance=1, min_chunk_pages=1,
                                                   qo_indptr=[0, 3, 5])
     assert info["num_merge_tasks"] == 5 and info["queries_per_item"] == 4
-    parts = info["num_partials"] * 32
-    header = a(a(256 + info["num_items"] * 32) + info["num_merge_tasks"] * 16)
-    assert info["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+    assert info["workspace_bytes"] == _layout_bytes(info["num_items"], info["num_merge_tasks"],
+                                                    info["num_partials"] * 32, 8)
     # fixed capacity: the layout follows the capacities, not the plan
     cap = dict(items=100, merge_tasks=40, partials=300, qo_len=4)
     info2, *_ = pk.plan_partition([0, 5, 9], [16, 7], 32, 8, 128, 16, slots=64, balance=1,
                                   min_chunk_pages=1, qo_indptr=[0, 3, 5], capacity=cap)
-    parts = 300 * 32
-    header = a(a(256 + 100 * 32) + 40 * 16)
-    assert info2["workspace_bytes"] == a(a(header + parts * 8) + parts * 128 * 4)
+    assert info2["workspace_bytes"] == _layout_bytes(100, 40, 300 * 32, 8)
 
 
 def test_capacity_limits_are_enforced():
