@@ -541,6 +541,7 @@ def main(argv=None) -> int:
                        "fixed-capacity plan" if args.fixed_capacity else "exact plan"),
         },
         "us_per_step": round(mean_step * 1e3, 2),
+        "us_per_step_median": round(statistics.median(step_ms) * 1e3, 2),
         "us_per_step_p10_p90": [round(q[0] * 1e3, 2), round(q[-1] * 1e3, 2)],
         "pct_of_peak_hbm": round(100.0 * gbs / PEAK_HBM_GBS, 2),
         "kv_bytes_per_step": nbytes,
