@@ -46,7 +46,7 @@ def kv_bytes(w, table, logical: bool = False) -> int:
     once, plus for e4m3 the fp32 K and V scale of every (page, KV head). With a
     shared prefix (cascade) each group's prefix counts once, unless `logical`
     (every request's full context, as plain decode would read it)."""
-    elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    elem = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}[w.kv_dtype]
     tokens = int(table["kv_lens"].sum())
     if w.shared_prefix is not None and not logical:
         groups, prefix = w.shared_prefix
@@ -223,7 +223,7 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
     kept = []
     kept_bytes = 0
     kept_kv = 0
-    elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    elem = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}[w.kv_dtype]
     t_total = 0.0
     idx = dcase["indices"]
     with threadpool_limits(limits=1):

@@ -50,6 +50,7 @@ extern "C" {
 #define PKD_DTYPE_F32 0   /* IEEE binary32 */
 #define PKD_DTYPE_BF16 1  /* bfloat16 */
 #define PKD_DTYPE_E4M3 2  /* OCP FP8 E4M3FN byte, with fp32 per-(page, KV head) scales */
+#define PKD_DTYPE_F16 3   /* IEEE binary16 */
 
 /* Columns of one work item as returned by pkd_plan_get_worklist:
  * request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible
@@ -72,9 +73,11 @@ typedef struct pkd_plan pkd_plan;
  *  head_dim         64 or 128; query heads per KV head 1, 2, 4 or 8, and also
  *                   16 for bf16 queries with bf16 or e4m3 KV at head_dim 128
  *  page_size        tokens per page, a power of two in [1, 1024]
- *  q_dtype          PKD_DTYPE_F32 or PKD_DTYPE_BF16
- *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_E4M3
- *  out_dtype        PKD_DTYPE_F32 or PKD_DTYPE_BF16 (bf16 rounds to nearest even)
+ *  q_dtype          PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16
+ *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16, PKD_DTYPE_E4M3 or PKD_DTYPE_F16;
+ *                   fp16 KV takes fp16 q (and fp16 q fp16 KV) at head_dim 128
+ *  out_dtype        PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16 (16-bit
+ *                   outputs round to nearest even)
  *  sm_scale         logit scale; 0 selects 1/sqrt(head_dim)
  *  slots            workgroups the device keeps resident at once; 0 queries
  *                   the device (compute units x resident workgroups per CU
@@ -292,8 +295,8 @@ void pkd_plan_destroy(pkd_plan* plan);
  *
  *  rows, num_heads, head_dim   shape [rows, num_heads, head_dim] of v_a, v_b
  *                              and v_out; head_dim a multiple of 4
- *  in_dtype                    PKD_DTYPE_F32 or PKD_DTYPE_BF16 (v_a, v_b)
- *  out_dtype                   PKD_DTYPE_F32 or PKD_DTYPE_BF16 (v_out)
+ *  in_dtype                    PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16 (v_a, v_b)
+ *  out_dtype                   PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16 (v_out)
  *  v_a, s_a, v_b, s_b          two normalised attention results over disjoint
  *                              token sets: output rows and their natural-log
  *                              log-sum-exp, float [rows, num_heads];
@@ -303,7 +306,7 @@ void pkd_plan_destroy(pkd_plan* plan);
  *                              may alias s_a or s_b
  *  stream                      hipStream_t
  *
- * Pointers to f32 rows must be 16-byte aligned, to bf16 rows 8-byte aligned. */
+ * Pointers to f32 rows must be 16-byte aligned, to 16-bit rows 8-byte aligned. */
 typedef struct {
   int64_t rows;
   int32_t num_heads;

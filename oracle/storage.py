@@ -3,6 +3,7 @@
 Every stored format here is a subset of float64, so widening is exact:
 
 * ``"f32"``  — IEEE binary32 -> binary64.
+* ``"f16"``  — IEEE binary16 -> binary64.
 * ``"bf16"`` — the 16 stored bits are the top half of a binary32 pattern:
   ``uint16 -> uint32 << 16 -> float32 -> float64``.
 * ``"e4m3"`` — the OCP E4M3FN table of ``oracle.e4m3``, then multiplied by the
@@ -26,6 +27,8 @@ def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     """Stored values (no scale) -> float64."""
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
     if dtype == "bf16":
         bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)

@@ -21,6 +21,7 @@ PKD_ERR_HIP = -5
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
 DTYPE_E4M3 = 2
+DTYPE_F16 = 3
 ITEM_COLS = 8  # request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible
 STAGE_DECODE = 1
 STAGE_MERGE = 2

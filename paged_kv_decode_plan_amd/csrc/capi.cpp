@@ -42,7 +42,21 @@ int ok() { return PKD_OK; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-int elem_bytes(int dtype) { return dtype == PKD_DTYPE_F32 ? 4 : dtype == PKD_DTYPE_BF16 ? 2 : 1; }
+int elem_bytes(int dtype) {
+  return dtype == PKD_DTYPE_F32 ? 4 : (dtype == PKD_DTYPE_BF16 || dtype == PKD_DTYPE_F16) ? 2 : 1;
+}
+
+// Query / output element format as the kernels see it.
+int kind_of(int dtype) {
+  return dtype == PKD_DTYPE_BF16 ? pkd::kQBF16 : dtype == PKD_DTYPE_F16 ? pkd::kQF16 : pkd::kQF32;
+}
+
+// KV element format as the kernels see it (row-wise e4m3 scales are a form
+// of their own).
+int kv_form(int dtype, int per_token) {
+  if (per_token) return pkd::kE4M3T;
+  return dtype == PKD_DTYPE_F16 ? pkd::kF16 : dtype;
+}
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
@@ -129,13 +143,13 @@ int32_t default_wgs_cap(bool mfma, bool one_token) { return mfma && one_token ? 
 int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
                  int32_t group, int32_t rows, int32_t page_size, int32_t wgs_cap,
                  int32_t* wgs_per_cu, int32_t* num_cus) {
-  const int q_bf16 = q_dtype == PKD_DTYPE_BF16;
-  if (!pkd::decode_supported(kv_dtype, head_dim, group, rows, q_bf16, page_size))
+  const int q_kind = kind_of(q_dtype);
+  if (!pkd::decode_supported(kv_dtype, head_dim, group, rows, q_kind, page_size))
     return fail(PKD_ERR_UNSUPPORTED,
                 "no kernel for kv_dtype=%d head_dim=%d group=%d rows=%d q_dtype=%d", kv_dtype,
                 head_dim, group, rows, q_dtype);
   const auto key = std::make_tuple(int(device), int(kv_dtype), int(head_dim), int(group),
-                                   int(rows), q_bf16, page_size >= 16 ? 16 : 1, int(wgs_cap));
+                                   int(rows), q_kind, page_size >= 16 ? 16 : 1, int(wgs_cap));
   {
     std::lock_guard<std::mutex> lk(g_slots_mu);
     auto it = g_slots.find(key);
@@ -153,7 +167,7 @@ int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head
   int cus = 0, wgs = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e == hipSuccess)
-    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_bf16, page_size, wgs_cap,
+    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_kind, page_size, wgs_cap,
                               &wgs);
   if (prev != device) hipSetDevice(prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
@@ -196,9 +210,10 @@ int pkd_version(void) { return 200; }
 int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
                      int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus) {
   if (!wgs_per_cu || !num_cus) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
-  const bool mfma = pkd::decode_uses_mfma(kv_dtype, head_dim, group, group,
-                                          q_dtype == PKD_DTYPE_BF16, page_size);
-  return device_slots(device, q_dtype, kv_dtype, head_dim, group, group, page_size,
+  const int form = kv_form(kv_dtype, 0);
+  const bool mfma = pkd::decode_uses_mfma(form, head_dim, group, group, kind_of(q_dtype),
+                                          page_size);
+  return device_slots(device, q_dtype, form, head_dim, group, group, page_size,
                       default_wgs_cap(mfma, true), wgs_per_cu, num_cus);
 }
 
@@ -213,24 +228,27 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                 "num_qo_heads (%d) must be a positive multiple of num_kv_heads (%d)",
                 a->num_qo_heads, a->num_kv_heads);
   const int group = a->num_qo_heads / a->num_kv_heads;
-  if (a->q_dtype != PKD_DTYPE_F32 && a->q_dtype != PKD_DTYPE_BF16)
+  auto is_float = [](int d) {
+    return d == PKD_DTYPE_F32 || d == PKD_DTYPE_BF16 || d == PKD_DTYPE_F16;
+  };
+  if (!is_float(a->q_dtype))
     return fail(PKD_ERR_UNSUPPORTED, "q_dtype %d not supported", a->q_dtype);
-  if (a->out_dtype != PKD_DTYPE_F32 && a->out_dtype != PKD_DTYPE_BF16)
+  if (!is_float(a->out_dtype))
     return fail(PKD_ERR_UNSUPPORTED, "out_dtype %d not supported", a->out_dtype);
-  if (a->kv_dtype != PKD_DTYPE_F32 && a->kv_dtype != PKD_DTYPE_BF16 &&
-      a->kv_dtype != PKD_DTYPE_E4M3)
+  if (!is_float(a->kv_dtype) && a->kv_dtype != PKD_DTYPE_E4M3)
     return fail(PKD_ERR_UNSUPPORTED, "kv_dtype %d not supported", a->kv_dtype);
   if (a->kv_scale_per_token != 0 && a->kv_scale_per_token != 1)
     return fail(PKD_ERR_INVALID_ARGUMENT, "kv_scale_per_token must be 0 or 1");
   if (a->kv_scale_per_token && a->kv_dtype != PKD_DTYPE_E4M3)
     return fail(PKD_ERR_INVALID_ARGUMENT, "kv_scale_per_token applies to e4m3 KV only");
   // The kernels' view of the KV format: row-wise e4m3 scales are their own form.
-  const int32_t kv_impl = a->kv_scale_per_token ? pkd::kE4M3T : a->kv_dtype;
+  const int32_t kv_impl = kv_form(a->kv_dtype, a->kv_scale_per_token);
+  const int q_kind = kind_of(a->q_dtype);
   if (!is_pow2(a->page_size) || a->page_size > 1024)
     return fail(PKD_ERR_UNSUPPORTED, "page_size %d is not a power of two in [1, 1024]",
                 a->page_size);
   if (!pkd::decode_supported(kv_impl, a->head_dim, group, group,
-                             a->q_dtype == PKD_DTYPE_BF16, a->page_size))
+                             q_kind, a->page_size))
     return fail(PKD_ERR_UNSUPPORTED,
                 "no kernel for head_dim=%d group=%d kv_dtype=%d q_dtype=%d%s", a->head_dim, group,
                 a->kv_dtype, a->q_dtype,
@@ -266,7 +284,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   const int32_t queries_per_item = qo_shape > 1 ? std::max(1, 16 / group) : 1;
   const int32_t rows = group * std::min(queries_per_item, qo_shape);
   if (max_q > 1 && !pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
-                                          a->q_dtype == PKD_DTYPE_BF16, a->page_size))
+                                          q_kind, a->page_size))
     return fail(PKD_ERR_UNSUPPORTED,
                 "several query tokens per request need bf16 q, bf16 or e4m3 KV and head_dim 128 "
                 "(group %d, head_dim %d, kv_dtype %d, q_dtype %d)",
@@ -275,7 +293,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     return fail(PKD_ERR_INVALID_ARGUMENT,
                 "slots, balance, min_chunk_pages and max_wgs_per_cu must be >= 0");
   const bool mfma = pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
-                                          a->q_dtype == PKD_DTYPE_BF16, a->page_size);
+                                          q_kind, a->page_size);
   const int32_t wgs_cap =
       a->max_wgs_per_cu ? a->max_wgs_per_cu : default_wgs_cap(mfma, rows == group);
   if (!(a->sm_scale >= 0.f) || std::isinf(a->sm_scale))
@@ -522,8 +540,8 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.num_qo_heads = a.num_qo_heads;
   L.page_size_log2 = ilog2(a.page_size);
   L.sm_scale_log2 = float(double(p->sm_scale) * 1.4426950408889634);
-  L.q_bf16 = a.q_dtype == PKD_DTYPE_BF16;
-  L.out_bf16 = a.out_dtype == PKD_DTYPE_BF16;
+  L.q_kind = kind_of(a.q_dtype);
+  L.out_kind = kind_of(a.out_dtype);
   L.q = r->q;
   L.k = r->k;
   L.v = r->v;
@@ -570,8 +588,8 @@ int pkd_merge_states(const pkd_merge_states_args* m) {
     return fail(PKD_ERR_INVALID_ARGUMENT,
                 "rows must be >= 0, num_heads >= 1 and head_dim a positive multiple of 4");
   for (int dt : {m->in_dtype, m->out_dtype})
-    if (dt != PKD_DTYPE_F32 && dt != PKD_DTYPE_BF16)
-      return fail(PKD_ERR_UNSUPPORTED, "merge_states takes f32 or bf16 rows (dtype %d)", dt);
+    if (dt != PKD_DTYPE_F32 && dt != PKD_DTYPE_BF16 && dt != PKD_DTYPE_F16)
+      return fail(PKD_ERR_UNSUPPORTED, "merge_states takes f32, bf16 or f16 rows (dtype %d)", dt);
   if (m->rows == 0) return ok();
   if (!m->v_a || !m->s_a || !m->v_b || !m->s_b || !m->v_out)
     return fail(PKD_ERR_INVALID_ARGUMENT, "v_a, s_a, v_b, s_b and v_out must not be NULL");
@@ -586,8 +604,8 @@ int pkd_merge_states(const pkd_merge_states_args* m) {
   L.rows = m->rows;
   L.num_heads = m->num_heads;
   L.head_dim = m->head_dim;
-  L.in_bf16 = m->in_dtype == PKD_DTYPE_BF16;
-  L.out_bf16 = m->out_dtype == PKD_DTYPE_BF16;
+  L.in_kind = kind_of(m->in_dtype);
+  L.out_kind = kind_of(m->out_dtype);
   L.v_a = m->v_a;
   L.s_a = m->s_a;
   L.v_b = m->v_b;

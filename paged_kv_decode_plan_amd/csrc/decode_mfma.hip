@@ -55,6 +55,9 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
@@ -74,19 +77,53 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 #endif
 template <int KV>
 constexpr bool fp8() { return KV == kE4M3 || KV == kE4M3T; }
+// 16-bit KV rows (bf16 or fp16): 256 bytes per row at head_dim 128.
+template <int KV>
+constexpr bool wide16() { return KV == kBF16 || KV == kF16; }
 template <int KV>
 constexpr int nsub() { return fp8<KV>() ? PKD_E4M3_NSUB : PKD_BF16_NSUB; }
 template <int KV>
 constexpr int tile_tokens() { return kSub * nsub<KV>(); }
 
-__device__ inline f32x4_t mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+// k = 32 step of S = K.q^T on eight 16-bit values per lane: fp16 for fp16 KV
+// (with fp16 q), bf16 for every other form (bf16 q).
+template <int KV>
+__device__ inline f32x4_t mfma(const u32x4_t& a, const u32x4_t& b, const f32x4_t& c) {
+  if constexpr (KV == kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// k = 16 variant; operands are four bf16 bit patterns.
+// k = 16 step of O = P.V; operands are four 16-bit bit patterns.
+template <int KV>
 __device__ inline f32x4_t mfma16(uint2 a, uint2 b, const f32x4_t& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+  if constexpr (KV == kF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+
+// p (fp32) as a hi + lo pair of the MFMA's 16-bit type: hi = round(p),
+// lo = round(p - hi); together they carry 16 (bf16) or 22 (fp16) bits.
+template <int KV>
+__device__ inline void split16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  const f32x2_t pp = {p0, p1};
+  if constexpr (KV == kF16) {
+    const f16x2_t h = __builtin_convertvector(pp, f16x2_t);
+    const f16x2_t l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2_t), f16x2_t);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+  } else {
+    const bf16x2_t h = __builtin_convertvector(pp, bf16x2_t);
+    const bf16x2_t l = __builtin_convertvector(pp - __builtin_convertvector(h, f32x2_t), bf16x2_t);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
+  }
 }
 
 // Pack the low (sel_hi = false) or high 16-bit halves of two words: lo of the
@@ -95,7 +132,6 @@ __device__ inline uint32_t pack_halves(uint32_t a, uint32_t b, bool sel_hi) {
   return __builtin_amdgcn_perm(b, a, sel_hi ? 0x07060302u : 0x05040100u);
 }
 
-__device__ inline bf16x8_t as_bf16x8(const u32x4_t& v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // Raw buffer loads: a wavefront-uniform descriptor (the tile's first row) plus
 // a 32-bit lane offset and a wavefront-uniform offset, so a tile's loads need
@@ -140,6 +176,9 @@ struct Loads<kBF16> {
 };
 
 template <>
+struct Loads<kF16> : Loads<kBF16> {};
+
+template <>
 struct Loads<kE4M3> {
   u32x4_t k[2];  // [h]: 16 dims of token l%16, 64 contiguous bytes per token and instruction
   uint2 v[4];    // [e]: dims 8*(l%16)..+8 of token 4*(l/16) + e
@@ -162,7 +201,7 @@ struct Loads<kE4M3T> {
 // into dc = 2h (first 8) and dc = 2h + 1 (last 8).
 template <int KV>
 __device__ inline int qk_dim(int dc, int q, int e) {
-  if constexpr (KV == kBF16)
+  if constexpr (wide16<KV>())
     return 8 * (4 * dc + q) + e;
   else
     return 16 * (4 * (dc >> 1) + q) + 8 * (dc & 1) + e;
@@ -208,7 +247,7 @@ template <int KV, bool PAGE16, bool FULL>
 __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
   constexpr int kElem = Loads<KV>::kElem;
   const int last = c.kv_len - 1;
-  constexpr int NK = KV == kBF16 ? 4 : 2;
+  constexpr int NK = wide16<KV>() ? 4 : 2;
   if constexpr (PAGE16) {
     // One page per sub-tile: a wavefront-uniform base plus lane offsets. A
     // sub-tile past the end loads from the last sub-tile's rows (tp.page is
@@ -236,7 +275,7 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
         voff = (uint32_t(tv) * uint32_t(c.token_stride) + uint32_t(8 * c.j)) * kElem;
         soff = 0;
       }
-      if constexpr (KV == kBF16)
+      if constexpr (wide16<KV>())
         ld.v[e] = bload16<PKD_V_CPOL>(vr, voff, soff);
       else
         ld.v[e] = bload8<PKD_V_CPOL>(vr, voff, soff);
@@ -248,7 +287,7 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
       const int64_t row = page * c.page_stride + int64_t(t & c.pmask) * c.token_stride + c.head_off;
 #pragma unroll
       for (int x = 0; x < NK; ++x) {
-        const int dim = KV == kBF16 ? qk_dim<KV>(x, c.q4, 0) : qk_dim<KV>(2 * x, c.q4, 0);
+        const int dim = wide16<KV>() ? qk_dim<KV>(x, c.q4, 0) : qk_dim<KV>(2 * x, c.q4, 0);
         ld.k[x] = *reinterpret_cast<const u32x4_t*>(c.kbase + (row + dim) * kElem);
       }
     }
@@ -259,7 +298,7 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
       const int64_t off =
           (page * c.page_stride + int64_t(t & c.pmask) * c.token_stride + c.head_off + 8 * c.j) *
           kElem;
-      if constexpr (KV == kBF16)
+      if constexpr (wide16<KV>())
         ld.v[e] = *reinterpret_cast<const u32x4_t*>(c.vbase + off);
       else
         ld.v[e] = *reinterpret_cast<const uint2*>(c.vbase + off);
@@ -321,13 +360,13 @@ __device__ inline float token_scale(const float* sc, const Ctx& c, const KernelA
 // QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens valid).
 template <int KV, bool PAGE16, bool FULL>
 __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TilePages& tp, const bf16x8_t (&qb)[4],
+                                    int t0, const TilePages& tp, const u32x4_t (&qb)[4],
                                     f32x4_t (&acc)[8], float& m_run, float& d_run) {
   // ---- S = K . q^T: lane l gets tokens 4*q4 + r of head j
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (KV == kBF16) {
+  if constexpr (wide16<KV>()) {
 #pragma unroll
-    for (int dc = 0; dc < 4; ++dc) s = mfma(as_bf16x8(ld.k[dc]), qb[dc], s);
+    for (int dc = 0; dc < 4; ++dc) s = mfma<KV>(ld.k[dc], qb[dc], s);
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -341,8 +380,8 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
       hi[1] = e4m3x2_to_bf16x2(w[2], true);
       hi[2] = e4m3x2_to_bf16x2(w[3], false);
       hi[3] = e4m3x2_to_bf16x2(w[3], true);
-      s = mfma(as_bf16x8(lo), qb[2 * h], s);
-      s = mfma(as_bf16x8(hi), qb[2 * h + 1], s);
+      s = mfma<KV>(lo, qb[2 * h], s);
+      s = mfma<KV>(hi, qb[2 * h + 1], s);
     }
   }
 
@@ -409,26 +448,14 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     for (int e = 0; e < 4; ++e) p[e] *= ld.vs[e];
   }
   uint2 p_hi, p_lo;
-  {
-    uint32_t hw[2], lw[2];
-#pragma unroll
-    for (int e = 0; e < 4; e += 2) {
-      const f32x2_t pp = {p[e], p[e + 1]};
-      const bf16x2_t h = __builtin_convertvector(pp, bf16x2_t);
-      const f32x2_t rest = pp - __builtin_convertvector(h, f32x2_t);
-      const bf16x2_t l = __builtin_convertvector(rest, bf16x2_t);
-      hw[e >> 1] = __builtin_bit_cast(uint32_t, h);
-      lw[e >> 1] = __builtin_bit_cast(uint32_t, l);
-    }
-    p_hi = uint2{hw[0], hw[1]};
-    p_lo = uint2{lw[0], lw[1]};
-  }
+  split16<KV>(p[0], p[1], p_hi.x, p_lo.x);
+  split16<KV>(p[2], p[3], p_hi.y, p_lo.y);
 
   // ---- O += P . V, column j of MFMA nc is dim 8*j + nc
 #pragma unroll
   for (int nc = 0; nc < 8; ++nc) {
     uint2 vb;
-    if constexpr (KV == kBF16) {
+    if constexpr (wide16<KV>()) {
       const int w = nc >> 1;
       const bool hi = nc & 1;
       vb.x = pack_halves(ld.v[0][w], ld.v[1][w], hi);
@@ -443,14 +470,14 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
       vb.x = pack_halves(x[0], x[1], hib);
       vb.y = pack_halves(x[2], x[3], hib);
     }
-    acc[nc] = mfma16(p_hi, vb, acc[nc]);
-    acc[nc] = mfma16(p_lo, vb, acc[nc]);
+    acc[nc] = mfma16<KV>(p_hi, vb, acc[nc]);
+    acc[nc] = mfma16<KV>(p_lo, vb, acc[nc]);
   }
 }
 
 template <int KV, bool PAGE16, bool FULL>
 __device__ inline void process_tile(const Tile<KV>& T, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TileP<KV>& tp, const bf16x8_t (&qb)[4],
+                                    int t0, const TileP<KV>& tp, const u32x4_t (&qb)[4],
                                     f32x4_t (&acc)[8], float& m_run, float& d_run) {
 #pragma unroll
   for (int s = 0; s < nsub<KV>(); ++s)
@@ -530,7 +557,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   }
 
   // q^T as the B operand of S = K.q^T: column j = row j (zero beyond the block).
-  bf16x8_t qb[4];
+  u32x4_t qb[4];  // eight 16-bit q values (bf16, or fp16 for fp16 KV)
   {
     const uint16_t* qp =
         static_cast<const uint16_t*>(a.q) +
@@ -539,7 +566,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     for (int dc = 0; dc < 4; ++dc) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (row_ok) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
-      qb[dc] = as_bf16x8(w);
+      qb[dc] = w;
     }
   }
 
@@ -662,6 +689,7 @@ DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size)
     case kBF16: return p16 ? pick_group<kBF16, true>(rows) : pick_group<kBF16, false>(rows);
     case kE4M3: return p16 ? pick_group<kE4M3, true>(rows) : pick_group<kE4M3, false>(rows);
     case kE4M3T: return p16 ? pick_group<kE4M3T, true>(rows) : pick_group<kE4M3T, false>(rows);
+    case kF16: return p16 ? pick_group<kF16, true>(rows) : pick_group<kF16, false>(rows);
     default: return nullptr;
   }
 }

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(KernelArgs a) {
     for (int p = 0; p < G; ++p) {
       const int h = p ^ own;
       const int64_t off = qbase + int64_t(h) * D;
-      if (a.q_bf16) {
+      if (a.q_kind == kQBF16) {
         const uint16_t* qp = static_cast<const uint16_t*>(a.q) + off;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) qr[p][e] = bf16_bits_to_float(qp[e]);

@@ -19,13 +19,22 @@ static int pow2_ceil(int x) {
   return p;
 }
 
-static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
+// Forms the MFMA kernel takes: bf16 queries over bf16 or e4m3 KV (both
+// contractions on bf16 MFMA), fp16 queries over fp16 KV (fp16 MFMA).
+static bool mfma_form(int kv_dtype, int q_kind) {
+  return (q_kind == kQBF16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T)) ||
+         (q_kind == kQF16 && kv_dtype == kF16);
+}
+
+static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                        int page_size) {
   if ((group & (group - 1)) || rows < group || rows % group) return nullptr;
-  if (q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T)) {
+  if (mfma_form(kv_dtype, q_kind)) {
     if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size)) return f;
   }
-  if (rows != group || kv_dtype == kE4M3T) return nullptr;  // MFMA-only forms
+  // The vector-ALU kernel: one token per request, fp32 or bf16 q over fp32,
+  // bf16 or e4m3 KV (per-page scales).
+  if (rows != group || q_kind == kQF16 || kv_dtype == kE4M3T || kv_dtype == kF16) return nullptr;
   return valu_decode_kernel(kv_dtype, head_dim, group);
 }
 
@@ -45,18 +54,17 @@ static hipError_t cap_lds(DecodeFn fn, int cap, size_t* bytes) {
   return hipSuccess;
 }
 
-bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size) {
-  return choose(kv_dtype, head_dim, group, rows, q_bf16, page_size) != nullptr;
+bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size) {
+  return choose(kv_dtype, head_dim, group, rows, q_kind, page_size) != nullptr;
 }
 
-bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size) {
-  return q_bf16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T) &&
-         rows >= group &&
+bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size) {
+  return mfma_form(kv_dtype, q_kind) && rows >= group &&
          mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size) != nullptr;
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
-  DecodeFn fn = choose(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_bf16, 1 << L.page_size_log2);
+  DecodeFn fn = choose(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_kind, 1 << L.page_size_log2);
   if (!fn) return hipErrorInvalidValue;
   KernelArgs a;
   a.q = L.q;
@@ -84,8 +92,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.group_log2 = ilog2(L.group);
   a.page_size_log2 = L.page_size_log2;
   a.sm_scale_log2 = L.sm_scale_log2;
-  a.q_bf16 = L.q_bf16;
-  a.out_bf16 = L.out_bf16;
+  a.q_kind = L.q_kind;
+  a.out_kind = L.out_kind;
   const unsigned grid = decode_grid_size(L.num_items, L.num_kv_heads, a.xcd_group);
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, L.wgs_cap, &lds); e != hipSuccess) return e;
@@ -93,9 +101,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                             int page_size, int wgs_cap, int* wgs_per_cu) {
-  DecodeFn fn = choose(kv_dtype, head_dim, group, rows, q_bf16, page_size);
+  DecodeFn fn = choose(kv_dtype, head_dim, group, rows, q_kind, page_size);
   if (!fn) return hipErrorInvalidValue;
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, wgs_cap, &lds); e != hipSuccess) return e;

@@ -42,8 +42,8 @@ struct KernelArgs {
   int group_log2;  // query heads per KV head (a power of two), as log2
   int page_size_log2;
   float sm_scale_log2;  // logit scale times log2(e): scores are kept in log2 units
-  int q_bf16;
-  int out_bf16;
+  int q_kind;    // kQF32, kQBF16 or kQF16
+  int out_kind;  // kQF32, kQBF16 or kQF16
 };
 
 using DecodeFn = void (*)(KernelArgs);
@@ -76,11 +76,24 @@ __device__ inline int launch_items(const KernelArgs& a) {
 
 __device__ inline float bf16_bits_to_float(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
 
+__device__ inline uint16_t float_to_f16_rne(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // round to nearest even
+}
+
 __device__ inline uint16_t float_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);  // quiet NaN
   u += 0x7fffu + ((u >> 16) & 1u);
   return uint16_t(u >> 16);
+}
+
+// Four values rounded to the 16-bit output format (kQBF16 or kQF16), packed.
+__device__ inline uint2 pack4_16(float x, float y, float z, float w, int kind) {
+  if (kind == kQF16)
+    return uint2{uint32_t(float_to_f16_rne(x)) | (uint32_t(float_to_f16_rne(y)) << 16),
+                 uint32_t(float_to_f16_rne(z)) | (uint32_t(float_to_f16_rne(w)) << 16)};
+  return uint2{uint32_t(float_to_bf16_rne(x)) | (uint32_t(float_to_bf16_rne(y)) << 16),
+               uint32_t(float_to_bf16_rne(z)) | (uint32_t(float_to_bf16_rne(w)) << 16)};
 }
 
 // The merge of a split request, folded into the decode kernel: every
@@ -144,10 +157,9 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
     }
     const int64_t row = int64_t(mt.out_row + i) * a.num_qo_heads + hq;
     const float inv = 1.0f / Dn;
-    if (a.out_bf16) {
+    if (a.out_kind != kQF32) {
       reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] =
-          uint2{uint32_t(float_to_bf16_rne(O.x * inv)) | (uint32_t(float_to_bf16_rne(O.y * inv)) << 16),
-                uint32_t(float_to_bf16_rne(O.z * inv)) | (uint32_t(float_to_bf16_rne(O.w * inv)) << 16)};
+          pack4_16(O.x * inv, O.y * inv, O.z * inv, O.w * inv, a.out_kind);
     } else {
       reinterpret_cast<float4*>(a.out)[row * kQuads + qd] =
           float4{O.x * inv, O.y * inv, O.z * inv, O.w * inv};
@@ -195,8 +207,10 @@ __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelA
     const int64_t row = int64_t(it.q_row + i) * a.num_qo_heads + hq;
     if (it.partial_slot < 0) {
       const float val = O / Dn;
-      if (a.out_bf16)
+      if (a.out_kind == kQBF16)
         static_cast<uint16_t*>(a.out)[row * D + d] = float_to_bf16_rne(val);
+      else if (a.out_kind == kQF16)
+        static_cast<uint16_t*>(a.out)[row * D + d] = float_to_f16_rne(val);
       else
         static_cast<float*>(a.out)[row * D + d] = val;
       if (a.lse && d == 0) a.lse[row] = (M + log2f(Dn)) * kLn2;

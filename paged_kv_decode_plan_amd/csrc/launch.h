@@ -9,7 +9,9 @@ namespace pkd {
 
 // KV element formats as the kernels see them: kE4M3T is e4m3 with one scale
 // per (token, KV head) instead of one per (page, KV head).
-enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE4M3T = 3 };
+enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE4M3T = 3, kF16 = 4 };
+// Query / output element formats.
+enum : int { kQF32 = 0, kQBF16 = 1, kQF16 = 2 };
 
 // Device-side layout of one work item (32 bytes): pages
 // [page_begin, page_begin + ceil(kv_len / page_size)) of the page table for
@@ -47,8 +49,8 @@ struct DecodeLaunch {
   int num_qo_heads = 0;
   int page_size_log2 = 0;
   float sm_scale_log2 = 0.f;  // sm_scale * log2(e)
-  int q_bf16 = 0;
-  int out_bf16 = 0;
+  int q_kind = 0;    // kQF32, kQBF16 or kQF16
+  int out_kind = 0;  // kQF32, kQBF16 or kQF16
   const void* q = nullptr;
   const void* k = nullptr;
   const void* v = nullptr;
@@ -79,19 +81,19 @@ struct DecodeLaunch {
 
 // `rows` is group x (query tokens per work item); rows > group (several new
 // tokens per request) is served by the MFMA kernel only.
-bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size);
-bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_bf16, int page_size);
+bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size);
+bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
-hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_bf16,
+hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                             int page_size, int wgs_cap, int* wgs_per_cu);
 
 struct MergeStatesLaunch {
   int64_t rows = 0;
   int num_heads = 0;
   int head_dim = 0;
-  int in_bf16 = 0;
-  int out_bf16 = 0;
+  int in_kind = 0;   // kQF32, kQBF16 or kQF16
+  int out_kind = 0;
   const void* v_a = nullptr;
   const float* s_a = nullptr;
   const void* v_b = nullptr;

@@ -35,7 +35,7 @@ struct MergeArgs {
   void* out;
   float* lse;
   int num_qo_heads;
-  int out_bf16;
+  int out_kind;  // kQF32, kQBF16 or kQF16
 };
 
 constexpr int kMergeThreads = 512;
@@ -107,11 +107,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     }
     const int64_t row = int64_t(t.out_row) * H + h;
     const float inv = 1.0f / Dt;
-    if (a.out_bf16) {
-      const uint2 packed = {
-          uint32_t(float_to_bf16_rne(A.x * inv)) | (uint32_t(float_to_bf16_rne(A.y * inv)) << 16),
-          uint32_t(float_to_bf16_rne(A.z * inv)) | (uint32_t(float_to_bf16_rne(A.w * inv)) << 16)};
-      reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] = packed;
+    if (a.out_kind != kQF32) {
+      reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] =
+          pack4_16(A.x * inv, A.y * inv, A.z * inv, A.w * inv, a.out_kind);
     } else {
       reinterpret_cast<float4*>(a.out)[row * kQuads + qd] =
           float4{A.x * inv, A.y * inv, A.z * inv, A.w * inv};
@@ -132,7 +130,7 @@ hipError_t launch_merge(const DecodeLaunch& L, hipStream_t stream) {
   a.out = L.out;
   a.lse = L.lse;
   a.num_qo_heads = L.num_qo_heads;
-  a.out_bf16 = L.out_bf16;
+  a.out_kind = L.out_kind;
   const unsigned grid = unsigned(L.num_split) * unsigned(L.num_qo_heads);
   if (L.head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kMergeThreads), 0, stream, a);

@@ -24,11 +24,16 @@ namespace {
 constexpr int kMsThreads = 256;
 constexpr float kLog2e = 1.44269504088896340736f;
 
-__device__ inline float4 load4(const void* p, int64_t i, int bf16) {
-  if (bf16) {
+__device__ inline float4 load4(const void* p, int64_t i, int kind) {
+  if (kind == kQBF16) {
     const uint2 w = reinterpret_cast<const uint2*>(p)[i];
     return float4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                   __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+  }
+  if (kind == kQF16) {
+    const uint2 w = reinterpret_cast<const uint2*>(p)[i];
+    auto h = [](uint32_t b) { return float(__builtin_bit_cast(_Float16, uint16_t(b))); };
+    return float4{h(w.x & 0xffffu), h(w.x >> 16), h(w.y & 0xffffu), h(w.y >> 16)};
   }
   return reinterpret_cast<const float4*>(p)[i];
 }
@@ -45,14 +50,12 @@ __global__ __launch_bounds__(kMsThreads) void merge_states_kernel(MergeStatesLau
     const float wb = sb == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((sb - m) * kLog2e);
     const float wsum = wa + wb;
     const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-    const float4 va = load4(a.v_a, i, a.in_bf16);
-    const float4 vb = load4(a.v_b, i, a.in_bf16);
+    const float4 va = load4(a.v_a, i, a.in_kind);
+    const float4 vb = load4(a.v_b, i, a.in_kind);
     const float4 v = {(va.x * wa + vb.x * wb) * inv, (va.y * wa + vb.y * wb) * inv,
                       (va.z * wa + vb.z * wb) * inv, (va.w * wa + vb.w * wb) * inv};
-    if (a.out_bf16) {
-      reinterpret_cast<uint2*>(a.v_out)[i] =
-          uint2{uint32_t(float_to_bf16_rne(v.x)) | (uint32_t(float_to_bf16_rne(v.y)) << 16),
-                uint32_t(float_to_bf16_rne(v.z)) | (uint32_t(float_to_bf16_rne(v.w)) << 16)};
+    if (a.out_kind != kQF32) {
+      reinterpret_cast<uint2*>(a.v_out)[i] = pack4_16(v.x, v.y, v.z, v.w, a.out_kind);
     } else {
       reinterpret_cast<float4*>(a.v_out)[i] = v;
     }

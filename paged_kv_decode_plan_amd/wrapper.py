@@ -31,6 +31,8 @@ def _dtype_code(dt) -> int:
         return _lib.DTYPE_BF16
     if dt in (torch.float8_e4m3fn, torch.uint8, "e4m3", "float8_e4m3fn"):
         return _lib.DTYPE_E4M3
+    if dt in (torch.float16, "f16", "float16"):
+        return _lib.DTYPE_F16
     raise ValueError(f"unsupported dtype {dt}")
 
 
@@ -250,7 +252,8 @@ class BatchDecodeWithPagedKVCacheWrapper:
             raise _lib.PkdError(_lib.PKD_ERR_PLAN_MISMATCH, "q/KV dtypes differ from the plan")
         if k.shape[1] != p.page_size or k.shape[2] != p.num_kv_heads or k.shape[3] != p.head_dim:
             raise ValueError("KV pool shape disagrees with the plan")
-        out_dt = torch.float32 if p.out_dtype == _lib.DTYPE_F32 else torch.bfloat16
+        out_dt = {_lib.DTYPE_F32: torch.float32, _lib.DTYPE_BF16: torch.bfloat16,
+                  _lib.DTYPE_F16: torch.float16}[p.out_dtype]
         if out is None:
             out = torch.empty(q.shape, dtype=out_dt, device=q.device)
         elif out.dtype != out_dt or out.shape != q.shape or not out.is_contiguous():

@@ -8,7 +8,7 @@ import torch
 import paged_kv_decode_plan_amd as pk
 from oracle import attention
 
-TOL = {"f32": 2e-3, "bf16": 2e-3, "e4m3": 3e-2}
+TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "e4m3": 3e-2}
 DEV = "cuda:0"
 
 
@@ -54,7 +54,7 @@ def run_hip(dcase: dict, out_dtype="f32", slots=0, balance=0, min_chunk_pages=0,
             ws_bytes=pk.DEFAULT_WORKSPACE_BYTES, kv=None, indices=None):
     w = dcase["workload"]
     wrapper = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(ws_bytes), "NHD")
-    odt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[out_dtype]
     wrapper.plan(dcase["indptr"], dcase["indices"] if indices is None else indices,
                  dcase["last_page_len"], w.num_qo_heads, w.num_kv_heads, w.head_dim,
                  w.page_size, q_data_type=dcase["q"].dtype,
@@ -84,7 +84,7 @@ def compare(out, lse, ref_out, ref_lse, kv_dtype, out_dtype="f32", rows=None):
     assert np.all(np.isfinite(o)), "non-finite output"
     tol = TOL[kv_dtype]
     err = np.abs(o - ref_out)
-    bound = tol + (np.abs(ref_out) * 2.0 ** -8 if out_dtype == "bf16" else 0.0)
+    bound = tol + (np.abs(ref_out) * {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}.get(out_dtype, 0.0))
     worst = float(err.max())
     assert np.all(err <= bound), f"max-abs error {worst:.3e} above tolerance {tol}"
     if lse is not None:
@@ -113,7 +113,7 @@ def sample_request_case(dcase: dict, r: int) -> dict:
     kv = dcase["kv"].index_select(0, pages)
     if w.kv_dtype == "bf16":
         kvh = kv.view(torch.int16).cpu().numpy().view(np.uint16)
-    elif w.kv_dtype == "f32":
+    elif w.kv_dtype in ("f32", "f16"):
         kvh = kv.cpu().numpy()
     else:
         kvh = kv.cpu().numpy().view(np.uint8)

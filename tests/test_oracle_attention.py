@@ -24,7 +24,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 def _scalar(x, dtype):
     """One stored value -> Python float, without the oracle's helpers."""
-    if dtype == "f32":
+    if dtype in ("f32", "f16"):
         return float(x)
     if dtype == "bf16":
         return struct.unpack("<f", struct.pack("<I", int(x) << 16))[0]
@@ -285,3 +285,13 @@ def test_rowwise_scales_equal_to_page_scales_give_page_results():
     out1, lse1 = attention.decode_case(tok)
     np.testing.assert_array_equal(out0, out1)
     np.testing.assert_array_equal(lse0, lse1)
+
+
+def test_f16_storage_matches_brute_force():
+    w = custom_workload(3, 8, 2, 8, 4, "f16", "f16", [13, 2, 40], pool_pages=20)
+    case = host_case(w, 21, poison=True)
+    assert case["kv"].dtype == np.float16 and case["q"].dtype == np.float16
+    out, lse = attention.decode_case(case)
+    bo, bl = brute_force(case, w.scale())
+    np.testing.assert_allclose(out, bo, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, rtol=1e-12, atol=1e-12)

@@ -13,10 +13,11 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def _both(indptr, last, P, hkv, slots, balance, cmin, hq=None, d=128, kv="bf16",
-          qo_indptr=None):
+          qo_indptr=None, qd=None):
     hq = hq or hkv
+    qd = qd or ("f16" if kv == "f16" else "bf16")
     info, items, merge, split = pk.plan_partition(indptr, last, hq, hkv, d, P, kv_dtype=kv,
-                                                  q_dtype="bf16", slots=slots, balance=balance,
+                                                  q_dtype=qd, slots=slots, balance=balance,
                                                   min_chunk_pages=cmin, qo_indptr=qo_indptr)
     ref = oplan.plan(indptr, last, P, info["units_per_item"], slots, balance, cmin, qo_indptr,
                      info["queries_per_item"])
@@ -119,7 +120,8 @@ def test_workload_tables_bit_exact(name, slots):
     t = page_table(w, seed=list(CONFIGS).index(name) + 1)
     cmin = max(1, -(-256 // w.page_size))
     out = _both(t["indptr"], t["last_page_len"], w.page_size, w.num_kv_heads, slots, 2, cmin,
-                hq=w.num_qo_heads, d=w.head_dim, kv=w.kv_dtype, qo_indptr=t["qo_indptr"])
+                hq=w.num_qo_heads, d=w.head_dim, kv=w.kv_dtype, qo_indptr=t["qo_indptr"],
+                qd=w.q_dtype)
     _assert_same(*out[:4], out[4])
 
 
@@ -212,3 +214,11 @@ def test_non_causal_tables_bit_exact(seed):
                      info["queries_per_item"], causal=False)
     _assert_same(info, items, merge, split, ref)
     assert np.array_equal(items[:, 7], items[:, 3])
+
+
+@pytest.mark.parametrize("q,kv,d", [("bf16", "f16", 128), ("f16", "bf16", 128),
+                                    ("f16", "f16", 64), ("f32", "f16", 128)])
+def test_fp16_needs_fp16_q_over_fp16_kv_at_128(q, kv, d):
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 2], [5], 8, 2, d, 16, kv_dtype=kv, q_dtype=q)
+    assert e.value.code == pk._lib.PKD_ERR_UNSUPPORTED

@@ -5,7 +5,7 @@ bytes itself):
 
 * ``kv`` is the combined NHD page pool ``[num_pages, 2, page_size,
   num_kv_heads, head_dim]``; index 0 of the second axis holds K, index 1 holds V.
-* ``"f32"`` storage is ``float32``; ``"bf16"`` storage is the raw 16-bit
+* ``"f32"`` storage is ``float32``, ``"f16"`` storage ``float16``; ``"bf16"`` storage is the raw 16-bit
   pattern as ``uint16``; ``"e4m3"`` storage is the raw OCP E4M3FN byte as
   ``uint8`` with fp32 scales ``k_scale``/``v_scale`` of shape
   ``[num_pages, num_kv_heads]`` (one per page and KV head) or, for a
@@ -36,8 +36,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-KV_DTYPES = ("f32", "bf16", "e4m3")
-Q_DTYPES = ("f32", "bf16")
+KV_DTYPES = ("f32", "bf16", "f16", "e4m3")
+Q_DTYPES = ("f32", "bf16", "f16")
 E4M3_MAX = 448.0
 BF16_NAN_BITS = 0x7FC0
 E4M3_NAN_BYTE = 0x7F
@@ -109,6 +109,9 @@ CONFIGS = {
     "fp8_rowwise_e4m3": Workload(
         "fp8_rowwise_e4m3", 128, 32, 8, 128, 16, "e4m3", "bf16", ("uniform", 1024, 32768),
         kv_scale="token"),
+    # The Llama-3-8B-shaped batch in fp16 (q, KV and output).
+    "llama3_8b_f16": Workload(
+        "llama3_8b_f16", 64, 32, 8, 128, 16, "f16", "f16", ("fixed", 2048)),
     # Cascade: 64 requests share one 8192-token prefix (a long system prompt or
     # document) and each has 512 tokens of its own.
     "cascade_prefix8k_bf16": Workload(
@@ -295,17 +298,23 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
     k_scale = v_scale = None
     if w.kv_dtype == "f32":
         kv = pool32
+    elif w.kv_dtype == "f16":
+        kv = pool32.astype(np.float16)
     elif w.kv_dtype == "bf16":
         kv = _to_bf16_bits(pool32)
     elif w.kv_dtype == "e4m3":
         kv, k_scale, v_scale = _quantize_pool_e4m3(pool32, w.kv_scale == "token")
     else:
         raise ValueError(w.kv_dtype)
-    q = q32 if w.q_dtype == "f32" else _to_bf16_bits(q32)
+    q = {"f32": q32, "f16": None, "bf16": None}[w.q_dtype]
+    if w.q_dtype == "f16":
+        q = q32.astype(np.float16)
+    elif w.q_dtype == "bf16":
+        q = _to_bf16_bits(q32)
     if poison:
         unread = ~read_mask(table, P)
-        nan = {"f32": np.float32(np.nan), "bf16": np.uint16(BF16_NAN_BITS),
-               "e4m3": np.uint8(E4M3_NAN_BYTE)}[w.kv_dtype]
+        nan = {"f32": np.float32(np.nan), "f16": np.float16(np.nan),
+               "bf16": np.uint16(BF16_NAN_BITS), "e4m3": np.uint8(E4M3_NAN_BYTE)}[w.kv_dtype]
         kv = kv.copy()
         kv[:, 0][unread] = nan
         kv[:, 1][unread] = nan
@@ -332,12 +341,12 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
     g.manual_seed(int(seed) * 7919 + 17)
     P, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
     npg = table["num_pages"]
-    qdt = torch.float32 if w.q_dtype == "f32" else torch.bfloat16
+    qdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.q_dtype]
     q = torch.randn((query_rows(table), w.num_qo_heads, D), generator=g, device=device,
                     dtype=torch.float32).to(qdt)
     k_scale = v_scale = None
-    if w.kv_dtype in ("f32", "bf16"):
-        kdt = torch.float32 if w.kv_dtype == "f32" else torch.bfloat16
+    if w.kv_dtype in ("f32", "bf16", "f16"):
+        kdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.kv_dtype]
         kv = torch.randn((npg, 2, P, Hkv, D), generator=g, device=device, dtype=kdt)
     elif w.kv_dtype == "e4m3":
         kv = torch.empty((npg, 2, P, Hkv, D), device=device, dtype=torch.uint8)
