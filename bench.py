@@ -41,18 +41,24 @@ METRIC = "KV-read HBM GB/s (% of peak) + µs per batched decode step"
 CSRC = os.path.join(ROOT, "paged_kv_decode_plan_amd", "csrc")
 
 
+ELEM_BITS = {"f32": 32, "bf16": 16, "f16": 16, "e4m3": 8, "e2m1": 4}
+
+
 def kv_bytes(w, table, logical: bool = False) -> int:
     """Algorithmic bytes the decode kernel must read: every valid K and V element
-    once, plus for e4m3 the fp32 K and V scale of every (page, KV head). With a
-    shared prefix (cascade) each group's prefix counts once, unless `logical`
-    (every request's full context, as plain decode would read it)."""
-    elem = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}[w.kv_dtype]
+    once, plus for e4m3 the fp32 K and V scale of every (page, KV head) (or
+    token and KV head) and for e2m1 the fp32 K and V scale of every (KV head,
+    channel). With a shared prefix (cascade) each group's prefix counts once,
+    unless `logical` (every request's full context, as plain decode would read
+    it)."""
     tokens = int(table["kv_lens"].sum())
     if w.shared_prefix is not None and not logical:
         groups, prefix = w.shared_prefix
         tokens = tokens - len(table["kv_lens"]) * prefix + groups * prefix
-    b = tokens * w.num_kv_heads * w.head_dim * 2 * elem
-    if w.kv_dtype == "e4m3" and w.kv_scale == "token":
+    b = tokens * w.num_kv_heads * w.head_dim * 2 * ELEM_BITS[w.kv_dtype] // 8
+    if w.kv_dtype == "e2m1":
+        b += w.num_kv_heads * w.head_dim * 2 * 4
+    elif w.kv_dtype == "e4m3" and w.kv_scale == "token":
         b += tokens * w.num_kv_heads * 2 * 4
     elif w.kv_dtype == "e4m3":
         pages = int(table["indptr"][-1])
@@ -71,7 +77,9 @@ def kernel_source_sha() -> str:
 
 
 def decode_kernel_name(w) -> str:
-    mfma = w.kv_dtype in ("bf16", "e4m3") and w.q_dtype == "bf16" and w.head_dim == 128
+    mfma = w.head_dim == 128 and (
+        (w.q_dtype == "bf16" and w.kv_dtype in ("bf16", "e4m3", "e2m1"))
+        or (w.q_dtype == "f16" and w.kv_dtype == "f16"))
     return "decode_mfma_kernel" if mfma else "decode_kernel"
 
 
@@ -223,7 +231,6 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
     kept = []
     kept_bytes = 0
     kept_kv = 0
-    elem = {"f32": 4, "bf16": 2, "f16": 2, "e4m3": 1}[w.kv_dtype]
     t_total = 0.0
     idx = dcase["indices"]
     with threadpool_limits(limits=1):
@@ -233,7 +240,7 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
             kv = dcase["kv"].index_select(0, pages)
             if w.kv_dtype == "bf16":
                 kvh = kv.view(torch.int16).cpu().numpy().view(np.uint16)
-            elif w.kv_dtype == "e4m3":
+            elif w.kv_dtype in ("e4m3", "e2m1"):
                 kvh = kv.cpu().numpy().view(np.uint8)
             else:
                 kvh = kv.cpu().numpy()
@@ -245,12 +252,15 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
             if w.kv_dtype == "e4m3":
                 ks = dcase["k_scale"].index_select(0, pages).cpu().numpy()
                 vs = dcase["v_scale"].index_select(0, pages).cpu().numpy()
+            elif w.kv_dtype == "e2m1":
+                ks = dcase["k_scale"].cpu().numpy()
+                vs = dcase["v_scale"].cpu().numpy()
             item = (qh, kvh, len(pages), int(dcase["last_page_len"][r]), ks, vs)
             t0 = time.perf_counter()
             _oracle_request(w, item)
             t_total += time.perf_counter() - t0
             done.append(r)
-            req_bytes = int(lens[r]) * w.num_kv_heads * w.head_dim * 2 * elem
+            req_bytes = int(lens[r]) * w.num_kv_heads * w.head_dim * 2 * ELEM_BITS[w.kv_dtype] // 8
             done_bytes += req_bytes
             if kept_bytes + kvh.nbytes <= keep_bytes:
                 kept.append(item)
@@ -358,7 +368,7 @@ def main(argv=None) -> int:
 
     ws = torch.empty(pk.DEFAULT_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     q_dt = dcase["q"].dtype
-    kv_dt = "e4m3" if w.kv_dtype == "e4m3" else dcase["kv"].dtype
+    kv_dt = w.kv_dtype if w.kv_dtype in ("e4m3", "e2m1") else dcase["kv"].dtype
     cascade = w.shared_prefix is not None
     if cascade:
         # Two levels (shared prefixes once for all their requests' queries,

@@ -51,6 +51,13 @@ extern "C" {
 #define PKD_DTYPE_BF16 1  /* bfloat16 */
 #define PKD_DTYPE_E4M3 2  /* OCP FP8 E4M3FN byte, with fp32 per-(page, KV head) scales */
 #define PKD_DTYPE_F16 3   /* IEEE binary16 */
+/* OCP FP4 E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit; values
+ * 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two elements per byte with
+ * the lower-indexed one in the low nibble, with fp32 scales per (KV head,
+ * channel): the FP4 PageAttention with per-channel scaling factors of
+ * "FlashInfer vs FlashAttention-3: GPU Kernel Optimization & FP8 Serving
+ * Latency", §"Decision Matrix: Choosing the Right Attention Engine". KV only. */
+#define PKD_DTYPE_E2M1 4
 
 /* Columns of one work item as returned by pkd_plan_get_worklist:
  * request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible
@@ -71,11 +78,13 @@ typedef struct pkd_plan pkd_plan;
  *  num_qo_heads     query heads Hq; num_kv_heads divides it and query head h
  *                   reads KV head h / (Hq / Hkv)
  *  head_dim         64 or 128; query heads per KV head 1, 2, 4 or 8, and also
- *                   16 for bf16 queries with bf16 or e4m3 KV at head_dim 128
+ *                   16 for bf16 queries with bf16, e4m3 or e2m1 KV at
+ *                   head_dim 128
  *  page_size        tokens per page, a power of two in [1, 1024]
  *  q_dtype          PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16
- *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16, PKD_DTYPE_E4M3 or PKD_DTYPE_F16;
- *                   fp16 KV takes fp16 q (and fp16 q fp16 KV) at head_dim 128
+ *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16, PKD_DTYPE_E4M3, PKD_DTYPE_F16
+ *                   or PKD_DTYPE_E2M1; fp16 KV takes fp16 q (and fp16 q fp16
+ *                   KV) at head_dim 128; e2m1 KV takes bf16 q at head_dim 128
  *  out_dtype        PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16 (16-bit
  *                   outputs round to nearest even)
  *  sm_scale         logit scale; 0 selects 1/sqrt(head_dim)
@@ -95,8 +104,9 @@ typedef struct pkd_plan pkd_plan;
  *                   most its KV token count, which are its last q_r KV
  *                   tokens in order; new token i attends to the first
  *                   L_r - q_r + 1 + i KV tokens. More than one token per
- *                   request needs bf16 q, bf16 or e4m3 KV and head_dim 128
- *                   (else UNSUPPORTED); a work item then carries up to
+ *                   request needs head_dim 128 and bf16 q with bf16, e4m3 or
+ *                   e2m1 KV, or fp16 q with fp16 KV (else UNSUPPORTED); a
+ *                   work item then carries up to
  *                   16 / group of a request's tokens.
  *  non_causal       0: the causal rule above. 1: every q row of request r
  *                   sees all of its KV tokens and q_r may exceed them: the
@@ -196,15 +206,21 @@ typedef struct {
  *               k = base, v = base + page_size*Hkv*head_dim,
  *               page_stride = 2*page_size*Hkv*head_dim,
  *               token_stride = Hkv*head_dim, head_stride = head_dim.
- *               Strides are in elements; k, v and every stride must be
- *               16-byte aligned for f32/bf16 and 8-byte aligned for e4m3.
+ *               Strides are in elements (e2m1: two per byte, so the
+ *               combined pool's strides above hold with head_dim counted in
+ *               elements); k, v and every stride must be 16-byte aligned for
+ *               f32/bf16/f16/e2m1 and 8-byte aligned for e4m3.
  *  indices      int32 page ids of the page table (length indptr[B]); ids may
  *               repeat across requests (shared prefixes) and are not range
  *               checked
- *  k_scale,     float [num_pages, Hkv] contiguous (or, with
- *  v_scale      kv_scale_per_token, [num_pages, Hkv, page_size]); required for
- *               e4m3 KV, ignored otherwise. Stored K (V) bytes are multiplied
- *               by the scale of their (page, KV head) or (token, KV head).
+ *  k_scale,     e4m3: float [num_pages, Hkv] contiguous (or, with
+ *  v_scale      kv_scale_per_token, [num_pages, Hkv, page_size]): stored K
+ *               (V) bytes are multiplied by the scale of their (page, KV
+ *               head) or (token, KV head). e2m1: float [Hkv, head_dim]
+ *               contiguous, element (h, d) multiplying channel d of every
+ *               K (V) row of KV head h. Required for e4m3 and e2m1 KV,
+ *               ignored otherwise; row-wise and per-channel arrays must be
+ *               16-byte aligned.
  *  out          [rows, Hq, head_dim] contiguous, out_dtype
  *  lse          float [rows, Hq] or NULL: natural-log log-sum-exp of the
  *               scaled logits of each (q row, query head)

@@ -1,5 +1,5 @@
-// MFMA split-KV paged decode kernel, for gfx950 (bf16 or e4m3 KV, bf16 q,
-// head_dim 128, up to 16 query rows per KV head).
+// MFMA split-KV paged decode kernel, for gfx950 (bf16, e4m3 or e2m1 KV with
+// bf16 q, fp16 KV with fp16 q; head_dim 128, up to 16 query rows per KV head).
 //
 // What is computed ("FlashDecoding + FlashInfer — the decode-time attention
 // story"): for each query token of a request and each query head h, the
@@ -43,6 +43,13 @@
 // which keeps its 16 significant bits; V is exact in bf16 (e4m3 widens to
 // bf16 exactly and its per-page scale is folded into P), and K.q products are
 // exact with fp32 accumulation.
+//
+// FP4 E2M1 KV (64-byte rows, one fp32 scale per KV head and channel): a lane
+// loads 16 bytes = 32 dims of its K token (the four lanes of a token read the
+// whole row) and 4 bytes = 8 dims of each of its four V tokens. E2M1 widens to
+// bf16 exactly; the K channel scales are folded into q (q * k_scale as a hi +
+// lo bf16 pair, two MFMAs per k step) and the V channel scales multiply the
+// finished O columns.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -75,13 +82,33 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 #ifndef PKD_BF16_NSUB
 #define PKD_BF16_NSUB 1
 #endif
+#ifndef PKD_E2M1_NSUB
+#define PKD_E2M1_NSUB 4
+#endif
 template <int KV>
 constexpr bool fp8() { return KV == kE4M3 || KV == kE4M3T; }
+template <int KV>
+constexpr bool fp4() { return KV == kE2M1; }
 // 16-bit KV rows (bf16 or fp16): 256 bytes per row at head_dim 128.
 template <int KV>
 constexpr bool wide16() { return KV == kBF16 || KV == kF16; }
 template <int KV>
-constexpr int nsub() { return fp8<KV>() ? PKD_E4M3_NSUB : PKD_BF16_NSUB; }
+constexpr int nsub() { return fp8<KV>() ? PKD_E4M3_NSUB : fp4<KV>() ? PKD_E2M1_NSUB : PKD_BF16_NSUB; }
+// Byte offset of an element offset (e2m1: two elements per byte; offsets
+// handed to this are even).
+template <int KV>
+__device__ inline int64_t kv_bytes(int64_t elems) {
+  if constexpr (fp4<KV>())
+    return elems >> 1;
+  else
+    return elems * (wide16<KV>() ? 2 : 1);
+}
+// 16-byte K loads per lane and sub-tile.
+template <int KV>
+constexpr int k_loads() { return wide16<KV>() ? 4 : fp8<KV>() ? 2 : 1; }
+// q operands per lane: four k steps, and for e2m1 a hi and a lo half each.
+template <int KV>
+constexpr int q_ops() { return fp4<KV>() ? 8 : 4; }
 template <int KV>
 constexpr int tile_tokens() { return kSub * nsub<KV>(); }
 
@@ -158,11 +185,26 @@ template <int CPOL>
 __device__ inline uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, int(voff), int(soff), CPOL));
 }
+template <int CPOL>
+__device__ inline uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, int(voff), int(soff), CPOL);
+}
 
 // Two e4m3 bytes (half `hi` of a word) -> two bf16 (exact).
 __device__ inline uint32_t e4m3x2_to_bf16x2(uint32_t w, bool hi) {
   return hi ? __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, true))
             : __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(int(w), 1.0f, false));
+}
+
+// Byte B of a word (two e2m1 codes, the low nibble first) -> two bf16 (exact).
+template <int B>
+__device__ inline uint32_t e2m1x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, B));
+}
+// Eight e2m1 codes (a word, element 0 in the low nibble) -> eight bf16.
+__device__ inline u32x4_t e2m1x8_to_bf16x8(uint32_t w) {
+  return u32x4_t{e2m1x2_to_bf16x2<0>(w), e2m1x2_to_bf16x2<1>(w), e2m1x2_to_bf16x2<2>(w),
+                 e2m1x2_to_bf16x2<3>(w)};
 }
 
 template <int KV>
@@ -172,7 +214,6 @@ template <>
 struct Loads<kBF16> {
   u32x4_t k[4];  // [dc]: 8 dims of token l%16
   u32x4_t v[4];  // [e]: dims 8*(l%16)..+8 of token 4*(l/16) + e
-  static constexpr int kElem = 2;
 };
 
 template <>
@@ -182,7 +223,6 @@ template <>
 struct Loads<kE4M3> {
   u32x4_t k[2];  // [h]: 16 dims of token l%16, 64 contiguous bytes per token and instruction
   uint2 v[4];    // [e]: dims 8*(l%16)..+8 of token 4*(l/16) + e
-  static constexpr int kElem = 1;
 };
 
 // e4m3 with row-wise scales: the same bytes, plus the K and V scales of the
@@ -193,16 +233,26 @@ struct Loads<kE4M3T> {
   uint2 v[4];
   float ks[4];
   float vs[4];
-  static constexpr int kElem = 1;
+};
+
+// e2m1: 32 dims of token l%16 (word dc holds dims 8*dc..+8 of them), and
+// dims 8*(l%16)..+8 of token 4*(l/16) + e.
+template <>
+struct Loads<kE2M1> {
+  u32x4_t k[1];
+  uint32_t v[4];
 };
 
 // The head_dim index visited by QK k-slot (dc, q, e): bf16 lanes load 8 dims at
 // chunk 4*dc + q; e4m3 lanes load 16 dims at chunk 4*h + q and split them
-// into dc = 2h (first 8) and dc = 2h + 1 (last 8).
+// into dc = 2h (first 8) and dc = 2h + 1 (last 8); e2m1 lanes load dims
+// 32*q..+32 and take 8 of them per step.
 template <int KV>
 __device__ inline int qk_dim(int dc, int q, int e) {
   if constexpr (wide16<KV>())
     return 8 * (4 * dc + q) + e;
+  else if constexpr (fp4<KV>())
+    return 32 * q + 8 * dc + e;
   else
     return 16 * (4 * (dc >> 1) + q) + 8 * (dc & 1) + e;
 }
@@ -245,22 +295,21 @@ struct Ctx {
 // tile's math.
 template <int KV, bool PAGE16, bool FULL>
 __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
-  constexpr int kElem = Loads<KV>::kElem;
   const int last = c.kv_len - 1;
-  constexpr int NK = wide16<KV>() ? 4 : 2;
+  constexpr int NK = k_loads<KV>();
   if constexpr (PAGE16) {
     // One page per sub-tile: a wavefront-uniform base plus lane offsets. A
     // sub-tile past the end loads from the last sub-tile's rows (tp.page is
     // that sub-tile's page).
     const int tb = FULL ? t0 : min(t0, last & ~(kSub - 1));
     const int64_t base =
-        (tp.page * c.page_stride + int64_t(tb & c.pmask) * c.token_stride + c.head_off) * kElem;
+        kv_bytes<KV>(tp.page * c.page_stride + int64_t(tb & c.pmask) * c.token_stride + c.head_off);
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase + base);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase + base);
     uint32_t koff = c.koff;
     if constexpr (!FULL) {
       const int tk = min(t0 + c.j, last) - tb;
-      koff = (uint32_t(tk) * uint32_t(c.token_stride) + uint32_t(qk_dim<KV>(0, c.q4, 0))) * kElem;
+      koff = uint32_t(kv_bytes<KV>(int64_t(tk) * c.token_stride + qk_dim<KV>(0, c.q4, 0)));
     }
 #pragma unroll
     for (int x = 0; x < NK; ++x) ld.k[x] = bload16<PKD_K_CPOL>(kr, koff + 64 * x, 0);
@@ -272,11 +321,13 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
         soff = uint32_t(e * c.vrow_bytes);
       } else {
         const int tv = min(t0 + 4 * c.q4 + e, last) - tb;
-        voff = (uint32_t(tv) * uint32_t(c.token_stride) + uint32_t(8 * c.j)) * kElem;
+        voff = uint32_t(kv_bytes<KV>(int64_t(tv) * c.token_stride + 8 * c.j));
         soff = 0;
       }
       if constexpr (wide16<KV>())
         ld.v[e] = bload16<PKD_V_CPOL>(vr, voff, soff);
+      else if constexpr (fp4<KV>())
+        ld.v[e] = bload4<PKD_V_CPOL>(vr, voff, soff);
       else
         ld.v[e] = bload8<PKD_V_CPOL>(vr, voff, soff);
     }
@@ -288,18 +339,19 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
 #pragma unroll
       for (int x = 0; x < NK; ++x) {
         const int dim = wide16<KV>() ? qk_dim<KV>(x, c.q4, 0) : qk_dim<KV>(2 * x, c.q4, 0);
-        ld.k[x] = *reinterpret_cast<const u32x4_t*>(c.kbase + (row + dim) * kElem);
+        ld.k[x] = *reinterpret_cast<const u32x4_t*>(c.kbase + kv_bytes<KV>(row + dim));
       }
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = FULL ? t0 + 4 * c.q4 + e : min(t0 + 4 * c.q4 + e, last);
       const int64_t page = c.page_ids[t >> c.log2p];
-      const int64_t off =
-          (page * c.page_stride + int64_t(t & c.pmask) * c.token_stride + c.head_off + 8 * c.j) *
-          kElem;
+      const int64_t off = kv_bytes<KV>(page * c.page_stride + int64_t(t & c.pmask) * c.token_stride +
+                                       c.head_off + 8 * c.j);
       if constexpr (wide16<KV>())
         ld.v[e] = *reinterpret_cast<const u32x4_t*>(c.vbase + off);
+      else if constexpr (fp4<KV>())
+        ld.v[e] = *reinterpret_cast<const uint32_t*>(c.vbase + off);
       else
         ld.v[e] = *reinterpret_cast<const uint2*>(c.vbase + off);
     }
@@ -360,13 +412,20 @@ __device__ inline float token_scale(const float* sc, const Ctx& c, const KernelA
 // QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens valid).
 template <int KV, bool PAGE16, bool FULL>
 __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TilePages& tp, const u32x4_t (&qb)[4],
+                                    int t0, const TilePages& tp, const u32x4_t (&qb)[q_ops<KV>()],
                                     f32x4_t (&acc)[8], float& m_run, float& d_run) {
   // ---- S = K . q^T: lane l gets tokens 4*q4 + r of head j
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
   if constexpr (wide16<KV>()) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) s = mfma<KV>(ld.k[dc], qb[dc], s);
+  } else if constexpr (fp4<KV>()) {
+#pragma unroll
+    for (int dc = 0; dc < 4; ++dc) {
+      const u32x4_t kb = e2m1x8_to_bf16x8(ld.k[0][dc]);
+      s = mfma<KV>(kb, qb[dc], s);      // q * k_scale, hi part
+      s = mfma<KV>(kb, qb[4 + dc], s);  // lo part
+    }
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -460,6 +519,21 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
       const bool hi = nc & 1;
       vb.x = pack_halves(ld.v[0][w], ld.v[1][w], hi);
       vb.y = pack_halves(ld.v[2][w], ld.v[3][w], hi);
+    } else if constexpr (fp4<KV>()) {
+      // byte nc/2 of each token's word holds dims 8*j + nc (nibble nc&1)
+      const bool hi = nc & 1;
+      uint32_t x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        switch (nc >> 1) {
+          case 0: x[e] = e2m1x2_to_bf16x2<0>(ld.v[e]); break;
+          case 1: x[e] = e2m1x2_to_bf16x2<1>(ld.v[e]); break;
+          case 2: x[e] = e2m1x2_to_bf16x2<2>(ld.v[e]); break;
+          default: x[e] = e2m1x2_to_bf16x2<3>(ld.v[e]); break;
+        }
+      }
+      vb.x = pack_halves(x[0], x[1], hi);
+      vb.y = pack_halves(x[2], x[3], hi);
     } else {
       const int w = nc >> 2;           // word of the 8 loaded bytes
       const bool hiw = (nc >> 1) & 1;  // which byte pair in the word
@@ -477,7 +551,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
 
 template <int KV, bool PAGE16, bool FULL>
 __device__ inline void process_tile(const Tile<KV>& T, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TileP<KV>& tp, const u32x4_t (&qb)[4],
+                                    int t0, const TileP<KV>& tp, const u32x4_t (&qb)[q_ops<KV>()],
                                     f32x4_t (&acc)[8], float& m_run, float& d_run) {
 #pragma unroll
   for (int s = 0; s < nsub<KV>(); ++s)
@@ -509,10 +583,11 @@ __device__ inline void load_pid_block(const Ctx& c, const KernelArgs& a, int kvh
 // 16-token sub-tile of pages >= 16; larger tiles and per-lane page lookups need
 // up to 168 (3 wavefronts per SIMD); row-wise e4m3 scales ride along with the
 // loads and get up to 256 (2 per SIMD, still twice what one workgroup per CU
-// uses).
+// uses). e2m1 keeps four 16-token sub-tiles and the q hi/lo pair in flight
+// and takes the same 256.
 template <int KV, bool PAGE16>
 constexpr int waves_per_simd() {
-  return KV == kE4M3T ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
+  return KV == kE4M3T || fp4<KV>() ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
 }
 
 template <int KV, int G, bool PAGE16>
@@ -548,16 +623,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   const int hh = c.j & ((1 << a.group_log2) - 1);
   const bool row_ok = c.j < G && qi < it.q_len;
   c.lim = row_ok ? min(it.kv_len, it.visible + qi) : it.kv_len;
-  {
-    constexpr uint32_t kElem = Loads<KV>::kElem;
-    const uint32_t ts = uint32_t(a.token_stride);
-    c.koff = (uint32_t(c.j) * ts + uint32_t(qk_dim<KV>(0, c.q4, 0))) * kElem;
-    c.voff = (uint32_t(4 * c.q4) * ts + uint32_t(8 * c.j)) * kElem;
-    c.vrow_bytes = a.token_stride * kElem;
-  }
+  c.koff = uint32_t(kv_bytes<KV>(int64_t(c.j) * a.token_stride + qk_dim<KV>(0, c.q4, 0)));
+  c.voff = uint32_t(kv_bytes<KV>(int64_t(4 * c.q4) * a.token_stride + 8 * c.j));
+  c.vrow_bytes = kv_bytes<KV>(a.token_stride);
 
   // q^T as the B operand of S = K.q^T: column j = row j (zero beyond the block).
-  u32x4_t qb[4];  // eight 16-bit q values (bf16, or fp16 for fp16 KV)
+  u32x4_t qb[q_ops<KV>()];  // eight 16-bit q values per k step (bf16, or fp16 for fp16 KV)
   {
     const uint16_t* qp =
         static_cast<const uint16_t*>(a.q) +
@@ -566,7 +637,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     for (int dc = 0; dc < 4; ++dc) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (row_ok) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
-      qb[dc] = w;
+      if constexpr (fp4<KV>()) {
+        // q * k_scale over this step's eight dims, as hi + lo bf16
+        const float* ksp = a.k_scale + int64_t(kvh) * kD + qk_dim<KV>(dc, c.q4, 0);
+        const float4 s0 = *reinterpret_cast<const float4*>(ksp);
+        const float4 s1 = *reinterpret_cast<const float4*>(ksp + 4);
+        const float ksv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float q0 = __builtin_bit_cast(float, w[x] << 16) * ksv[2 * x];
+          const float q1 = __builtin_bit_cast(float, w[x] & 0xffff0000u) * ksv[2 * x + 1];
+          uint32_t h, l;
+          split16<KV>(q0, q1, h, l);
+          hi[x] = h;
+          lo[x] = l;
+        }
+        qb[dc] = hi;
+        qb[4 + dc] = lo;
+      } else {
+        qb[dc] = w;
+      }
     }
   }
 
@@ -650,6 +741,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 
   // ---- per-wavefront state -> shared memory
   const int q4 = c.q4, j = c.j;
+  if constexpr (fp4<KV>()) {
+    // V channel scales: column j of MFMA nc is dim 8*j + nc
+    const float* vsp = a.v_scale + int64_t(kvh) * kD + 8 * j;
+    const float4 s0 = *reinterpret_cast<const float4*>(vsp);
+    const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
+    const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int nc = 0; nc < 8; ++nc) acc[nc] *= vsv[nc];
+  }
   d_run += __shfl_xor(d_run, 16, 64);
   d_run += __shfl_xor(d_run, 32, 64);
 #pragma unroll
@@ -690,6 +790,7 @@ DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size)
     case kE4M3: return p16 ? pick_group<kE4M3, true>(rows) : pick_group<kE4M3, false>(rows);
     case kE4M3T: return p16 ? pick_group<kE4M3T, true>(rows) : pick_group<kE4M3T, false>(rows);
     case kF16: return p16 ? pick_group<kF16, true>(rows) : pick_group<kF16, false>(rows);
+    case kE2M1: return p16 ? pick_group<kE2M1, true>(rows) : pick_group<kE2M1, false>(rows);
     default: return nullptr;
   }
 }

@@ -1,8 +1,8 @@
 // Kernel choice and launch for the decode stage.
 //
 // The MFMA kernel runs wherever both contractions can take bf16 operands
-// exactly: bf16 or e4m3 KV with bf16 queries and head_dim 128 (group sizes
-// 1..16). fp32 KV or queries, and head_dim 64, use the vector-ALU kernel,
+// exactly: bf16, e4m3 or e2m1 KV with bf16 queries and head_dim 128 (group
+// sizes 1..16), and fp16 KV with fp16 queries on fp16 MFMA. fp32 KV or queries, and head_dim 64, use the vector-ALU kernel,
 // which handles one query token per request only. A work item of several new
 // tokens of a request puts group x tokens rows (at most 16) on the MFMA
 // columns; the kernel instance is the one for that row count rounded up to a
@@ -19,10 +19,11 @@ static int pow2_ceil(int x) {
   return p;
 }
 
-// Forms the MFMA kernel takes: bf16 queries over bf16 or e4m3 KV (both
+// Forms the MFMA kernel takes: bf16 queries over bf16, e4m3 or e2m1 KV (both
 // contractions on bf16 MFMA), fp16 queries over fp16 KV (fp16 MFMA).
 static bool mfma_form(int kv_dtype, int q_kind) {
-  return (q_kind == kQBF16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T)) ||
+  return (q_kind == kQBF16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T ||
+                               kv_dtype == kE2M1)) ||
          (q_kind == kQF16 && kv_dtype == kF16);
 }
 
@@ -34,7 +35,9 @@ static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_ki
   }
   // The vector-ALU kernel: one token per request, fp32 or bf16 q over fp32,
   // bf16 or e4m3 KV (per-page scales).
-  if (rows != group || q_kind == kQF16 || kv_dtype == kE4M3T || kv_dtype == kF16) return nullptr;
+  if (rows != group || q_kind == kQF16 || kv_dtype == kE4M3T || kv_dtype == kF16 ||
+      kv_dtype == kE2M1)
+    return nullptr;
   return valu_decode_kernel(kv_dtype, head_dim, group);
 }
 
@@ -86,7 +89,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.num_items = L.num_items;
-  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T) ? 8 : 1;
+  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1) ? 8 : 1;
   a.num_kv_heads = L.num_kv_heads;
   a.num_qo_heads = L.num_qo_heads;
   a.group_log2 = ilog2(L.group);

@@ -33,6 +33,8 @@ def _dtype_code(dt) -> int:
         return _lib.DTYPE_E4M3
     if dt in (torch.float16, "f16", "float16"):
         return _lib.DTYPE_F16
+    if dt in (getattr(torch, "float4_e2m1fn_x2", "e2m1"), "e2m1", "float4_e2m1fn_x2"):
+        return _lib.DTYPE_E2M1
     raise ValueError(f"unsupported dtype {dt}")
 
 
@@ -148,11 +150,13 @@ def _capacity(capacity) -> Tuple[int, int, int, int]:
 
 def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                    kv_dtype="bf16", q_dtype="bf16", out_dtype="f32", slots=1024, balance=0,
-                   min_chunk_pages=0, qo_indptr=None, causal=True, capacity=None):
+                   min_chunk_pages=0, qo_indptr=None, causal=True, capacity=None,
+                   kv_scale="page"):
     """Host-only: build a plan with an explicit slot count and return its decisions."""
     p = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
              _dtype_code(q_dtype), _dtype_code(kv_dtype), _dtype_code(out_dtype), None, slots,
-             balance, min_chunk_pages, qo_indptr=qo_indptr, causal=causal, capacity=capacity)
+             balance, min_chunk_pages, qo_indptr=qo_indptr, causal=causal, capacity=capacity,
+             kv_scale=kv_scale)
     items, merge, split = p.worklist()
     info = dict(p.info)
     p.close()
@@ -203,7 +207,10 @@ class BatchDecodeWithPagedKVCacheWrapper:
         arguments for every such plan, so a captured HIP graph of run() stays
         valid across plan()/upload of new batches. ``kv_scale`` (e4m3 KV):
         ``"page"`` for one scale per (page, KV head), ``"token"`` for one per
-        (token, KV head)."""
+        (token, KV head). FP4 E2M1 KV (``kv_data_type`` "e2m1" or
+        ``torch.float4_e2m1fn_x2``) is a byte pool ``[..., head_dim // 2]``
+        (uint8 or float4_e2m1fn_x2, element 2i in the low nibble of byte i)
+        with scales ``[num_kv_heads, head_dim]`` per channel."""
         import torch
         if pos_encoding_mode != "NONE":
             raise ValueError("only pos_encoding_mode='NONE' is supported")
@@ -248,9 +255,13 @@ class BatchDecodeWithPagedKVCacheWrapper:
         if q.shape != (p.query_rows, p.num_qo_heads, p.head_dim) or not q.is_contiguous():
             raise ValueError(
                 f"q must be contiguous [{p.query_rows}, {p.num_qo_heads}, {p.head_dim}]")
-        if _dtype_code(q.dtype) != p.q_dtype or _dtype_code(k.dtype) != p.kv_dtype:
+        fp4 = p.kv_dtype == _lib.DTYPE_E2M1
+        kv_ok = (k.dtype in (torch.uint8, getattr(torch, "float4_e2m1fn_x2", torch.uint8)) if fp4
+                 else _dtype_code(k.dtype) == p.kv_dtype)
+        if _dtype_code(q.dtype) != p.q_dtype or not kv_ok:
             raise _lib.PkdError(_lib.PKD_ERR_PLAN_MISMATCH, "q/KV dtypes differ from the plan")
-        if k.shape[1] != p.page_size or k.shape[2] != p.num_kv_heads or k.shape[3] != p.head_dim:
+        row = p.head_dim // 2 if fp4 else p.head_dim  # storage units per row
+        if k.shape[1] != p.page_size or k.shape[2] != p.num_kv_heads or k.shape[3] != row:
             raise ValueError("KV pool shape disagrees with the plan")
         out_dt = {_lib.DTYPE_F32: torch.float32, _lib.DTYPE_BF16: torch.bfloat16,
                   _lib.DTYPE_F16: torch.float16}[p.out_dtype]
@@ -266,13 +277,23 @@ class BatchDecodeWithPagedKVCacheWrapper:
         a.q = q.data_ptr()
         a.k = k.data_ptr()
         a.v = v.data_ptr()
-        a.page_stride, a.token_stride, a.head_stride = k.stride(0), k.stride(1), k.stride(2)
+        per = 2 if fp4 else 1  # strides in elements: two e2m1 codes per byte
+        a.page_stride, a.token_stride, a.head_stride = (per * k.stride(0), per * k.stride(1),
+                                                        per * k.stride(2))
         a.indices = self._indices.data_ptr()
         if p.kv_dtype == _lib.DTYPE_E4M3:
             if k_scale is None or v_scale is None:
                 raise ValueError("e4m3 KV needs k_scale and v_scale [num_pages, num_kv_heads]")
             want = ((k.shape[0], p.num_kv_heads, p.page_size) if p.kv_scale == "token"
                     else (k.shape[0], p.num_kv_heads))
+            for s in (k_scale, v_scale):
+                if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != want:
+                    raise ValueError(f"scales must be contiguous float32 {list(want)}")
+            a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
+        elif fp4:
+            want = (p.num_kv_heads, p.head_dim)
+            if k_scale is None or v_scale is None:
+                raise ValueError(f"e2m1 KV needs k_scale and v_scale {list(want)}")
             for s in (k_scale, v_scale):
                 if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != want:
                     raise ValueError(f"scales must be contiguous float32 {list(want)}")

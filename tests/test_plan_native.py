@@ -72,7 +72,7 @@ def test_random_multi_query_tables_bit_exact(seed):
     hkv = int(rng.choice([1, 2, 8]))
     g = int(rng.choice([1, 2, 4, 8, 16]))
     out = _both(indptr, last, P, hkv, int(rng.integers(1, 4096)), int(rng.integers(1, 4)),
-                int(rng.integers(1, 32)), hq=hkv * g, kv=str(rng.choice(["bf16", "e4m3"])),
+                int(rng.integers(1, 32)), hq=hkv * g, kv=str(rng.choice(["bf16", "e4m3", "e2m1"])),
                 qo_indptr=qo)
     info = out[0]
     assert info["queries_per_item"] == (max(1, 16 // g) if nq.max() > 1 else 1)
@@ -222,3 +222,28 @@ def test_fp16_needs_fp16_q_over_fp16_kv_at_128(q, kv, d):
     with pytest.raises(pk.PkdError) as e:
         pk.plan_partition([0, 2], [5], 8, 2, d, 16, kv_dtype=kv, q_dtype=q)
     assert e.value.code == pk._lib.PKD_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("q,d", [("f32", 128), ("f16", 128), ("bf16", 64)])
+def test_e2m1_needs_bf16_q_at_128(q, d):
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 2], [5], 8, 2, d, 16, kv_dtype="e2m1", q_dtype=q)
+    assert e.value.code == pk._lib.PKD_ERR_UNSUPPORTED
+
+
+def test_e2m1_has_no_row_wise_scales():
+    with pytest.raises(pk.PkdError) as e:
+        pk.plan_partition([0, 2], [5], 8, 2, 128, 16, kv_dtype="e2m1", q_dtype="bf16",
+                          kv_scale="token")
+    assert e.value.code == pk._lib.PKD_ERR_INVALID_ARGUMENT
+
+
+def test_e2m1_plans_match_the_oracle():
+    rng = np.random.default_rng(11)
+    lens = rng.integers(1, 3000, size=37)
+    P = 16
+    npg = -(-lens // P)
+    indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+    last = (lens - (npg - 1) * P).astype(np.int32)
+    for g in (1, 4, 16):
+        _assert_same(*_both(indptr, last, P, 8, 256, 1, 16, hq=8 * g, kv="e2m1"))

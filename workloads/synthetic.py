@@ -11,7 +11,10 @@ bytes itself):
   ``[num_pages, num_kv_heads]`` (one per page and KV head) or, for a
   workload with ``kv_scale="token"``, ``[num_pages, num_kv_heads,
   page_size]`` (one per token and KV head; a head's scales of a page are
-  contiguous).
+  contiguous). ``"e2m1"`` storage is packed FP4 E2M1 codes as ``uint8``
+  ``[num_pages, 2, page_size, num_kv_heads, head_dim / 2]`` (element 2i in the
+  low nibble of byte i) with fp32 per-channel scales ``k_scale``/``v_scale``
+  of shape ``[num_kv_heads, head_dim]``.
 * ``q`` is ``[rows, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
   storage: one row per request, or, for a workload with several new tokens
   per request, the ragged rows ``qo_indptr[r]:qo_indptr[r+1]`` of request r
@@ -36,11 +39,12 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-KV_DTYPES = ("f32", "bf16", "f16", "e4m3")
+KV_DTYPES = ("f32", "bf16", "f16", "e4m3", "e2m1")
 Q_DTYPES = ("f32", "bf16", "f16")
 E4M3_MAX = 448.0
 BF16_NAN_BITS = 0x7FC0
 E4M3_NAN_BYTE = 0x7F
+E2M1_POISON_BYTE = 0x77  # E2M1 has no NaN: both codes +6, the largest value
 
 
 @dataclasses.dataclass(frozen=True)
@@ -112,6 +116,9 @@ CONFIGS = {
     # The Llama-3-8B-shaped batch in fp16 (q, KV and output).
     "llama3_8b_f16": Workload(
         "llama3_8b_f16", 64, 32, 8, 128, 16, "f16", "f16", ("fixed", 2048)),
+    # FP4 (E2M1) KV with per-channel fp32 scales, the fp8 workload's shape.
+    "fp4_kv_e2m1": Workload(
+        "fp4_kv_e2m1", 128, 32, 8, 128, 16, "e2m1", "bf16", ("uniform", 1024, 32768)),
     # Cascade: 64 requests share one 8192-token prefix (a long system prompt or
     # document) and each has 512 tokens of its own.
     "cascade_prefix8k_bf16": Workload(
@@ -287,6 +294,34 @@ def _quantize_pool_e4m3(pool32: np.ndarray, per_token: bool = False):
     return _to_e4m3_bytes(y), scale[:, 0, :].copy(), scale[:, 1, :].copy()
 
 
+# FP4 E2M1 codes by round-to-nearest-even onto the grid 0, 0.5, 1, 1.5, 2, 3,
+# 4, 6 with saturation: the magnitude code is the number of rounding
+# boundaries passed; at a boundary the even code (mantissa bit 0) wins, so
+# boundaries below an odd code are exclusive and those below an even code
+# inclusive.
+E2M1_BOUNDS = ((0.25, False), (0.75, True), (1.25, False), (1.75, True), (2.5, False),
+               (3.5, True), (5.0, False))
+
+
+def _e2m1_codes(y: np.ndarray) -> np.ndarray:
+    a = np.abs(y)
+    idx = np.zeros(y.shape, np.uint8)
+    for b, inclusive in E2M1_BOUNDS:
+        idx += (a >= b) if inclusive else (a > b)
+    return idx | (np.signbit(y).astype(np.uint8) << 3)
+
+
+def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _channel_magnitudes(draw, shape):
+    """Per-(K/V, KV head, channel) magnitudes m = exp(0.5 z): values are m * z'
+    for standard normal z', stored as E2M1 codes of z' / s with scale s = m / 2
+    (so codes saturate at 3 standard deviations of their channel)."""
+    return np.exp(0.5 * draw(shape))
+
+
 def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict] = None) -> dict:
     """Small-case inputs as numpy storage arrays (see module docstring)."""
     if table is None:
@@ -304,6 +339,11 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
         kv = _to_bf16_bits(pool32)
     elif w.kv_dtype == "e4m3":
         kv, k_scale, v_scale = _quantize_pool_e4m3(pool32, w.kv_scale == "token")
+    elif w.kv_dtype == "e2m1":
+        m = _channel_magnitudes(lambda sh: rng.standard_normal(sh), (2, Hkv, D))
+        scale = (m / 2).astype(np.float32)
+        kv = _pack_nibbles(_e2m1_codes(2 * pool32))
+        k_scale, v_scale = scale[0].copy(), scale[1].copy()
     else:
         raise ValueError(w.kv_dtype)
     q = {"f32": q32, "f16": None, "bf16": None}[w.q_dtype]
@@ -314,7 +354,8 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
     if poison:
         unread = ~read_mask(table, P)
         nan = {"f32": np.float32(np.nan), "f16": np.float16(np.nan),
-               "bf16": np.uint16(BF16_NAN_BITS), "e4m3": np.uint8(E4M3_NAN_BYTE)}[w.kv_dtype]
+               "bf16": np.uint16(BF16_NAN_BITS), "e4m3": np.uint8(E4M3_NAN_BYTE),
+               "e2m1": np.uint8(E2M1_POISON_BYTE)}[w.kv_dtype]
         kv = kv.copy()
         kv[:, 0][unread] = nan
         kv[:, 1][unread] = nan
@@ -330,8 +371,8 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
     """Full-size inputs drawn directly in device memory with a seeded torch generator.
 
     Returns torch tensors: ``q`` (float32 or bfloat16), ``kv`` (float32,
-    bfloat16 or uint8 bytes for e4m3), ``k_scale``/``v_scale`` (float32, e4m3
-    only), and the numpy page table.
+    bfloat16, or uint8 bytes for e4m3 and packed e2m1), ``k_scale``/``v_scale``
+    (float32, e4m3 and e2m1 only), and the numpy page table.
     """
     import torch
 
@@ -371,12 +412,31 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
             del x, y
         k_scale = scale[:, 0].contiguous()
         v_scale = scale[:, 1].contiguous()
+    elif w.kv_dtype == "e2m1":
+        m = torch.exp(0.5 * torch.randn((2, Hkv, D), generator=g, device=device,
+                                        dtype=torch.float32))
+        scale = m / 2
+        k_scale, v_scale = scale[0].contiguous(), scale[1].contiguous()
+        kv = torch.empty((npg, 2, P, Hkv, D // 2), device=device, dtype=torch.uint8)
+        for p0 in range(0, npg, chunk_pages):
+            p1 = min(npg, p0 + chunk_pages)
+            y = 2 * torch.randn((p1 - p0, 2, P, Hkv, D), generator=g, device=device,
+                                dtype=torch.float32)
+            a = y.abs()
+            idx = torch.zeros(y.shape, device=device, dtype=torch.uint8)
+            for b, inclusive in E2M1_BOUNDS:
+                idx += (a >= b if inclusive else a > b).to(torch.uint8)
+            codes = idx | (torch.signbit(y).to(torch.uint8) << 3)
+            kv[p0:p1] = codes[..., 0::2] | (codes[..., 1::2] << 4)
+            del y, a, idx, codes
     else:
         raise ValueError(w.kv_dtype)
     if poison:
         unread = torch.from_numpy(~read_mask(table, P)).to(device)
         if w.kv_dtype == "e4m3":
             fill = E4M3_NAN_BYTE
+        elif w.kv_dtype == "e2m1":
+            fill = E2M1_POISON_BYTE
         else:
             fill = float("nan")
         kvv = kv.permute(0, 2, 1, 3, 4)  # [pages, P, 2, Hkv, D] view
