@@ -348,8 +348,11 @@ typedef struct {
 int pkd_merge_states(const pkd_merge_states_args* args);
 
 /* Workgroups of the decode kernel selected for (q_dtype, kv_dtype, head_dim,
- * group, page_size) that one compute unit holds at once, and the device's
- * compute-unit count. */
+ * group, page_size) and one query token per request that one compute unit
+ * holds at once, and the device's compute-unit count. On the MFMA path with
+ * an even number of KV heads and pages of at least 16 tokens one workgroup
+ * serves a pair of KV heads (info.units_per_item of a plan gives the
+ * workgroups per work item). */
 int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
                      int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus);
 

@@ -133,7 +133,7 @@ void pinned_release(PinnedBlock b) {
 
 // Resident workgroups per CU and CU count, per (device, kernel choice).
 std::mutex g_slots_mu;
-std::map<std::tuple<int, int, int, int, int, int, int, int>, std::pair<int, int>> g_slots;
+std::map<std::tuple<int, int, int, int, int, int, int, int, int>, std::pair<int, int>> g_slots;
 
 // Decode workgroups per compute unit the library allows by default. One
 // workgroup per CU (four wavefronts) is the fastest residency measured on
@@ -144,15 +144,16 @@ std::map<std::tuple<int, int, int, int, int, int, int, int>, std::pair<int, int>
 int32_t default_wgs_cap(bool mfma, bool one_token) { return mfma && one_token ? 1 : 0; }
 
 int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
-                 int32_t group, int32_t rows, int32_t page_size, int32_t wgs_cap,
-                 int32_t* wgs_per_cu, int32_t* num_cus) {
+                 int32_t group, int32_t rows, int32_t page_size, int32_t heads_per_wg,
+                 int32_t wgs_cap, int32_t* wgs_per_cu, int32_t* num_cus) {
   const int q_kind = kind_of(q_dtype);
   if (!pkd::decode_supported(kv_dtype, head_dim, group, rows, q_kind, page_size))
     return fail(PKD_ERR_UNSUPPORTED,
                 "no kernel for kv_dtype=%d head_dim=%d group=%d rows=%d q_dtype=%d", kv_dtype,
                 head_dim, group, rows, q_dtype);
   const auto key = std::make_tuple(int(device), int(kv_dtype), int(head_dim), int(group),
-                                   int(rows), q_kind, page_size >= 16 ? 16 : 1, int(wgs_cap));
+                                   int(rows), q_kind, page_size >= 16 ? 16 : 1, int(wgs_cap),
+                                   int(heads_per_wg));
   {
     std::lock_guard<std::mutex> lk(g_slots_mu);
     auto it = g_slots.find(key);
@@ -170,8 +171,8 @@ int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head
   int cus = 0, wgs = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device);
   if (e == hipSuccess)
-    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_kind, page_size, wgs_cap,
-                              &wgs);
+    e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_kind, page_size, heads_per_wg,
+                              wgs_cap, &wgs);
   if (prev != device) hipSetDevice(prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
   *wgs_per_cu = wgs;
@@ -189,6 +190,7 @@ struct pkd_plan {
   pkd::Partition part;
   pkd_plan_info info{};
   int rows = 0;  // query rows per work item and KV head (kernel choice)
+  int heads_per_wg = 1;  // KV heads per decode workgroup (1, or 2: a pair)
   int kv_impl = 0;  // KV format as the kernels see it (pkd::kF32 .. kE4M3T)
   int wgs_cap = 0;  // decode workgroups per compute unit at most (0: no cap)
   bool fixed = false;    // fixed-capacity plan: grids from capacities, counts read on device
@@ -216,7 +218,10 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
   const int form = kv_form(kv_dtype, 0);
   const bool mfma = pkd::decode_uses_mfma(form, head_dim, group, group, kind_of(q_dtype),
                                           page_size);
-  return device_slots(device, q_dtype, form, head_dim, group, group, page_size,
+  // the kernel chosen for an even number of KV heads (head pairs where they apply)
+  const int hp = pkd::decode_heads_per_wg(form, head_dim, group, group, kind_of(q_dtype),
+                                          page_size, 2);
+  return device_slots(device, q_dtype, form, head_dim, group, group, page_size, hp,
                       default_wgs_cap(mfma, true), wgs_per_cu, num_cus);
 }
 
@@ -302,6 +307,9 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                                           q_kind, a->page_size);
   const int32_t wgs_cap =
       a->max_wgs_per_cu ? a->max_wgs_per_cu : default_wgs_cap(mfma, rows == group);
+  // A workgroup per work item and KV head, or per pair of KV heads.
+  const int32_t heads_per_wg = pkd::decode_heads_per_wg(kv_impl, a->head_dim, group, rows,
+                                                        q_kind, a->page_size, a->num_kv_heads);
   if (!(a->sm_scale >= 0.f) || std::isinf(a->sm_scale))
     return fail(PKD_ERR_INVALID_ARGUMENT, "sm_scale must be finite and >= 0");
 
@@ -309,7 +317,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (slots == 0) {
     int32_t wgs = 0, cus = 0;
     int rc = device_slots(a->device, a->q_dtype, kv_impl, a->head_dim, group, rows,
-                          a->page_size, wgs_cap, &wgs, &cus);
+                          a->page_size, heads_per_wg, wgs_cap, &wgs, &cus);
     if (rc != PKD_OK) return rc;
     slots = wgs * cus;
     if (slots < 1) return fail(PKD_ERR_HIP, "device reports no resident workgroups");
@@ -322,7 +330,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   pin.queries_per_item = queries_per_item;
   pin.causal = a->non_causal == 0;
   pin.page_size = a->page_size;
-  pin.units_per_item = a->num_kv_heads;
+  pin.units_per_item = a->num_kv_heads / heads_per_wg;
   pin.slots = slots;
   pin.balance = a->balance ? a->balance : 1;
   pin.min_chunk_pages = a->min_chunk_pages ? a->min_chunk_pages : (256 + a->page_size - 1) / a->page_size;
@@ -341,6 +349,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   p->rows = rows;
   p->kv_impl = kv_impl;
   p->wgs_cap = wgs_cap;
+  p->heads_per_wg = heads_per_wg;
   p->device = a->device;
   p->sm_scale = a->sm_scale > 0.f ? a->sm_scale : 1.0f / std::sqrt(float(a->head_dim));
 
@@ -546,6 +555,7 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.group = a.num_qo_heads / a.num_kv_heads;
   L.rows = p->rows;
   L.wgs_cap = p->wgs_cap;
+  L.heads_per_wg = p->heads_per_wg;
   L.num_items = p->launch_items;
   L.num_kv_heads = a.num_kv_heads;
   L.num_qo_heads = a.num_qo_heads;

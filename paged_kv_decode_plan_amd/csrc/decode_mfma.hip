@@ -45,11 +45,23 @@
 // exact with fp32 accumulation.
 //
 // FP4 E2M1 KV (64-byte rows, one fp32 scale per KV head and channel): a lane
-// loads 16 bytes = 32 dims of its K token (the four lanes of a token read the
-// whole row) and 4 bytes = 8 dims of each of its four V tokens. E2M1 widens to
-// bf16 exactly; the K channel scales are folded into q (q * k_scale as a hi +
-// lo bf16 pair, two MFMAs per k step) and the V channel scales multiply the
-// finished O columns.
+// loads 16 bytes = 32 dims of its K row and 4 bytes = 8 dims of each of its
+// four V rows. E2M1 widens to bf16 exactly; the K channel scales are folded
+// into q (q * k_scale as a hi + lo bf16 pair, two MFMAs per k step) and the V
+// channel scales multiply the finished O columns.
+//
+// Two KV heads per workgroup (HP = 2): a 64-byte e2m1 row is half a 128-byte
+// cache line whose other half is the next KV head's row, and an e4m3 row is
+// one line. Workgroups that each read one head's e2m1 rows reach only about
+// 55% of HBM bandwidth on MI355X, and with one resident workgroup per CU the
+// bytes a workgroup reads contiguously per token keep mattering up to 256
+// (one bf16 row). So a workgroup may take an even-odd pair of KV heads, and a
+// sub-tile's 16 S rows are 8 tokens x 2 heads (row rho is token rho % 8 of
+// head rho / 8), so that each load instruction reads both heads' rows of a
+// token side by side. The S columns are the pair's 2 * group query heads; a
+// lane's four S values all belong to one head (quarter q4 / 2), and those
+// whose head is not their column's are masked to -inf, so P.V over the 16
+// rows sums each column's own head only. The MFMA work per head is unchanged.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -109,8 +121,22 @@ constexpr int k_loads() { return wide16<KV>() ? 4 : fp8<KV>() ? 2 : 1; }
 // q operands per lane: four k steps, and for e2m1 a hi and a lo half each.
 template <int KV>
 constexpr int q_ops() { return fp4<KV>() ? 8 : 4; }
-template <int KV>
-constexpr int tile_tokens() { return kSub * nsub<KV>(); }
+// Tokens per sub-tile: 16, or 16 / HP when the 16 rows are HP KV heads' rows.
+template <int HP>
+constexpr int sub_tokens() { return kSub / HP; }
+template <int HP>
+constexpr int sub_tokens_log2() {
+  static_assert(HP == 1 || HP == 2, "one or two KV heads per workgroup");
+  return HP == 1 ? 4 : 3;
+}
+// Token (within the sub-tile) of S row 4*q4 + r, and the KV head (within the
+// workgroup's HP) of the lane's rows 4*q4 .. 4*q4 + 3.
+template <int HP>
+__device__ inline int row_token(int q4, int r) { return ((4 * q4) & (sub_tokens<HP>() - 1)) + r; }
+template <int HP>
+__device__ inline int row_head(int q4) { return (4 * q4) >> sub_tokens_log2<HP>(); }
+template <int KV, int HP>
+constexpr int tile_tokens() { return sub_tokens<HP>() * nsub<KV>(); }
 
 // k = 32 step of S = K.q^T on eight 16-bit values per lane: fp16 for fp16 KV
 // (with fp16 q), bf16 for every other form (bf16 q).
@@ -257,17 +283,23 @@ __device__ inline int qk_dim(int dc, int q, int e) {
     return 16 * (4 * (dc >> 1) + q) + 8 * (dc & 1) + e;
 }
 
-// Where a sub-tile lives: with pages of at least 16 tokens a 16-token
-// sub-tile lies in one page (sub-tiles start at multiples of 16 and items at
-// page boundaries), so it needs one page id (and, for e4m3, one K and one V
-// scale), all wavefront-uniform. A sub-tile wholly past the item's end is
+// Where a sub-tile lives: with pages of at least 16 tokens a sub-tile (16 or
+// 8 tokens) lies in one page (sub-tiles start at multiples of their size and
+// items at page boundaries), so it needs one page id (and, for e4m3, one K
+// and one V scale per head), all wavefront-uniform. A sub-tile wholly past the item's end is
 // given the page of the item's last sub-tile (its loads repeat valid tokens
 // and its weights are 0).
 struct TilePages {
   int64_t page;
-  float ks;
-  float vs;
+  float ks[2], vs[2];  // e4m3 per-page scales of the workgroup's KV heads
 };
+
+// The value of KV head h (0 .. HP-1) among the workgroup's heads.
+template <int HP>
+__device__ inline float head_pick(const float (&x)[2], int h) {
+  if constexpr (HP == 1) return x[0];
+  return h ? x[1] : x[0];
+}
 
 struct Ctx {
   const char* kbase;
@@ -275,10 +307,14 @@ struct Ctx {
   const int32_t* page_ids;  // the item's slice of the page table
   const float* k_scale;     // row-wise e4m3 scales (kE4M3T only)
   const float* v_scale;
-  int num_kv_heads, kvh;
-  int64_t page_stride, token_stride, head_off;
+  int num_kv_heads, kvh;  // KV heads of the pool; this workgroup's (first) head
+  int64_t page_stride, token_stride, head_stride, head_off;
   int log2p, pmask, kv_len, q4, j;
   int lim;  // tokens of the item seen by this lane's row (column j of S)
+  // Several heads: the head (0 .. HP-1) of this lane's S rows and V rows, and
+  // whether it differs from the head of the lane's column (scores masked).
+  int head_lane;
+  bool cross;
   // Byte offsets of this lane's first K and V load from the tile's first row
   // (the same for every tile when a tile lies in one page); the other loads
   // add 64 bytes (K) or one token row (V), both wavefront-uniform.
@@ -287,29 +323,37 @@ struct Ctx {
   int64_t vrow_bytes;
 };
 
-// Issue every K and V load of the 16-token sub-tile starting at token t0.
+// Issue every K and V load of the sub-tile starting at token t0.
 // Every lane issues every load on every path: a token past the end of the
 // item reads the item's last token instead (its score is masked to -inf and
 // its P weight is 0, so it never contributes), which keeps the number of loads
 // in flight the same on all paths and lets the next tile's loads overlap this
 // tile's math.
-template <int KV, bool PAGE16, bool FULL>
+template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
+  static_assert(HP == 1 || (PAGE16 && KV != kE4M3T), "head groups: pages >= 16, per-page scales");
+  constexpr int STL = sub_tokens_log2<HP>();
   const int last = c.kv_len - 1;
   constexpr int NK = k_loads<KV>();
   if constexpr (PAGE16) {
     // One page per sub-tile: a wavefront-uniform base plus lane offsets. A
     // sub-tile past the end loads from the last sub-tile's rows (tp.page is
     // that sub-tile's page).
-    const int tb = FULL ? t0 : min(t0, last & ~(kSub - 1));
+    const int tb = FULL ? t0 : min(t0, last & ~(sub_tokens<HP>() - 1));
     const int64_t base =
         kv_bytes<KV>(tp.page * c.page_stride + int64_t(tb & c.pmask) * c.token_stride + c.head_off);
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase + base);
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase + base);
     uint32_t koff = c.koff;
     if constexpr (!FULL) {
-      const int tk = min(t0 + c.j, last) - tb;
-      koff = uint32_t(kv_bytes<KV>(int64_t(tk) * c.token_stride + qk_dim<KV>(0, c.q4, 0)));
+      if constexpr (HP > 1) {  // row j: token j % (16 / HP) of head j / (16 / HP)
+        const int tk = min(t0 + (c.j & ((1 << STL) - 1)), last) - tb;
+        koff = uint32_t(kv_bytes<KV>(int64_t(tk) * c.token_stride + (c.j >> STL) * c.head_stride +
+                                     qk_dim<KV>(0, c.q4, 0)));
+      } else {
+        const int tk = min(t0 + c.j, last) - tb;
+        koff = uint32_t(kv_bytes<KV>(int64_t(tk) * c.token_stride + qk_dim<KV>(0, c.q4, 0)));
+      }
     }
 #pragma unroll
     for (int x = 0; x < NK; ++x) ld.k[x] = bload16<PKD_K_CPOL>(kr, koff + 64 * x, 0);
@@ -320,8 +364,14 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
         voff = c.voff;
         soff = uint32_t(e * c.vrow_bytes);
       } else {
-        const int tv = min(t0 + 4 * c.q4 + e, last) - tb;
-        voff = uint32_t(kv_bytes<KV>(int64_t(tv) * c.token_stride + 8 * c.j));
+        if constexpr (HP > 1) {  // rows 4*q4 + e of head head_lane
+          const int tv = min(t0 + row_token<HP>(c.q4, e), last) - tb;
+          voff = uint32_t(kv_bytes<KV>(int64_t(tv) * c.token_stride + c.head_lane * c.head_stride +
+                                       8 * c.j));
+        } else {
+          const int tv = min(t0 + 4 * c.q4 + e, last) - tb;
+          voff = uint32_t(kv_bytes<KV>(int64_t(tv) * c.token_stride + 8 * c.j));
+        }
         soff = 0;
       }
       if constexpr (wide16<KV>())
@@ -390,14 +440,15 @@ struct TileP {
   TilePages sub[nsub<KV>()];
 };
 
-template <int KV, bool PAGE16, bool FULL>
+template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void issue_tile(Tile<KV>& T, const Ctx& c, int t0, const TileP<KV>& tp) {
+  constexpr int ST = sub_tokens<HP>();
 #pragma unroll
   for (int s = 0; s < nsub<KV>(); ++s) {
-    if (FULL || t0 + kSub * (s + 1) <= c.kv_len)
-      issue_sub<KV, PAGE16, true>(T.sub[s], c, t0 + kSub * s, tp.sub[s]);
+    if (FULL || t0 + ST * (s + 1) <= c.kv_len)
+      issue_sub<KV, PAGE16, true, HP>(T.sub[s], c, t0 + ST * s, tp.sub[s]);
     else
-      issue_sub<KV, PAGE16, false>(T.sub[s], c, t0 + kSub * s, tp.sub[s]);
+      issue_sub<KV, PAGE16, false, HP>(T.sub[s], c, t0 + ST * s, tp.sub[s]);
   }
 }
 
@@ -406,26 +457,26 @@ __device__ inline void issue_tile(Tile<KV>& T, const Ctx& c, int t0, const TileP
 __device__ inline float token_scale(const float* sc, const Ctx& c, const KernelArgs& a, int kvh,
                                     int t) {
   const int tt = min(t, c.kv_len - 1);
-  return sc[int64_t(c.page_ids[tt >> c.log2p]) * a.num_kv_heads + kvh];
+  return sc[int64_t(c.page_ids[tt >> c.log2p]) * c.num_kv_heads + kvh];
 }
 
-// QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens valid).
-template <int KV, bool PAGE16, bool FULL>
-__device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TilePages& tp, const u32x4_t (&qb)[q_ops<KV>()],
-                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
-  // ---- S = K . q^T: lane l gets tokens 4*q4 + r of head j
+// S = K . q^T of one loaded sub-tile: lane l gets tokens 4*q4 + r of head j.
+template <int KV>
+__device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>()]) {
   f32x4_t s = {0.f, 0.f, 0.f, 0.f};
   if constexpr (wide16<KV>()) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) s = mfma<KV>(ld.k[dc], qb[dc], s);
   } else if constexpr (fp4<KV>()) {
+    // two independent accumulation chains (hi and lo parts of q * k_scale)
+    f32x4_t s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
       const u32x4_t kb = e2m1x8_to_bf16x8(ld.k[0][dc]);
-      s = mfma<KV>(kb, qb[dc], s);      // q * k_scale, hi part
-      s = mfma<KV>(kb, qb[4 + dc], s);  // lo part
+      s = mfma<KV>(kb, qb[dc], s);
+      s2 = mfma<KV>(kb, qb[4 + dc], s2);
     }
+    s += s2;
   } else {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -443,29 +494,43 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
       s = mfma<KV>(hi, qb[2 * h + 1], s);
     }
   }
+  return s;
+}
 
-  // ---- scale and mask
+// Scores in log2 units (sm_scale, and e4m3 K scales, applied), -inf past the
+// row's causal limit; `grow` is set when one exceeds the reference max by more
+// than the slack.
+template <int KV, bool PAGE16, bool FULL, int HP>
+__device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const Ctx& c,
+                                  const KernelArgs& a, int kvh, int t0, const TilePages& tp,
+                                  float m_run, float (&sc)[4], bool& grow) {
   float ks = a.sm_scale_log2;
-  if constexpr (KV == kE4M3 && PAGE16) ks *= tp.ks;
-  float sc[4];
-  bool grow = false;
+  if constexpr (KV == kE4M3 && PAGE16) ks *= head_pick<HP>(tp.ks, c.head_lane);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const int t = t0 + 4 * c.q4 + r;
+    const int t = t0 + row_token<HP>(c.q4, r);
     float kr = ks;
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
     if constexpr (KV == kE4M3T) kr = ks * ld.ks[r];
-    const float v = (FULL || t < c.lim) ? s[r] * kr : -INFINITY;
+    const bool ok = (FULL || t < c.lim) && (HP == 1 || !c.cross);
+    const float v = ok ? s[r] * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
   }
+}
 
-  // ---- lazy reference max: p = 2^(s - m) may reach 2^kSlack; only when a
-  // score exceeds that does the wavefront move m (to the exact running max of
-  // each head) and rescale d and O by 2^(m_old - m_new). The first tile always
-  // moves it (m starts at -inf). Results do not depend on m beyond rounding.
+// Lazy reference max: p = 2^(s - m) may reach 2^kSlack; only when a score
+// exceeds that does the wavefront move m (to the exact running max of each
+// head) and rescale d and O by 2^(m_old - m_new). The first tile always moves
+// it (m starts at -inf). Results do not depend on m beyond rounding.
+template <bool FULL, int N>
+__device__ inline void move_max(const float (&sc)[N][4], const Ctx& c, bool grow,
+                                f32x4_t (&acc)[8], float& m_run, float& d_run) {
   if (__any(grow)) {
-    float mt = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    float mt = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+      mt = fmaxf(mt, fmaxf(fmaxf(sc[n][0], sc[n][1]), fmaxf(sc[n][2], sc[n][3])));
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
@@ -482,13 +547,21 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
       for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= ar;
     }
   }
+}
 
-  // ---- P (hi + lo bf16); k-slot e of quarter q4 is token 4*q4 + e
+// P of one sub-tile as hi + lo 16-bit pairs (k-slot e of quarter q4 is token
+// 4*q4 + e), its sum added to d, and e4m3 V scales folded in.
+template <int KV, bool PAGE16, bool FULL, int HP>
+__device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ctx& c,
+                             const KernelArgs& a, int kvh, int t0, const TilePages& tp,
+                             float m_run, float& d_run, uint2& p_hi, uint2& p_lo) {
   float p[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     p[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
-    if constexpr (!FULL) p[e] = sc[e] == -INFINITY ? 0.f : p[e];  // also when m_run = -inf
+    // masked scores give 0, also when m_run = -inf (head pairs mask the
+    // other head's lanes in full tiles too, while m_run is already finite)
+    if constexpr (!FULL) p[e] = sc[e] == -INFINITY ? 0.f : p[e];
     d_run += p[e];
   }
   if constexpr (KV == kE4M3) {
@@ -496,7 +569,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     for (int e = 0; e < 4; ++e) {
       float vs;
       if constexpr (PAGE16)
-        vs = tp.vs;
+        vs = head_pick<HP>(tp.vs, c.head_lane);
       else
         vs = token_scale(a.v_scale, c, a, kvh, t0 + 4 * c.q4 + e);
       p[e] *= vs;
@@ -506,57 +579,170 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
 #pragma unroll
     for (int e = 0; e < 4; ++e) p[e] *= ld.vs[e];
   }
-  uint2 p_hi, p_lo;
   split16<KV>(p[0], p[1], p_hi.x, p_lo.x);
   split16<KV>(p[2], p[3], p_hi.y, p_lo.y);
+}
 
-  // ---- O += P . V, column j of MFMA nc is dim 8*j + nc
+// V as the B operand of P.V for output columns nc: four 16-bit values,
+// V[token 4*q4 + e][dim 8*j + nc] for e = 0..3 (nc is a constant after
+// unrolling).
+template <int KV>
+__device__ inline uint2 v_operand(const Loads<KV>& ld, int nc) {
+  uint2 vb;
+  if constexpr (wide16<KV>()) {
+    const int w = nc >> 1;
+    const bool hi = nc & 1;
+    vb.x = pack_halves(ld.v[0][w], ld.v[1][w], hi);
+    vb.y = pack_halves(ld.v[2][w], ld.v[3][w], hi);
+  } else if constexpr (fp4<KV>()) {
+    // byte nc/2 of each token's word holds dims 8*j + nc (nibble nc&1)
+    const bool hi = nc & 1;
+    uint32_t x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      switch (nc >> 1) {
+        case 0: x[e] = e2m1x2_to_bf16x2<0>(ld.v[e]); break;
+        case 1: x[e] = e2m1x2_to_bf16x2<1>(ld.v[e]); break;
+        case 2: x[e] = e2m1x2_to_bf16x2<2>(ld.v[e]); break;
+        default: x[e] = e2m1x2_to_bf16x2<3>(ld.v[e]); break;
+      }
+    }
+    vb.x = pack_halves(x[0], x[1], hi);
+    vb.y = pack_halves(x[2], x[3], hi);
+  } else {
+    const int w = nc >> 2;           // word of the 8 loaded bytes
+    const bool hiw = (nc >> 1) & 1;  // which byte pair in the word
+    const bool hib = nc & 1;         // which byte of the pair
+    uint32_t x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = e4m3x2_to_bf16x2(w ? ld.v[e].y : ld.v[e].x, hiw);
+    vb.x = pack_halves(x[0], x[1], hib);
+    vb.y = pack_halves(x[2], x[3], hib);
+  }
+  return vb;
+}
+
+#ifndef PKD_FP4_VT
+#define PKD_FP4_VT 1
+#endif
+// e2m1 V of one sub-tile regrouped for P.V: the four token words of a lane
+// (dims 8*j..+8 of tokens 4*q4 + e) interleaved nibble by nibble in pairs of
+// tokens, so that byte b of w[2*h + o] holds dim 8*j + 2*b + o of tokens
+// 2*h (low nibble) and 2*h + 1 (high nibble): one conversion then yields
+// the two bf16 values of a B-operand word.
+struct VPairs {
+  uint32_t w[4];
+};
+__device__ inline VPairs fp4_v_pairs(const uint32_t (&v)[4]) {
+  constexpr uint32_t kLo = 0x0F0F0F0Fu;
+  VPairs r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = v[2 * h], b = v[2 * h + 1];
+    r.w[2 * h] = (a & kLo) | ((b << 4) & ~kLo);      // even dims
+    r.w[2 * h + 1] = ((a >> 4) & kLo) | (b & ~kLo);  // odd dims
+  }
+  return r;
+}
+__device__ inline uint2 fp4_v_operand(const VPairs& vp, int nc) {
+  const int o = nc & 1;
+  uint2 vb;
+  switch (nc >> 1) {
+    case 0: vb.x = e2m1x2_to_bf16x2<0>(vp.w[o]), vb.y = e2m1x2_to_bf16x2<0>(vp.w[2 + o]); break;
+    case 1: vb.x = e2m1x2_to_bf16x2<1>(vp.w[o]), vb.y = e2m1x2_to_bf16x2<1>(vp.w[2 + o]); break;
+    case 2: vb.x = e2m1x2_to_bf16x2<2>(vp.w[o]), vb.y = e2m1x2_to_bf16x2<2>(vp.w[2 + o]); break;
+    default: vb.x = e2m1x2_to_bf16x2<3>(vp.w[o]), vb.y = e2m1x2_to_bf16x2<3>(vp.w[2 + o]); break;
+  }
+  return vb;
+}
+
+// QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens
+// valid); P.V on the k = 16 MFMA.
+template <int KV, bool PAGE16, bool FULL, int HP>
+__device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
+                                    int t0, const TilePages& tp, const u32x4_t (&qb)[q_ops<KV>()],
+                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
+  const f32x4_t s = qk<KV>(ld, qb);
+  float sc[1][4];
+  bool grow = false;
+  scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, m_run, sc[0], grow);
+  move_max<FULL, 1>(sc, c, grow, acc, m_run, d_run);
+  uint2 p_hi, p_lo;
+  probs<KV, PAGE16, FULL, HP>(sc[0], ld, c, a, kvh, t0, tp, m_run, d_run, p_hi, p_lo);
+  // O += P . V, column j of MFMA nc is dim 8*j + nc
 #pragma unroll
   for (int nc = 0; nc < 8; ++nc) {
-    uint2 vb;
-    if constexpr (wide16<KV>()) {
-      const int w = nc >> 1;
-      const bool hi = nc & 1;
-      vb.x = pack_halves(ld.v[0][w], ld.v[1][w], hi);
-      vb.y = pack_halves(ld.v[2][w], ld.v[3][w], hi);
-    } else if constexpr (fp4<KV>()) {
-      // byte nc/2 of each token's word holds dims 8*j + nc (nibble nc&1)
-      const bool hi = nc & 1;
-      uint32_t x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        switch (nc >> 1) {
-          case 0: x[e] = e2m1x2_to_bf16x2<0>(ld.v[e]); break;
-          case 1: x[e] = e2m1x2_to_bf16x2<1>(ld.v[e]); break;
-          case 2: x[e] = e2m1x2_to_bf16x2<2>(ld.v[e]); break;
-          default: x[e] = e2m1x2_to_bf16x2<3>(ld.v[e]); break;
-        }
-      }
-      vb.x = pack_halves(x[0], x[1], hi);
-      vb.y = pack_halves(x[2], x[3], hi);
-    } else {
-      const int w = nc >> 2;           // word of the 8 loaded bytes
-      const bool hiw = (nc >> 1) & 1;  // which byte pair in the word
-      const bool hib = nc & 1;         // which byte of the pair
-      uint32_t x[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = e4m3x2_to_bf16x2(w ? ld.v[e].y : ld.v[e].x, hiw);
-      vb.x = pack_halves(x[0], x[1], hib);
-      vb.y = pack_halves(x[2], x[3], hib);
-    }
+    const uint2 vb = v_operand<KV>(ld, nc);
     acc[nc] = mfma16<KV>(p_hi, vb, acc[nc]);
     acc[nc] = mfma16<KV>(p_lo, vb, acc[nc]);
   }
 }
 
-template <int KV, bool PAGE16, bool FULL>
+// Two consecutive sub-tiles A and B at once: their 32 tokens share one
+// reference-max update and feed P.V on the k = 32 MFMA, whose k-slots
+// 8*q4 + e are token 4*q4 + e of A (e < 4) and 4*q4 + e - 4 of B, so the A
+// and B operands are the two sub-tiles' k = 16 operands side by side (half
+// the P.V instructions of two k = 16 passes).
+template <int KV, bool PAGE16, bool FULL, int HP>
+__device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, const Ctx& c,
+                                    const KernelArgs& a, int kvh, int t0, const TilePages& ta,
+                                    const TilePages& tb, const u32x4_t (&qb)[q_ops<KV>()],
+                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
+  constexpr int ST = sub_tokens<HP>();
+  const f32x4_t sa = qk<KV>(la, qb);
+  const f32x4_t sb = qk<KV>(lb, qb);
+  float sc[2][4];
+  bool grow = false;
+  scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, m_run, sc[0], grow);
+  scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, m_run, sc[1], grow);
+  move_max<FULL, 2>(sc, c, grow, acc, m_run, d_run);
+  uint2 pa_hi, pa_lo, pb_hi, pb_lo;
+  probs<KV, PAGE16, FULL, HP>(sc[0], la, c, a, kvh, t0, ta, m_run, d_run, pa_hi, pa_lo);
+  probs<KV, PAGE16, FULL, HP>(sc[1], lb, c, a, kvh, t0 + ST, tb, m_run, d_run, pb_hi, pb_lo);
+  const u32x4_t p_hi = {pa_hi.x, pa_hi.y, pb_hi.x, pb_hi.y};
+  const u32x4_t p_lo = {pa_lo.x, pa_lo.y, pb_lo.x, pb_lo.y};
+  VPairs vpa, vpb;
+  if constexpr (fp4<KV>() && PKD_FP4_VT) {
+    vpa = fp4_v_pairs(la.v);
+    vpb = fp4_v_pairs(lb.v);
+  }
+#pragma unroll
+  for (int nc = 0; nc < 8; ++nc) {
+    uint2 va, vb;
+    if constexpr (fp4<KV>() && PKD_FP4_VT) {
+      va = fp4_v_operand(vpa, nc);
+      vb = fp4_v_operand(vpb, nc);
+    } else {
+      va = v_operand<KV>(la, nc);
+      vb = v_operand<KV>(lb, nc);
+    }
+    const u32x4_t v = {va.x, va.y, vb.x, vb.y};
+    acc[nc] = mfma<KV>(p_hi, v, acc[nc]);
+    acc[nc] = mfma<KV>(p_lo, v, acc[nc]);
+  }
+}
+
+#ifndef PKD_PAIR_PV
+#define PKD_PAIR_PV 1
+#endif
+
+template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void process_tile(const Tile<KV>& T, const Ctx& c, const KernelArgs& a, int kvh,
                                     int t0, const TileP<KV>& tp, const u32x4_t (&qb)[q_ops<KV>()],
                                     f32x4_t (&acc)[8], float& m_run, float& d_run) {
+  constexpr int NS = nsub<KV>();
+  constexpr int ST = sub_tokens<HP>();
+  if constexpr (PKD_PAIR_PV && NS % 2 == 0) {
 #pragma unroll
-  for (int s = 0; s < nsub<KV>(); ++s)
-    process_sub<KV, PAGE16, FULL>(T.sub[s], c, a, kvh, t0 + kSub * s, tp.sub[s], qb, acc, m_run,
-                                  d_run);
+    for (int s = 0; s < NS; s += 2)
+      process_pair<KV, PAGE16, FULL, HP>(T.sub[s], T.sub[s + 1], c, a, kvh, t0 + ST * s,
+                                         tp.sub[s], tp.sub[s + 1], qb, acc, m_run, d_run);
+  } else {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      process_sub<KV, PAGE16, FULL, HP>(T.sub[s], c, a, kvh, t0 + ST * s, tp.sub[s], qb, acc,
+                                        m_run, d_run);
+  }
 }
 
 // Page ids (and e4m3 scales) of a block of consecutive tiles of one
@@ -565,17 +751,27 @@ __device__ inline void process_tile(const Tile<KV>& T, const Ctx& c, const Kerne
 template <int KV>
 constexpr int pid_block_tiles() { return 64 / nsub<KV>(); }
 
-template <int KV>
-__device__ inline void load_pid_block(const Ctx& c, const KernelArgs& a, int kvh, int wave,
-                                      int first_tile, int lane, int32_t& pid, float& ks,
-                                      float& vs) {
+struct PidBlock {
+  int32_t pid = 0;
+  float ks[2] = {1.f, 1.f};  // e4m3: the page's scales of the workgroup's KV heads
+  float vs[2] = {1.f, 1.f};
+};
+
+template <int KV, int HP>
+__device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, int lane,
+                                      PidBlock& b) {
+  constexpr int ST = sub_tokens<HP>();
   const int tile = first_tile + lane / nsub<KV>();
-  const int t = (wave + kWaves * tile) * tile_tokens<KV>() + kSub * (lane % nsub<KV>());
-  const int tt = min(t, (c.kv_len - 1) & ~(kSub - 1));
-  pid = c.page_ids[tt >> c.log2p];
+  const int t = (wave + kWaves * tile) * tile_tokens<KV, HP>() + ST * (lane % nsub<KV>());
+  const int tt = min(t, (c.kv_len - 1) & ~(ST - 1));
+  b.pid = c.page_ids[tt >> c.log2p];
   if constexpr (KV == kE4M3) {
-    ks = a.k_scale[int64_t(pid) * a.num_kv_heads + kvh];
-    vs = a.v_scale[int64_t(pid) * a.num_kv_heads + kvh];
+    const int64_t idx = int64_t(b.pid) * c.num_kv_heads + c.kvh;
+#pragma unroll
+    for (int h = 0; h < HP; ++h) {
+      b.ks[h] = c.k_scale[idx + h];
+      b.vs[h] = c.v_scale[idx + h];
+    }
   }
 }
 
@@ -583,16 +779,21 @@ __device__ inline void load_pid_block(const Ctx& c, const KernelArgs& a, int kvh
 // 16-token sub-tile of pages >= 16; larger tiles and per-lane page lookups need
 // up to 168 (3 wavefronts per SIMD); row-wise e4m3 scales ride along with the
 // loads and get up to 256 (2 per SIMD, still twice what one workgroup per CU
-// uses). e2m1 keeps four 16-token sub-tiles and the q hi/lo pair in flight
-// and takes the same 256.
-template <int KV, bool PAGE16>
+// uses). e2m1 keeps four sub-tiles and the q hi/lo pair in flight and takes
+// the same 256, as do head pairs (two scales per page for e4m3).
+template <int KV, bool PAGE16, int HP>
 constexpr int waves_per_simd() {
-  return KV == kE4M3T || fp4<KV>() ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
+  return KV == kE4M3T || fp4<KV>() || HP > 1 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
 }
 
-template <int KV, int G, bool PAGE16>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16>()))) void decode_mfma_kernel(KernelArgs a) {
+// G: S columns (query rows) per workgroup. HP = 2: the workgroup's "KV head"
+// kvh of the launch is a pair of KV heads 2*kvh, 2*kvh + 1 with G / 2 query
+// heads each (the launch passes num_kv_heads / 2 and group_log2 + 1, so the
+// epilogue and the merge address query heads as usual).
+template <int KV, int G, bool PAGE16, int HP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16, HP>()))) void decode_mfma_kernel(KernelArgs a) {
   static_assert(G >= 1 && G <= 16, "at most 16 query rows per KV head");
+  static_assert(HP == 1 || (G >= HP && PAGE16), "head groups: HP heads' rows, pages >= 16");
   __shared__ WaveStates<G, kD> st;
 
   int item, kvh;
@@ -608,11 +809,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   c.page_ids = a.indices + it.page_begin;
   c.k_scale = a.k_scale;
   c.v_scale = a.v_scale;
-  c.num_kv_heads = a.num_kv_heads;
-  c.kvh = kvh;
+  c.num_kv_heads = a.num_kv_heads * HP;
+  c.kvh = kvh * HP;  // first (or only) KV head of this workgroup
   c.page_stride = a.page_stride;
   c.token_stride = a.token_stride;
-  c.head_off = int64_t(kvh) * a.head_stride;
+  c.head_stride = a.head_stride;
+  c.head_off = int64_t(c.kvh) * a.head_stride;
   c.log2p = a.page_size_log2;
   c.pmask = (1 << a.page_size_log2) - 1;
   c.kv_len = it.kv_len;
@@ -623,8 +825,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   const int hh = c.j & ((1 << a.group_log2) - 1);
   const bool row_ok = c.j < G && qi < it.q_len;
   c.lim = row_ok ? min(it.kv_len, it.visible + qi) : it.kv_len;
-  c.koff = uint32_t(kv_bytes<KV>(int64_t(c.j) * a.token_stride + qk_dim<KV>(0, c.q4, 0)));
-  c.voff = uint32_t(kv_bytes<KV>(int64_t(4 * c.q4) * a.token_stride + 8 * c.j));
+  // Head pairs: the column's head is hh / (G / 2); the lane's rows' head q4 / 2.
+  // Several heads: the column's head is hh / (query heads per KV head).
+  constexpr int HPL = HP == 1 ? 0 : 1;
+  constexpr int STL = sub_tokens_log2<HP>();
+  const int col_head = hh >> (a.group_log2 - HPL);
+  c.head_lane = row_head<HP>(c.q4);
+  c.cross = HP > 1 && c.head_lane != col_head;
+  if constexpr (HP > 1) {
+    c.koff = uint32_t(kv_bytes<KV>(int64_t(c.j & ((1 << STL) - 1)) * a.token_stride +
+                                   (c.j >> STL) * a.head_stride + qk_dim<KV>(0, c.q4, 0)));
+    c.voff = uint32_t(kv_bytes<KV>(int64_t(row_token<HP>(c.q4, 0)) * a.token_stride +
+                                   c.head_lane * a.head_stride + 8 * c.j));
+  } else {
+    c.koff = uint32_t(kv_bytes<KV>(int64_t(c.j) * a.token_stride + qk_dim<KV>(0, c.q4, 0)));
+    c.voff = uint32_t(kv_bytes<KV>(int64_t(4 * c.q4) * a.token_stride + 8 * c.j));
+  }
   c.vrow_bytes = kv_bytes<KV>(a.token_stride);
 
   // q^T as the B operand of S = K.q^T: column j = row j (zero beyond the block).
@@ -639,7 +855,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
       if (row_ok) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
       if constexpr (fp4<KV>()) {
         // q * k_scale over this step's eight dims, as hi + lo bf16
-        const float* ksp = a.k_scale + int64_t(kvh) * kD + qk_dim<KV>(dc, c.q4, 0);
+        const float* ksp = a.k_scale + int64_t(c.kvh + col_head) * kD + qk_dim<KV>(dc, c.q4, 0);
         const float4 s0 = *reinterpret_cast<const float4*>(ksp);
         const float4 s1 = *reinterpret_cast<const float4*>(ksp + 4);
         const float ksv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
@@ -668,44 +884,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   float d_run = 0.f;        // head j: sum of p over this lane's tokens
 
   // Tiles of this wavefront: tokens [(wave + 4i) * TT, +TT) for i < n, with
-  // TT = tile_tokens<KV>().
-  constexpr int TT = tile_tokens<KV>();
+  // TT = tile_tokens<KV, HP>().
+  constexpr int TT = tile_tokens<KV, HP>();
   constexpr int NS = nsub<KV>();
   constexpr int kBlk = pid_block_tiles<KV>();
   const int first = wave * TT;
   const int n = first < c.kv_len ? (c.kv_len - first + kWaves * TT - 1) / (kWaves * TT) : 0;
   if (n > 0) {
-    int32_t pid_cur = 0, pid_next = 0;
-    float ks_cur = 1.f, vs_cur = 1.f, ks_next = 1.f, vs_next = 1.f;
+    PidBlock blk_cur, blk_next;
     if constexpr (PAGE16) {
-      load_pid_block<KV>(c, a, kvh, wave, 0, lane, pid_cur, ks_cur, vs_cur);
-      if (n > kBlk) load_pid_block<KV>(c, a, kvh, wave, kBlk, lane, pid_next, ks_next, vs_next);
+      load_pid_block<KV, HP>(c, wave, 0, lane, blk_cur);
+      if (n > kBlk) load_pid_block<KV, HP>(c, wave, kBlk, lane, blk_next);
     }
+    auto lane_float = [](float x, int slot) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), slot));
+    };
     // Pages of tile i (tiles are issued in order, so the id block only moves forward).
     auto pages_of = [&](int i) {
       TileP<KV> tp;
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
         tp.sub[s2].page = 0;
-        tp.sub[s2].ks = tp.sub[s2].vs = 1.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) tp.sub[s2].ks[h] = tp.sub[s2].vs[h] = 1.f;
       }
       if constexpr (PAGE16) {
         if (i > 0 && (i % kBlk) == 0) {
-          pid_cur = pid_next;
-          ks_cur = ks_next;
-          vs_cur = vs_next;
-          if (i + kBlk < n)
-            load_pid_block<KV>(c, a, kvh, wave, i + kBlk, lane, pid_next, ks_next, vs_next);
+          blk_cur = blk_next;
+          if (i + kBlk < n) load_pid_block<KV, HP>(c, wave, i + kBlk, lane, blk_next);
         }
 #pragma unroll
         for (int s2 = 0; s2 < NS; ++s2) {
           const int slot = (i % kBlk) * NS + s2;
-          tp.sub[s2].page = __builtin_amdgcn_readlane(pid_cur, slot);
+          tp.sub[s2].page = __builtin_amdgcn_readlane(blk_cur.pid, slot);
           if constexpr (KV == kE4M3) {
-            tp.sub[s2].ks = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ks_cur), slot));
-            tp.sub[s2].vs = __builtin_bit_cast(
-                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, vs_cur), slot));
+#pragma unroll
+            for (int h = 0; h < HP; ++h) {
+              tp.sub[s2].ks[h] = lane_float(blk_cur.ks[h], slot);
+              tp.sub[s2].vs[h] = lane_float(blk_cur.vs[h], slot);
+            }
           }
         }
       }
@@ -720,35 +937,41 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     // it is issued and computed after the loop.
     Tile<KV> cur, nxt;
     TileP<KV> pc = pages_of(0), pn;
+    const int h0 = c.kvh;
     if (n == 1) {
-      issue_tile<KV, PAGE16, false>(cur, c, tok(0), pc);
-      process_tile<KV, PAGE16, false>(cur, c, a, kvh, tok(0), pc, qb, acc, m_run, d_run);
+      issue_tile<KV, PAGE16, false, HP>(cur, c, tok(0), pc);
+      process_tile<KV, PAGE16, false, HP>(cur, c, a, h0, tok(0), pc, qb, acc, m_run, d_run);
     } else {
-      issue_tile<KV, PAGE16, true>(cur, c, tok(0), pc);
+      issue_tile<KV, PAGE16, true, HP>(cur, c, tok(0), pc);
       for (int i = 0; i + 2 < n; ++i) {
         pn = pages_of(i + 1);
-        issue_tile<KV, PAGE16, true>(nxt, c, tok(i + 1), pn);
-        process_tile<KV, PAGE16, true>(cur, c, a, kvh, tok(i), pc, qb, acc, m_run, d_run);
+        issue_tile<KV, PAGE16, true, HP>(nxt, c, tok(i + 1), pn);
+        process_tile<KV, PAGE16, true, HP>(cur, c, a, h0, tok(i), pc, qb, acc, m_run, d_run);
         cur = nxt;
         pc = pn;
       }
       pn = pages_of(n - 1);
-      issue_tile<KV, PAGE16, false>(nxt, c, tok(n - 1), pn);
-      process_tile<KV, PAGE16, true>(cur, c, a, kvh, tok(n - 2), pc, qb, acc, m_run, d_run);
-      process_tile<KV, PAGE16, false>(nxt, c, a, kvh, tok(n - 1), pn, qb, acc, m_run, d_run);
+      issue_tile<KV, PAGE16, false, HP>(nxt, c, tok(n - 1), pn);
+      process_tile<KV, PAGE16, true, HP>(cur, c, a, h0, tok(n - 2), pc, qb, acc, m_run, d_run);
+      process_tile<KV, PAGE16, false, HP>(nxt, c, a, h0, tok(n - 1), pn, qb, acc, m_run, d_run);
     }
   }
 
   // ---- per-wavefront state -> shared memory
   const int q4 = c.q4, j = c.j;
   if constexpr (fp4<KV>()) {
-    // V channel scales: column j of MFMA nc is dim 8*j + nc
-    const float* vsp = a.v_scale + int64_t(kvh) * kD + 8 * j;
-    const float4 s0 = *reinterpret_cast<const float4*>(vsp);
-    const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
-    const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    // V channel scales: column j of MFMA nc is dim 8*j + nc, of the KV head
+    // of O row 4*q4 + r (row / query heads per KV head, within the group)
 #pragma unroll
-    for (int nc = 0; nc < 8; ++nc) acc[nc] *= vsv[nc];
+    for (int r = 0; r < 4; ++r) {
+      const int hsel = min((4 * q4 + r) >> (a.group_log2 - HPL), HP - 1);
+      const float* vsp = a.v_scale + int64_t(c.kvh + hsel) * kD + 8 * j;
+      const float4 s0 = *reinterpret_cast<const float4*>(vsp);
+      const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
+      const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+      for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= vsv[nc];
+    }
   }
   d_run += __shfl_xor(d_run, 16, 64);
   d_run += __shfl_xor(d_run, 32, 64);
@@ -771,20 +994,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 template <int KV, bool P16>
 DecodeFn pick_group(int g) {
   switch (g) {
-    case 1: return decode_mfma_kernel<KV, 1, P16>;
-    case 2: return decode_mfma_kernel<KV, 2, P16>;
-    case 4: return decode_mfma_kernel<KV, 4, P16>;
-    case 8: return decode_mfma_kernel<KV, 8, P16>;
-    case 16: return decode_mfma_kernel<KV, 16, P16>;
+    case 1: return decode_mfma_kernel<KV, 1, P16, 1>;
+    case 2: return decode_mfma_kernel<KV, 2, P16, 1>;
+    case 4: return decode_mfma_kernel<KV, 4, P16, 1>;
+    case 8: return decode_mfma_kernel<KV, 8, P16, 1>;
+    case 16: return decode_mfma_kernel<KV, 16, P16, 1>;
+    default: return nullptr;
+  }
+}
+
+// Pairs of KV heads per workgroup: `cols` = 2 x query heads per KV head.
+template <int KV>
+DecodeFn pick_pair(int cols) {
+  switch (cols) {
+    case 2: return decode_mfma_kernel<KV, 2, true, 2>;
+    case 4: return decode_mfma_kernel<KV, 4, true, 2>;
+    case 8: return decode_mfma_kernel<KV, 8, true, 2>;
+    case 16: return decode_mfma_kernel<KV, 16, true, 2>;
     default: return nullptr;
   }
 }
 
 }  // namespace
 
-DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size) {
+DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size, int hp) {
   if (head_dim != kD) return nullptr;
   const bool p16 = page_size >= 16;
+  if (hp == 2) {
+    if (!p16) return nullptr;
+    switch (kv_dtype) {
+      case kBF16: return pick_pair<kBF16>(rows);
+      case kE4M3: return pick_pair<kE4M3>(rows);
+      case kF16: return pick_pair<kF16>(rows);
+      case kE2M1: return pick_pair<kE2M1>(rows);
+      default: return nullptr;
+    }
+  }
+  if (hp != 1) return nullptr;
   switch (kv_dtype) {
     case kBF16: return p16 ? pick_group<kBF16, true>(rows) : pick_group<kBF16, false>(rows);
     case kE4M3: return p16 ? pick_group<kE4M3, true>(rows) : pick_group<kE4M3, false>(rows);

@@ -28,10 +28,15 @@ static bool mfma_form(int kv_dtype, int q_kind) {
 }
 
 static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_kind,
-                       int page_size) {
+                       int page_size, int hp = 1) {
   if ((group & (group - 1)) || rows < group || rows % group) return nullptr;
+  if (hp > 1)
+    return mfma_form(kv_dtype, q_kind) && rows == group && hp * rows <= 16
+               ? mfma_decode_kernel(kv_dtype, head_dim, hp * rows, page_size, hp)
+               : nullptr;
   if (mfma_form(kv_dtype, q_kind)) {
-    if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size)) return f;
+    if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size, 1))
+      return f;
   }
   // The vector-ALU kernel: one token per request, fp32 or bf16 q over fp32,
   // bf16 or e4m3 KV (per-page scales).
@@ -63,11 +68,38 @@ bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_kin
 
 bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size) {
   return mfma_form(kv_dtype, q_kind) && rows >= group &&
-         mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size) != nullptr;
+         mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size, 1) != nullptr;
+}
+
+// KV heads per workgroup, per form (1, or 2: a pair). A pair reads a token's
+// rows of both heads as one contiguous run (e2m1 rows are 64 bytes at
+// head_dim 128, e4m3 128, bf16/fp16 256) and halves the workgroup count;
+// measured on MI355X with one workgroup per CU, pairs are faster for bf16
+// (7-8%), fp16 and e4m3 (4%) and even for e2m1.
+#ifndef PKD_HEADS_E2M1
+#define PKD_HEADS_E2M1 2
+#endif
+#ifndef PKD_HEADS_E4M3
+#define PKD_HEADS_E4M3 2
+#endif
+#ifndef PKD_HEADS_BF16
+#define PKD_HEADS_BF16 2
+#endif
+int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_kind,
+                        int page_size, int num_kv_heads) {
+  const int hp = kv_dtype == kE2M1 ? PKD_HEADS_E2M1
+                 : kv_dtype == kE4M3 ? PKD_HEADS_E4M3
+                 : (kv_dtype == kBF16 || kv_dtype == kF16) ? PKD_HEADS_BF16
+                                                           : 1;
+  if (hp != 2 || rows != group || num_kv_heads % 2 || 2 * group > 16) return 1;
+  return choose(kv_dtype, head_dim, group, rows, q_kind, page_size, 2) ? 2 : 1;
 }
 
 hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
-  DecodeFn fn = choose(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_kind, 1 << L.page_size_log2);
+  const int hp = L.heads_per_wg;
+  if ((hp != 1 && hp != 2) || L.num_kv_heads % hp) return hipErrorInvalidValue;
+  DecodeFn fn =
+      choose(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_kind, 1 << L.page_size_log2, hp);
   if (!fn) return hipErrorInvalidValue;
   KernelArgs a;
   a.q = L.q;
@@ -90,14 +122,15 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.part_md = L.part_md;
   a.num_items = L.num_items;
   a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1) ? 8 : 1;
-  a.num_kv_heads = L.num_kv_heads;
+  // A pair of KV heads is one workgroup "head" of 2 x group query heads.
+  a.num_kv_heads = L.num_kv_heads / hp;
   a.num_qo_heads = L.num_qo_heads;
-  a.group_log2 = ilog2(L.group);
+  a.group_log2 = ilog2(L.group * hp);
   a.page_size_log2 = L.page_size_log2;
   a.sm_scale_log2 = L.sm_scale_log2;
   a.q_kind = L.q_kind;
   a.out_kind = L.out_kind;
-  const unsigned grid = decode_grid_size(L.num_items, L.num_kv_heads, a.xcd_group);
+  const unsigned grid = decode_grid_size(L.num_items, a.num_kv_heads, a.xcd_group);
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, L.wgs_cap, &lds); e != hipSuccess) return e;
   hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, a);
@@ -105,8 +138,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
 }
 
 hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_kind,
-                            int page_size, int wgs_cap, int* wgs_per_cu) {
-  DecodeFn fn = choose(kv_dtype, head_dim, group, rows, q_kind, page_size);
+                            int page_size, int heads_per_wg, int wgs_cap, int* wgs_per_cu) {
+  DecodeFn fn = choose(kv_dtype, head_dim, group, rows, q_kind, page_size, heads_per_wg);
   if (!fn) return hipErrorInvalidValue;
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, wgs_cap, &lds); e != hipSuccess) return e;

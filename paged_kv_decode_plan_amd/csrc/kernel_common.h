@@ -227,8 +227,9 @@ __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelA
 }
 
 // Kernel selection (each translation unit provides its family). `rows` is the
-// number of (query token, query head) rows one workgroup handles.
+// number of (query token, query head) rows one workgroup handles, over `hp`
+// KV heads (2: a pair of KV heads per workgroup).
 DecodeFn valu_decode_kernel(int kv_dtype, int head_dim, int group);
-DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size);
+DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size, int hp);
 
 }  // namespace pkd

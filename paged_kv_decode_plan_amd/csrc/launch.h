@@ -44,6 +44,7 @@ struct DecodeLaunch {
   int head_dim = 0;
   int group = 0;
   int rows = 0;  // query rows per work item and KV head: group x query tokens per item
+  int heads_per_wg = 1;  // KV heads per decode workgroup (see decode_heads_per_wg)
   int wgs_cap = 0;  // at most this many decode workgroups per compute unit (0: no cap)
   int num_items = 0;
   int num_kv_heads = 0;
@@ -84,10 +85,16 @@ struct DecodeLaunch {
 // tokens per request) is served by the MFMA kernel only.
 bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size);
 bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size);
+// KV heads one decode workgroup handles: 2 (a pair, read as one contiguous
+// run per token) on the MFMA path where the KV head count is even and the
+// pair's query heads fit the 16 MFMA columns (one query token per request,
+// pages of at least 16 tokens); otherwise 1.
+int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_kind,
+                        int page_size, int num_kv_heads);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
 hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
 hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_kind,
-                            int page_size, int wgs_cap, int* wgs_per_cu);
+                            int page_size, int heads_per_wg, int wgs_cap, int* wgs_per_cu);
 
 struct MergeStatesLaunch {
   int64_t rows = 0;

@@ -41,6 +41,23 @@ def test_small_ragged_fp4(g, split):
     compare(out, lse, ref_out, ref_lse, "e2m1")
 
 
+# KV heads per workgroup: a pair where the KV head count is even
+HEADS_PER_WG = {1: 1, 2: 2, 3: 1, 4: 2, 8: 2}
+
+
+@pytest.mark.parametrize("hkv", sorted(HEADS_PER_WG))
+def test_fp4_kv_head_counts(hkv):
+    """One KV head or a pair of KV heads per workgroup, against the oracle."""
+    w = custom_workload(len(LENS), 4 * hkv, hkv, 128, 16, "e2m1", "bf16", LENS,
+                        pool_pages=_pool(LENS, 16, 5))
+    case = host_case(w, 900 + hkv, poison=True)
+    ref_out, ref_lse = oracle_for(case)
+    for kw in ({}, dict(slots=64, balance=1, min_chunk_pages=1)):
+        out, lse, info = run_hip(to_device(case), **kw)
+        assert info["units_per_item"] == hkv // HEADS_PER_WG[hkv]
+        compare(out, lse, ref_out, ref_lse, "e2m1")
+
+
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64])
 def test_fp4_page_sizes(P):
     lens = [1, P, P + 1, 3 * P + 5, 257]

@@ -53,6 +53,24 @@ def test_small_ragged_matches_oracle(kv, d, g, qd, split):
     compare(out, lse, ref_out, ref_lse, kv)
 
 
+@pytest.mark.parametrize("kv,qd", [("bf16", "bf16"), ("e4m3", "bf16"), ("f16", "f16")])
+@pytest.mark.parametrize("hkv", [3, 4])
+@pytest.mark.parametrize("split", ["auto", "forced"])
+def test_one_or_two_kv_heads_per_workgroup(kv, qd, hkv, split):
+    """An odd KV head count keeps one KV head per workgroup; an even one may
+    take pairs (per form): both against the oracle."""
+    lens = [1, 15, 16, 17, 100, 333, 700, 64, 3]
+    w = custom_workload(len(lens), 4 * hkv, hkv, 128, 16, kv, qd, lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 5)
+    case = host_case(w, 300 + hkv, poison=True)
+    _say("kv heads", kv, hkv, split)
+    ref_out, ref_lse = oracle_for(case)
+    kw = dict(slots=8, balance=1, min_chunk_pages=1) if split == "forced" else {}
+    out, lse, info = run_hip(to_device(case), **kw)
+    assert info["units_per_item"] in (hkv, hkv // 2)
+    compare(out, lse, ref_out, ref_lse, kv)
+
+
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 @pytest.mark.parametrize("P", [1, 2, 4, 8, 16, 32, 64, 128])
 def test_page_sizes(P, kv):

@@ -247,3 +247,18 @@ def test_e2m1_plans_match_the_oracle():
     last = (lens - (npg - 1) * P).astype(np.int32)
     for g in (1, 4, 16):
         _assert_same(*_both(indptr, last, P, 8, 256, 1, 16, hq=8 * g, kv="e2m1"))
+
+
+@pytest.mark.parametrize("hkv,g,P,qo,want", [
+    (8, 4, 16, None, 4),     # pairs of KV heads: 4 workgroups per item
+    (2, 8, 16, None, 1),
+    (3, 4, 16, None, 3),     # odd KV head count: one head per workgroup
+    (2, 16, 16, None, 2),    # 2 x 16 query heads exceed the 16 MFMA columns
+    (8, 4, 8, None, 8),      # pages below 16 tokens
+    (8, 4, 16, [0, 2, 3], 8),  # several query tokens per request
+])
+@pytest.mark.parametrize("kv", ["e2m1", "e4m3"])
+def test_head_pair_workgroups_per_item(kv, hkv, g, P, qo, want):
+    info, *_ = pk.plan_partition([0, 3, 5], [5, P], hkv * g, hkv, 128, P, kv_dtype=kv,
+                                 q_dtype="bf16", qo_indptr=qo)
+    assert info["units_per_item"] == want
