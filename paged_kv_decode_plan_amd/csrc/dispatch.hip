@@ -13,6 +13,11 @@
 
 namespace pkd {
 
+// Workgroup-id grouping (see decode_block) for 16-bit KV.
+#ifndef PKD_XCD_GROUP_16BIT
+#define PKD_XCD_GROUP_16BIT 1
+#endif
+
 static int pow2_ceil(int x) {
   int p = 1;
   while (p < x) p <<= 1;
@@ -121,7 +126,9 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.num_items = L.num_items;
-  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1) ? 8 : 1;
+  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1)
+                    ? 8
+                    : PKD_XCD_GROUP_16BIT;
   // A pair of KV heads is one workgroup "head" of 2 x group query heads.
   a.num_kv_heads = L.num_kv_heads / hp;
   a.num_qo_heads = L.num_qo_heads;
