@@ -331,7 +331,7 @@ struct Ctx {
 // tile's math.
 template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const TilePages& tp) {
-  static_assert(HP == 1 || (PAGE16 && KV != kE4M3T), "head groups: pages >= 16, per-page scales");
+  static_assert(HP == 1 || PAGE16, "head pairs: pages >= 16");
   constexpr int STL = sub_tokens_log2<HP>();
   const int last = c.kv_len - 1;
   constexpr int NK = k_loads<KV>();
@@ -407,12 +407,14 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
     }
   }
   if constexpr (KV == kE4M3T) {
-    // Row-wise scales [pages, Hkv, page_size] of this lane's four tokens
-    // 4*(l/16)..+4: with 16-token sub-tiles in one page they are four
-    // consecutive floats (one 16-byte load each for K and V); otherwise one
-    // lookup per token, clamped like the rows themselves.
+    // Row-wise scales [pages, Hkv, page_size] of this lane's four tokens (of
+    // its KV head): with sub-tiles in one page they are four consecutive
+    // floats (one 16-byte load each for K and V); otherwise one lookup per
+    // token, clamped like the rows themselves.
+    const int64_t hrow = c.kvh + c.head_lane;
     if constexpr (PAGE16 && FULL) {
-      const int64_t idx = ((tp.page * c.num_kv_heads + c.kvh) << c.log2p) + (t0 & c.pmask) + 4 * c.q4;
+      const int64_t idx =
+          ((tp.page * c.num_kv_heads + hrow) << c.log2p) + (t0 & c.pmask) + row_token<HP>(c.q4, 0);
       const float4 k4 = *reinterpret_cast<const float4*>(c.k_scale + idx);
       const float4 v4 = *reinterpret_cast<const float4*>(c.v_scale + idx);
       ld.ks[0] = k4.x, ld.ks[1] = k4.y, ld.ks[2] = k4.z, ld.ks[3] = k4.w;
@@ -420,9 +422,9 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int t = min(t0 + 4 * c.q4 + e, last);
+        const int t = min(t0 + row_token<HP>(c.q4, e), last);
         const int64_t page = PAGE16 ? tp.page : int64_t(c.page_ids[t >> c.log2p]);
-        const int64_t idx = ((page * c.num_kv_heads + c.kvh) << c.log2p) + (t & c.pmask);
+        const int64_t idx = ((page * c.num_kv_heads + hrow) << c.log2p) + (t & c.pmask);
         ld.ks[e] = c.k_scale[idx];
         ld.vs[e] = c.v_scale[idx];
       }
@@ -1025,6 +1027,7 @@ DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size,
     switch (kv_dtype) {
       case kBF16: return pick_pair<kBF16>(rows);
       case kE4M3: return pick_pair<kE4M3>(rows);
+      case kE4M3T: return pick_pair<kE4M3T>(rows);
       case kF16: return pick_pair<kF16>(rows);
       case kE2M1: return pick_pair<kE2M1>(rows);
       default: return nullptr;

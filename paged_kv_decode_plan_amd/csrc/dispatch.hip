@@ -93,7 +93,7 @@ bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kin
 int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                         int page_size, int num_kv_heads) {
   const int hp = kv_dtype == kE2M1 ? PKD_HEADS_E2M1
-                 : kv_dtype == kE4M3 ? PKD_HEADS_E4M3
+                 : (kv_dtype == kE4M3 || kv_dtype == kE4M3T) ? PKD_HEADS_E4M3
                  : (kv_dtype == kBF16 || kv_dtype == kF16) ? PKD_HEADS_BF16
                                                            : 1;
   if (hp != 2 || rows != group || num_kv_heads % 2 || 2 * group > 16) return 1;
