@@ -404,7 +404,15 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   p->launch_items = int32_t(lay_items);
   p->launch_tasks = fixed ? caps[1] : int32_t(n_tasks);
   p->num_blocks = int32_t(n_blocks);
-  p->fuse_ok = !fixed && max_chunks <= kFuseChunks;
+  // Folding costs every split workgroup a device-scope release fence (and the
+  // last one an acquire), which on MI355X write back and invalidate its XCD's
+  // L2: cheap for a few workgroups (a lone long request: 25 -> 21.6 us), ruinous
+  // for hundreds (64 requests of 512 tokens split in two: 33 -> 109 us).
+  constexpr size_t kFuseMaxWgs = 64;
+  size_t split_wgs = 0;
+  for (const auto& it : part.items)
+    if (it.partial_slot >= 0) split_wgs += size_t(a->num_kv_heads / heads_per_wg);
+  p->fuse_ok = !fixed && max_chunks <= kFuseChunks && split_wgs <= kFuseMaxWgs;
   p->off_items = 256;
   p->off_split = align256(p->off_items + lay_items * sizeof(pkd::DeviceItem));
   p->off_blocks = align256(p->off_split + lay_tasks * sizeof(pkd::MergeTask));
@@ -584,8 +592,9 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   L.block_merges = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_blocks);
   L.counters = reinterpret_cast<int32_t*>(ws + p->off_counters);
   // A whole run of an exact plan whose split requests have at most
-  // kFuseChunks chunks folds the merge into the decode kernel (one launch
-  // instead of two: what matters when the batch is small). Longer folds run
+  // kFuseChunks chunks, over at most kFuseMaxWgs workgroups, folds the merge
+  // into the decode kernel (one launch instead of two: what matters when the
+  // batch is small). Longer folds run
   // faster in the separate merge kernel, which spreads them over many more
   // workgroups; fixed-capacity plans keep both launches so that one captured
   // graph fits every plan; the stages alone always keep them apart.

@@ -262,3 +262,17 @@ def test_head_pair_workgroups_per_item(kv, hkv, g, P, qo, want):
     info, *_ = pk.plan_partition([0, 3, 5], [5, P], hkv * g, hkv, 128, P, kv_dtype=kv,
                                  q_dtype="bf16", qo_indptr=qo)
     assert info["units_per_item"] == want
+
+
+def test_many_split_workgroups_keep_the_merge_kernel():
+    """The merge folds into the decode kernel only for a few split workgroups
+    (each pays device-scope fences); a batch of split requests keeps the
+    separate merge kernel."""
+    P = 16
+    few = pk.plan_partition([0, 32], [16], 4, 4, 64, P, kv_dtype="f32", q_dtype="f32",
+                            slots=1024, min_chunk_pages=16)[0]
+    assert few["num_split_requests"] == 1 and few["merge_folded"] == 1
+    indptr = np.arange(0, 64 * 32 + 1, 32, dtype=np.int32)
+    many = pk.plan_partition(indptr, [16] * 64, 32, 8, 128, P, kv_dtype="bf16", q_dtype="bf16",
+                             slots=1024, min_chunk_pages=16)[0]
+    assert many["num_split_requests"] == 64 and many["merge_folded"] == 0
