@@ -13,14 +13,19 @@ The rule adopted (a reading; the design doc lists it):
 1. ``n_r = indptr[r+1] - indptr[r]`` pages and
    ``L_r = (n_r - 1) * P + last_page_len[r]`` tokens per request.
 2. With ``S = sum_r n_r``, ``N = max_r n_r``, ``H`` work units per item (the
-   workgroups one item runs as: one per KV head) and ``slots`` workgroups
-   resident on the device at once:
+   workgroups one item runs as: one per KV head, or per pair of KV heads),
+   ``slots`` workgroups resident on the device at once and ``slots_per_cu``
+   of them on one compute unit:
 
    * a batch of near-equal requests (``8 * N * B <= 9 * S``: the longest is
-     within 1/8 of the mean) that already yields at least half the resident
-     slots in work units (``2 * B * H >= slots``) is not split: ``C = N``;
-     splitting it would add partial states and a merge without evening
-     anything out;
+     within 1/8 of the mean) is cut into ``k`` chunks per request,
+     ``C = ceil(N / k)``, where ``k`` in ``[1, max(1, N // C_min)]``
+     minimises ``ceil(B * H * k / (CUs * balance)) * (ceil(N / k) + 2 * C_min)``
+     (the number of waves of equal work units over the compute units,
+     ``CUs = ceil(slots / slots_per_cu)``, times one unit's pages plus
+     ``2 * C_min`` pages standing for a workgroup's start and its share of
+     the merge), the smallest such ``k`` on ties: equal requests that already
+     fill the device stay whole, fewer are cut just enough to fill it;
    * otherwise ``C = min(N, max(C_min, ceil(S * H / (slots * balance))))``:
      no work unit is longer than ``1/balance`` of a slot's fair share of the
      batch, nor shorter than ``C_min`` pages (which bounds the partial-state
@@ -70,7 +75,7 @@ ITEM_COLUMNS = ("request", "page_begin", "page_end", "kv_len", "partial_slot", "
 
 def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
          balance: int, min_chunk_pages: int, qo_indptr=None, queries_per_item: int = 1,
-         causal: bool = True) -> dict:
+         causal: bool = True, slots_per_cu: int = 1) -> dict:
     indptr = [int(x) for x in indptr]
     last = [int(x) for x in last_page_len]
     B = len(last)
@@ -98,8 +103,15 @@ def plan(indptr, last_page_len, page_size: int, num_kv_heads: int, slots: int,
     units = sum(U)
     S = sum(n[r] * U[r] for r in range(B))
     N = max(n)
-    if 8 * N * units <= 9 * S and 2 * units * num_kv_heads >= slots:
-        C = N
+    if 8 * N * units <= 9 * S:
+        best_k, best_cost = 1, None
+        for k in range(1, max(1, N // min_chunk_pages) + 1):
+            waves = _ceil_div(units * num_kv_heads * k,
+                              _ceil_div(slots, max(1, slots_per_cu)) * balance)
+            cost = waves * (_ceil_div(N, k) + 2 * min_chunk_pages)
+            if best_cost is None or cost < best_cost:
+                best_k, best_cost = k, cost
+        C = _ceil_div(N, best_k)
     else:
         cap = _ceil_div(S * num_kv_heads, slots * balance)
         C = min(N, max(min_chunk_pages, cap))

@@ -314,12 +314,14 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     return fail(PKD_ERR_INVALID_ARGUMENT, "sm_scale must be finite and >= 0");
 
   int slots = a->slots;
+  int slots_per_cu = 1;  // explicit slots are taken as one per compute unit
   if (slots == 0) {
     int32_t wgs = 0, cus = 0;
     int rc = device_slots(a->device, a->q_dtype, kv_impl, a->head_dim, group, rows,
                           a->page_size, heads_per_wg, wgs_cap, &wgs, &cus);
     if (rc != PKD_OK) return rc;
     slots = wgs * cus;
+    slots_per_cu = std::max(1, int(wgs));
     if (slots < 1) return fail(PKD_ERR_HIP, "device reports no resident workgroups");
   }
   pkd::PartitionInput pin;
@@ -332,6 +334,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   pin.page_size = a->page_size;
   pin.units_per_item = a->num_kv_heads / heads_per_wg;
   pin.slots = slots;
+  pin.slots_per_cu = slots_per_cu;
   pin.balance = a->balance ? a->balance : 1;
   pin.min_chunk_pages = a->min_chunk_pages ? a->min_chunk_pages : (256 + a->page_size - 1) / a->page_size;
 

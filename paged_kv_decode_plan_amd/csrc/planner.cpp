@@ -65,15 +65,32 @@ std::string build_partition(const PartitionInput& in, Partition* out) {
   if (total_pages > INT32_MAX) return "page table longer than 2^31 entries";
   if (in.qo_indptr && int64_t(in.qo_indptr[B]) > INT32_MAX / 2) return "too many query rows";
 
-  // A batch of near-equal requests that already yields at least half the
-  // resident slots in work units is left whole: splitting it would only add
-  // partial states and a merge. Otherwise bound every work unit by
-  // 1/balance of a resident slot's fair share (and by min_chunk_pages below).
+  // A batch of near-equal requests is cut into k equal chunks per request,
+  // k chosen to minimise the makespan of its work units over the compute
+  // units: waves(k) = ceil(units * k / (CUs * balance)), each costing a chunk
+  // (ceil(N / k) pages) plus a fixed 2 * min_chunk_pages for starting a
+  // workgroup (and its share of the merge); ties keep the smaller k, and no chunk is
+  // shorter than min_chunk_pages. (Several resident workgroups of one CU
+  // share its bandwidth, so a CU, not a slot, is the machine here.)
+  // Otherwise bound every work unit by 1/balance of a resident slot's fair
+  // share (and by min_chunk_pages below).
   int64_t C;
   const bool near_equal = 8 * max_pages * blocks <= 9 * block_pages;
-  const bool enough_units = 2 * blocks * in.units_per_item >= in.slots;
-  if (near_equal && enough_units) {
-    C = max_pages;
+  if (near_equal) {
+    const int64_t units = blocks * in.units_per_item;
+    const int64_t resident =
+        ceil_div(int64_t(in.slots), std::max<int64_t>(1, in.slots_per_cu)) * in.balance;
+    const int64_t k_max = std::max<int64_t>(1, max_pages / in.min_chunk_pages);
+    int64_t best_k = 1, best_cost = -1;
+    for (int64_t k = 1; k <= k_max; ++k) {
+      const int64_t cost =
+          ceil_div(units * k, resident) * (ceil_div(max_pages, k) + 2 * int64_t(in.min_chunk_pages));
+      if (best_cost < 0 || cost < best_cost) {
+        best_cost = cost;
+        best_k = k;
+      }
+    }
+    C = ceil_div(max_pages, best_k);
   } else {
     const int64_t cap =
         ceil_div(block_pages * in.units_per_item, int64_t(in.slots) * in.balance);

@@ -32,6 +32,7 @@ struct PartitionInput {
   int32_t page_size = 0;
   int32_t units_per_item = 1;  // workgroups launched per item (one per KV head)
   int32_t slots = 1;           // workgroups resident on the device at once
+  int32_t slots_per_cu = 1;    // of which one compute unit holds (slots / this = CUs)
   int32_t balance = 1;
   int32_t min_chunk_pages = 1;
 };
@@ -49,9 +50,12 @@ struct Partition {
 
 // Returns an empty string on success, else a description of what is wrong
 // with the page table. The rule: a batch whose longest request is within 1/8
-// of the mean (8 N B <= 9 S) and that gives at least half the resident slots
-// in work units (2 B units >= slots) is not split (C = N); otherwise the chunk
-// length is
+// of the mean (8 N B <= 9 S) is cut into k chunks per request, C = ceil(N/k),
+// k in [1, max(1, N / min_chunk_pages)] minimising
+//   ceil(B * units * k / (CUs * balance)) * (ceil(N / k) + 2 * min_chunk_pages)
+// (waves of equal work units over the compute units, CUs = slots /
+// slots_per_cu, each costing a chunk plus a workgroup's start), the smallest
+// k on ties; otherwise the chunk length is
 //   C = min(N, max(min_chunk_pages, ceil(S * units / (slots * balance))))
 // so that no work unit exceeds 1/balance of one slot's fair share. Request r
 // becomes ceil(n_r / C) items; items are ordered by descending token count,

@@ -135,15 +135,44 @@ def test_multi_query_partition_invariants(seed):
     assert keys == sorted(keys)
 
 
-def test_uniform_batch_that_fills_the_device_is_not_split():
-    indptr = np.arange(0, 65 * 4, 4, dtype=np.int32)
+def test_uniform_batch_is_cut_to_fill_the_device():
+    """Near-equal requests: k chunks per request minimising
+    ceil(units * k / CUs) * (ceil(N / k) + 2 * C_min), worked by hand."""
+    indptr = np.arange(0, 65 * 4, 4, dtype=np.int32)  # 64 requests of 4 pages
     last = np.full(64, 16, np.int32)
-    # 64 requests x 8 heads = 512 units >= half of 1024 slots: left whole
-    p = oplan.plan(indptr, last, 16, 8, slots=1024, balance=1, min_chunk_pages=1)
+    # 512 units, 512 slots: k=1 costs 1*(4+2)=6, k=2 2*(2+2)=8, k=3 3*4=12, k=4 4*3=12 -> whole
+    p = oplan.plan(indptr, last, 16, 8, slots=512, balance=1, min_chunk_pages=1)
     assert p["chunk_pages"] == 4 and p["num_partials"] == 0
-    # twice as many slots: not enough units, split to the balance bound
+    # 1024 slots: 6, 1*4=4, 2*4=8, 2*3=6 -> k=2, C=2: every request in two chunks
+    p = oplan.plan(indptr, last, 16, 8, slots=1024, balance=1, min_chunk_pages=1)
+    assert p["chunk_pages"] == 2 and p["num_partials"] == 128
+    # 2048 slots: 6, 4, 1*4=4, 1*3=3 -> k=4, C=1
     p = oplan.plan(indptr, last, 16, 8, slots=2048, balance=1, min_chunk_pages=1)
     assert p["chunk_pages"] == 1 and p["num_partials"] == 256
+    # C_min bounds k: with C_min=4 only k=1 is allowed
+    p = oplan.plan(indptr, last, 16, 8, slots=2048, balance=1, min_chunk_pages=4)
+    assert p["chunk_pages"] == 4 and p["num_partials"] == 0
+
+
+def test_waves_count_compute_units_not_slots():
+    # 512 units, 1024 slots at 4 per CU = 256 CUs: k=1 costs 2*(4+2)=12,
+    # k=2 4*(2+2)=16, k=3 6*4=24, k=4 8*3=24 -> whole (every CU already busy)
+    indptr = np.arange(0, 65 * 4, 4, dtype=np.int32)
+    last = np.full(64, 16, np.int32)
+    p = oplan.plan(indptr, last, 16, 8, slots=1024, balance=1, min_chunk_pages=1,
+                   slots_per_cu=4)
+    assert p["chunk_pages"] == 4 and p["num_partials"] == 0
+
+
+def test_uniform_batch_just_over_the_device_is_cut_into_waves():
+    # 72 requests of 128 pages, 4 units each = 288 units on 256 slots, C_min=16:
+    # k=1: 2*(128+32)=320; k=2: 3*(64+32)=288; k=3: 4*(43+32)=300;
+    # k=4: 5*(32+32)=320; k=5: 6*(26+32)=348; k=6: 7*(22+32)=378;
+    # k=7: 8*(19+32)=408; k=8: 9*(16+32)=432 -> k=2, C=64
+    indptr = np.arange(0, 73 * 128, 128, dtype=np.int32)
+    last = np.full(72, 16, np.int32)
+    p = oplan.plan(indptr, last, 16, 4, slots=256, balance=1, min_chunk_pages=16)
+    assert p["chunk_pages"] == 64 and p["num_partials"] == 72 * 2
 
 
 def test_unequal_batch_is_split_even_with_enough_units():
