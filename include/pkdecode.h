@@ -78,8 +78,9 @@ typedef struct pkd_plan pkd_plan;
  *  num_qo_heads     query heads Hq; num_kv_heads divides it and query head h
  *                   reads KV head h / (Hq / Hkv)
  *  head_dim         64 or 128; query heads per KV head 1, 2, 4 or 8, and also
- *                   16 for bf16 queries with bf16, e4m3 or e2m1 KV at
- *                   head_dim 128
+ *                   16 on the MFMA path (head_dim 128: bf16 q over bf16, e4m3
+ *                   or e2m1 KV, fp16 q over fp16 KV) and 32 there except for
+ *                   e2m1 KV
  *  page_size        tokens per page, a power of two in [1, 1024]
  *  q_dtype          PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16
  *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16, PKD_DTYPE_E4M3, PKD_DTYPE_F16

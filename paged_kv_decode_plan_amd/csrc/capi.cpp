@@ -291,7 +291,13 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     return fail(PKD_ERR_INVALID_ARGUMENT, "a request has %d new tokens; capacity_qo_len is %d",
                 max_q, caps[3]);
   const int32_t qo_shape = fixed ? caps[3] : max_q;
-  const int32_t queries_per_item = qo_shape > 1 ? std::max(1, 16 / group) : 1;
+  // One column group (16 rows) per work item, or two (32 rows, sharing every
+  // K/V load) when a request's new tokens need more than one group and the
+  // KV form has the two-group kernel: fewer query blocks, fewer KV re-reads.
+  int32_t queries_per_item = qo_shape > 1 ? std::max(1, 16 / group) : 1;
+  if (qo_shape > 1 && qo_shape * group > 16 && group <= 16 &&
+      pkd::decode_uses_mfma(kv_impl, a->head_dim, group, 32, q_kind, a->page_size))
+    queries_per_item = 32 / group;
   const int32_t rows = group * std::min(queries_per_item, qo_shape);
   if (max_q > 1 && !pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
                                           q_kind, a->page_size))

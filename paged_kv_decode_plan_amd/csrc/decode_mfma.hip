@@ -310,7 +310,6 @@ struct Ctx {
   int num_kv_heads, kvh;  // KV heads of the pool; this workgroup's (first) head
   int64_t page_stride, token_stride, head_stride, head_off;
   int log2p, pmask, kv_len, q4, j;
-  int lim;  // tokens of the item seen by this lane's row (column j of S)
   // Several heads: the head (0 .. HP-1) of this lane's S rows and V rows, and
   // whether it differs from the head of the lane's column (scores masked).
   int head_lane;
@@ -505,7 +504,7 @@ __device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>(
 template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const Ctx& c,
                                   const KernelArgs& a, int kvh, int t0, const TilePages& tp,
-                                  float m_run, float (&sc)[4], bool& grow) {
+                                  int lim, float m_run, float (&sc)[4], bool& grow) {
   float ks = a.sm_scale_log2;
   if constexpr (KV == kE4M3 && PAGE16) ks *= head_pick<HP>(tp.ks, c.head_lane);
 #pragma unroll
@@ -514,7 +513,7 @@ __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const C
     float kr = ks;
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
     if constexpr (KV == kE4M3T) kr = ks * ld.ks[r];
-    const bool ok = (FULL || t < c.lim) && (HP == 1 || !c.cross);
+    const bool ok = (FULL || t < lim) && (HP == 1 || !c.cross);
     const float v = ok ? s[r] * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
@@ -658,25 +657,45 @@ __device__ inline uint2 fp4_v_operand(const VPairs& vp, int nc) {
   return vb;
 }
 
+// Per column group (16 S columns each; two groups when a work item carries
+// 17-32 query rows): the q operands, the running softmax state and O of the
+// lane's column, and the tokens that column's row sees. Both groups consume
+// the same K and V loads and the same V operands.
+template <int KV, int NG>
+struct Groups {
+  u32x4_t qb[NG][q_ops<KV>()];
+  f32x4_t acc[NG][8];
+  float m_run[NG];  // reference max (log2 units), uniform over quarters
+  float d_run[NG];  // sum of p over this lane's tokens
+  int lim[NG];      // tokens of the item seen by this lane's row (column j of S)
+};
+
 // QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens
 // valid); P.V on the k = 16 MFMA.
-template <int KV, bool PAGE16, bool FULL, int HP>
+template <int KV, bool PAGE16, bool FULL, int HP, int NG>
 __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TilePages& tp, const u32x4_t (&qb)[q_ops<KV>()],
-                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
-  const f32x4_t s = qk<KV>(ld, qb);
-  float sc[1][4];
-  bool grow = false;
-  scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, m_run, sc[0], grow);
-  move_max<FULL, 1>(sc, c, grow, acc, m_run, d_run);
-  uint2 p_hi, p_lo;
-  probs<KV, PAGE16, FULL, HP>(sc[0], ld, c, a, kvh, t0, tp, m_run, d_run, p_hi, p_lo);
+                                    int t0, const TilePages& tp, Groups<KV, NG>& gs) {
+  uint2 p_hi[NG], p_lo[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const f32x4_t s = qk<KV>(ld, gs.qb[g]);
+    float sc[1][4];
+    bool grow = false;
+    scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, gs.lim[g], gs.m_run[g], sc[0],
+                                     grow);
+    move_max<FULL, 1>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
+    probs<KV, PAGE16, FULL, HP>(sc[0], ld, c, a, kvh, t0, tp, gs.m_run[g], gs.d_run[g], p_hi[g],
+                                p_lo[g]);
+  }
   // O += P . V, column j of MFMA nc is dim 8*j + nc
 #pragma unroll
   for (int nc = 0; nc < 8; ++nc) {
     const uint2 vb = v_operand<KV>(ld, nc);
-    acc[nc] = mfma16<KV>(p_hi, vb, acc[nc]);
-    acc[nc] = mfma16<KV>(p_lo, vb, acc[nc]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      gs.acc[g][nc] = mfma16<KV>(p_hi[g], vb, gs.acc[g][nc]);
+      gs.acc[g][nc] = mfma16<KV>(p_lo[g], vb, gs.acc[g][nc]);
+    }
   }
 }
 
@@ -685,24 +704,31 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
 // 8*q4 + e are token 4*q4 + e of A (e < 4) and 4*q4 + e - 4 of B, so the A
 // and B operands are the two sub-tiles' k = 16 operands side by side (half
 // the P.V instructions of two k = 16 passes).
-template <int KV, bool PAGE16, bool FULL, int HP>
+template <int KV, bool PAGE16, bool FULL, int HP, int NG>
 __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, const Ctx& c,
                                     const KernelArgs& a, int kvh, int t0, const TilePages& ta,
-                                    const TilePages& tb, const u32x4_t (&qb)[q_ops<KV>()],
-                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
+                                    const TilePages& tb, Groups<KV, NG>& gs) {
   constexpr int ST = sub_tokens<HP>();
-  const f32x4_t sa = qk<KV>(la, qb);
-  const f32x4_t sb = qk<KV>(lb, qb);
-  float sc[2][4];
-  bool grow = false;
-  scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, m_run, sc[0], grow);
-  scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, m_run, sc[1], grow);
-  move_max<FULL, 2>(sc, c, grow, acc, m_run, d_run);
-  uint2 pa_hi, pa_lo, pb_hi, pb_lo;
-  probs<KV, PAGE16, FULL, HP>(sc[0], la, c, a, kvh, t0, ta, m_run, d_run, pa_hi, pa_lo);
-  probs<KV, PAGE16, FULL, HP>(sc[1], lb, c, a, kvh, t0 + ST, tb, m_run, d_run, pb_hi, pb_lo);
-  const u32x4_t p_hi = {pa_hi.x, pa_hi.y, pb_hi.x, pb_hi.y};
-  const u32x4_t p_lo = {pa_lo.x, pa_lo.y, pb_lo.x, pb_lo.y};
+  u32x4_t p_hi[NG], p_lo[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const f32x4_t sa = qk<KV>(la, gs.qb[g]);
+    const f32x4_t sb = qk<KV>(lb, gs.qb[g]);
+    float sc[2][4];
+    bool grow = false;
+    scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, gs.lim[g], gs.m_run[g], sc[0],
+                                     grow);
+    scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, gs.lim[g], gs.m_run[g],
+                                     sc[1], grow);
+    move_max<FULL, 2>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
+    uint2 pa_hi, pa_lo, pb_hi, pb_lo;
+    probs<KV, PAGE16, FULL, HP>(sc[0], la, c, a, kvh, t0, ta, gs.m_run[g], gs.d_run[g], pa_hi,
+                                pa_lo);
+    probs<KV, PAGE16, FULL, HP>(sc[1], lb, c, a, kvh, t0 + ST, tb, gs.m_run[g], gs.d_run[g],
+                                pb_hi, pb_lo);
+    p_hi[g] = u32x4_t{pa_hi.x, pa_hi.y, pb_hi.x, pb_hi.y};
+    p_lo[g] = u32x4_t{pa_lo.x, pa_lo.y, pb_lo.x, pb_lo.y};
+  }
   VPairs vpa, vpb;
   if constexpr (fp4<KV>() && PKD_FP4_VT) {
     vpa = fp4_v_pairs(la.v);
@@ -719,8 +745,11 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
       vb = v_operand<KV>(lb, nc);
     }
     const u32x4_t v = {va.x, va.y, vb.x, vb.y};
-    acc[nc] = mfma<KV>(p_hi, v, acc[nc]);
-    acc[nc] = mfma<KV>(p_lo, v, acc[nc]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      gs.acc[g][nc] = mfma<KV>(p_hi[g], v, gs.acc[g][nc]);
+      gs.acc[g][nc] = mfma<KV>(p_lo[g], v, gs.acc[g][nc]);
+    }
   }
 }
 
@@ -728,22 +757,20 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
 #define PKD_PAIR_PV 1
 #endif
 
-template <int KV, bool PAGE16, bool FULL, int HP>
+template <int KV, bool PAGE16, bool FULL, int HP, int NG>
 __device__ inline void process_tile(const Tile<KV>& T, const Ctx& c, const KernelArgs& a, int kvh,
-                                    int t0, const TileP<KV>& tp, const u32x4_t (&qb)[q_ops<KV>()],
-                                    f32x4_t (&acc)[8], float& m_run, float& d_run) {
+                                    int t0, const TileP<KV>& tp, Groups<KV, NG>& gs) {
   constexpr int NS = nsub<KV>();
   constexpr int ST = sub_tokens<HP>();
   if constexpr (PKD_PAIR_PV && NS % 2 == 0) {
 #pragma unroll
     for (int s = 0; s < NS; s += 2)
-      process_pair<KV, PAGE16, FULL, HP>(T.sub[s], T.sub[s + 1], c, a, kvh, t0 + ST * s,
-                                         tp.sub[s], tp.sub[s + 1], qb, acc, m_run, d_run);
+      process_pair<KV, PAGE16, FULL, HP, NG>(T.sub[s], T.sub[s + 1], c, a, kvh, t0 + ST * s,
+                                             tp.sub[s], tp.sub[s + 1], gs);
   } else {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-      process_sub<KV, PAGE16, FULL, HP>(T.sub[s], c, a, kvh, t0 + ST * s, tp.sub[s], qb, acc,
-                                        m_run, d_run);
+      process_sub<KV, PAGE16, FULL, HP, NG>(T.sub[s], c, a, kvh, t0 + ST * s, tp.sub[s], gs);
   }
 }
 
@@ -783,9 +810,9 @@ __device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, in
 // loads and get up to 256 (2 per SIMD, still twice what one workgroup per CU
 // uses). e2m1 keeps four sub-tiles and the q hi/lo pair in flight and takes
 // the same 256, as do head pairs (two scales per page for e4m3).
-template <int KV, bool PAGE16, int HP>
+template <int KV, bool PAGE16, int HP, int G>
 constexpr int waves_per_simd() {
-  return KV == kE4M3T || fp4<KV>() || HP > 1 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
+  return KV == kE4M3T || fp4<KV>() || HP > 1 || G > 16 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
 }
 
 // G: S columns (query rows) per workgroup. HP = 2: the workgroup's "KV head"
@@ -793,9 +820,10 @@ constexpr int waves_per_simd() {
 // heads each (the launch passes num_kv_heads / 2 and group_log2 + 1, so the
 // epilogue and the merge address query heads as usual).
 template <int KV, int G, bool PAGE16, int HP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16, HP>()))) void decode_mfma_kernel(KernelArgs a) {
-  static_assert(G >= 1 && G <= 16, "at most 16 query rows per KV head");
-  static_assert(HP == 1 || (G >= HP && PAGE16), "head groups: HP heads' rows, pages >= 16");
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16, HP, G>()))) void decode_mfma_kernel(KernelArgs a) {
+  static_assert(G >= 1 && G <= 32, "at most 32 query rows per KV head");
+  static_assert(HP == 1 || (G >= HP && G <= 16 && PAGE16), "head pairs: 16 columns, pages >= 16");
+  constexpr int NG = G > 16 ? 2 : 1;  // column groups of 16
   __shared__ WaveStates<G, kD> st;
 
   int item, kvh;
@@ -822,16 +850,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   c.kv_len = it.kv_len;
   c.q4 = lane >> 4;
   c.j = lane & 15;
-  // Row j of S: query token qi of the item's block, query head kvh*group + hh.
-  const int qi = c.j >> a.group_log2;
-  const int hh = c.j & ((1 << a.group_log2) - 1);
-  const bool row_ok = c.j < G && qi < it.q_len;
-  c.lim = row_ok ? min(it.kv_len, it.visible + qi) : it.kv_len;
-  // Head pairs: the column's head is hh / (G / 2); the lane's rows' head q4 / 2.
-  // Several heads: the column's head is hh / (query heads per KV head).
+  Groups<KV, NG> gs;
+  // Column j of group g is row rho = 16*g + j of the item: query token qi of
+  // the item's block, query head kvh*group + hh.
+  const int hh0 = c.j & ((1 << a.group_log2) - 1);
+  // Head pairs: the column's head is hh / (query heads per KV head); the
+  // lane's rows' head is q4 / 2.
   constexpr int HPL = HP == 1 ? 0 : 1;
   constexpr int STL = sub_tokens_log2<HP>();
-  const int col_head = hh >> (a.group_log2 - HPL);
+  const int col_head = HP == 1 ? 0 : hh0 >> (a.group_log2 - HPL);
   c.head_lane = row_head<HP>(c.q4);
   c.cross = HP > 1 && c.head_lane != col_head;
   if constexpr (HP > 1) {
@@ -845,9 +872,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   }
   c.vrow_bytes = kv_bytes<KV>(a.token_stride);
 
-  // q^T as the B operand of S = K.q^T: column j = row j (zero beyond the block).
-  u32x4_t qb[q_ops<KV>()];  // eight 16-bit q values per k step (bf16, or fp16 for fp16 KV)
-  {
+  // q^T as the B operand of S = K.q^T: column j of group g = row 16*g + j
+  // (zero beyond the block): eight 16-bit q values per k step (bf16, or fp16
+  // for fp16 KV).
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int rho = 16 * g + c.j;
+    const int qi = rho >> a.group_log2;
+    const int hh = rho & ((1 << a.group_log2) - 1);
+    const bool row_ok = rho < G && qi < it.q_len;
+    gs.lim[g] = row_ok ? min(it.kv_len, it.visible + qi) : it.kv_len;
+    u32x4_t (&qb)[q_ops<KV>()] = gs.qb[g];
     const uint16_t* qp =
         static_cast<const uint16_t*>(a.q) +
         (int64_t(it.q_row + qi) * a.num_qo_heads + (int64_t(kvh) << a.group_log2) + hh) * kD;
@@ -879,11 +914,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     }
   }
 
-  f32x4_t acc[8];
 #pragma unroll
-  for (int nc = 0; nc < 8; ++nc) acc[nc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;  // head j: reference max (log2 units), uniform over quarters
-  float d_run = 0.f;        // head j: sum of p over this lane's tokens
+  for (int g = 0; g < NG; ++g) {
+#pragma unroll
+    for (int nc = 0; nc < 8; ++nc) gs.acc[g][nc] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    gs.m_run[g] = -INFINITY;
+    gs.d_run[g] = 0.f;
+  }
 
   // Tiles of this wavefront: tokens [(wave + 4i) * TT, +TT) for i < n, with
   // TT = tile_tokens<KV, HP>().
@@ -942,52 +979,57 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     const int h0 = c.kvh;
     if (n == 1) {
       issue_tile<KV, PAGE16, false, HP>(cur, c, tok(0), pc);
-      process_tile<KV, PAGE16, false, HP>(cur, c, a, h0, tok(0), pc, qb, acc, m_run, d_run);
+      process_tile<KV, PAGE16, false, HP, NG>(cur, c, a, h0, tok(0), pc, gs);
     } else {
       issue_tile<KV, PAGE16, true, HP>(cur, c, tok(0), pc);
       for (int i = 0; i + 2 < n; ++i) {
         pn = pages_of(i + 1);
         issue_tile<KV, PAGE16, true, HP>(nxt, c, tok(i + 1), pn);
-        process_tile<KV, PAGE16, true, HP>(cur, c, a, h0, tok(i), pc, qb, acc, m_run, d_run);
+        process_tile<KV, PAGE16, true, HP, NG>(cur, c, a, h0, tok(i), pc, gs);
         cur = nxt;
         pc = pn;
       }
       pn = pages_of(n - 1);
       issue_tile<KV, PAGE16, false, HP>(nxt, c, tok(n - 1), pn);
-      process_tile<KV, PAGE16, true, HP>(cur, c, a, h0, tok(n - 2), pc, qb, acc, m_run, d_run);
-      process_tile<KV, PAGE16, false, HP>(nxt, c, a, h0, tok(n - 1), pn, qb, acc, m_run, d_run);
+      process_tile<KV, PAGE16, true, HP, NG>(cur, c, a, h0, tok(n - 2), pc, gs);
+      process_tile<KV, PAGE16, false, HP, NG>(nxt, c, a, h0, tok(n - 1), pn, gs);
     }
   }
 
   // ---- per-wavefront state -> shared memory
   const int q4 = c.q4, j = c.j;
-  if constexpr (fp4<KV>()) {
-    // V channel scales: column j of MFMA nc is dim 8*j + nc, of the KV head
-    // of O row 4*q4 + r (row / query heads per KV head, within the group)
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    f32x4_t (&acc)[8] = gs.acc[g];
+    if constexpr (fp4<KV>()) {
+      // V channel scales: column j of MFMA nc is dim 8*j + nc, of the KV head
+      // of O row 4*q4 + r (row / query heads per KV head, within the pair)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hsel = min((4 * q4 + r) >> (a.group_log2 - HPL), HP - 1);
+        const float* vsp = a.v_scale + int64_t(c.kvh + hsel) * kD + 8 * j;
+        const float4 s0 = *reinterpret_cast<const float4*>(vsp);
+        const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
+        const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= vsv[nc];
+      }
+    }
+    float d_run = gs.d_run[g];
+    d_run += __shfl_xor(d_run, 16, 64);
+    d_run += __shfl_xor(d_run, 32, 64);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int hsel = min((4 * q4 + r) >> (a.group_log2 - HPL), HP - 1);
-      const float* vsp = a.v_scale + int64_t(c.kvh + hsel) * kD + 8 * j;
-      const float4 s0 = *reinterpret_cast<const float4*>(vsp);
-      const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
-      const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+      const int h = 16 * g + 4 * q4 + r;
+      if (h < G) {
 #pragma unroll
-      for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= vsv[nc];
+        for (int nc = 0; nc < 8; ++nc) st.o[wave][h][8 * j + nc] = acc[nc][r];
+      }
     }
-  }
-  d_run += __shfl_xor(d_run, 16, 64);
-  d_run += __shfl_xor(d_run, 32, 64);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * q4 + r;
-    if (h < G) {
-#pragma unroll
-      for (int nc = 0; nc < 8; ++nc) st.o[wave][h][8 * j + nc] = acc[nc][r];
+    if (q4 == 0 && 16 * g + j < G) {
+      st.m[wave][16 * g + j] = gs.m_run[g];
+      st.d[wave][16 * g + j] = d_run;
     }
-  }
-  if (q4 == 0 && j < G) {
-    st.m[wave][j] = m_run;
-    st.d[wave][j] = d_run;
   }
   __syncthreads();
   finish_workgroup<G, kD>(st, a, it, kvh);
@@ -1001,6 +1043,9 @@ DecodeFn pick_group(int g) {
     case 4: return decode_mfma_kernel<KV, 4, P16, 1>;
     case 8: return decode_mfma_kernel<KV, 8, P16, 1>;
     case 16: return decode_mfma_kernel<KV, 16, P16, 1>;
+    case 32:  // two column groups (not e2m1: its q hi/lo pairs would not fit the registers)
+      if constexpr (!fp4<KV>()) return decode_mfma_kernel<KV, 32, P16, 1>;
+      return nullptr;
     default: return nullptr;
   }
 }

@@ -70,7 +70,7 @@ def _create(**kw):
     (dict(last=[17, 4]), _lib.PKD_ERR_INVALID_ARGUMENT),
     (dict(num_qo_heads=7), _lib.PKD_ERR_INVALID_ARGUMENT),                   # Hq % Hkv
     (dict(head_dim=96), _lib.PKD_ERR_UNSUPPORTED),
-    (dict(num_qo_heads=64), _lib.PKD_ERR_UNSUPPORTED),                       # group 32
+    (dict(num_qo_heads=128), _lib.PKD_ERR_UNSUPPORTED),                      # group 64
     (dict(num_qo_heads=32, q_dtype=_lib.DTYPE_F32), _lib.PKD_ERR_UNSUPPORTED),  # group 16, fp32 q
     (dict(page_size=12), _lib.PKD_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), _lib.PKD_ERR_UNSUPPORTED),

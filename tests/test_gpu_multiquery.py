@@ -40,10 +40,43 @@ def test_small_ragged_multi_query_matches_oracle(kv, g, split):
     kw = dict(slots=64, balance=1, min_chunk_pages=1) if split == "forced" else {}
     out, lse, info = run_hip(to_device(case), **kw)
     assert out.shape == (int(case["qo_indptr"][-1]), w.num_qo_heads, 128)
-    assert info["queries_per_item"] == max(1, 16 // g)
+    max_q = int(np.diff(case["qo_indptr"]).max())
+    assert info["queries_per_item"] == (32 // g if max_q * g > 16 else max(1, 16 // g))
     if split == "forced":
         assert info["num_split_requests"] > 0
     compare(out, lse, ref_out, ref_lse, kv)
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "f16"])
+@pytest.mark.parametrize("g", [1, 4, 16, 32])
+@pytest.mark.parametrize("split", ["auto", "forced"])
+def test_two_column_groups(kv, g, split):
+    """Items of 17-32 query rows (two 16-column groups sharing every K/V load):
+    many new tokens per request, and 32 query heads per KV head."""
+    lens, nq = [40, 333, 17, 100, 700], [30, 7, 4, 16, 25]
+    if g >= 16:
+        nq = [min(x, 5) for x in nq]
+    qd = "f16" if kv == "f16" else "bf16"
+    w = custom_workload(len(lens), 2 * g, 2, 128, 16, kv, qd, lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 3, qo_lens=nq)
+    case = host_case(w, 60 + g, poison=True)
+    _say("two groups", kv, g, split)
+    ref_out, ref_lse = oracle_for(case)
+    kw = dict(slots=32, balance=1, min_chunk_pages=1) if split == "forced" else {}
+    out, lse, info = run_hip(to_device(case), **kw)
+    assert info["queries_per_item"] == (32 // g if g < 32 else 1)
+    compare(out, lse, ref_out, ref_lse, kv)
+
+
+def test_group_32_one_token():
+    lens = [1, 15, 16, 17, 100, 333, 700]
+    w = custom_workload(len(lens), 64, 2, 128, 16, "bf16", "bf16", lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 3)
+    case = host_case(w, 77, poison=True)
+    ref_out, ref_lse = oracle_for(case)
+    for kw in ({}, dict(slots=16, balance=1, min_chunk_pages=1)):
+        out, lse, _ = run_hip(to_device(case), **kw)
+        compare(out, lse, ref_out, ref_lse, "bf16")
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])

@@ -1,7 +1,7 @@
 """Seeded random configurations against the oracle.
 
 Each case draws a KV format (fp32, bf16, fp16, e4m3 with per-page or per-token
-scales, e2m1), a query/KV head layout (group 1-16, 1-4 KV heads: single heads
+scales, e2m1), a query/KV head layout (group 1-32, 1-4 KV heads: single heads
 and pairs), a page size, ragged lengths (page-aligned and not), one or several
 new tokens per request, an automatic or forced split and an output dtype, and
 compares the HIP path with the oracle at the format's tolerance.
@@ -29,7 +29,7 @@ def draw_case(seed: int) -> dict:
     d = 128 if (mfma or rng.random() < 0.5) else 64
     if mfma:
         qd = "f16" if kv == "f16" else "bf16"
-        g = int(rng.choice([1, 2, 4, 8, 16]))
+        g = int(rng.choice([1, 2, 4, 8, 16] + ([32] if kv != "e2m1" else [])))
     else:
         qd = "f32" if kv == "f32" else str(rng.choice(["f32", "bf16"]))
         g = int(rng.choice([1, 2, 4, 8]))

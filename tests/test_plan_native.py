@@ -43,14 +43,25 @@ def test_golden_partitions_native():
         _assert_same(info, items, merge, split, ref)
 
 
+def expected_queries_per_item(max_q: int, g: int, kv: str) -> int:
+    """One token per request: 1; else a 16-row column group of tokens, or two
+    (32 rows) when the tokens need more than one and the form has them."""
+    if max_q == 1:
+        return 1
+    if max_q * g > 16 and kv != "e2m1":
+        return 32 // g
+    return max(1, 16 // g)
+
+
 def test_golden_multi_query_partitions_native():
-    """Eight query heads per KV head: a work item carries 16 / 8 = 2 new tokens."""
+    """Eight query heads per KV head over e2m1 KV (one 16-row column group per
+    item): a work item carries 16 / 8 = 2 new tokens."""
     with open(os.path.join(GOLDEN, "plan_worked_example.json")) as f:
         ex = json.load(f)
     for c in ex["multi_query_cases"]:
         info, items, merge, split, ref = _both(
             c["indptr"], c["last_page_len"], ex["page_size"], 1, c["slots"], c["balance"],
-            c["min_chunk_pages"], hq=8, qo_indptr=c["qo_indptr"])
+            c["min_chunk_pages"], hq=8, qo_indptr=c["qo_indptr"], kv="e2m1")
         assert info["queries_per_item"] == c["queries_per_item"]
         assert items.tolist() == c["items"]
         assert info["num_partials"] == c["num_partials"]
@@ -71,11 +82,11 @@ def test_random_multi_query_tables_bit_exact(seed):
     qo = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
     hkv = int(rng.choice([1, 2, 8]))
     g = int(rng.choice([1, 2, 4, 8, 16]))
+    kv = str(rng.choice(["bf16", "e4m3", "e2m1"]))
     out = _both(indptr, last, P, hkv, int(rng.integers(1, 4096)), int(rng.integers(1, 4)),
-                int(rng.integers(1, 32)), hq=hkv * g, kv=str(rng.choice(["bf16", "e4m3", "e2m1"])),
-                qo_indptr=qo)
+                int(rng.integers(1, 32)), hq=hkv * g, kv=kv, qo_indptr=qo)
     info = out[0]
-    assert info["queries_per_item"] == (max(1, 16 // g) if nq.max() > 1 else 1)
+    assert info["queries_per_item"] == expected_queries_per_item(int(nq.max()), g, kv)
     assert info["max_qo_len"] == nq.max() and info["query_rows"] == qo[-1]
     _assert_same(*out[:4], out[4])
 
