@@ -310,10 +310,8 @@ struct Ctx {
   int num_kv_heads, kvh;  // KV heads of the pool; this workgroup's (first) head
   int64_t page_stride, token_stride, head_stride, head_off;
   int log2p, pmask, kv_len, q4, j;
-  // Several heads: the head (0 .. HP-1) of this lane's S rows and V rows, and
-  // whether it differs from the head of the lane's column (scores masked).
+  // Head pairs: the head (0, 1) of this lane's S rows and V rows.
   int head_lane;
-  bool cross;
   // Byte offsets of this lane's first K and V load from the tile's first row
   // (the same for every tile when a tile lies in one page); the other loads
   // add 64 bytes (K) or one token row (V), both wavefront-uniform.
@@ -504,7 +502,7 @@ __device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>(
 template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const Ctx& c,
                                   const KernelArgs& a, int kvh, int t0, const TilePages& tp,
-                                  int lim, float m_run, float (&sc)[4], bool& grow) {
+                                  int lim, bool cross, float m_run, float (&sc)[4], bool& grow) {
   float ks = a.sm_scale_log2;
   if constexpr (KV == kE4M3 && PAGE16) ks *= head_pick<HP>(tp.ks, c.head_lane);
 #pragma unroll
@@ -513,7 +511,7 @@ __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const C
     float kr = ks;
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
     if constexpr (KV == kE4M3T) kr = ks * ld.ks[r];
-    const bool ok = (FULL || t < lim) && (HP == 1 || !c.cross);
+    const bool ok = (FULL || t < lim) && (HP == 1 || !cross);
     const float v = ok ? s[r] * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
@@ -668,6 +666,7 @@ struct Groups {
   float m_run[NG];  // reference max (log2 units), uniform over quarters
   float d_run[NG];  // sum of p over this lane's tokens
   int lim[NG];      // tokens of the item seen by this lane's row (column j of S)
+  bool cross[NG];   // head pairs: the lane's S rows are not its column's head (masked)
 };
 
 // QK, online softmax and PV for one loaded sub-tile (FULL: all 16 tokens
@@ -681,8 +680,8 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     const f32x4_t s = qk<KV>(ld, gs.qb[g]);
     float sc[1][4];
     bool grow = false;
-    scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, gs.lim[g], gs.m_run[g], sc[0],
-                                     grow);
+    scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, gs.lim[g], gs.cross[g],
+                                     gs.m_run[g], sc[0], grow);
     move_max<FULL, 1>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
     probs<KV, PAGE16, FULL, HP>(sc[0], ld, c, a, kvh, t0, tp, gs.m_run[g], gs.d_run[g], p_hi[g],
                                 p_lo[g]);
@@ -716,10 +715,10 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
     const f32x4_t sb = qk<KV>(lb, gs.qb[g]);
     float sc[2][4];
     bool grow = false;
-    scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, gs.lim[g], gs.m_run[g], sc[0],
-                                     grow);
-    scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, gs.lim[g], gs.m_run[g],
-                                     sc[1], grow);
+    scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, gs.lim[g], gs.cross[g],
+                                     gs.m_run[g], sc[0], grow);
+    scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, gs.lim[g], gs.cross[g],
+                                     gs.m_run[g], sc[1], grow);
     move_max<FULL, 2>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
     uint2 pa_hi, pa_lo, pb_hi, pb_lo;
     probs<KV, PAGE16, FULL, HP>(sc[0], la, c, a, kvh, t0, ta, gs.m_run[g], gs.d_run[g], pa_hi,
@@ -822,7 +821,7 @@ constexpr int waves_per_simd() {
 template <int KV, int G, bool PAGE16, int HP>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16, HP, G>()))) void decode_mfma_kernel(KernelArgs a) {
   static_assert(G >= 1 && G <= 32, "at most 32 query rows per KV head");
-  static_assert(HP == 1 || (G >= HP && G <= 16 && PAGE16), "head pairs: 16 columns, pages >= 16");
+  static_assert(HP == 1 || (G >= HP && PAGE16), "head pairs: pages >= 16");
   constexpr int NG = G > 16 ? 2 : 1;  // column groups of 16
   __shared__ WaveStates<G, kD> st;
 
@@ -852,15 +851,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
   c.j = lane & 15;
   Groups<KV, NG> gs;
   // Column j of group g is row rho = 16*g + j of the item: query token qi of
-  // the item's block, query head kvh*group + hh.
-  const int hh0 = c.j & ((1 << a.group_log2) - 1);
-  // Head pairs: the column's head is hh / (query heads per KV head); the
-  // lane's rows' head is q4 / 2.
+  // the item's block, query head kvh*group + hh. Head pairs: the column's
+  // head is hh / (query heads per KV head); the lane's rows' head is q4 / 2.
   constexpr int HPL = HP == 1 ? 0 : 1;
   constexpr int STL = sub_tokens_log2<HP>();
-  const int col_head = HP == 1 ? 0 : hh0 >> (a.group_log2 - HPL);
   c.head_lane = row_head<HP>(c.q4);
-  c.cross = HP > 1 && c.head_lane != col_head;
   if constexpr (HP > 1) {
     c.koff = uint32_t(kv_bytes<KV>(int64_t(c.j & ((1 << STL) - 1)) * a.token_stride +
                                    (c.j >> STL) * a.head_stride + qk_dim<KV>(0, c.q4, 0)));
@@ -882,6 +877,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     const int hh = rho & ((1 << a.group_log2) - 1);
     const bool row_ok = rho < G && qi < it.q_len;
     gs.lim[g] = row_ok ? min(it.kv_len, it.visible + qi) : it.kv_len;
+    const int col_head = HP == 1 ? 0 : hh >> (a.group_log2 - HPL);
+    gs.cross[g] = HP > 1 && c.head_lane != col_head;
     u32x4_t (&qb)[q_ops<KV>()] = gs.qb[g];
     const uint16_t* qp =
         static_cast<const uint16_t*>(a.q) +
@@ -1006,7 +1003,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
       // of O row 4*q4 + r (row / query heads per KV head, within the pair)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int hsel = min((4 * q4 + r) >> (a.group_log2 - HPL), HP - 1);
+        const int hrow = (16 * g + 4 * q4 + r) & ((1 << a.group_log2) - 1);
+        const int hsel = HP == 1 ? 0 : hrow >> (a.group_log2 - HPL);
         const float* vsp = a.v_scale + int64_t(c.kvh + hsel) * kD + 8 * j;
         const float4 s0 = *reinterpret_cast<const float4*>(vsp);
         const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
@@ -1050,7 +1048,7 @@ DecodeFn pick_group(int g) {
   }
 }
 
-// Pairs of KV heads per workgroup: `cols` = 2 x query heads per KV head.
+// Pairs of KV heads per workgroup: `cols` = 2 x the rows of one head.
 template <int KV>
 DecodeFn pick_pair(int cols) {
   switch (cols) {
@@ -1058,6 +1056,9 @@ DecodeFn pick_pair(int cols) {
     case 4: return decode_mfma_kernel<KV, 4, true, 2>;
     case 8: return decode_mfma_kernel<KV, 8, true, 2>;
     case 16: return decode_mfma_kernel<KV, 16, true, 2>;
+    case 32:  // two column groups (not e2m1, as for one head)
+      if constexpr (!fp4<KV>()) return decode_mfma_kernel<KV, 32, true, 2>;
+      return nullptr;
     default: return nullptr;
   }
 }

@@ -36,8 +36,8 @@ static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_ki
                        int page_size, int hp = 1) {
   if ((group & (group - 1)) || rows < group || rows % group) return nullptr;
   if (hp > 1)
-    return mfma_form(kv_dtype, q_kind) && rows == group && hp * rows <= 16
-               ? mfma_decode_kernel(kv_dtype, head_dim, hp * rows, page_size, hp)
+    return mfma_form(kv_dtype, q_kind) && hp * rows <= 32
+               ? mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(hp * rows), page_size, hp)
                : nullptr;
   if (mfma_form(kv_dtype, q_kind)) {
     if (DecodeFn f = mfma_decode_kernel(kv_dtype, head_dim, pow2_ceil(rows), page_size, 1))
@@ -96,7 +96,9 @@ int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_k
                  : (kv_dtype == kE4M3 || kv_dtype == kE4M3T) ? PKD_HEADS_E4M3
                  : (kv_dtype == kBF16 || kv_dtype == kF16) ? PKD_HEADS_BF16
                                                            : 1;
-  if (hp != 2 || rows != group || num_kv_heads % 2 || 2 * group > 16) return 1;
+  // A pair doubles the columns: at most 16 rows per head (one column group
+  // of one head, two for the pair).
+  if (hp != 2 || num_kv_heads % 2 || rows > 16) return 1;
   return choose(kv_dtype, head_dim, group, rows, q_kind, page_size, 2) ? 2 : 1;
 }
 

@@ -86,9 +86,9 @@ struct DecodeLaunch {
 bool decode_supported(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size);
 bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kind, int page_size);
 // KV heads one decode workgroup handles: 2 (a pair, read as one contiguous
-// run per token) on the MFMA path where the KV head count is even and the
-// pair's query heads fit the 16 MFMA columns (one query token per request,
-// pages of at least 16 tokens); otherwise 1.
+// run per token) on the MFMA path where the KV head count is even, a head has
+// at most 16 rows per work item (the pair's then fill at most two 16-column
+// groups) and pages hold at least 16 tokens; otherwise 1.
 int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                         int page_size, int num_kv_heads);
 hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);

@@ -260,19 +260,20 @@ def test_e2m1_plans_match_the_oracle():
         _assert_same(*_both(indptr, last, P, 8, 256, 1, 16, hq=8 * g, kv="e2m1"))
 
 
-@pytest.mark.parametrize("hkv,g,P,qo,want", [
-    (8, 4, 16, None, 4),     # pairs of KV heads: 4 workgroups per item
-    (2, 8, 16, None, 1),
-    (3, 4, 16, None, 3),     # odd KV head count: one head per workgroup
-    (2, 16, 16, None, 2),    # 2 x 16 query heads exceed the 16 MFMA columns
-    (8, 4, 8, None, 8),      # pages below 16 tokens
-    (8, 4, 16, [0, 2, 3], 8),  # several query tokens per request
+@pytest.mark.parametrize("hkv,g,P,qo,want_e2m1,want_e4m3", [
+    (8, 4, 16, None, 4, 4),     # pairs of KV heads: 4 workgroups per item
+    (2, 8, 16, None, 1, 1),
+    (3, 4, 16, None, 3, 3),     # odd KV head count: one head per workgroup
+    (2, 16, 16, None, 2, 1),    # 2 x 16 rows: two column groups (not for e2m1)
+    (8, 4, 8, None, 8, 8),      # pages below 16 tokens
+    (8, 4, 16, [0, 2, 3], 4, 4),   # two new tokens: 8 rows per head, pairs
+    (8, 4, 16, [0, 9, 10], 8, 8),  # more than 16 rows per head: one head
 ])
 @pytest.mark.parametrize("kv", ["e2m1", "e4m3"])
-def test_head_pair_workgroups_per_item(kv, hkv, g, P, qo, want):
+def test_head_pair_workgroups_per_item(kv, hkv, g, P, qo, want_e2m1, want_e4m3):
     info, *_ = pk.plan_partition([0, 3, 5], [5, P], hkv * g, hkv, 128, P, kv_dtype=kv,
                                  q_dtype="bf16", qo_indptr=qo)
-    assert info["units_per_item"] == want
+    assert info["units_per_item"] == (want_e2m1 if kv == "e2m1" else want_e4m3)
 
 
 def test_many_split_workgroups_keep_the_merge_kernel():
