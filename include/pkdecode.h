@@ -107,8 +107,9 @@ typedef struct pkd_plan pkd_plan;
  *                   L_r - q_r + 1 + i KV tokens. More than one token per
  *                   request needs head_dim 128 and bf16 q with bf16, e4m3 or
  *                   e2m1 KV, or fp16 q with fp16 KV (else UNSUPPORTED); a
- *                   work item then carries up to
- *                   16 / group of a request's tokens.
+ *                   work item then carries up to 16 / group of a request's
+ *                   tokens, or 32 / group (e2m1: 16 / group) when a request
+ *                   has more (info.queries_per_item).
  *  non_causal       0: the causal rule above. 1: every q row of request r
  *                   sees all of its KV tokens and q_r may exceed them: the
  *                   shared-prefix level of cascade attention, where the

@@ -263,9 +263,9 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                 a->kv_scale_per_token ? " with row-wise scales (needs bf16 q, head_dim 128)"
                 : a->kv_dtype == PKD_DTYPE_E2M1 ? " (e2m1 KV needs bf16 q and head_dim 128)"
                                                 : "");
-  // Several new tokens per request: a work item carries up to 16 / group of
-  // one request's tokens, so that its group x tokens rows fill the columns of
-  // one MFMA tile.
+  // Several new tokens per request: a work item carries up to 16 / group (or
+  // 32 / group, below) of one request's tokens, so that its group x tokens
+  // rows fill one (two) groups of MFMA columns.
   int32_t max_q = 1;
   if (a->non_causal != 0 && a->non_causal != 1)
     return fail(PKD_ERR_INVALID_ARGUMENT, "non_causal must be 0 or 1");

@@ -1,5 +1,6 @@
 // MFMA split-KV paged decode kernel, for gfx950 (bf16, e4m3 or e2m1 KV with
-// bf16 q, fp16 KV with fp16 q; head_dim 128, up to 16 query rows per KV head).
+// bf16 q, fp16 KV with fp16 q; head_dim 128, up to 32 query rows per
+// workgroup in one or two groups of 16 MFMA columns).
 //
 // What is computed ("FlashDecoding + FlashInfer — the decode-time attention
 // story"): for each query token of a request and each query head h, the
@@ -12,12 +13,14 @@
 // same rule. Its G rows are (query token i, query head hh of the group) with
 // row = i * group + hh: the group's heads for one token per request, or, with
 // several new tokens per request (the ragged q rows of §"Ragged attention"),
-// up to 16 / group tokens, token i seeing the first min(kv_len, visible + i)
-// tokens of the item (causal within the new tokens).
+// up to 32 / group tokens, token i seeing the first min(kv_len, visible + i)
+// tokens of the item (causal within the new tokens). Rows 16..31 form a
+// second group of MFMA columns that shares every K and V load.
 //
 // Both contractions run on MFMA: S = K.q^T on v_mfma_f32_16x16x32_bf16 and
-// O = P.V on v_mfma_f32_16x16x16_bf16 (lane l holds A row l%16 / B column
-// l%16 for a k-slice chosen by l/16, and C rows 4*(l/16)..+4 of column l%16).
+// O = P.V on v_mfma_f32_16x16x16_bf16, or on the k = 32 form over two
+// sub-tiles (lane l holds A row l%16 / B column l%16 for a k-slice chosen by
+// l/16, and C rows 4*(l/16)..+4 of column l%16).
 // The order in which a contraction visits its index is free as long as A and B
 // agree; both products use that freedom so that every operand comes straight
 // from coalesced loads. A wavefront works on 16-token tiles:
@@ -58,7 +61,8 @@
 // (one bf16 row). So a workgroup may take an even-odd pair of KV heads, and a
 // sub-tile's 16 S rows are 8 tokens x 2 heads (row rho is token rho % 8 of
 // head rho / 8), so that each load instruction reads both heads' rows of a
-// token side by side. The S columns are the pair's 2 * group query heads; a
+// token side by side. The S columns are the pair's rows (2 * group query
+// heads per token; two column groups when they exceed 16); a
 // lane's four S values all belong to one head (quarter q4 / 2), and those
 // whose head is not their column's are masked to -inf, so P.V over the 16
 // rows sums each column's own head only. The MFMA work per head is unchanged.

@@ -2,11 +2,12 @@
 //
 // The MFMA kernel runs wherever both contractions can take bf16 operands
 // exactly: bf16, e4m3 or e2m1 KV with bf16 queries and head_dim 128 (group
-// sizes 1..16), and fp16 KV with fp16 queries on fp16 MFMA. fp32 KV or queries, and head_dim 64, use the vector-ALU kernel,
-// which handles one query token per request only. A work item of several new
-// tokens of a request puts group x tokens rows (at most 16) on the MFMA
-// columns; the kernel instance is the one for that row count rounded up to a
-// power of two.
+// sizes 1..32; 32 not for e2m1), and fp16 KV with fp16 queries on fp16 MFMA.
+// fp32 KV or queries, and head_dim 64, use the vector-ALU kernel, which
+// handles one query token per request only. A work item of several new
+// tokens of a request puts group x tokens rows (at most 32: one or two groups
+// of 16 MFMA columns) on the columns; the kernel instance is the one for that
+// row count (doubled for a pair of KV heads) rounded up to a power of two.
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
