@@ -334,6 +334,7 @@ def main(argv=None) -> int:
 
     if args.summarize_counters:
         t = summarize_counters(*args.summarize_counters, args.config, args.counter_command)
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
         path = os.path.join(ROOT, "profiles", f"traffic_decode_{args.config}.json")
         with open(path, "w") as f:
             json.dump(t, f, indent=1)
@@ -452,7 +453,7 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         has_merge = False
 
-    def step(ev=None):
+    def step(ev=None, kernel_ev=None):
         """One run(). Timed steps bracket it with events; with --separate-merge
         the decode and merge stages are launched and bracketed apart (an event
         pair costs a few µs itself)."""
@@ -462,6 +463,14 @@ def main(argv=None) -> int:
             graph.replay()
             if ev is not None:
                 ev[1].record()
+            return
+        if kernel_ev is not None:  # events stamped by the decode kernel's own dispatch
+            if has_merge:
+                wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_DECODE,
+                            decode_events=kernel_ev, **run_kw)
+                wrapper.run(dcase["q"], dcase["kv"], stages=_lib.STAGE_MERGE, **run_kw)
+            else:
+                wrapper.run(dcase["q"], dcase["kv"], decode_events=kernel_ev, **run_kw)
             return
         if ev is None:
             wrapper.run(dcase["q"], dcase["kv"], **run_kw)
@@ -494,7 +503,27 @@ def main(argv=None) -> int:
         step(evs[i])
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    dec_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    bracket_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = bracket_ms
+    # Decode kernel time: a second series of as many cold steps whose decode
+    # launches record events in the kernel's own dispatch (hipExtLaunchKernel).
+    # Events around a launch add the queue's packet overhead (a few µs), and
+    # the dispatch-stamped ones slow the launch itself, so each series times
+    # one thing: the steps above, the kernel here. A cascade step (several
+    # launches) and a graph replay keep the bracket.
+    kernel_events = graph is None and not cascade
+    if kernel_events:
+        kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for e in kevs:  # create the events before the timed series
+            e[0].record()
+            e[1].record()
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            if not args.warm:
+                flush_i64.max()
+            step(kernel_ev=kevs[i])
+        torch.cuda.synchronize()
+        dec_ms = [e[0].elapsed_time(e[1]) for e in kevs]
     mrg_ms = [e[1].elapsed_time(e[2]) for e in evs] if has_merge else [0.0]
     step_ms = [e[0].elapsed_time(e[2 if has_merge else 1]) for e in evs]
     print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
@@ -582,6 +611,10 @@ def main(argv=None) -> int:
             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
             "traffic": traffic,
             "decode_us": round(mean_dec * 1e3, 2),
+            "decode_timing": ("events recorded by the decode kernel's dispatch (hipExtLaunchKernel), "
+                              f"{args.steps} more cold steps" if kernel_events
+                              else "events around the step"),
+            "decode_bracket_us": round(statistics.fmean(bracket_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": nbytes,
         },
     }

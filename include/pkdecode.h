@@ -304,6 +304,19 @@ int pkd_run(const pkd_plan* plan, const pkd_run_args* args);
 #define PKD_STAGE_ALL 3
 int pkd_run_stages(const pkd_plan* plan, const pkd_run_args* args, int32_t stages);
 
+/* pkd_run_stages, with the decode kernel's own dispatch recording two HIP
+ * events: `decode_start` when the kernel begins executing and `decode_stop`
+ * when it has completed (hipExtLaunchKernel's kernel events), so that
+ * hipEventElapsedTime between them is the kernel's duration without the
+ * queue's packet overhead that events recorded around the launch include.
+ * Both are hipEvent_t passed as void*, created on the plan's device with
+ * timing enabled and owned by the caller; either may be NULL (then it is
+ * not recorded). They are ignored when `stages` does not include
+ * PKD_STAGE_DECODE. For callers that measure the decode kernel; the work
+ * enqueued is that of pkd_run_stages. */
+int pkd_run_timed(const pkd_plan* plan, const pkd_run_args* args, int32_t stages,
+                  void* decode_start, void* decode_stop);
+
 /* Free the handle. Its pinned staging block returns to a process-wide pool
  * and is handed to another plan only after its last copy has completed, so
  * destroying a plan never waits. NULL is a no-op. */

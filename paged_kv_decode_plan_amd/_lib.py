@@ -151,6 +151,9 @@ def load() -> ctypes.CDLL:
     lib.pkd_run.restype = ctypes.c_int
     lib.pkd_run_stages.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs), ctypes.c_int32]
     lib.pkd_run_stages.restype = ctypes.c_int
+    lib.pkd_run_timed.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs), ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    lib.pkd_run_timed.restype = ctypes.c_int
     lib.pkd_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.pkd_plan_destroy.restype = None
     lib.pkd_merge_states.argtypes = [ctypes.POINTER(MergeStatesArgs)]

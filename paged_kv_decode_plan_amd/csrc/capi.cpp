@@ -533,6 +533,11 @@ int pkd_plan_upload(pkd_plan* p, void* workspace, size_t workspace_bytes, void* 
 int pkd_run(const pkd_plan* p, const pkd_run_args* r) { return pkd_run_stages(p, r, PKD_STAGE_ALL); }
 
 int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
+  return pkd_run_timed(p, r, stages, nullptr, nullptr);
+}
+
+int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void* decode_start,
+                  void* decode_stop) {
   if (!p || !r) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
   if (stages < 1 || stages > PKD_STAGE_ALL)
     return fail(PKD_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of PKD_STAGE_ALL");
@@ -611,7 +616,8 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
   hipStream_t s = static_cast<hipStream_t>(r->stream);
   hipError_t e;
   if (stages & PKD_STAGE_DECODE) {
-    e = pkd::launch_decode(L, s);
+    e = pkd::launch_decode(L, s, static_cast<hipEvent_t>(decode_start),
+                           static_cast<hipEvent_t>(decode_stop));
     if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   }
   if ((stages & PKD_STAGE_MERGE) && !L.fuse_merge) {

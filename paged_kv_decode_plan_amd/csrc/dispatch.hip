@@ -8,6 +8,7 @@
 // tokens of a request puts group x tokens rows (at most 32: one or two groups
 // of 16 MFMA columns) on the columns; the kernel instance is the one for that
 // row count (doubled for a pair of KV heads) rounded up to a power of two.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "kernel_common.h"
@@ -103,7 +104,8 @@ int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_k
   return choose(kv_dtype, head_dim, group, rows, q_kind, page_size, 2) ? 2 : 1;
 }
 
-hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
+hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream, hipEvent_t start,
+                         hipEvent_t stop) {
   const int hp = L.heads_per_wg;
   if ((hp != 1 && hp != 2) || L.num_kv_heads % hp) return hipErrorInvalidValue;
   DecodeFn fn =
@@ -143,7 +145,10 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream) {
   const unsigned grid = decode_grid_size(L.num_items, a.num_kv_heads, a.xcd_group);
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, L.wgs_cap, &lds); e != hipSuccess) return e;
-  hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, a);
+  if (start || stop)
+    hipExtLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, start, stop, 0, a);
+  else
+    hipLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 

@@ -91,7 +91,10 @@ bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kin
 // groups) and pages hold at least 16 tokens; otherwise 1.
 int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                         int page_size, int num_kv_heads);
-hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream);
+// start / stop: events the kernel's dispatch records as it begins and
+// completes (nullptr: a plain launch).
+hipError_t launch_decode(const DecodeLaunch& a, hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
 hipError_t launch_merge(const DecodeLaunch& a, hipStream_t stream);
 hipError_t decode_occupancy(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                             int page_size, int heads_per_wg, int wgs_cap, int* wgs_per_cu);

@@ -121,8 +121,12 @@ class Plan:
                                              ctypes.c_size_t(workspace_bytes),
                                              ctypes.c_void_p(stream_ptr)))
 
-    def run_raw(self, args: "_lib.RunArgs", stages: int = _lib.STAGE_ALL) -> None:
-        if stages == _lib.STAGE_ALL:
+    def run_raw(self, args: "_lib.RunArgs", stages: int = _lib.STAGE_ALL, events=None) -> None:
+        if events is not None:  # raw hipEvent_t handles stamped by the decode kernel's dispatch
+            _lib.check(self._lib.pkd_run_timed(self._handle, ctypes.byref(args), stages,
+                                               ctypes.c_void_p(events[0]),
+                                               ctypes.c_void_p(events[1])))
+        elif stages == _lib.STAGE_ALL:
             _lib.check(self._lib.pkd_run(self._handle, ctypes.byref(args)))
         else:
             _lib.check(self._lib.pkd_run_stages(self._handle, ctypes.byref(args), stages))
@@ -246,7 +250,10 @@ class BatchDecodeWithPagedKVCacheWrapper:
 
     # -- run -----------------------------------------------------------------
     def run(self, q, paged_kv_cache, out=None, lse=None, return_lse: bool = False,
-            k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL):
+            k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL, decode_events=None):
+        """``decode_events``: an optional pair of ``torch.cuda.Event(enable_timing=True)``
+        that the decode kernel's own dispatch records as it starts and completes
+        (``pkd_run_timed``); ``start.elapsed_time(stop)`` is then the kernel's time."""
         import torch
         p = self._plan
         if p is None:
@@ -303,7 +310,13 @@ class BatchDecodeWithPagedKVCacheWrapper:
         a.workspace = self._ws.data_ptr()
         a.workspace_bytes = self._ws.numel() * self._ws.element_size()
         a.stream = torch.cuda.current_stream(q.device).cuda_stream
-        p.run_raw(a, stages)
+        events = None
+        if decode_events is not None:
+            for ev in decode_events:
+                if not ev.cuda_event:  # torch creates the HIP event at its first record
+                    ev.record()
+            events = (decode_events[0].cuda_event, decode_events[1].cuda_event)
+        p.run_raw(a, stages, events)
         return (out, lse) if (return_lse or lse is not None) else out
 
     forward = run
