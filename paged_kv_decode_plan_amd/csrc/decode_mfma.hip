@@ -288,22 +288,16 @@ __device__ inline int qk_dim(int dc, int q, int e) {
 }
 
 // Where a sub-tile lives: with pages of at least 16 tokens a sub-tile (16 or
-// 8 tokens) lies in one page (sub-tiles start at multiples of their size and
-// items at page boundaries), so it needs one page id (and, for e4m3, one K
-// and one V scale per head), all wavefront-uniform. A sub-tile wholly past the item's end is
-// given the page of the item's last sub-tile (its loads repeat valid tokens
-// and its weights are 0).
+// 8 tokens) lies in one page (sub-tiles start at multiples of their size
+// and items at page boundaries), so it needs one page id (wavefront-uniform)
+// and, for e4m3, the page's K and V scale of the lane's own KV head (the head
+// of its S rows and V rows), picked once when the page id is read. A sub-tile
+// wholly past the item's end is given the page of the item's last sub-tile
+// (its loads repeat valid tokens and its weights are 0).
 struct TilePages {
   int64_t page;
-  float ks[2], vs[2];  // e4m3 per-page scales of the workgroup's KV heads
+  float ks, vs;  // e4m3 per-page scales of this lane's KV head
 };
-
-// The value of KV head h (0 .. HP-1) among the workgroup's heads.
-template <int HP>
-__device__ inline float head_pick(const float (&x)[2], int h) {
-  if constexpr (HP == 1) return x[0];
-  return h ? x[1] : x[0];
-}
 
 struct Ctx {
   const char* kbase;
@@ -508,7 +502,7 @@ __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const C
                                   const KernelArgs& a, int kvh, int t0, const TilePages& tp,
                                   int lim, bool cross, float m_run, float (&sc)[4], bool& grow) {
   float ks = a.sm_scale_log2;
-  if constexpr (KV == kE4M3 && PAGE16) ks *= head_pick<HP>(tp.ks, c.head_lane);
+  if constexpr (KV == kE4M3 && PAGE16) ks *= tp.ks;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = t0 + row_token<HP>(c.q4, r);
@@ -572,7 +566,7 @@ __device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ct
     for (int e = 0; e < 4; ++e) {
       float vs;
       if constexpr (PAGE16)
-        vs = head_pick<HP>(tp.vs, c.head_lane);
+        vs = tp.vs;
       else
         vs = token_scale(a.v_scale, c, a, kvh, t0 + 4 * c.q4 + e);
       p[e] *= vs;
@@ -945,8 +939,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 #pragma unroll
       for (int s2 = 0; s2 < NS; ++s2) {
         tp.sub[s2].page = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) tp.sub[s2].ks[h] = tp.sub[s2].vs[h] = 1.f;
+        tp.sub[s2].ks = tp.sub[s2].vs = 1.f;
       }
       if constexpr (PAGE16) {
         if (i > 0 && (i % kBlk) == 0) {
@@ -958,10 +951,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
           const int slot = (i % kBlk) * NS + s2;
           tp.sub[s2].page = __builtin_amdgcn_readlane(blk_cur.pid, slot);
           if constexpr (KV == kE4M3) {
+            // the workgroup's heads' scales (uniform), then this lane's head's
 #pragma unroll
             for (int h = 0; h < HP; ++h) {
-              tp.sub[s2].ks[h] = lane_float(blk_cur.ks[h], slot);
-              tp.sub[s2].vs[h] = lane_float(blk_cur.vs[h], slot);
+              const float ksh = lane_float(blk_cur.ks[h], slot);
+              const float vsh = lane_float(blk_cur.vs[h], slot);
+              if (h == 0 || c.head_lane == h) {
+                tp.sub[s2].ks = ksh;
+                tp.sub[s2].vs = vsh;
+              }
             }
           }
         }
@@ -1072,6 +1070,7 @@ DecodeFn pick_pair(int cols) {
 DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size, int hp) {
   if (head_dim != kD) return nullptr;
   const bool p16 = page_size >= 16;
+
   if (hp == 2) {
     if (!p16) return nullptr;
     switch (kv_dtype) {
