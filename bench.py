@@ -41,14 +41,14 @@ METRIC = "KV-read HBM GB/s (% of peak) + µs per batched decode step"
 CSRC = os.path.join(ROOT, "paged_kv_decode_plan_amd", "csrc")
 
 
-ELEM_BITS = {"f32": 32, "bf16": 16, "f16": 16, "e4m3": 8, "e2m1": 4}
+ELEM_BITS = {"f32": 32, "bf16": 16, "f16": 16, "e4m3": 8, "e2m1": 4, "i4": 4}
 
 
 def kv_bytes(w, table, logical: bool = False) -> int:
     """Algorithmic bytes the decode kernel must read: every valid K and V element
     once, plus for e4m3 the fp32 K and V scale of every (page, KV head) (or
-    token and KV head) and for e2m1 the fp32 K and V scale of every (KV head,
-    channel). With a shared prefix (cascade) each group's prefix counts once,
+    token and KV head) and for e2m1 and int4 the fp32 K and V scale of every
+    (KV head, channel). With a shared prefix (cascade) each group's prefix counts once,
     unless `logical` (every request's full context, as plain decode would read
     it)."""
     tokens = int(table["kv_lens"].sum())
@@ -56,7 +56,7 @@ def kv_bytes(w, table, logical: bool = False) -> int:
         groups, prefix = w.shared_prefix
         tokens = tokens - len(table["kv_lens"]) * prefix + groups * prefix
     b = tokens * w.num_kv_heads * w.head_dim * 2 * ELEM_BITS[w.kv_dtype] // 8
-    if w.kv_dtype == "e2m1":
+    if w.kv_dtype in ("e2m1", "i4"):
         b += w.num_kv_heads * w.head_dim * 2 * 4
     elif w.kv_dtype == "e4m3" and w.kv_scale == "token":
         b += tokens * w.num_kv_heads * 2 * 4
@@ -78,9 +78,18 @@ def kernel_source_sha() -> str:
 
 def decode_kernel_name(w) -> str:
     mfma = w.head_dim == 128 and (
-        (w.q_dtype == "bf16" and w.kv_dtype in ("bf16", "e4m3", "e2m1"))
+        (w.q_dtype == "bf16" and w.kv_dtype in ("bf16", "e4m3", "e2m1", "i4"))
         or (w.q_dtype == "f16" and w.kv_dtype == "f16"))
     return "decode_mfma_kernel" if mfma else "decode_kernel"
+
+
+def compute_dtype(w) -> str:
+    """Operand type of the decode kernel's products: the MFMA kernel multiplies
+    16-bit operands (bf16; fp16 for fp16 KV; e4m3, e2m1 and int4 codes widen to
+    bf16 exactly) into fp32 accumulators; the vector-ALU kernel works in fp32."""
+    if decode_kernel_name(w) != "decode_mfma_kernel":
+        return "f32"
+    return "f16" if w.kv_dtype == "f16" else "bf16"
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> dict:
@@ -240,7 +249,7 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
             kv = dcase["kv"].index_select(0, pages)
             if w.kv_dtype == "bf16":
                 kvh = kv.view(torch.int16).cpu().numpy().view(np.uint16)
-            elif w.kv_dtype in ("e4m3", "e2m1"):
+            elif w.kv_dtype in ("e4m3", "e2m1", "i4"):
                 kvh = kv.cpu().numpy().view(np.uint8)
             else:
                 kvh = kv.cpu().numpy()
@@ -252,7 +261,7 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
             if w.kv_dtype == "e4m3":
                 ks = dcase["k_scale"].index_select(0, pages).cpu().numpy()
                 vs = dcase["v_scale"].index_select(0, pages).cpu().numpy()
-            elif w.kv_dtype == "e2m1":
+            elif w.kv_dtype in ("e2m1", "i4"):
                 ks = dcase["k_scale"].cpu().numpy()
                 vs = dcase["v_scale"].cpu().numpy()
             item = (qh, kvh, len(pages), int(dcase["last_page_len"][r]), ks, vs)
@@ -369,7 +378,7 @@ def main(argv=None) -> int:
 
     ws = torch.empty(pk.DEFAULT_WORKSPACE_BYTES, dtype=torch.uint8, device=dev)
     q_dt = dcase["q"].dtype
-    kv_dt = w.kv_dtype if w.kv_dtype in ("e4m3", "e2m1") else dcase["kv"].dtype
+    kv_dt = w.kv_dtype if w.kv_dtype in ("e4m3", "e2m1", "i4") else dcase["kv"].dtype
     cascade = w.shared_prefix is not None
     if cascade:
         # Two levels (shared prefixes once for all their requests' queries,
@@ -567,7 +576,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": compute_dtype(w),
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.batch, "num_qo_heads": w.num_qo_heads,

@@ -58,6 +58,13 @@ extern "C" {
  * "FlashInfer vs FlashAttention-3: GPU Kernel Optimization & FP8 Serving
  * Latency", §"Decision Matrix: Choosing the Right Attention Engine". KV only. */
 #define PKD_DTYPE_E2M1 4
+/* Signed 4-bit integers in two's complement (codes -8 .. 7), two elements per
+ * byte with the lower-indexed one in the low nibble, with fp32 scales per (KV
+ * head, channel): value = code x scale. The int4 PageAttention with
+ * per-channel scaling factors of the same section of the same page, which
+ * gives no encoding; the symmetric two's-complement code is the reading
+ * taken. KV only; layout and scales as for PKD_DTYPE_E2M1. */
+#define PKD_DTYPE_I4 5
 
 /* Columns of one work item as returned by pkd_plan_get_worklist:
  * request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible

@@ -10,6 +10,7 @@ Modules, each citing the passage it follows:
 
 * ``e4m3``      — OCP E4M3FN byte -> value, from the bit formula.
 * ``e2m1``      — OCP FP4 E2M1 code -> value (two codes per byte).
+* ``int4``      — two's-complement int4 code -> value (two codes per byte).
 * ``storage``   — exact widening of stored K/V/q values to float64.
 * ``attention`` — the definition: softmax(scale * q . K^T) . V per request and
                   query head, with K/V gathered through the page table.
@@ -20,5 +21,5 @@ Every function here has a pin in ``tests/test_oracle_*.py`` that checks it
 against something other than itself (brute force, closed forms, invariants,
 library routines, worked examples from the pages).
 """
-from . import attention, e2m1, e4m3, merge, plan, storage  # noqa: F401
+from . import attention, e2m1, e4m3, int4, merge, plan, storage  # noqa: F401
 from .attention import decode, gather_request  # noqa: F401

@@ -47,7 +47,7 @@ from typing import Iterable, Optional
 
 import numpy as np
 
-from . import e2m1
+from . import e2m1, int4
 from .storage import widen
 
 
@@ -73,17 +73,18 @@ def gather_request(kv, indptr, indices, last_page_len, r: int, kv_head: int, kv_
     ``[num_pages, Hkv]`` (one per page and KV head) or ``[num_pages, Hkv,
     page_size]`` (one per token and KV head: the row-wise scaling of
     "FlashInfer vs FlashAttention-3: GPU Kernel Optimization & FP8 Serving
-    Latency", §"Production War Story"). e2m1 rows hold two codes per byte
-    (``[..., D/2]``) and their scales are per channel, ``[Hkv, D]``.
+    Latency", §"Production War Story"). e2m1 and int4 rows hold two codes
+    per byte (``[..., D/2]``) and their scales are per channel, ``[Hkv, D]``.
     """
     page_size = kv.shape[2]
     page, slot = token_locations(indptr, indices, last_page_len, page_size, r)
-    if kv_dtype == "e2m1":
+    if kv_dtype in ("e2m1", "i4"):
         # packed rows [L, D/2] -> [L, D], times the per-channel scale of the head
+        dec = e2m1.decode_packed if kv_dtype == "e2m1" else int4.decode_packed
         ks = np.asarray(k_scale, dtype=np.float32).astype(np.float64)
         vs = np.asarray(v_scale, dtype=np.float32).astype(np.float64)
-        K = e2m1.decode_packed(kv[page, 0, slot, kv_head, :]) * ks[kv_head][None, :]
-        V = e2m1.decode_packed(kv[page, 1, slot, kv_head, :]) * vs[kv_head][None, :]
+        K = dec(kv[page, 0, slot, kv_head, :]) * ks[kv_head][None, :]
+        V = dec(kv[page, 1, slot, kv_head, :]) * vs[kv_head][None, :]
         return K, V
     K = widen(kv[page, 0, slot, kv_head, :], kv_dtype)
     V = widen(kv[page, 1, slot, kv_head, :], kv_dtype)

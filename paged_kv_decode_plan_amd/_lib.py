@@ -23,6 +23,7 @@ DTYPE_BF16 = 1
 DTYPE_E4M3 = 2
 DTYPE_F16 = 3
 DTYPE_E2M1 = 4  # FP4 E2M1, two per byte, per-(KV head, channel) fp32 scales
+DTYPE_I4 = 5    # two's-complement int4, two per byte, per-(KV head, channel) fp32 scales
 ITEM_COLS = 8  # request, page_begin, page_end, kv_len, partial_slot, q_row, q_len, visible
 STAGE_DECODE = 1
 STAGE_MERGE = 2

@@ -42,10 +42,13 @@ int ok() { return PKD_OK; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Bytes of `elems` KV elements (e2m1: two per byte; odd counts are rejected
-// by the callers' alignment checks before this matters).
+// 4-bit KV formats: two elements per byte.
+bool nibbles(int dtype) { return dtype == PKD_DTYPE_E2M1 || dtype == PKD_DTYPE_I4; }
+
+// Bytes of `elems` KV elements (4-bit formats: two per byte; odd counts are
+// rejected by the callers' alignment checks before this matters).
 int64_t kv_elems_bytes(int dtype, int64_t elems) {
-  if (dtype == PKD_DTYPE_E2M1) return elems / 2;
+  if (nibbles(dtype)) return elems / 2;
   return elems * (dtype == PKD_DTYPE_F32 ? 4 : (dtype == PKD_DTYPE_BF16 || dtype == PKD_DTYPE_F16) ? 2 : 1);
 }
 
@@ -58,7 +61,10 @@ int kind_of(int dtype) {
 // of their own).
 int kv_form(int dtype, int per_token) {
   if (per_token) return pkd::kE4M3T;
-  return dtype == PKD_DTYPE_F16 ? pkd::kF16 : dtype == PKD_DTYPE_E2M1 ? pkd::kE2M1 : dtype;
+  return dtype == PKD_DTYPE_F16    ? pkd::kF16
+         : dtype == PKD_DTYPE_E2M1 ? pkd::kE2M1
+         : dtype == PKD_DTYPE_I4   ? pkd::kI4
+                                   : dtype;
 }
 
 bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
@@ -243,7 +249,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     return fail(PKD_ERR_UNSUPPORTED, "q_dtype %d not supported", a->q_dtype);
   if (!is_float(a->out_dtype))
     return fail(PKD_ERR_UNSUPPORTED, "out_dtype %d not supported", a->out_dtype);
-  if (!is_float(a->kv_dtype) && a->kv_dtype != PKD_DTYPE_E4M3 && a->kv_dtype != PKD_DTYPE_E2M1)
+  if (!is_float(a->kv_dtype) && a->kv_dtype != PKD_DTYPE_E4M3 && !nibbles(a->kv_dtype))
     return fail(PKD_ERR_UNSUPPORTED, "kv_dtype %d not supported", a->kv_dtype);
   if (a->kv_scale_per_token != 0 && a->kv_scale_per_token != 1)
     return fail(PKD_ERR_INVALID_ARGUMENT, "kv_scale_per_token must be 0 or 1");
@@ -261,7 +267,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                 "no kernel for head_dim=%d group=%d kv_dtype=%d q_dtype=%d%s", a->head_dim, group,
                 a->kv_dtype, a->q_dtype,
                 a->kv_scale_per_token ? " with row-wise scales (needs bf16 q, head_dim 128)"
-                : a->kv_dtype == PKD_DTYPE_E2M1 ? " (e2m1 KV needs bf16 q and head_dim 128)"
+                : nibbles(a->kv_dtype) ? " (4-bit KV needs bf16 q and head_dim 128)"
                                                 : "");
   // Several new tokens per request: a work item carries up to 16 / group (or
   // 32 / group, below) of one request's tokens, so that its group x tokens
@@ -302,8 +308,8 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   if (max_q > 1 && !pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
                                           q_kind, a->page_size))
     return fail(PKD_ERR_UNSUPPORTED,
-                "several query tokens per request need head_dim 128 and bf16 q with bf16, e4m3 or "
-                "e2m1 KV, or fp16 q with fp16 KV "
+                "several query tokens per request need head_dim 128 and bf16 q with bf16, e4m3, "
+                "e2m1 or int4 KV, or fp16 q with fp16 KV "
                 "(group %d, head_dim %d, kv_dtype %d, q_dtype %d)",
                 group, a->head_dim, a->kv_dtype, a->q_dtype);
   if (a->slots < 0 || a->balance < 0 || a->min_chunk_pages < 0 || a->max_wgs_per_cu < 0)
@@ -544,10 +550,10 @@ int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void
   const pkd_plan_args& a = p->args;
   if (!r->q || !r->k || !r->v || !r->indices || !r->out || !r->workspace)
     return fail(PKD_ERR_INVALID_ARGUMENT, "q, k, v, indices, out and workspace must not be NULL");
-  if ((a.kv_dtype == PKD_DTYPE_E4M3 || a.kv_dtype == PKD_DTYPE_E2M1) &&
+  if ((a.kv_dtype == PKD_DTYPE_E4M3 || nibbles(a.kv_dtype)) &&
       (!r->k_scale || !r->v_scale))
-    return fail(PKD_ERR_INVALID_ARGUMENT, "e4m3 and e2m1 KV need k_scale and v_scale");
-  if ((a.kv_scale_per_token || a.kv_dtype == PKD_DTYPE_E2M1) &&
+    return fail(PKD_ERR_INVALID_ARGUMENT, "e4m3, e2m1 and int4 KV need k_scale and v_scale");
+  if ((a.kv_scale_per_token || nibbles(a.kv_dtype)) &&
       (reinterpret_cast<uintptr_t>(r->k_scale) % 16 || reinterpret_cast<uintptr_t>(r->v_scale) % 16))
     return fail(PKD_ERR_INVALID_ARGUMENT,
                 "row-wise and per-channel scale arrays must be 16-byte aligned");
@@ -559,7 +565,7 @@ int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void
   const int vec_bytes = a.kv_dtype == PKD_DTYPE_E4M3 ? 8 : 16;
   const uintptr_t kp = reinterpret_cast<uintptr_t>(r->k), vp = reinterpret_cast<uintptr_t>(r->v);
   auto stride_ok = [&](int64_t st) {
-    return (a.kv_dtype != PKD_DTYPE_E2M1 || st % 2 == 0) &&
+    return (!nibbles(a.kv_dtype) || st % 2 == 0) &&
            kv_elems_bytes(a.kv_dtype, st) % vec_bytes == 0;
   };
   if (kp % vec_bytes || vp % vec_bytes || !stride_ok(r->page_stride) ||

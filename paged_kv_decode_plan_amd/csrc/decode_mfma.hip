@@ -104,17 +104,17 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 template <int KV>
 constexpr bool fp8() { return KV == kE4M3 || KV == kE4M3T; }
 template <int KV>
-constexpr bool fp4() { return KV == kE2M1; }
+constexpr bool nib4() { return KV == kE2M1 || KV == kI4; }  // 4-bit codes, two per byte
 // 16-bit KV rows (bf16 or fp16): 256 bytes per row at head_dim 128.
 template <int KV>
 constexpr bool wide16() { return KV == kBF16 || KV == kF16; }
 template <int KV>
-constexpr int nsub() { return fp8<KV>() ? PKD_E4M3_NSUB : fp4<KV>() ? PKD_E2M1_NSUB : PKD_BF16_NSUB; }
+constexpr int nsub() { return fp8<KV>() ? PKD_E4M3_NSUB : nib4<KV>() ? PKD_E2M1_NSUB : PKD_BF16_NSUB; }
 // Byte offset of an element offset (e2m1: two elements per byte; offsets
 // handed to this are even).
 template <int KV>
 __device__ inline int64_t kv_bytes(int64_t elems) {
-  if constexpr (fp4<KV>())
+  if constexpr (nib4<KV>())
     return elems >> 1;
   else
     return elems * (wide16<KV>() ? 2 : 1);
@@ -124,7 +124,7 @@ template <int KV>
 constexpr int k_loads() { return wide16<KV>() ? 4 : fp8<KV>() ? 2 : 1; }
 // q operands per lane: four k steps, and for e2m1 a hi and a lo half each.
 template <int KV>
-constexpr int q_ops() { return fp4<KV>() ? 8 : 4; }
+constexpr int q_ops() { return nib4<KV>() ? 8 : 4; }
 // Tokens per sub-tile: 16, or 16 / HP when the 16 rows are HP KV heads' rows.
 template <int HP>
 constexpr int sub_tokens() { return kSub / HP; }
@@ -237,6 +237,21 @@ __device__ inline u32x4_t e2m1x8_to_bf16x8(uint32_t w) {
                  e2m1x2_to_bf16x2<3>(w)};
 }
 
+// Eight int4 codes (a word, element 0 in the low nibble, two's complement)
+// -> eight bf16 holding (code + 8) * 2^-9 exactly. XOR 8 turns code c into
+// the unsigned k = c + 8 in [0, 15], and a byte 0x0k read as e4m3 is exactly
+// k * 2^-9 (subnormals 0..7 and the first binade 8..15 continue one
+// another), so the fp8 conversion widens it. The output visits the word's
+// dims in the order 0, 2, 4, 6, 1, 3, 5, 7 (low nibbles, then high nibbles);
+// the q operand takes the same order, and the +8 and 2^-9 are undone in the
+// score (a per-row term) and in the output.
+__device__ inline u32x4_t i4x8_to_bf16x8(uint32_t w) {
+  const uint32_t x = w ^ 0x88888888u;
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;
+  return u32x4_t{e4m3x2_to_bf16x2(lo, false), e4m3x2_to_bf16x2(lo, true),
+                 e4m3x2_to_bf16x2(hi, false), e4m3x2_to_bf16x2(hi, true)};
+}
+
 template <int KV>
 struct Loads;
 
@@ -273,6 +288,9 @@ struct Loads<kE2M1> {
   uint32_t v[4];
 };
 
+template <>
+struct Loads<kI4> : Loads<kE2M1> {};
+
 // The head_dim index visited by QK k-slot (dc, q, e): bf16 lanes load 8 dims at
 // chunk 4*dc + q; e4m3 lanes load 16 dims at chunk 4*h + q and split them
 // into dc = 2h (first 8) and dc = 2h + 1 (last 8); e2m1 lanes load dims
@@ -281,7 +299,7 @@ template <int KV>
 __device__ inline int qk_dim(int dc, int q, int e) {
   if constexpr (wide16<KV>())
     return 8 * (4 * dc + q) + e;
-  else if constexpr (fp4<KV>())
+  else if constexpr (nib4<KV>())
     return 32 * q + 8 * dc + e;
   else
     return 16 * (4 * (dc >> 1) + q) + 8 * (dc & 1) + e;
@@ -371,7 +389,7 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
       }
       if constexpr (wide16<KV>())
         ld.v[e] = bload16<PKD_V_CPOL>(vr, voff, soff);
-      else if constexpr (fp4<KV>())
+      else if constexpr (nib4<KV>())
         ld.v[e] = bload4<PKD_V_CPOL>(vr, voff, soff);
       else
         ld.v[e] = bload8<PKD_V_CPOL>(vr, voff, soff);
@@ -395,7 +413,7 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
                                        c.head_off + 8 * c.j);
       if constexpr (wide16<KV>())
         ld.v[e] = *reinterpret_cast<const u32x4_t*>(c.vbase + off);
-      else if constexpr (fp4<KV>())
+      else if constexpr (nib4<KV>())
         ld.v[e] = *reinterpret_cast<const uint32_t*>(c.vbase + off);
       else
         ld.v[e] = *reinterpret_cast<const uint2*>(c.vbase + off);
@@ -464,12 +482,13 @@ __device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>(
   if constexpr (wide16<KV>()) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) s = mfma<KV>(ld.k[dc], qb[dc], s);
-  } else if constexpr (fp4<KV>()) {
+  } else if constexpr (nib4<KV>()) {
     // two independent accumulation chains (hi and lo parts of q * k_scale)
     f32x4_t s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
-      const u32x4_t kb = e2m1x8_to_bf16x8(ld.k[0][dc]);
+      const u32x4_t kb =
+          KV == kI4 ? i4x8_to_bf16x8(ld.k[0][dc]) : e2m1x8_to_bf16x8(ld.k[0][dc]);
       s = mfma<KV>(kb, qb[dc], s);
       s2 = mfma<KV>(kb, qb[4 + dc], s2);
     }
@@ -500,7 +519,8 @@ __device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>(
 template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const Ctx& c,
                                   const KernelArgs& a, int kvh, int t0, const TilePages& tp,
-                                  int lim, bool cross, float m_run, float (&sc)[4], bool& grow) {
+                                  int lim, bool cross, float corr, float m_run, float (&sc)[4],
+                                  bool& grow) {
   float ks = a.sm_scale_log2;
   if constexpr (KV == kE4M3 && PAGE16) ks *= tp.ks;
 #pragma unroll
@@ -510,7 +530,8 @@ __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const C
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
     if constexpr (KV == kE4M3T) kr = ks * ld.ks[r];
     const bool ok = (FULL || t < lim) && (HP == 1 || !cross);
-    const float v = ok ? s[r] * kr : -INFINITY;
+    // int4: remove the +8 of the widened K codes (corr = 8 * sum of q')
+    const float v = ok ? (KV == kI4 ? s[r] - corr : s[r]) * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
   }
@@ -559,7 +580,7 @@ __device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ct
     // masked scores give 0, also when m_run = -inf (head pairs mask the
     // other head's lanes in full tiles too, while m_run is already finite)
     if constexpr (!FULL) p[e] = sc[e] == -INFINITY ? 0.f : p[e];
-    d_run += p[e];
+    if constexpr (KV != kI4) d_run += p[e];
   }
   if constexpr (KV == kE4M3) {
 #pragma unroll
@@ -578,6 +599,14 @@ __device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ct
   }
   split16<KV>(p[0], p[1], p_hi.x, p_lo.x);
   split16<KV>(p[2], p[3], p_hi.y, p_lo.y);
+  if constexpr (KV == kI4) {
+    // d is the sum of the weights P.V is given (hi + lo), so that the +8 of
+    // the int4 V operands cancels exactly against 8 d in the epilogue
+    auto lo16 = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
+    auto hi16 = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
+    d_run += (lo16(p_hi.x) + lo16(p_lo.x)) + (hi16(p_hi.x) + hi16(p_lo.x)) +
+             (lo16(p_hi.y) + lo16(p_lo.y)) + (hi16(p_hi.y) + hi16(p_lo.y));
+  }
 }
 
 // V as the B operand of P.V for output columns nc: four 16-bit values,
@@ -585,13 +614,14 @@ __device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ct
 // unrolling).
 template <int KV>
 __device__ inline uint2 v_operand(const Loads<KV>& ld, int nc) {
+  static_assert(KV != kI4, "int4 V operands come from i4_v_words");
   uint2 vb;
   if constexpr (wide16<KV>()) {
     const int w = nc >> 1;
     const bool hi = nc & 1;
     vb.x = pack_halves(ld.v[0][w], ld.v[1][w], hi);
     vb.y = pack_halves(ld.v[2][w], ld.v[3][w], hi);
-  } else if constexpr (fp4<KV>()) {
+  } else if constexpr (nib4<KV>()) {
     // byte nc/2 of each token's word holds dims 8*j + nc (nibble nc&1)
     const bool hi = nc & 1;
     uint32_t x[4];
@@ -653,6 +683,40 @@ __device__ inline uint2 fp4_v_operand(const VPairs& vp, int nc) {
   return vb;
 }
 
+// int4 V of one sub-tile for P.V: the four token words of a lane (dims
+// 8*j..+8 of tokens 4*q4 + e) as unsigned k = code + 8 in the low nibble of
+// bytes, the bytes of tokens 2h and 2h + 1 side by side, so that one fp8
+// conversion (see i4x8_to_bf16x8) yields a B-operand word: w[h][x] holds
+// dims (2i, 2i') of tokens (2h, 2h + 1) from the low nibbles (x = 0: i = 0,
+// i' = 1; x = 1: i = 2, i' = 3) and dims (2i + 1, 2i' + 1) from the high
+// nibbles (x = 2, 3).
+struct I4Words {
+  uint32_t w[2][4];
+};
+__device__ inline I4Words i4_v_words(const uint32_t (&v)[4]) {
+  I4Words r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = v[2 * h] ^ 0x88888888u, b = v[2 * h + 1] ^ 0x88888888u;
+    const uint32_t alo = a & 0x0F0F0F0Fu, ahi = (a >> 4) & 0x0F0F0F0Fu;
+    const uint32_t blo = b & 0x0F0F0F0Fu, bhi = (b >> 4) & 0x0F0F0F0Fu;
+    // bytes (a.i, b.i, a.i', b.i'): selector bytes 0-3 pick the second
+    // operand's bytes, 4-7 the first's
+    r.w[h][0] = __builtin_amdgcn_perm(blo, alo, 0x05010400u);
+    r.w[h][1] = __builtin_amdgcn_perm(blo, alo, 0x07030602u);
+    r.w[h][2] = __builtin_amdgcn_perm(bhi, ahi, 0x05010400u);
+    r.w[h][3] = __builtin_amdgcn_perm(bhi, ahi, 0x07030602u);
+  }
+  return r;
+}
+// B operand of output columns nc (dim 8*j + nc): (k * 2^-9) of tokens 0, 1
+// and 2, 3.
+__device__ inline uint2 i4_v_operand(const I4Words& iw, int nc) {
+  const int x = (nc & 1 ? 2 : 0) + ((nc >> 2) & 1);
+  const bool second = (nc >> 1) & 1;  // dim 2i' of the word's pair of dims
+  return uint2{e4m3x2_to_bf16x2(iw.w[0][x], second), e4m3x2_to_bf16x2(iw.w[1][x], second)};
+}
+
 // Per column group (16 S columns each; two groups when a work item carries
 // 17-32 query rows): the q operands, the running softmax state and O of the
 // lane's column, and the tokens that column's row sees. Both groups consume
@@ -663,6 +727,7 @@ struct Groups {
   f32x4_t acc[NG][8];
   float m_run[NG];  // reference max (log2 units), uniform over quarters
   float d_run[NG];  // sum of p over this lane's tokens
+  float corr[NG];   // int4: what the +8 of the K codes adds to this column's scores
   int lim[NG];      // tokens of the item seen by this lane's row (column j of S)
   bool cross[NG];   // head pairs: the lane's S rows are not its column's head (masked)
 };
@@ -679,7 +744,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
     float sc[1][4];
     bool grow = false;
     scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, gs.lim[g], gs.cross[g],
-                                     gs.m_run[g], sc[0], grow);
+                                     gs.corr[g], gs.m_run[g], sc[0], grow);
     move_max<FULL, 1>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
     probs<KV, PAGE16, FULL, HP>(sc[0], ld, c, a, kvh, t0, tp, gs.m_run[g], gs.d_run[g], p_hi[g],
                                 p_lo[g]);
@@ -714,9 +779,9 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
     float sc[2][4];
     bool grow = false;
     scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, gs.lim[g], gs.cross[g],
-                                     gs.m_run[g], sc[0], grow);
+                                     gs.corr[g], gs.m_run[g], sc[0], grow);
     scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, gs.lim[g], gs.cross[g],
-                                     gs.m_run[g], sc[1], grow);
+                                     gs.corr[g], gs.m_run[g], sc[1], grow);
     move_max<FULL, 2>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
     uint2 pa_hi, pa_lo, pb_hi, pb_lo;
     probs<KV, PAGE16, FULL, HP>(sc[0], la, c, a, kvh, t0, ta, gs.m_run[g], gs.d_run[g], pa_hi,
@@ -727,14 +792,22 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
     p_lo[g] = u32x4_t{pa_lo.x, pa_lo.y, pb_lo.x, pb_lo.y};
   }
   VPairs vpa, vpb;
-  if constexpr (fp4<KV>() && PKD_FP4_VT) {
+  I4Words ia, ib;
+  if constexpr (KV == kE2M1 && PKD_FP4_VT) {
     vpa = fp4_v_pairs(la.v);
     vpb = fp4_v_pairs(lb.v);
+  }
+  if constexpr (KV == kI4) {
+    ia = i4_v_words(la.v);
+    ib = i4_v_words(lb.v);
   }
 #pragma unroll
   for (int nc = 0; nc < 8; ++nc) {
     uint2 va, vb;
-    if constexpr (fp4<KV>() && PKD_FP4_VT) {
+    if constexpr (KV == kI4) {
+      va = i4_v_operand(ia, nc);
+      vb = i4_v_operand(ib, nc);
+    } else if constexpr (KV == kE2M1 && PKD_FP4_VT) {
       va = fp4_v_operand(vpa, nc);
       vb = fp4_v_operand(vpb, nc);
     } else {
@@ -809,7 +882,7 @@ __device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, in
 // the same 256, as do head pairs (two scales per page for e4m3).
 template <int KV, bool PAGE16, int HP, int G>
 constexpr int waves_per_simd() {
-  return KV == kE4M3T || fp4<KV>() || HP > 1 || G > 16 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
+  return KV == kE4M3T || nib4<KV>() || HP > 1 || G > 16 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
 }
 
 // G: S columns (query rows) per workgroup. HP = 2: the workgroup's "KV head"
@@ -878,6 +951,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     const int col_head = HP == 1 ? 0 : hh >> (a.group_log2 - HPL);
     gs.cross[g] = HP > 1 && c.head_lane != col_head;
     u32x4_t (&qb)[q_ops<KV>()] = gs.qb[g];
+    float qsum = 0.f;  // int4: sum of this lane's q' (hi + lo as fed)
     const uint16_t* qp =
         static_cast<const uint16_t*>(a.q) +
         (int64_t(it.q_row + qi) * a.num_qo_heads + (int64_t(kvh) << a.group_log2) + hh) * kD;
@@ -885,21 +959,43 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     for (int dc = 0; dc < 4; ++dc) {
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (row_ok) w = *reinterpret_cast<const u32x4_t*>(qp + qk_dim<KV>(dc, c.q4, 0));
-      if constexpr (fp4<KV>()) {
+      if constexpr (nib4<KV>()) {
         // q * k_scale over this step's eight dims, as hi + lo bf16
         const float* ksp = a.k_scale + int64_t(c.kvh + col_head) * kD + qk_dim<KV>(dc, c.q4, 0);
         const float4 s0 = *reinterpret_cast<const float4*>(ksp);
         const float4 s1 = *reinterpret_cast<const float4*>(ksp + 4);
         const float ksv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         u32x4_t hi, lo;
+        if constexpr (KV == kI4) {
+          // q' = q * k_scale * 2^9 (the widened K codes carry 2^-9), in the
+          // dim order of i4x8_to_bf16x8: words (0, 2), (4, 6), (1, 3), (5, 7)
+          float qf[8];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float q0 = __builtin_bit_cast(float, w[x] << 16) * ksv[2 * x];
-          const float q1 = __builtin_bit_cast(float, w[x] & 0xffff0000u) * ksv[2 * x + 1];
-          uint32_t h, l;
-          split16<KV>(q0, q1, h, l);
-          hi[x] = h;
-          lo[x] = l;
+          for (int x = 0; x < 4; ++x) {
+            qf[2 * x] = __builtin_bit_cast(float, w[x] << 16) * ksv[2 * x] * 512.f;
+            qf[2 * x + 1] = __builtin_bit_cast(float, w[x] & 0xffff0000u) * ksv[2 * x + 1] * 512.f;
+          }
+          constexpr int kOrd[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            uint32_t h, l;
+            split16<KV>(qf[kOrd[2 * x]], qf[kOrd[2 * x + 1]], h, l);
+            hi[x] = h;
+            lo[x] = l;
+            qsum += (__builtin_bit_cast(float, h << 16) + __builtin_bit_cast(float, l << 16)) +
+                    (__builtin_bit_cast(float, h & 0xffff0000u) +
+                     __builtin_bit_cast(float, l & 0xffff0000u));
+          }
+        } else {
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const float q0 = __builtin_bit_cast(float, w[x] << 16) * ksv[2 * x];
+            const float q1 = __builtin_bit_cast(float, w[x] & 0xffff0000u) * ksv[2 * x + 1];
+            uint32_t h, l;
+            split16<KV>(q0, q1, h, l);
+            hi[x] = h;
+            lo[x] = l;
+          }
         }
         qb[dc] = hi;
         qb[4 + dc] = lo;
@@ -907,6 +1003,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
         qb[dc] = w;
       }
     }
+    // int4: the K operand is (code + 8) * 2^-9, so each score carries
+    // 8 * 2^-9 * (sum of q' over all 128 dims); the four quarters of a
+    // column hold 32 dims each
+    qsum += __shfl_xor(qsum, 16, 64);
+    qsum += __shfl_xor(qsum, 32, 64);
+    gs.corr[g] = qsum * (1.f / 64.f);
   }
 
 #pragma unroll
@@ -1000,7 +1102,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     f32x4_t (&acc)[8] = gs.acc[g];
-    if constexpr (fp4<KV>()) {
+    float d_run = gs.d_run[g];
+    d_run += __shfl_xor(d_run, 16, 64);
+    d_run += __shfl_xor(d_run, 32, 64);
+    if constexpr (nib4<KV>()) {
       // V channel scales: column j of MFMA nc is dim 8*j + nc, of the KV head
       // of O row 4*q4 + r (row / query heads per KV head, within the pair)
 #pragma unroll
@@ -1011,13 +1116,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
         const float4 s0 = *reinterpret_cast<const float4*>(vsp);
         const float4 s1 = *reinterpret_cast<const float4*>(vsp + 4);
         const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+        if constexpr (KV == kI4) {
+          // O holds sum P * (code + 8) * 2^-9 for row 4*q4 + r, whose d
+          // (the sum of P, in column lane 4*q4 + r) removes the + 8
+          const float dr = __shfl(d_run, 4 * q4 + r, 64) * (1.f / 64.f);
 #pragma unroll
-        for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= vsv[nc];
+          for (int nc = 0; nc < 8; ++nc) acc[nc][r] = (acc[nc][r] - dr) * (vsv[nc] * 512.f);
+        } else {
+#pragma unroll
+          for (int nc = 0; nc < 8; ++nc) acc[nc][r] *= vsv[nc];
+        }
       }
     }
-    float d_run = gs.d_run[g];
-    d_run += __shfl_xor(d_run, 16, 64);
-    d_run += __shfl_xor(d_run, 32, 64);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int h = 16 * g + 4 * q4 + r;
@@ -1043,8 +1153,8 @@ DecodeFn pick_group(int g) {
     case 4: return decode_mfma_kernel<KV, 4, P16, 1>;
     case 8: return decode_mfma_kernel<KV, 8, P16, 1>;
     case 16: return decode_mfma_kernel<KV, 16, P16, 1>;
-    case 32:  // two column groups (not e2m1: its q hi/lo pairs would not fit the registers)
-      if constexpr (!fp4<KV>()) return decode_mfma_kernel<KV, 32, P16, 1>;
+    case 32:  // two column groups (not 4-bit KV: its q hi/lo pairs would not fit the registers)
+      if constexpr (!nib4<KV>()) return decode_mfma_kernel<KV, 32, P16, 1>;
       return nullptr;
     default: return nullptr;
   }
@@ -1058,8 +1168,8 @@ DecodeFn pick_pair(int cols) {
     case 4: return decode_mfma_kernel<KV, 4, true, 2>;
     case 8: return decode_mfma_kernel<KV, 8, true, 2>;
     case 16: return decode_mfma_kernel<KV, 16, true, 2>;
-    case 32:  // two column groups (not e2m1, as for one head)
-      if constexpr (!fp4<KV>()) return decode_mfma_kernel<KV, 32, true, 2>;
+    case 32:  // two column groups (not 4-bit KV, as for one head)
+      if constexpr (!nib4<KV>()) return decode_mfma_kernel<KV, 32, true, 2>;
       return nullptr;
     default: return nullptr;
   }
@@ -1079,6 +1189,7 @@ DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size,
       case kE4M3T: return pick_pair<kE4M3T>(rows);
       case kF16: return pick_pair<kF16>(rows);
       case kE2M1: return pick_pair<kE2M1>(rows);
+      case kI4: return pick_pair<kI4>(rows);
       default: return nullptr;
     }
   }
@@ -1089,6 +1200,7 @@ DecodeFn mfma_decode_kernel(int kv_dtype, int head_dim, int rows, int page_size,
     case kE4M3T: return p16 ? pick_group<kE4M3T, true>(rows) : pick_group<kE4M3T, false>(rows);
     case kF16: return p16 ? pick_group<kF16, true>(rows) : pick_group<kF16, false>(rows);
     case kE2M1: return p16 ? pick_group<kE2M1, true>(rows) : pick_group<kE2M1, false>(rows);
+    case kI4: return p16 ? pick_group<kI4, true>(rows) : pick_group<kI4, false>(rows);
     default: return nullptr;
   }
 }

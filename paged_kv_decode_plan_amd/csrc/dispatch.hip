@@ -1,8 +1,9 @@
 // Kernel choice and launch for the decode stage.
 //
 // The MFMA kernel runs wherever both contractions can take bf16 operands
-// exactly: bf16, e4m3 or e2m1 KV with bf16 queries and head_dim 128 (group
-// sizes 1..32; 32 not for e2m1), and fp16 KV with fp16 queries on fp16 MFMA.
+// exactly: bf16, e4m3, e2m1 or int4 KV with bf16 queries and head_dim 128
+// (group sizes 1..32; 32 not for the 4-bit formats), and fp16 KV with fp16
+// queries on fp16 MFMA.
 // fp32 KV or queries, and head_dim 64, use the vector-ALU kernel, which
 // handles one query token per request only. A work item of several new
 // tokens of a request puts group x tokens rows (at most 32: one or two groups
@@ -26,11 +27,11 @@ static int pow2_ceil(int x) {
   return p;
 }
 
-// Forms the MFMA kernel takes: bf16 queries over bf16, e4m3 or e2m1 KV (both
+// Forms the MFMA kernel takes: bf16 queries over bf16, e4m3, e2m1 or int4 KV (both
 // contractions on bf16 MFMA), fp16 queries over fp16 KV (fp16 MFMA).
 static bool mfma_form(int kv_dtype, int q_kind) {
   return (q_kind == kQBF16 && (kv_dtype == kBF16 || kv_dtype == kE4M3 || kv_dtype == kE4M3T ||
-                               kv_dtype == kE2M1)) ||
+                               kv_dtype == kE2M1 || kv_dtype == kI4)) ||
          (q_kind == kQF16 && kv_dtype == kF16);
 }
 
@@ -48,7 +49,7 @@ static DecodeFn choose(int kv_dtype, int head_dim, int group, int rows, int q_ki
   // The vector-ALU kernel: one token per request, fp32 or bf16 q over fp32,
   // bf16 or e4m3 KV (per-page scales).
   if (rows != group || q_kind == kQF16 || kv_dtype == kE4M3T || kv_dtype == kF16 ||
-      kv_dtype == kE2M1)
+      kv_dtype == kE2M1 || kv_dtype == kI4)
     return nullptr;
   return valu_decode_kernel(kv_dtype, head_dim, group);
 }
@@ -94,7 +95,7 @@ bool decode_uses_mfma(int kv_dtype, int head_dim, int group, int rows, int q_kin
 #endif
 int decode_heads_per_wg(int kv_dtype, int head_dim, int group, int rows, int q_kind,
                         int page_size, int num_kv_heads) {
-  const int hp = kv_dtype == kE2M1 ? PKD_HEADS_E2M1
+  const int hp = (kv_dtype == kE2M1 || kv_dtype == kI4) ? PKD_HEADS_E2M1
                  : (kv_dtype == kE4M3 || kv_dtype == kE4M3T) ? PKD_HEADS_E4M3
                  : (kv_dtype == kBF16 || kv_dtype == kF16) ? PKD_HEADS_BF16
                                                            : 1;
@@ -131,7 +132,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream, hipEvent_t s
   a.part_o = L.part_o;
   a.part_md = L.part_md;
   a.num_items = L.num_items;
-  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1)
+  a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1 ||
+                 L.kv_dtype == kI4)
                     ? 8
                     : PKD_XCD_GROUP_16BIT;
   // A pair of KV heads is one workgroup "head" of 2 x group query heads.

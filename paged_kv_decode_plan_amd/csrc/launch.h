@@ -8,9 +8,10 @@
 namespace pkd {
 
 // KV element formats as the kernels see them: kE4M3T is e4m3 with one scale
-// per (token, KV head) instead of one per (page, KV head); kE2M1 is FP4 E2M1,
-// two elements per byte, with one scale per (KV head, channel).
-enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE4M3T = 3, kF16 = 4, kE2M1 = 5 };
+// per (token, KV head) instead of one per (page, KV head); kE2M1 is FP4 E2M1
+// and kI4 two's-complement int4, both two elements per byte, with one scale
+// per (KV head, channel).
+enum : int { kF32 = 0, kBF16 = 1, kE4M3 = 2, kE4M3T = 3, kF16 = 4, kE2M1 = 5, kI4 = 6 };
 // Query / output element formats.
 enum : int { kQF32 = 0, kQBF16 = 1, kQF16 = 2 };
 

@@ -35,6 +35,8 @@ def _dtype_code(dt) -> int:
         return _lib.DTYPE_F16
     if dt in (getattr(torch, "float4_e2m1fn_x2", "e2m1"), "e2m1", "float4_e2m1fn_x2"):
         return _lib.DTYPE_E2M1
+    if dt in ("i4", "int4"):
+        return _lib.DTYPE_I4
     raise ValueError(f"unsupported dtype {dt}")
 
 
@@ -214,7 +216,9 @@ class BatchDecodeWithPagedKVCacheWrapper:
         (token, KV head). FP4 E2M1 KV (``kv_data_type`` "e2m1" or
         ``torch.float4_e2m1fn_x2``) is a byte pool ``[..., head_dim // 2]``
         (uint8 or float4_e2m1fn_x2, element 2i in the low nibble of byte i)
-        with scales ``[num_kv_heads, head_dim]`` per channel."""
+        with scales ``[num_kv_heads, head_dim]`` per channel; int4 KV
+        (``kv_data_type`` "i4" or "int4": two's-complement codes -8 .. 7,
+        value = code x scale) is a uint8 pool of the same layout."""
         import torch
         if pos_encoding_mode != "NONE":
             raise ValueError("only pos_encoding_mode='NONE' is supported")
@@ -262,7 +266,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         if q.shape != (p.query_rows, p.num_qo_heads, p.head_dim) or not q.is_contiguous():
             raise ValueError(
                 f"q must be contiguous [{p.query_rows}, {p.num_qo_heads}, {p.head_dim}]")
-        fp4 = p.kv_dtype == _lib.DTYPE_E2M1
+        fp4 = p.kv_dtype in (_lib.DTYPE_E2M1, _lib.DTYPE_I4)  # 4-bit codes, two per byte
         kv_ok = (k.dtype in (torch.uint8, getattr(torch, "float4_e2m1fn_x2", torch.uint8)) if fp4
                  else _dtype_code(k.dtype) == p.kv_dtype)
         if _dtype_code(q.dtype) != p.q_dtype or not kv_ok:
@@ -284,7 +288,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         a.q = q.data_ptr()
         a.k = k.data_ptr()
         a.v = v.data_ptr()
-        per = 2 if fp4 else 1  # strides in elements: two e2m1 codes per byte
+        per = 2 if fp4 else 1  # strides in elements: two 4-bit codes per byte
         a.page_stride, a.token_stride, a.head_stride = (per * k.stride(0), per * k.stride(1),
                                                         per * k.stride(2))
         a.indices = self._indices.data_ptr()
@@ -300,7 +304,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
         elif fp4:
             want = (p.num_kv_heads, p.head_dim)
             if k_scale is None or v_scale is None:
-                raise ValueError(f"e2m1 KV needs k_scale and v_scale {list(want)}")
+                raise ValueError(f"4-bit KV needs k_scale and v_scale {list(want)}")
             for s in (k_scale, v_scale):
                 if s.dtype != torch.float32 or not s.is_contiguous() or tuple(s.shape) != want:
                     raise ValueError(f"scales must be contiguous float32 {list(want)}")

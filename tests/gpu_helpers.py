@@ -8,9 +8,10 @@ import torch
 import paged_kv_decode_plan_amd as pk
 from oracle import attention
 
-# e2m1 is compared against the same dequantised values with the arithmetic of
-# the bf16 path (exact widening, fp32 accumulation), so it keeps 2e-3.
-TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "e4m3": 3e-2, "e2m1": 2e-3}
+# e2m1 and int4 are compared against the same dequantised values with the
+# arithmetic of the bf16 path (exact widening, fp32 accumulation), so they keep
+# 2e-3.
+TOL = {"f32": 2e-3, "bf16": 2e-3, "f16": 2e-3, "e4m3": 3e-2, "e2m1": 2e-3, "i4": 2e-3}
 DEV = "cuda:0"
 
 
@@ -36,7 +37,7 @@ def to_device(case: dict, device=DEV) -> dict:
         "workload": w,
         "qo_indptr": case.get("qo_indptr"),
     }
-    if w.kv_dtype in ("e4m3", "e2m1"):
+    if w.kv_dtype in ("e4m3", "e2m1", "i4"):
         d["k_scale"] = torch.from_numpy(case["k_scale"]).to(device).contiguous()
         d["v_scale"] = torch.from_numpy(case["v_scale"]).to(device).contiguous()
     return d
@@ -60,7 +61,8 @@ def run_hip(dcase: dict, out_dtype="f32", slots=0, balance=0, min_chunk_pages=0,
     wrapper.plan(dcase["indptr"], dcase["indices"] if indices is None else indices,
                  dcase["last_page_len"], w.num_qo_heads, w.num_kv_heads, w.head_dim,
                  w.page_size, q_data_type=dcase["q"].dtype,
-                 kv_data_type=(w.kv_dtype if w.kv_dtype in ("e4m3", "e2m1") else dcase["kv"].dtype),
+                 kv_data_type=(w.kv_dtype if w.kv_dtype in ("e4m3", "e2m1", "i4")
+                               else dcase["kv"].dtype),
                  out_data_type=odt, sm_scale=w.scale(), slots=slots, balance=balance,
                  min_chunk_pages=min_chunk_pages, qo_indptr=dcase.get("qo_indptr"),
                  kv_scale=w.kv_scale)
@@ -137,7 +139,7 @@ def sample_request_case(dcase: dict, r: int) -> dict:
     if w.kv_dtype == "e4m3":
         sub["k_scale"] = dcase["k_scale"].index_select(0, pages).cpu().numpy()
         sub["v_scale"] = dcase["v_scale"].index_select(0, pages).cpu().numpy()
-    elif w.kv_dtype == "e2m1":  # per channel: not tied to pages
+    elif w.kv_dtype in ("e2m1", "i4"):  # per channel: not tied to pages
         sub["k_scale"] = dcase["k_scale"].cpu().numpy()
         sub["v_scale"] = dcase["v_scale"].cpu().numpy()
     return sub

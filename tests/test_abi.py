@@ -74,6 +74,8 @@ def _create(**kw):
     (dict(num_qo_heads=32, q_dtype=_lib.DTYPE_F32), _lib.PKD_ERR_UNSUPPORTED),  # group 16, fp32 q
     (dict(page_size=12), _lib.PKD_ERR_UNSUPPORTED),
     (dict(kv_dtype=7), _lib.PKD_ERR_UNSUPPORTED),
+    (dict(kv_dtype=_lib.DTYPE_I4, q_dtype=_lib.DTYPE_F32), _lib.PKD_ERR_UNSUPPORTED),  # int4: bf16 q
+    (dict(kv_dtype=_lib.DTYPE_I4, head_dim=64), _lib.PKD_ERR_UNSUPPORTED),             # int4: D 128
     (dict(q_dtype=_lib.DTYPE_E4M3), _lib.PKD_ERR_UNSUPPORTED),
     (dict(out_dtype=_lib.DTYPE_E4M3), _lib.PKD_ERR_UNSUPPORTED),
     (dict(sm_scale=-1.0), _lib.PKD_ERR_INVALID_ARGUMENT),

@@ -1,7 +1,7 @@
 """Seeded random configurations against the oracle.
 
 Each case draws a KV format (fp32, bf16, fp16, e4m3 with per-page or per-token
-scales, e2m1), a query/KV head layout (group 1-32, 1-4 KV heads: single heads
+scales, e2m1 or int4), a query/KV head layout (group 1-32, 1-4 KV heads: single heads
 and pairs), a page size, ragged lengths (page-aligned and not), one or several
 new tokens per request, an automatic or forced split and an output dtype, and
 compares the HIP path with the oracle at the format's tolerance.
@@ -23,13 +23,17 @@ def draw_case(seed: int) -> dict:
     kv = str(rng.choice(["f32", "bf16", "f16", "e4m3", "e4m3t", "e2m1"]))
     kv_scale = "token" if kv == "e4m3t" else "page"
     kv = "e4m3" if kv == "e4m3t" else kv
-    mfma = kv in ("bf16", "f16", "e2m1") or (kv == "e4m3" and (kv_scale == "token" or rng.random() < 0.7))
+    # half of the 4-bit cases are int4 (a stream of its own, so that the other
+    # cases' draws do not move)
+    if kv == "e2m1" and np.random.default_rng([seed, 4]).random() < 0.5:
+        kv = "i4"
+    mfma = kv in ("bf16", "f16", "e2m1", "i4") or (kv == "e4m3" and (kv_scale == "token" or rng.random() < 0.7))
     if kv == "f32":
         mfma = False
     d = 128 if (mfma or rng.random() < 0.5) else 64
     if mfma:
         qd = "f16" if kv == "f16" else "bf16"
-        g = int(rng.choice([1, 2, 4, 8, 16] + ([32] if kv != "e2m1" else [])))
+        g = int(rng.choice([1, 2, 4, 8, 16] + ([32] if kv not in ("e2m1", "i4") else [])))
     else:
         qd = "f32" if kv == "f32" else str(rng.choice(["f32", "bf16"]))
         g = int(rng.choice([1, 2, 4, 8]))

@@ -143,3 +143,21 @@ def test_rowwise_scale_slot_mixup_is_caught():
     out, _ = attention.decode_case(wrong)
     bo, _ = brute_force(case, w.scale())
     assert not np.allclose(out, bo, rtol=1e-9, atol=1e-9)
+
+
+@pytest.mark.parametrize("mistake", ["unsigned", "offset_binary", "high_nibble_first"])
+def test_int4_decoding_mistakes_are_caught(mistake, monkeypatch):
+    """A plausible misreading of the int4 codes (no sign extension, an
+    offset-binary code, the high nibble first) fails the int4 pins."""
+    from oracle import int4
+    if mistake == "unsigned":
+        monkeypatch.setattr(int4, "_TABLE", np.arange(16, dtype=np.float64))
+    elif mistake == "offset_binary":
+        monkeypatch.setattr(int4, "_TABLE", np.arange(16, dtype=np.float64) - 8)
+    else:
+        t = int4.table()
+        monkeypatch.setattr(int4, "decode_packed", lambda b: np.stack(
+            [t[np.asarray(b) >> 4], t[np.asarray(b) & 0xF]], axis=-1).reshape(
+                np.asarray(b).shape[:-1] + (-1,)))
+    got = int4.decode_packed(np.array([[0x8F, 0x70, 0x19]], np.uint8))[0]
+    assert not np.array_equal(got, [-1.0, -8.0, 0.0, 7.0, -7.0, 1.0])

@@ -269,11 +269,11 @@ def test_e2m1_plans_match_the_oracle():
     (8, 4, 16, [0, 2, 3], 4, 4),   # two new tokens: 8 rows per head, pairs
     (8, 4, 16, [0, 9, 10], 8, 8),  # more than 16 rows per head: one head
 ])
-@pytest.mark.parametrize("kv", ["e2m1", "e4m3"])
+@pytest.mark.parametrize("kv", ["e2m1", "i4", "e4m3"])
 def test_head_pair_workgroups_per_item(kv, hkv, g, P, qo, want_e2m1, want_e4m3):
     info, *_ = pk.plan_partition([0, 3, 5], [5, P], hkv * g, hkv, 128, P, kv_dtype=kv,
                                  q_dtype="bf16", qo_indptr=qo)
-    assert info["units_per_item"] == (want_e2m1 if kv == "e2m1" else want_e4m3)
+    assert info["units_per_item"] == (want_e2m1 if kv in ("e2m1", "i4") else want_e4m3)
 
 
 def test_many_split_workgroups_keep_the_merge_kernel():

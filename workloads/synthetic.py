@@ -14,7 +14,8 @@ bytes itself):
   contiguous). ``"e2m1"`` storage is packed FP4 E2M1 codes as ``uint8``
   ``[num_pages, 2, page_size, num_kv_heads, head_dim / 2]`` (element 2i in the
   low nibble of byte i) with fp32 per-channel scales ``k_scale``/``v_scale``
-  of shape ``[num_kv_heads, head_dim]``.
+  of shape ``[num_kv_heads, head_dim]``; ``"i4"`` storage is the same with
+  two's-complement int4 codes (-8 .. 7) in the nibbles.
 * ``q`` is ``[rows, num_qo_heads, head_dim]`` in ``"f32"`` or ``"bf16"``
   storage: one row per request, or, for a workload with several new tokens
   per request, the ragged rows ``qo_indptr[r]:qo_indptr[r+1]`` of request r
@@ -39,12 +40,14 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-KV_DTYPES = ("f32", "bf16", "f16", "e4m3", "e2m1")
+KV_DTYPES = ("f32", "bf16", "f16", "e4m3", "e2m1", "i4")
 Q_DTYPES = ("f32", "bf16", "f16")
 E4M3_MAX = 448.0
 BF16_NAN_BITS = 0x7FC0
 E4M3_NAN_BYTE = 0x7F
 E2M1_POISON_BYTE = 0x77  # E2M1 has no NaN: both codes +6, the largest value
+I4_POISON_BYTE = 0x77  # int4 has no NaN: both codes +7, the largest value
+I4_STEPS_PER_SIGMA = 7.0 / 3.0  # int4 codes: 3 standard deviations of a channel map to 7
 
 
 @dataclasses.dataclass(frozen=True)
@@ -119,6 +122,9 @@ CONFIGS = {
     # FP4 (E2M1) KV with per-channel fp32 scales, the fp8 workload's shape.
     "fp4_kv_e2m1": Workload(
         "fp4_kv_e2m1", 128, 32, 8, 128, 16, "e2m1", "bf16", ("uniform", 1024, 32768)),
+    # int4 KV (two's complement) with per-channel fp32 scales, the same shape.
+    "int4_kv": Workload(
+        "int4_kv", 128, 32, 8, 128, 16, "i4", "bf16", ("uniform", 1024, 32768)),
     # Cascade: 64 requests share one 8192-token prefix (a long system prompt or
     # document) and each has 512 tokens of its own.
     "cascade_prefix8k_bf16": Workload(
@@ -317,8 +323,10 @@ def _pack_nibbles(codes: np.ndarray) -> np.ndarray:
 
 def _channel_magnitudes(draw, shape):
     """Per-(K/V, KV head, channel) magnitudes m = exp(0.5 z): values are m * z'
-    for standard normal z', stored as E2M1 codes of z' / s with scale s = m / 2
-    (so codes saturate at 3 standard deviations of their channel)."""
+    for standard normal z', stored as 4-bit codes of m z' / s: E2M1 with scale
+    s = m / 2 (codes saturate at 3 standard deviations of their channel), int4
+    with s = 3 m / 7 (7 at 3 standard deviations, round half to even, clipped
+    to -8 .. 7)."""
     return np.exp(0.5 * draw(shape))
 
 
@@ -344,6 +352,12 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
         scale = (m / 2).astype(np.float32)
         kv = _pack_nibbles(_e2m1_codes(2 * pool32))
         k_scale, v_scale = scale[0].copy(), scale[1].copy()
+    elif w.kv_dtype == "i4":
+        m = _channel_magnitudes(lambda sh: rng.standard_normal(sh), (2, Hkv, D))
+        scale = (m / I4_STEPS_PER_SIGMA).astype(np.float32)
+        codes = np.clip(np.rint(pool32 * np.float32(I4_STEPS_PER_SIGMA)), -8, 7).astype(np.int8)
+        kv = _pack_nibbles(codes.view(np.uint8) & np.uint8(0xF))
+        k_scale, v_scale = scale[0].copy(), scale[1].copy()
     else:
         raise ValueError(w.kv_dtype)
     q = {"f32": q32, "f16": None, "bf16": None}[w.q_dtype]
@@ -355,7 +369,7 @@ def host_case(w: Workload, seed: int, poison: bool = True, table: Optional[dict]
         unread = ~read_mask(table, P)
         nan = {"f32": np.float32(np.nan), "f16": np.float16(np.nan),
                "bf16": np.uint16(BF16_NAN_BITS), "e4m3": np.uint8(E4M3_NAN_BYTE),
-               "e2m1": np.uint8(E2M1_POISON_BYTE)}[w.kv_dtype]
+               "e2m1": np.uint8(E2M1_POISON_BYTE), "i4": np.uint8(I4_POISON_BYTE)}[w.kv_dtype]
         kv = kv.copy()
         kv[:, 0][unread] = nan
         kv[:, 1][unread] = nan
@@ -371,8 +385,9 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
     """Full-size inputs drawn directly in device memory with a seeded torch generator.
 
     Returns torch tensors: ``q`` (float32 or bfloat16), ``kv`` (float32,
-    bfloat16, or uint8 bytes for e4m3 and packed e2m1), ``k_scale``/``v_scale``
-    (float32, e4m3 and e2m1 only), and the numpy page table.
+    bfloat16, or uint8 bytes for e4m3 and packed e2m1 / int4),
+    ``k_scale``/``v_scale`` (float32, e4m3, e2m1 and int4 only), and the numpy
+    page table.
     """
     import torch
 
@@ -429,6 +444,20 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
             codes = idx | (torch.signbit(y).to(torch.uint8) << 3)
             kv[p0:p1] = codes[..., 0::2] | (codes[..., 1::2] << 4)
             del y, a, idx, codes
+    elif w.kv_dtype == "i4":
+        m = torch.exp(0.5 * torch.randn((2, Hkv, D), generator=g, device=device,
+                                        dtype=torch.float32))
+        scale = m / I4_STEPS_PER_SIGMA
+        k_scale, v_scale = scale[0].contiguous(), scale[1].contiguous()
+        kv = torch.empty((npg, 2, P, Hkv, D // 2), device=device, dtype=torch.uint8)
+        for p0 in range(0, npg, chunk_pages):
+            p1 = min(npg, p0 + chunk_pages)
+            y = torch.randn((p1 - p0, 2, P, Hkv, D), generator=g, device=device,
+                            dtype=torch.float32)
+            codes = torch.round(y * I4_STEPS_PER_SIGMA).clamp_(-8, 7).to(torch.int8)
+            codes = codes.view(torch.uint8) & 0xF
+            kv[p0:p1] = codes[..., 0::2] | (codes[..., 1::2] << 4)
+            del y, codes
     else:
         raise ValueError(w.kv_dtype)
     if poison:
@@ -437,6 +466,8 @@ def device_case(w: Workload, seed: int, device, poison: bool = False,
             fill = E4M3_NAN_BYTE
         elif w.kv_dtype == "e2m1":
             fill = E2M1_POISON_BYTE
+        elif w.kv_dtype == "i4":
+            fill = I4_POISON_BYTE
         else:
             fill = float("nan")
         kvv = kv.permute(0, 2, 1, 3, 4)  # [pages, P, 2, Hkv, D] view
