@@ -145,9 +145,16 @@ std::map<std::tuple<int, int, int, int, int, int, int, int, int>, std::pair<int,
 // workgroup per CU (four wavefronts) is the fastest residency measured on
 // MI355X for the one-token MFMA kernel on every bf16 and e4m3 workload (the
 // eight KV heads of a work item are then read at the same time, and far
-// fewer pages are open at once); several new tokens per item carry more math
-// per byte and keep the occupancy registers allow. 0: no cap.
-int32_t default_wgs_cap(bool mfma, bool one_token) { return mfma && one_token ? 1 : 0; }
+// fewer pages are open at once). The 4-bit forms (e2m1, int4) keep a SIMD
+// 70-80 % busy widening codes and multiplying (VALU + MFMA busy counters),
+// so a second wavefront per SIMD hides the loads the first one waits on:
+// two workgroups per CU measured 8-9 % faster for both, and 8 % slower for
+// e4m3. Several new tokens per item carry more math per byte and keep the
+// occupancy registers allow. 0: no cap.
+int32_t default_wgs_cap(bool mfma, bool one_token, int kv_form) {
+  if (!mfma || !one_token) return 0;
+  return kv_form == pkd::kE2M1 || kv_form == pkd::kI4 ? 2 : 1;
+}
 
 int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
                  int32_t group, int32_t rows, int32_t page_size, int32_t heads_per_wg,
@@ -228,7 +235,7 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
   const int hp = pkd::decode_heads_per_wg(form, head_dim, group, group, kind_of(q_dtype),
                                           page_size, 2);
   return device_slots(device, q_dtype, form, head_dim, group, group, page_size, hp,
-                      default_wgs_cap(mfma, true), wgs_per_cu, num_cus);
+                      default_wgs_cap(mfma, true, form), wgs_per_cu, num_cus);
 }
 
 int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
@@ -318,7 +325,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   const bool mfma = pkd::decode_uses_mfma(kv_impl, a->head_dim, group, rows,
                                           q_kind, a->page_size);
   const int32_t wgs_cap =
-      a->max_wgs_per_cu ? a->max_wgs_per_cu : default_wgs_cap(mfma, rows == group);
+      a->max_wgs_per_cu ? a->max_wgs_per_cu : default_wgs_cap(mfma, rows == group, kv_impl);
   // A workgroup per work item and KV head, or per pair of KV heads.
   const int32_t heads_per_wg = pkd::decode_heads_per_wg(kv_impl, a->head_dim, group, rows,
                                                         q_kind, a->page_size, a->num_kv_heads);

@@ -64,6 +64,7 @@ def _create(**kw):
 
 @pytest.mark.parametrize("kw,code", [
     (dict(indptr=[0, 3, 3], last=[16, 4]), _lib.PKD_ERR_INVALID_ARGUMENT),   # empty request
+    (dict(indptr=[0], last=[]), _lib.PKD_ERR_INVALID_ARGUMENT),              # empty batch
     (dict(indptr=[0, 3, 2], last=[16, 4]), _lib.PKD_ERR_INVALID_ARGUMENT),   # decreasing indptr
     (dict(indptr=[1, 3, 5], last=[16, 4]), _lib.PKD_ERR_INVALID_ARGUMENT),   # indptr[0] != 0
     (dict(last=[0, 4]), _lib.PKD_ERR_INVALID_ARGUMENT),
