@@ -85,14 +85,15 @@ typedef struct pkd_plan pkd_plan;
  *  num_qo_heads     query heads Hq; num_kv_heads divides it and query head h
  *                   reads KV head h / (Hq / Hkv)
  *  head_dim         64 or 128; query heads per KV head 1, 2, 4 or 8, and also
- *                   16 on the MFMA path (head_dim 128: bf16 q over bf16, e4m3
- *                   or e2m1 KV, fp16 q over fp16 KV) and 32 there except for
- *                   e2m1 KV
+ *                   16 on the MFMA path (head_dim 128: bf16 q over bf16, e4m3,
+ *                   e2m1 or int4 KV, fp16 q over fp16 KV) and 32 there except
+ *                   for e2m1 and int4 KV
  *  page_size        tokens per page, a power of two in [1, 1024]
  *  q_dtype          PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16
  *  kv_dtype         PKD_DTYPE_F32, PKD_DTYPE_BF16, PKD_DTYPE_E4M3, PKD_DTYPE_F16
- *                   or PKD_DTYPE_E2M1; fp16 KV takes fp16 q (and fp16 q fp16
- *                   KV) at head_dim 128; e2m1 KV takes bf16 q at head_dim 128
+ *                   PKD_DTYPE_E2M1 or PKD_DTYPE_I4; fp16 KV takes fp16 q (and
+ *                   fp16 q fp16 KV) at head_dim 128; e2m1 and int4 KV take
+ *                   bf16 q at head_dim 128
  *  out_dtype        PKD_DTYPE_F32, PKD_DTYPE_BF16 or PKD_DTYPE_F16 (16-bit
  *                   outputs round to nearest even)
  *  sm_scale         logit scale; 0 selects 1/sqrt(head_dim)
@@ -112,10 +113,11 @@ typedef struct pkd_plan pkd_plan;
  *                   most its KV token count, which are its last q_r KV
  *                   tokens in order; new token i attends to the first
  *                   L_r - q_r + 1 + i KV tokens. More than one token per
- *                   request needs head_dim 128 and bf16 q with bf16, e4m3 or
- *                   e2m1 KV, or fp16 q with fp16 KV (else UNSUPPORTED); a
- *                   work item then carries up to 16 / group of a request's
- *                   tokens, or 32 / group (e2m1: 16 / group) when a request
+ *                   request needs head_dim 128 and bf16 q with bf16, e4m3,
+ *                   e2m1 or int4 KV, or fp16 q with fp16 KV (else
+ *                   UNSUPPORTED); a work item then carries up to 16 / group
+ *                   of a request's tokens, or 32 / group (e2m1 and int4:
+ *                   16 / group) when a request
  *                   has more (info.queries_per_item).
  *  non_causal       0: the causal rule above. 1: every q row of request r
  *                   sees all of its KV tokens and q_r may exceed them: the
@@ -217,19 +219,19 @@ typedef struct {
  *               k = base, v = base + page_size*Hkv*head_dim,
  *               page_stride = 2*page_size*Hkv*head_dim,
  *               token_stride = Hkv*head_dim, head_stride = head_dim.
- *               Strides are in elements (e2m1: two per byte, so the
+ *               Strides are in elements (e2m1 and int4: two per byte, so the
  *               combined pool's strides above hold with head_dim counted in
  *               elements); k, v and every stride must be 16-byte aligned for
- *               f32/bf16/f16/e2m1 and 8-byte aligned for e4m3.
+ *               f32/bf16/f16/e2m1/int4 and 8-byte aligned for e4m3.
  *  indices      int32 page ids of the page table (length indptr[B]); ids may
  *               repeat across requests (shared prefixes) and are not range
- *               checked
+ *               checked (pkd_check_page_ids does that off the hot path)
  *  k_scale,     e4m3: float [num_pages, Hkv] contiguous (or, with
  *  v_scale      kv_scale_per_token, [num_pages, Hkv, page_size]): stored K
  *               (V) bytes are multiplied by the scale of their (page, KV
- *               head) or (token, KV head). e2m1: float [Hkv, head_dim]
+ *               head) or (token, KV head). e2m1 and int4: float [Hkv, head_dim]
  *               contiguous, element (h, d) multiplying channel d of every
- *               K (V) row of KV head h. Required for e4m3 and e2m1 KV,
+ *               K (V) row of KV head h. Required for e4m3, e2m1 and int4 KV,
  *               ignored otherwise; row-wise and per-channel arrays must be
  *               16-byte aligned.
  *  out          [rows, Hq, head_dim] contiguous, out_dtype
@@ -325,6 +327,18 @@ int pkd_run_stages(const pkd_plan* plan, const pkd_run_args* args, int32_t stage
  * enqueued is that of pkd_run_stages. */
 int pkd_run_timed(const pkd_plan* plan, const pkd_run_args* args, int32_t stages,
                   void* decode_start, void* decode_stop);
+
+/* Count the page ids among indices[0 .. count) (device memory) that lie
+ * outside [0, num_pages), the pool's page count, after the work already
+ * queued on `stream`: the call copies the ids to the host and synchronises
+ * the stream. *bad_out receives the count and *first_bad_out (may be NULL)
+ * the position of the first such id, or -1. run() does not range-check
+ * page ids (they are read on the hot path, per tile), and an id outside the
+ * pool makes the decode kernel read outside it; this is the check for
+ * callers that validate a page table once before using it (the Python
+ * wrapper runs it before run() when asked to). Allocates host memory only. */
+int pkd_check_page_ids(const int32_t* indices, int64_t count, int32_t num_pages, void* stream,
+                       int64_t* bad_out, int64_t* first_bad_out);
 
 /* Free the handle. Its pinned staging block returns to a process-wide pool
  * and is handed to another plan only after its last copy has completed, so

@@ -155,6 +155,10 @@ def load() -> ctypes.CDLL:
     lib.pkd_run_timed.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs), ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p]
     lib.pkd_run_timed.restype = ctypes.c_int
+    lib.pkd_check_page_ids.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                       ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                       ctypes.POINTER(ctypes.c_int64)]
+    lib.pkd_check_page_ids.restype = ctypes.c_int
     lib.pkd_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.pkd_plan_destroy.restype = None
     lib.pkd_merge_states.argtypes = [ctypes.POINTER(MergeStatesArgs)]

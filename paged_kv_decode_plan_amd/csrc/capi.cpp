@@ -640,6 +640,33 @@ int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void
   return ok();
 }
 
+int pkd_check_page_ids(const int32_t* indices, int64_t count, int32_t num_pages, void* stream,
+                       int64_t* bad_out, int64_t* first_bad_out) {
+  if (!bad_out) return fail(PKD_ERR_INVALID_ARGUMENT, "null output pointer");
+  if (count < 0 || num_pages < 0)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "count and num_pages must be >= 0");
+  if (count > 0 && !indices) return fail(PKD_ERR_INVALID_ARGUMENT, "null indices");
+  std::vector<int32_t> ids(static_cast<size_t>(count));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (count > 0 &&
+      (e = hipMemcpyAsync(ids.data(), indices, size_t(count) * sizeof(int32_t),
+                          hipMemcpyDeviceToHost, s)) != hipSuccess)
+    return fail(PKD_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  if ((e = hipStreamSynchronize(s)) != hipSuccess)
+    return fail(PKD_ERR_HIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  int64_t bad = 0, first = -1;
+  for (int64_t i = 0; i < count; ++i) {
+    if (ids[size_t(i)] < 0 || ids[size_t(i)] >= num_pages) {
+      if (first < 0) first = i;
+      ++bad;
+    }
+  }
+  *bad_out = bad;
+  if (first_bad_out) *first_bad_out = first;
+  return ok();
+}
+
 int pkd_merge_states(const pkd_merge_states_args* m) {
   if (!m) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
   if (m->rows < 0 || m->num_heads < 1 || m->head_dim < 4 || m->head_dim % 4)

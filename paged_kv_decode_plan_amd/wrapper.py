@@ -14,6 +14,7 @@ device memory and the current stream only.
 from __future__ import annotations
 
 import ctypes
+import os
 from typing import Optional, Sequence, Tuple, Union
 
 import numpy as np
@@ -254,10 +255,15 @@ class BatchDecodeWithPagedKVCacheWrapper:
 
     # -- run -----------------------------------------------------------------
     def run(self, q, paged_kv_cache, out=None, lse=None, return_lse: bool = False,
-            k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL, decode_events=None):
+            k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL, decode_events=None,
+            check_page_ids: bool = False):
         """``decode_events``: an optional pair of ``torch.cuda.Event(enable_timing=True)``
         that the decode kernel's own dispatch records as it starts and completes
-        (``pkd_run_timed``); ``start.elapsed_time(stop)`` is then the kernel's time."""
+        (``pkd_run_timed``); ``start.elapsed_time(stop)`` is then the kernel's time.
+        ``check_page_ids`` (or ``PKD_DEBUG_CHECKS=1`` in the environment): before
+        launching, count the plan's page ids outside the pool
+        (``pkd_check_page_ids``, which synchronises the stream) and raise
+        ``PkdError`` (INVALID_ARGUMENT) instead of running on such a table."""
         import torch
         p = self._plan
         if p is None:
@@ -314,6 +320,17 @@ class BatchDecodeWithPagedKVCacheWrapper:
         a.workspace = self._ws.data_ptr()
         a.workspace_bytes = self._ws.numel() * self._ws.element_size()
         a.stream = torch.cuda.current_stream(q.device).cuda_stream
+        if check_page_ids or os.environ.get("PKD_DEBUG_CHECKS") == "1":
+            bad, first = ctypes.c_int64(), ctypes.c_int64()
+            _lib.check(_lib.load().pkd_check_page_ids(
+                ctypes.c_void_p(self._indices.data_ptr()), ctypes.c_int64(self._indices.numel()),
+                ctypes.c_int32(k.shape[0]), ctypes.c_void_p(a.stream), ctypes.byref(bad),
+                ctypes.byref(first)))
+            if bad.value:
+                raise _lib.PkdError(
+                    _lib.PKD_ERR_INVALID_ARGUMENT,
+                    f"{bad.value} page ids lie outside the pool of {k.shape[0]} pages "
+                    f"(the first at position {first.value} of indices)")
         events = None
         if decode_events is not None:
             for ev in decode_events:

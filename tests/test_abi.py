@@ -144,3 +144,15 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_check_page_ids_rejects_bad_arguments():
+    lib = pk.load()
+    cnt = ctypes.c_int64()
+    assert lib.pkd_check_page_ids(None, 4, 8, None, None, None) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_check_page_ids(None, -1, 8, None, ctypes.byref(cnt), None) == \
+        _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_check_page_ids(None, 4, -1, None, ctypes.byref(cnt), None) == \
+        _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_check_page_ids(None, 4, 8, None, ctypes.byref(cnt), None) == \
+        _lib.PKD_ERR_INVALID_ARGUMENT  # null indices with a positive count

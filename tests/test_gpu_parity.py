@@ -5,6 +5,8 @@ same dequantised values), compared in fp32 output before rounding; bf16
 output adds half an ulp of rounding. Index-exact properties (the gather
 probe, page-permutation invariance, determinism, single key) are bit-exact.
 """
+import ctypes
+
 import numpy as np
 import pytest
 import torch
@@ -330,3 +332,40 @@ def test_long_splits_use_the_merge_kernel():
     out, lse, info = run_hip(to_device(case), slots=256, balance=1, min_chunk_pages=1)
     assert info["num_split_requests"] > 0 and info["merge_folded"] == 0
     compare(out, lse, ref_out, ref_lse, "bf16")
+
+
+def test_page_id_check_rejects_ids_outside_the_pool():
+    """pkd_check_page_ids counts ids outside the pool; run(check_page_ids=True)
+    raises on such a table before launching anything and runs normally on a
+    valid one."""
+    import paged_kv_decode_plan_amd as pk
+    from paged_kv_decode_plan_amd import _lib
+    lens = [40, 17, 100]
+    w = custom_workload(3, 8, 2, 128, 16, "bf16", "bf16", lens, pool_pages=20)
+    case = host_case(w, 61, poison=True)
+    dc = to_device(case)
+    num_pages = int(dc["kv"].shape[0])
+    ref_out, ref_lse = oracle_for(case)
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(torch.empty(1 << 20, dtype=torch.uint8,
+                                                           device="cuda:0"), "NHD")
+    wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], 8, 2, 128, 16,
+            q_data_type=torch.bfloat16, kv_data_type=torch.bfloat16,
+            out_data_type=torch.float32)
+    out, lse = wr.run(dc["q"], dc["kv"], return_lse=True, check_page_ids=True)
+    torch.cuda.synchronize()
+    compare(out, lse, ref_out, ref_lse, "bf16")
+    for pos, bad_id in [(3, num_pages), (int(dc["indices"].numel()) - 1, -1)]:
+        bad = dc["indices"].clone()
+        bad[pos] = bad_id
+        cnt, first = ctypes.c_int64(), ctypes.c_int64()
+        _lib.check(_lib.load().pkd_check_page_ids(
+            ctypes.c_void_p(bad.data_ptr()), ctypes.c_int64(bad.numel()), ctypes.c_int32(num_pages),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream), ctypes.byref(cnt),
+            ctypes.byref(first)))
+        assert (cnt.value, first.value) == (1, pos)
+        wr.plan(dc["indptr"], bad, dc["last_page_len"], 8, 2, 128, 16,
+                q_data_type=torch.bfloat16, kv_data_type=torch.bfloat16,
+                out_data_type=torch.float32)
+        with pytest.raises(_lib.PkdError, match="outside the pool"):
+            wr.run(dc["q"], dc["kv"], check_page_ids=True)
+    wr.close()
