@@ -156,7 +156,8 @@ typedef struct pkd_plan pkd_plan;
  *                   §"Production War Story" (bf16 q and head_dim 128 only).
  *  max_wgs_per_cu   0: the library's default residency for the KV dtype (one
  *                   token per request: one decode workgroup per compute unit,
- *                   two for e2m1 and int4 KV; several tokens: no cap).
+ *                   two for e2m1 KV, three for int4 KV; several tokens: no
+ *                   cap).
  *                   1..4: run() reserves LDS so that at most this many decode
  *                   workgroups share a compute unit (and slots == 0 counts
  *                   them); larger values add no reservation.

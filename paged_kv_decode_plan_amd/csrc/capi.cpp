@@ -147,13 +147,14 @@ std::map<std::tuple<int, int, int, int, int, int, int, int, int>, std::pair<int,
 // eight KV heads of a work item are then read at the same time, and far
 // fewer pages are open at once). The 4-bit forms (e2m1, int4) keep a SIMD
 // 70-80 % busy widening codes and multiplying (VALU + MFMA busy counters),
-// so a second wavefront per SIMD hides the loads the first one waits on:
-// two workgroups per CU measured 8-9 % faster for both, and 8 % slower for
-// e4m3. Several new tokens per item carry more math per byte and keep the
+// so more wavefronts per SIMD hide the loads one waits on: two workgroups
+// per CU measured 8-9 % faster than one for both (and 8 % slower for e4m3);
+// three were 4 % faster again for int4, the busiest, and 3 % slower for
+// e2m1. Several new tokens per item carry more math per byte and keep the
 // occupancy registers allow. 0: no cap.
 int32_t default_wgs_cap(bool mfma, bool one_token, int kv_form) {
   if (!mfma || !one_token) return 0;
-  return kv_form == pkd::kE2M1 || kv_form == pkd::kI4 ? 2 : 1;
+  return kv_form == pkd::kI4 ? 3 : kv_form == pkd::kE2M1 ? 2 : 1;
 }
 
 int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,

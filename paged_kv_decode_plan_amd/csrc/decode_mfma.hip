@@ -880,8 +880,11 @@ __device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, in
 // loads and get up to 256 (2 per SIMD, still twice what one workgroup per CU
 // uses). e2m1 keeps four sub-tiles and the q hi/lo pair in flight and takes
 // the same 256, as do head pairs (two scales per page for e4m3).
+// int4 (the most VALU work per byte) gets 168 so that three workgroups fit a
+// CU, at the price of a few spilled registers outside the tile loop.
 template <int KV, bool PAGE16, int HP, int G>
 constexpr int waves_per_simd() {
+  if constexpr (KV == kI4) return G <= 16 ? 3 : 2;
   return KV == kE4M3T || nib4<KV>() || HP > 1 || G > 16 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
 }
 
