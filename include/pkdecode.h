@@ -105,7 +105,7 @@ typedef struct pkd_plan pkd_plan;
  *                   round of workgroups; longest-first ordering absorbs the
  *                   raggedness)
  *  min_chunk_pages  shortest chunk a request is split into; 0 selects
- *                   ceil(256 / page_size)
+ *                   ceil(64 / page_size)
  *  device           HIP device ordinal used when slots == 0
  *  qo_indptr        host int32[B+1] or NULL. NULL: one query token per
  *                   request (q row r). Otherwise request r owns the q rows

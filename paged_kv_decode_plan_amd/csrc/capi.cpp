@@ -356,7 +356,11 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   pin.slots = slots;
   pin.slots_per_cu = slots_per_cu;
   pin.balance = a->balance ? a->balance : 1;
-  pin.min_chunk_pages = a->min_chunk_pages ? a->min_chunk_pages : (256 + a->page_size - 1) / a->page_size;
+  // Default shortest chunk: 64 tokens. It binds only for a batch too small to
+  // give every slot a share of that size, where the step is latency-bound and
+  // more, shorter chunks finish sooner (the single-sequence workload: 21.0 us
+  // per step with 256-token chunks, 12.6 us with 64).
+  pin.min_chunk_pages = a->min_chunk_pages ? a->min_chunk_pages : (64 + a->page_size - 1) / a->page_size;
 
   pkd_plan* p = new (std::nothrow) pkd_plan();
   if (!p) return fail(PKD_ERR_INVALID_ARGUMENT, "out of host memory");

@@ -138,9 +138,11 @@ def test_workload_tables_bit_exact(name, slots):
 
 def test_default_balance_and_min_chunk():
     info, *_ = pk.plan_partition([0, 5, 9], [16, 7], 4, 1, 128, 16, slots=8)
-    assert info["balance"] == 1 and info["min_chunk_pages"] == 16
+    assert info["balance"] == 1 and info["min_chunk_pages"] == 4
     info, *_ = pk.plan_partition([0, 5, 9], [16, 7], 4, 1, 128, 64, slots=8)
-    assert info["min_chunk_pages"] == 4
+    assert info["min_chunk_pages"] == 1
+    info, *_ = pk.plan_partition([0, 5, 9], [1, 1], 4, 1, 128, 1, slots=8)
+    assert info["min_chunk_pages"] == 64
 
 
 def _layout_bytes(items, tasks, parts_rows, hkv, d=128):
