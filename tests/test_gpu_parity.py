@@ -88,6 +88,24 @@ def test_page_sizes(P, kv):
         compare(out, lse, ref_out, ref_lse, kv)
 
 
+@pytest.mark.parametrize("kv,qd,d", [("f32", "f32", 64), ("bf16", "bf16", 128), ("e4m3", "bf16", 128),
+                                      ("f16", "f16", 128), ("e2m1", "bf16", 128), ("i4", "bf16", 128)])
+@pytest.mark.parametrize("P", [256, 1024])
+def test_large_pages(P, kv, qd, d):
+    """Pages up to the largest size plan() accepts (1024 tokens), on every
+    kernel form: lengths inside one page, at page ends and across several."""
+    lens = [1, P - 1, P, P + 3, 2 * P + 17]
+    w = custom_workload(len(lens), 8, 2, d, P, kv, qd, lens,
+                        pool_pages=sum(-(-x // P) for x in lens) + 2)
+    case = host_case(w, 70 + P, poison=True)
+    _say("large pages", P, kv, qd, d)
+    ref_out, ref_lse = oracle_for(case)
+    dc = to_device(case)
+    for kw in ({}, dict(slots=8, balance=1, min_chunk_pages=1)):
+        out, lse, _ = run_hip(dc, **kw)
+        compare(out, lse, ref_out, ref_lse, kv)
+
+
 @pytest.mark.parametrize("kv", ["f32", "bf16", "e4m3"])
 def test_bf16_output_rounding(kv):
     lens = [5, 200, 31]
