@@ -387,3 +387,47 @@ def test_page_id_check_rejects_ids_outside_the_pool():
         with pytest.raises(_lib.PkdError, match="outside the pool"):
             wr.run(dc["q"], dc["kv"], check_page_ids=True)
     wr.close()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3", "e2m1"])
+def test_separate_k_and_v_pools(kv):
+    """A (k, v) pair of pools gives the combined pool's result bit for bit:
+    as views into the combined tensor, as separate contiguous tensors, and
+    as pools whose pages are padded (page stride larger than the page)."""
+    lens = [1, 37, 300, 64, 129]
+    w = custom_workload(len(lens), 16, 4, 128, 16, kv, "bf16", lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 4)
+    case = host_case(w, 520, poison=True)
+    _say("separate pools", kv)
+    dc = to_device(case)
+    out0, lse0, _ = run_hip(dc)
+    k, v = dc["kv"][:, 0], dc["kv"][:, 1]
+    padded = torch.zeros((k.shape[0], k.shape[1] + 3) + tuple(k.shape[2:]), dtype=k.dtype,
+                         device=k.device)
+    kp, vp = padded.clone(), padded.clone()
+    kp[:, :k.shape[1]] = k
+    vp[:, :v.shape[1]] = v
+    for pools in [(k, v), (k.contiguous(), v.contiguous()),
+                  (kp[:, :k.shape[1]], vp[:, :v.shape[1]])]:
+        out, lse, _ = run_hip(dc, kv=pools)
+        assert torch.equal(out, out0) and torch.equal(lse, lse0)
+
+
+def test_large_batch_of_short_requests():
+    """Two thousand requests of 1-400 tokens: a plan of thousands of work
+    items and a grid of thousands of workgroups, checked on sampled requests
+    against the oracle."""
+    rng = np.random.default_rng(77)
+    lens = [int(x) for x in rng.integers(1, 401, 2048)]
+    w = custom_workload(len(lens), 8, 2, 128, 16, "bf16", "bf16", lens)
+    _say("large batch", len(lens), "requests", sum(lens), "tokens")
+    dc = device_case(w, 78, "cuda:0", poison=True)
+    out, lse, info = run_hip(dc)
+    _say("plan", info)
+    assert info["num_items"] >= len(lens)
+    o = out_to_f64(out)
+    assert np.all(np.isfinite(o))
+    for r in sorted({0, 1, 1023, 2047, int(np.argmax(lens)), int(np.argmin(lens))}):
+        sub = sample_request_case(dc, r)
+        ref_out, ref_lse = oracle_for(sub)
+        compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, "bf16")
