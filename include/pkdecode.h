@@ -241,6 +241,14 @@ typedef struct {
  *  workspace    the buffer the plan was uploaded to, at least
  *               info.workspace_bytes long
  *  stream       hipStream_t; run() only enqueues work and returns
+ *  prior_out,   NULL, or another normalised result of the same q rows over a
+ *  prior_lse    disjoint token set (the other level of cascade attention):
+ *               float [rows, Hq, head_dim] and its natural-log LSE float
+ *               [rows, Hq] (-inf: a result over no tokens), both contiguous,
+ *               16-byte aligned, not aliasing out or lse. run() then writes
+ *               the merge of its own result with it, by the rule of
+ *               pkd_merge_states, to out and lse (both sides empty: 0 and
+ *               -inf), in place of a separate merge launch. Both or neither.
  */
 typedef struct {
   const void* q;
@@ -257,6 +265,8 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   void* stream;
+  const float* prior_out;
+  const float* prior_lse;
 } pkd_run_args;
 
 /* Message describing the calling thread's most recent failure ("" if none). */

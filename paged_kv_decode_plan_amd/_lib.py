@@ -97,6 +97,8 @@ class RunArgs(ctypes.Structure):
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_size_t),
         ("stream", ctypes.c_void_p),
+        ("prior_out", ctypes.c_void_p),
+        ("prior_lse", ctypes.c_void_p),
     ]
 
 

@@ -588,6 +588,11 @@ int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void
     return fail(PKD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
   if (r->page_stride < 0 || r->token_stride < 0 || r->head_stride < 0)
     return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
+  if (!r->prior_out != !r->prior_lse)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out and prior_lse go together");
+  if (r->prior_out && (reinterpret_cast<uintptr_t>(r->prior_out) % 16 ||
+                       reinterpret_cast<uintptr_t>(r->prior_lse) % 4))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out must be 16-byte aligned");
 
   pkd::DecodeLaunch L;
   L.kv_dtype = p->kv_impl;
@@ -614,6 +619,8 @@ int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void
   L.v_scale = r->v_scale;
   L.out = r->out;
   L.lse = r->lse;
+  L.prior_out = r->prior_out;
+  L.prior_lse = r->prior_lse;
   char* ws = static_cast<char*>(r->workspace);
   L.items = reinterpret_cast<const pkd::DeviceItem*>(ws + p->off_items);
   L.merge_tasks = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_split);

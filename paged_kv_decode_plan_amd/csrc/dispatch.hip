@@ -124,6 +124,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream, hipEvent_t s
   a.v_scale = L.v_scale;
   a.out = L.out;
   a.lse = L.lse;
+  a.prior_out = L.prior_out;
+  a.prior_lse = L.prior_lse;
   a.items = L.items;
   a.counts = L.counts;
   a.block_merges = L.block_merges;

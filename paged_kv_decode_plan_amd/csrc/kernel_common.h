@@ -13,6 +13,7 @@ namespace pkd {
 constexpr int kWaves = 4;               // wavefronts per decode workgroup
 constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
 
@@ -28,6 +29,8 @@ struct KernelArgs {
   const float* v_scale;
   void* out;
   float* lse;
+  const float* prior_out;  // another result of the same rows to merge in, or nullptr
+  const float* prior_lse;
   const DeviceItem* items;
   const int32_t* counts;  // nullptr, or {work items, merge tasks} of the uploaded plan
   const MergeTask* block_merges;  // fused merge records (fuse_merge only)
@@ -96,6 +99,30 @@ __device__ inline uint2 pack4_16(float x, float y, float z, float w, int kind) {
                uint32_t(float_to_bf16_rne(z)) | (uint32_t(float_to_bf16_rne(w)) << 16)};
 }
 
+// Fold another normalised result of the same row (output value v_p per dim,
+// natural-log LSE lse_p; the cascade's other level) into the state (M in
+// log2 units, d, o) about to be written: the prior is the state
+// (lse_p * log2 e, 1, v_p) and the rule is the online-softmax merge. Returns
+// the weights of the state's o and of v_p and updates M and d; both sides
+// empty leaves d = 0 (the row is then 0 with LSE -inf).
+struct PriorWeights {
+  float self, prior;
+};
+__device__ inline PriorWeights fold_prior(float& M, float& Dn, float lse_p) {
+  const float mp = lse_p * kLog2e;
+  const float mn = fmaxf(M, mp);
+  PriorWeights w;
+  w.self = M == -INFINITY ? 0.f : exp2f(M - mn);
+  w.prior = mp == -INFINITY ? 0.f : exp2f(mp - mn);
+  Dn = Dn * w.self + w.prior;
+  M = mn;
+  return w;
+}
+__device__ inline float4 fold_prior4(float4 O, float4 vp, const PriorWeights& w) {
+  return float4{O.x * w.self + vp.x * w.prior, O.y * w.self + vp.y * w.prior,
+                O.z * w.self + vp.z * w.prior, O.w * w.self + vp.w * w.prior};
+}
+
 // The merge of a split request, folded into the decode kernel: every
 // workgroup of a chunk publishes its partial states (release fence), then
 // counts itself in with one atomic add on the (request, query block, KV head)
@@ -156,7 +183,11 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
       }
     }
     const int64_t row = int64_t(mt.out_row + i) * a.num_qo_heads + hq;
-    const float inv = 1.0f / Dn;
+    if (a.prior_out) {
+      const PriorWeights pw = fold_prior(M, Dn, a.prior_lse[row]);
+      O = fold_prior4(O, reinterpret_cast<const float4*>(a.prior_out)[row * kQuads + qd], pw);
+    }
+    const float inv = Dn > 0.f ? 1.0f / Dn : 0.f;
     if (a.out_kind != kQF32) {
       reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] =
           pack4_16(O.x * inv, O.y * inv, O.z * inv, O.w * inv, a.out_kind);
@@ -164,7 +195,7 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
       reinterpret_cast<float4*>(a.out)[row * kQuads + qd] =
           float4{O.x * inv, O.y * inv, O.z * inv, O.w * inv};
     }
-    if (a.lse && qd == 0) a.lse[row] = (M + log2f(Dn)) * kLn2;
+    if (a.lse && qd == 0) a.lse[row] = Dn > 0.f ? (M + log2f(Dn)) * kLn2 : -INFINITY;
   }
   if (threadIdx.x == 0) *counter = 0;
 }
@@ -206,14 +237,18 @@ __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelA
     const int hq = (kvh << a.group_log2) + (h & gmask);
     const int64_t row = int64_t(it.q_row + i) * a.num_qo_heads + hq;
     if (it.partial_slot < 0) {
-      const float val = O / Dn;
+      if (a.prior_out) {
+        const PriorWeights pw = fold_prior(M, Dn, a.prior_lse[row]);
+        O = O * pw.self + a.prior_out[row * D + d] * pw.prior;
+      }
+      const float val = Dn > 0.f ? O / Dn : 0.f;
       if (a.out_kind == kQBF16)
         static_cast<uint16_t*>(a.out)[row * D + d] = float_to_bf16_rne(val);
       else if (a.out_kind == kQF16)
         static_cast<uint16_t*>(a.out)[row * D + d] = float_to_f16_rne(val);
       else
         static_cast<float*>(a.out)[row * D + d] = val;
-      if (a.lse && d == 0) a.lse[row] = (M + log2f(Dn)) * kLn2;
+      if (a.lse && d == 0) a.lse[row] = Dn > 0.f ? (M + log2f(Dn)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = int64_t(it.partial_slot + i) * a.num_qo_heads + hq;
       a.part_o[prow * D + d] = O;

@@ -65,6 +65,10 @@ struct DecodeLaunch {
   const float* v_scale = nullptr;
   void* out = nullptr;
   float* lse = nullptr;
+  // Another normalised result of the same rows (fp32 rows, natural-log LSE)
+  // to merge into the output as it is written; nullptr: none.
+  const float* prior_out = nullptr;
+  const float* prior_lse = nullptr;
   const DeviceItem* items = nullptr;
   float* part_o = nullptr;   // [num_partials, Hq, head_dim]
   float* part_md = nullptr;  // [num_partials, Hq, 2]: (m in log2 units, d)

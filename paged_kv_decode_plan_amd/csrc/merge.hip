@@ -34,6 +34,8 @@ struct MergeArgs {
   const int32_t* counts;  // fixed-capacity plan: counts[1] merge tasks are live
   void* out;
   float* lse;
+  const float* prior_out;  // another result of the same rows to merge in, or nullptr
+  const float* prior_lse;
   int num_qo_heads;
   int out_kind;  // kQF32, kQBF16 or kQF16
 };
@@ -106,7 +108,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       A.w += so[k][qd].w * w;
     }
     const int64_t row = int64_t(t.out_row) * H + h;
-    const float inv = 1.0f / Dt;
+    if (a.prior_out) {
+      const PriorWeights pw = fold_prior(Mt, Dt, a.prior_lse[row]);
+      A = fold_prior4(A, reinterpret_cast<const float4*>(a.prior_out)[row * kQuads + qd], pw);
+    }
+    const float inv = Dt > 0.f ? 1.0f / Dt : 0.f;
     if (a.out_kind != kQF32) {
       reinterpret_cast<uint2*>(a.out)[row * kQuads + qd] =
           pack4_16(A.x * inv, A.y * inv, A.z * inv, A.w * inv, a.out_kind);
@@ -114,7 +120,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
       reinterpret_cast<float4*>(a.out)[row * kQuads + qd] =
           float4{A.x * inv, A.y * inv, A.z * inv, A.w * inv};
     }
-    if (a.lse && qd == 0) a.lse[row] = (Mt + log2f(Dt)) * kLn2;
+    if (a.lse && qd == 0) a.lse[row] = Dt > 0.f ? (Mt + log2f(Dt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -129,6 +135,8 @@ hipError_t launch_merge(const DecodeLaunch& L, hipStream_t stream) {
   a.counts = L.counts;
   a.out = L.out;
   a.lse = L.lse;
+  a.prior_out = L.prior_out;
+  a.prior_lse = L.prior_lse;
   a.num_qo_heads = L.num_qo_heads;
   a.out_kind = L.out_kind;
   const unsigned grid = unsigned(L.num_split) * unsigned(L.num_qo_heads);

@@ -256,14 +256,17 @@ class BatchDecodeWithPagedKVCacheWrapper:
     # -- run -----------------------------------------------------------------
     def run(self, q, paged_kv_cache, out=None, lse=None, return_lse: bool = False,
             k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL, decode_events=None,
-            check_page_ids: bool = False):
+            check_page_ids: bool = False, prior=None):
         """``decode_events``: an optional pair of ``torch.cuda.Event(enable_timing=True)``
         that the decode kernel's own dispatch records as it starts and completes
         (``pkd_run_timed``); ``start.elapsed_time(stop)`` is then the kernel's time.
         ``check_page_ids`` (or ``PKD_DEBUG_CHECKS=1`` in the environment): before
         launching, count the plan's page ids outside the pool
         (``pkd_check_page_ids``, which synchronises the stream) and raise
-        ``PkdError`` (INVALID_ARGUMENT) instead of running on such a table."""
+        ``PkdError`` (INVALID_ARGUMENT) instead of running on such a table.
+        ``prior``: ``(v, lse)``, another normalised result of the same rows over a
+        disjoint token set (float32 ``[rows, Hq, head_dim]`` and ``[rows, Hq]``),
+        merged into the output as it is written (cascade attention's levels)."""
         import torch
         p = self._plan
         if p is None:
@@ -317,6 +320,13 @@ class BatchDecodeWithPagedKVCacheWrapper:
             a.k_scale, a.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
         a.out = out.data_ptr()
         a.lse = lse.data_ptr() if lse is not None else None
+        if prior is not None:
+            pv, pl = prior
+            if (pv.dtype != torch.float32 or pl.dtype != torch.float32 or pv.shape != q.shape
+                    or tuple(pl.shape) != (p.query_rows, p.num_qo_heads)
+                    or not (pv.is_contiguous() and pl.is_contiguous())):
+                raise ValueError("prior must be contiguous float32 ([rows, Hq, D], [rows, Hq])")
+            a.prior_out, a.prior_lse = pv.data_ptr(), pl.data_ptr()
         a.workspace = self._ws.data_ptr()
         a.workspace_bytes = self._ws.numel() * self._ws.element_size()
         a.stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -382,8 +392,9 @@ def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, out_dtype=None):
 class CascadeBatchDecodeWrapper:
     """Two-level cascade decode: the queries of all requests that share a
     prefix attend to it once, as one non-causal request of the plan (level
-    0); each request attends to its own suffix pages (level 1); the two
-    normalised results merge with ``merge_state``.
+    0); each request attends to its own suffix pages (level 1), and level 1
+    merges level 0's normalised result into its rows as it writes them (the
+    rule of ``merge_state``, without a separate launch).
 
     Requests must be ordered by prefix group: group p owns the q rows
     ``shared_qo_indptr[p]:shared_qo_indptr[p+1]`` (one per request). The
@@ -412,21 +423,26 @@ class CascadeBatchDecodeWrapper:
                   balance=balance, min_chunk_pages=min_chunk_pages)
         self._levels[0].plan(shared_indptr, shared_indices, shared_last_page_len, num_qo_heads,
                              num_kv_heads, head_dim, page_size, qo_indptr=qo, causal=False, **kw)
+        self._out_dtype = out_data_type or q_data_type or torch.bfloat16
+        kw["out_data_type"] = self._out_dtype  # the second level writes the merged rows
         self._levels[1].plan(unique_indptr, unique_indices, unique_last_page_len, num_qo_heads,
                              num_kv_heads, head_dim, page_size, **kw)
         self._rows, self._heads, self._dim = rows, num_qo_heads, head_dim
-        self._out_dtype = out_data_type or q_data_type or torch.bfloat16
 
     def run(self, q, paged_kv_cache, out=None, return_lse: bool = False, k_scale=None,
             v_scale=None):
         import torch
         shape = (self._rows, self._heads, self._dim)
-        o = torch.empty((2,) + shape, dtype=torch.float32, device=q.device)
-        s = torch.empty((2,) + shape[:2], dtype=torch.float32, device=q.device)
-        for lvl in range(2):
-            self._levels[lvl].run(q, paged_kv_cache, out=o[lvl], lse=s[lvl], k_scale=k_scale,
-                                  v_scale=v_scale)
-        out, lse = merge_state(o[0], s[0], o[1], s[1], v_out=out, out_dtype=self._out_dtype)
+        # the shared level in float32, then each request's own pages with the
+        # shared result merged in as the output is written
+        o = torch.empty(shape, dtype=torch.float32, device=q.device)
+        s = torch.empty(shape[:2], dtype=torch.float32, device=q.device)
+        self._levels[0].run(q, paged_kv_cache, out=o, lse=s, k_scale=k_scale, v_scale=v_scale)
+        if out is None:
+            out = torch.empty(shape, dtype=self._out_dtype, device=q.device)
+        lse = torch.empty(shape[:2], dtype=torch.float32, device=q.device) if return_lse else None
+        self._levels[1].run(q, paged_kv_cache, out=out, lse=lse, k_scale=k_scale, v_scale=v_scale,
+                            prior=(o, s))
         return (out, lse) if return_lse else out
 
     def close(self) -> None:

@@ -159,3 +159,40 @@ def test_full_size_cascade_sampled_requests():
         compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, "bf16")
     del dc
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("mode", ["whole", "folded", "merge_kernel"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_run_merges_a_prior_result(mode, out_dtype):
+    """run(prior=(v, lse)) writes the merge of its own result with another
+    normalised result of the same rows (the cascade's other level), on the
+    three paths that write final rows: an unsplit item's epilogue, the merge
+    folded into the decode kernel, and the merge kernel. Rows whose prior is
+    empty (LSE -inf) keep the run's own result."""
+    lens = [300, 17, 90, 1]
+    w = custom_workload(len(lens), 16, 4, 128, 16, "bf16", "bf16", lens, pool_pages=40)
+    case = host_case(w, 333, poison=True)
+    ref_v, ref_s = attention.decode_case(case)
+    rng = np.random.default_rng(334)
+    pv = rng.standard_normal(ref_v.shape).astype(np.float32)
+    ps = (rng.standard_normal(ref_s.shape) * 3 + 5).astype(np.float32)
+    ps[1, :] = -np.inf  # an empty prior for every head of request 1
+    ps[2, 3] = -np.inf
+    want_v, want_s = merge.merge_normalized(ref_v, ref_s, pv.astype(np.float64), ps.astype(np.float64))
+    dc = to_device(case)
+    kw = {"whole": dict(min_chunk_pages=64), "folded": dict(slots=64, balance=1, min_chunk_pages=5),
+          "merge_kernel": dict(slots=64, balance=1, min_chunk_pages=1)}[mode]
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+    odt = {"f32": torch.float32, "bf16": torch.bfloat16}[out_dtype]
+    wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], 16, 4, 128, 16,
+            q_data_type=torch.bfloat16, kv_data_type=torch.bfloat16, out_data_type=odt, **kw)
+    info = wr.plan_info
+    if mode == "whole":
+        assert info["num_split_requests"] == 0
+    else:
+        assert info["num_split_requests"] > 0 and info["merge_folded"] == (mode == "folded")
+    out, lse = wr.run(dc["q"], dc["kv"], return_lse=True,
+                      prior=(torch.from_numpy(pv).cuda(), torch.from_numpy(ps).cuda()))
+    torch.cuda.synchronize()
+    wr.close()
+    compare(out, lse, want_v, want_s, "bf16", out_dtype=out_dtype)
