@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark: batched paged-KV decode attention on one MI355X.
 
-One step is one run() over the whole batch: the split-KV decode kernel, whose
-last workgroup of each split request also merges its partial states. The
+One step is one run() over the whole batch: the split-KV decode kernel and,
+for a plan that splits requests, the merge of their partial states (folded
+into the decode kernel for a few short splits, else the merge kernel). The
 default workload is the
 Llama-3-8B-shaped decode batch (B=64, 32 query / 8 KV heads, head_dim 128,
 16-token pages, every context 2048, bf16). Inputs are synthetic (seeded
@@ -13,9 +14,13 @@ Timing: W untimed warmup steps, then K timed steps. Before each timed step a
 KV; HIP events on the launch stream bracket every step (with
 ``--separate-merge``, the decode and merge stages apart). ``value`` is KV-read
 GB/s over the whole step (algorithmic KV bytes / mean step time).
-``roofline`` is for the decode kernel. ``cpu_baseline`` times the float64
-oracle on a bounded sample of the same batch on one host core (and its
-``parallel`` entry, the same sample over single-threaded worker processes);
+``roofline`` is for the decode kernel, timed over K more cold steps by
+events that its own dispatch records (hipExtLaunchKernel through
+pkd_run_timed); HBM traffic comes from the committed rocprofv3 counter
+summary when it was taken on the current kernel sources. ``cpu_baseline``
+times the float64 oracle on a bounded sample of the same batch (about 12 s
+of work) on one host core (and its ``parallel`` entry, the same sample over
+single-threaded worker processes);
 ``calibration`` is a plain 1 GiB streaming read timed on the same device.
 
 Prints one JSON line.
