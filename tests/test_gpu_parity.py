@@ -431,3 +431,49 @@ def test_large_batch_of_short_requests():
         sub = sample_request_case(dc, r)
         ref_out, ref_lse = oracle_for(sub)
         compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, "bf16")
+
+
+def test_two_streams_two_workspaces():
+    """Two plans with their own workspaces, planned and run on two streams
+    (default priority) with their launches interleaved, give the results of
+    the same runs made one after the other, bit for bit, and match the
+    oracle."""
+    import paged_kv_decode_plan_amd as pk
+    cases = []
+    for seed, (kv, lens) in enumerate([("bf16", [900, 33, 1, 2500]), ("e4m3", [64, 1700, 400])]):
+        w = custom_workload(len(lens), 16, 4, 128, 16, kv, "bf16", lens,
+                            pool_pages=sum(-(-x // 16) for x in lens) + 3)
+        cases.append(host_case(w, 880 + seed, poison=True))
+    seq = [run_hip(to_device(c), slots=32, balance=1, min_chunk_pages=1)[:2] for c in cases]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wrappers, dcs = [], []
+    for c, st in zip(cases, streams):
+        dc = to_device(c)
+        wr = pk.BatchDecodeWithPagedKVCacheWrapper(
+            torch.empty(16 << 20, dtype=torch.uint8, device="cuda:0"), "NHD")
+        w = dc["workload"]
+        with torch.cuda.stream(st):
+            wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], 16, 4, 128, 16,
+                    q_data_type=torch.bfloat16,
+                    kv_data_type=w.kv_dtype if w.kv_dtype == "e4m3" else torch.bfloat16,
+                    out_data_type=torch.float32, slots=32, balance=1, min_chunk_pages=1)
+        wrappers.append(wr)
+        dcs.append(dc)
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(4):  # interleaved launches on the two streams
+        res = []
+        for wr, dc, st in zip(wrappers, dcs, streams):
+            with torch.cuda.stream(st):
+                res.append(wr.run(dc["q"], dc["kv"], return_lse=True, k_scale=dc["k_scale"],
+                                  v_scale=dc["v_scale"]))
+        outs.append(res)
+    torch.cuda.synchronize()
+    for res in outs:
+        for (o, l), (so, sl) in zip(res, seq):
+            assert torch.equal(o, so) and torch.equal(l, sl)
+    for c, (o, l) in zip(cases, seq):
+        ref_out, ref_lse = oracle_for(c)
+        compare(o, l, ref_out, ref_lse, c["workload"].kv_dtype)
+    for wr in wrappers:
+        wr.close()

@@ -290,3 +290,50 @@ def test_many_split_workgroups_keep_the_merge_kernel():
     many = pk.plan_partition(indptr, [16] * 64, 32, 8, 128, P, kv_dtype="bf16", q_dtype="bf16",
                              slots=1024, min_chunk_pages=16)[0]
     assert many["num_split_requests"] == 64 and many["merge_folded"] == 0
+
+
+def test_plans_from_many_threads_match_sequential_plans():
+    """pkd_plan_create / get_worklist / destroy from eight host threads at
+    once (each with its own tables, and some calls failing on purpose so
+    that the thread-local error message is exercised) give the same work
+    lists as the same calls made one after another."""
+    import threading
+
+    from paged_kv_decode_plan_amd import _lib
+
+    rng = np.random.default_rng(2026)
+    cases = []
+    for _ in range(64):
+        B = int(rng.integers(1, 40))
+        P = int(rng.choice([1, 4, 16, 64]))
+        lens = rng.integers(1, 3000, B)
+        npg = -(-lens // P)
+        indptr = np.concatenate([[0], np.cumsum(npg)]).astype(np.int32)
+        last = (lens - (npg - 1) * P).astype(np.int32)
+        cases.append((indptr, last, P, int(rng.choice([64, 256, 1024]))))
+
+    def build(c):
+        indptr, last, P, slots = c
+        info, items, merge, split = pk.plan_partition(indptr, last, 32, 8, 128, P, slots=slots)
+        return info["num_items"], items.tobytes(), merge.tobytes(), split.tobytes()
+
+    want = [build(c) for c in cases]
+    got = [None] * len(cases)
+    errors = []
+
+    def worker(t):
+        try:
+            for i in range(t, len(cases), 8):
+                with pytest.raises(_lib.PkdError, match="indptr"):
+                    pk.plan_partition([1, 3], [4], 32, 8, 128, 16)  # indptr[0] != 0
+                got[i] = build(cases[i])
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    assert got == want
