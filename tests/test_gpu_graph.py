@@ -135,3 +135,38 @@ def test_graph_captured_once_serves_later_plans(kv, nq_max, split):
                 assert torch.equal(out_buf[:rows], first)
             del scratch
     wr.close()
+
+
+def test_fixed_capacity_plan_merges_a_prior_result():
+    """run(prior=...) on a fixed-capacity plan (grids from the capacities,
+    merge kernel always launched) gives the exact plan's bits, whole and
+    split, and the oracle's merge of the two results."""
+    from oracle import merge
+    lens = [1, 17, 300, 64, 1000]
+    w = custom_workload(5, 16, 4, 128, 16, "bf16", "bf16", lens, pool_pages=120)
+    case = host_case(w, 5, poison=True)
+    dc = to_device(case)
+    ref_out, ref_lse = attention.decode_case(case)
+    rng = np.random.default_rng(6)
+    pv = rng.standard_normal(ref_out.shape).astype(np.float32)
+    ps = (rng.standard_normal(ref_lse.shape) * 2 + 6).astype(np.float32)
+    ps[0, :5] = -np.inf
+    want_v, want_s = merge.merge_normalized(ref_out, ref_lse, pv.astype(np.float64),
+                                            ps.astype(np.float64))
+    prior = (torch.from_numpy(pv).to(DEV), torch.from_numpy(ps).to(DEV))
+    for kw in (dict(min_chunk_pages=64), dict(slots=16, balance=1, min_chunk_pages=1)):
+        res = []
+        for cap in (None, dict(CAP, qo_len=1)):
+            wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+            wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], 16, 4, 128, 16,
+                    q_data_type=torch.bfloat16, kv_data_type=torch.bfloat16,
+                    out_data_type=torch.float32, sm_scale=w.scale(), capacity=cap, **kw)
+            out = torch.empty(dc["q"].shape, dtype=torch.float32, device=DEV)
+            lse = torch.empty(dc["q"].shape[:2], dtype=torch.float32, device=DEV)
+            for st in (pk._lib.STAGE_DECODE, pk._lib.STAGE_MERGE):
+                wr.run(dc["q"], dc["kv"], out=out, lse=lse, stages=st, prior=prior)
+            torch.cuda.synchronize()
+            wr.close()
+            compare(out, lse, want_v, want_s, "bf16")
+            res.append((out, lse))
+        assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
