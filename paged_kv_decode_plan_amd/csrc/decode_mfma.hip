@@ -881,7 +881,8 @@ __device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, in
 // uses). e2m1 keeps four sub-tiles and the q hi/lo pair in flight and takes
 // the same 256, as do head pairs (two scales per page for e4m3).
 // int4 (the most VALU work per byte) gets 168 so that three workgroups fit a
-// CU, at the price of a few spilled registers outside the tile loop.
+// CU, at the price of a few spilled registers: stored before the tile loop
+// and reloaded after it, except one 4-byte value reloaded once per tile.
 template <int KV, bool PAGE16, int HP, int G>
 constexpr int waves_per_simd() {
   if constexpr (KV == kI4) return G <= 16 ? 3 : 2;
