@@ -91,7 +91,11 @@ constexpr int kSub = 16;        // tokens per MFMA sub-tile
 constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 
 // Sub-tiles per wavefront tile: a tile should bring about 8 KiB of K and V
-// per wavefront, so e4m3 (128-byte rows) takes two 16-token sub-tiles.
+// per wavefront, so e4m3 (128-byte rows) takes two 16-token sub-tiles. The
+// 4-bit forms, which run two or three workgroups per CU, take two (4 KiB):
+// measured on MI355X, e2m1 447 -> 409 us and int4 452 -> 433 us per step
+// against four sub-tiles (8 KiB), whose registers also made int4's third
+// workgroup spill.
 #ifndef PKD_E4M3_NSUB
 #define PKD_E4M3_NSUB 2
 #endif
@@ -99,7 +103,7 @@ constexpr float kSlack = 8.0f;  // log2 headroom of the lazy reference max
 #define PKD_BF16_NSUB 1
 #endif
 #ifndef PKD_E2M1_NSUB
-#define PKD_E2M1_NSUB 4
+#define PKD_E2M1_NSUB 2
 #endif
 template <int KV>
 constexpr bool fp8() { return KV == kE4M3 || KV == kE4M3T; }
@@ -881,8 +885,7 @@ __device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, in
 // uses). e2m1 keeps four sub-tiles and the q hi/lo pair in flight and takes
 // the same 256, as do head pairs (two scales per page for e4m3).
 // int4 (the most VALU work per byte) gets 168 so that three workgroups fit a
-// CU, at the price of a few spilled registers: stored before the tile loop
-// and reloaded after it, except one 4-byte value reloaded once per tile.
+// CU (its 4 KiB tiles need 148-159).
 template <int KV, bool PAGE16, int HP, int G>
 constexpr int waves_per_simd() {
   if constexpr (KV == kI4) return G <= 16 ? 3 : 2;
