@@ -621,7 +621,8 @@ def main(argv=None) -> int:
         "kv_bytes_per_step": nbytes,
         "warm_us_per_step": round(warm_ms * 1e3, 2) if warm_ms else None,
         "warm_gbs": round(nbytes / (warm_ms * 1e-3) / 1e9, 1) if warm_ms else None,
-        "merge_us": round(statistics.fmean(mrg_ms) * 1e3, 2),
+        # timed apart only with --separate-merge; otherwise inside the step
+        "merge_us": round(statistics.fmean(mrg_ms) * 1e3, 2) if has_merge else None,
         "merge": ("none (no request split)" if info["num_split_requests"] == 0 else
                   "separate stages (timed apart)" if has_merge else
                   "folded into the decode kernel" if info.get("merge_folded") else
