@@ -356,6 +356,10 @@ def main(argv=None) -> int:
     ap.add_argument("--separate-merge", action="store_true",
                     help="launch and time the decode and merge stages apart instead of one "
                          "run() with the merge folded into the decode kernel")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="run() calls per step, one per layer, each over its own copy of the "
+                         "KV pool and all with the step's one plan (one graph holds them all "
+                         "with --graph); times are reported per layer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--balance", type=int, default=0)
@@ -474,7 +478,15 @@ def main(argv=None) -> int:
 
     # By default a step is one run(): the decode kernel with the merge of split
     # requests folded in. --separate-merge times the two stages apart instead.
-    has_merge = args.separate_merge and not cascade and info["num_split_requests"] > 0
+    has_merge = (args.separate_merge and not cascade and args.layers == 1
+                 and info["num_split_requests"] > 0)
+    if args.layers < 1 or (args.layers > 1 and cascade):
+        print("--layers takes a count >= 1 and single-plan workloads only", file=sys.stderr)
+        return 2
+    # One KV pool per layer (the first is the generated one): every layer's
+    # run() reads its own bytes, as in a model, so no layer finds the previous
+    # one's KV in the caches.
+    kv_layers = [dcase["kv"]] + [dcase["kv"].clone() for _ in range(args.layers - 1)]
     graph = None
     if args.graph:
         if cascade:
@@ -484,7 +496,8 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+            for kv in kv_layers:
+                wrapper.run(dcase["q"], kv, **run_kw)
         torch.cuda.synchronize()
         has_merge = False
 
@@ -508,11 +521,13 @@ def main(argv=None) -> int:
                 wrapper.run(dcase["q"], dcase["kv"], decode_events=kernel_ev, **run_kw)
             return
         if ev is None:
-            wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+            for kv in kv_layers:
+                wrapper.run(dcase["q"], kv, **run_kw)
             return
-        if not has_merge:  # one bracket around the whole run
+        if not has_merge:  # one bracket around the whole run (every layer's)
             ev[0].record()
-            wrapper.run(dcase["q"], dcase["kv"], **run_kw)
+            for kv in kv_layers:
+                wrapper.run(dcase["q"], kv, **run_kw)
             ev[1].record()
             return
         ev[0].record()
@@ -546,7 +561,7 @@ def main(argv=None) -> int:
     # the dispatch-stamped ones slow the launch itself, so each series times
     # one thing: the steps above, the kernel here. A cascade step (several
     # launches) and a graph replay keep the bracket.
-    kernel_events = graph is None and not cascade
+    kernel_events = graph is None and not cascade and args.layers == 1
     if kernel_events:
         kevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
         for e in kevs:  # create the events before the timed series
@@ -561,6 +576,10 @@ def main(argv=None) -> int:
         dec_ms = [e[0].elapsed_time(e[1]) for e in kevs]
     mrg_ms = [e[1].elapsed_time(e[2]) for e in evs] if has_merge else [0.0]
     step_ms = [e[0].elapsed_time(e[2 if has_merge else 1]) for e in evs]
+    if args.layers > 1:  # per layer
+        step_ms = [t / args.layers for t in step_ms]
+        bracket_ms = [t / args.layers for t in bracket_ms]
+        dec_ms = bracket_ms
     print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
 
     # Calibration: the plain 1 GiB read used as the cache flush, timed alone.
@@ -582,7 +601,7 @@ def main(argv=None) -> int:
             step()
         e1.record()
         torch.cuda.synchronize()
-        warm_ms = e0.elapsed_time(e1) / args.steps
+        warm_ms = e0.elapsed_time(e1) / args.steps / args.layers
 
     mean_step = statistics.fmean(step_ms)
     mean_dec = statistics.fmean(dec_ms)
@@ -611,6 +630,7 @@ def main(argv=None) -> int:
             "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype, "context": list(w.context),
             "total_kv_tokens": int(dcase["kv_lens"].sum()), "seed": seed,
             "cache": "warm" if args.warm else "cold (1 GiB read between steps)",
+            "layers": args.layers,
             "launch": ("hip graph replay, fixed-capacity plan" if args.graph else
                        "fixed-capacity plan" if args.fixed_capacity else "exact plan"),
         },
@@ -649,7 +669,9 @@ def main(argv=None) -> int:
             "decode_us": round(mean_dec * 1e3, 2),
             "decode_timing": ("events recorded by the decode kernel's dispatch (hipExtLaunchKernel), "
                               f"{args.steps} more cold steps" if kernel_events
-                              else "events around the step"),
+                              else "events around the step" if args.layers == 1
+                              else f"events around the step's {args.layers} layers, divided by "
+                                   f"{args.layers}"),
             "decode_bracket_us": round(statistics.fmean(bracket_ms) * 1e3, 2),
             "algorithmic_bytes_per_launch": nbytes,
         },
