@@ -14,6 +14,9 @@ Timing: W untimed warmup steps, then K timed steps. Before each timed step a
 KV; HIP events on the launch stream bracket every step (with
 ``--separate-merge``, the decode and merge stages apart). ``value`` is KV-read
 GB/s over the whole step (algorithmic KV bytes / mean step time).
+With ``--layers L`` a step is L run() calls of its one plan, each over its
+own copy of the KV pool, and every time is reported per layer (the
+dispatch-stamped kernel series is then left out: the bracket is the figure).
 ``roofline`` is for the decode kernel, timed over K more cold steps by
 events that its own dispatch records (hipExtLaunchKernel through
 pkd_run_timed); HBM traffic comes from the committed rocprofv3 counter
