@@ -8,7 +8,7 @@ head_dim) and a per-request page list with the last page's fill selects them
 (§"Paged attention (vLLM)"); query heads share KV heads when num_kv_heads is
 smaller than num_qo_heads (§"The API you actually use (Python)").
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * Request r owns pages ``indices[indptr[r]:indptr[r+1]]`` (n_r >= 1 of them)
   and holds ``L_r = (n_r - 1) * page_size + last_page_len[r]`` tokens; token t

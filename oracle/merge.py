@@ -11,7 +11,7 @@
 with the same recurrence used per tile inside the main kernel and per split in
 the reduction kernel.
 
-Readings taken (listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * ``o`` is the unnormalised sum ``sum_t exp(s_t - m) v_t``: the rule rescales
   ``o`` by ``exp(m_a - m)`` alone, with no ``d`` weight, which is only right

@@ -8,7 +8,7 @@ not stall a batch of mixed short and long sequences (same page, §"What
 FlashInfer is", item 3); ``plan()`` does this once per batch shape and ``run()``
 reuses it (§"The API you actually use (Python)").
 
-The rule adopted (a reading; the design doc lists it):
+The rule adopted (a reading of the pages, not a rule they state):
 
 1. ``n_r = indptr[r+1] - indptr[r]`` pages and
    ``L_r = (n_r - 1) * P + last_page_len[r]`` tokens per request.
