@@ -123,10 +123,12 @@ typedef struct pkd_plan pkd_plan;
  *                   sees all of its KV tokens and q_r may exceed them: the
  *                   shared-prefix level of cascade attention, where the
  *                   queries of all requests sharing a prefix attend to it as
- *                   one request ("Cascade Attention" of "FlashInfer vs
- *                   FlashAttention-3: GPU Kernel Optimization & FP8 Serving
- *                   Latency", §"Key Features"); combine its output with the
- *                   per-request suffix level through pkd_merge_states.
+ *                   one request (the "Cascade Attention" operator of
+ *                   "GitHub Spotlight: FlashInfer", §"Core Superpowers:
+ *                   Breaking Down the Feature Set", and its shared-prefix
+ *                   use in §"Real-World Deployment Scenarios", Scenario A);
+ *                   combine its output with the per-request suffix level
+ *                   through pkd_merge_states.
  *  capacity_items,  all 0: the plan is laid out and launched for exactly its
  *  capacity_merge_tasks,  own work list. All > 0: a fixed-capacity plan for
  *  capacity_partials,     HIP graphs. Its workspace layout, launch grids,

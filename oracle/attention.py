@@ -26,9 +26,10 @@ Readings taken where the pages are silent:
   request are its last n KV tokens, in order, and new token i (0-based) sees
   the KV tokens up to and including its own position, i.e. the first
   ``L_r - n + 1 + i`` of them (causal within the new tokens).
-* Cascade attention over a shared prefix (the "Cascade Attention" of
-  "FlashInfer vs FlashAttention-3: GPU Kernel Optimization & FP8 Serving
-  Latency", §"Key Features"): the queries of every request that shares a
+* Cascade attention over a shared prefix (the "Cascade Attention" operator
+  of "GitHub Spotlight: FlashInfer", §"Core Superpowers: Breaking Down the
+  Feature Set", used for shared prompt prefixes in §"Real-World Deployment
+  Scenarios", Scenario A): the queries of every request that shares a
   prefix attend to it as one batch, so there the rows are not causal
   (``causal=False``: every row sees all of its request's tokens). The
   cascade's result is plain decode over prefix + suffix, which

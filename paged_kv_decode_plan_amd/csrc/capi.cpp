@@ -112,7 +112,7 @@ int pinned_acquire(size_t need, PinnedBlock* out) {
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "hipHostMalloc(%zu): %s", bytes, hipGetErrorString(e));
   e = hipEventCreateWithFlags(&b.done, hipEventDisableTiming);
   if (e != hipSuccess) {
-    hipHostFree(b.ptr);
+    (void)hipHostFree(b.ptr);
     return fail(PKD_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
   }
   *out = b;
@@ -131,8 +131,8 @@ void pinned_release(PinnedBlock b) {
           (victim < 0 || g_pool[i].bytes < g_pool[victim].bytes))
         victim = int(i);
     if (victim < 0) break;
-    hipEventDestroy(g_pool[victim].done);
-    hipHostFree(g_pool[victim].ptr);
+    (void)hipEventDestroy(g_pool[victim].done);
+    (void)hipHostFree(g_pool[victim].ptr);
     g_pool.erase(g_pool.begin() + victim);
   }
 }
@@ -187,7 +187,7 @@ int device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head
   if (e == hipSuccess)
     e = pkd::decode_occupancy(kv_dtype, head_dim, group, rows, q_kind, page_size, heads_per_wg,
                               wgs_cap, &wgs);
-  if (prev != device) hipSetDevice(prev);
+  if (prev != device) (void)hipSetDevice(prev);
   if (e != hipSuccess) return fail(PKD_ERR_HIP, "device query: %s", hipGetErrorString(e));
   *wgs_per_cu = wgs;
   *num_cus = cus;

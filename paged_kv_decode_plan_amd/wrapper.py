@@ -170,6 +170,15 @@ def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, 
     return info, items, merge, split
 
 
+def _same_device(device, **tensors):
+    """Every tensor given (None skipped) must live on `device`: the kernels take
+    raw pointers, and one on another device (or in host memory) would be read
+    as if it were on this one."""
+    for name, t in tensors.items():
+        if t is not None and t.device != device:
+            raise ValueError(f"{name} is on {t.device}; the workspace is on {device}")
+
+
 def _split_kv(paged_kv_cache):
     """(k, v) views from a combined [pages, 2, P, Hkv, D] tensor or a (k, v) pair."""
     if isinstance(paged_kv_cache, (tuple, list)):
@@ -226,9 +235,19 @@ class BatchDecodeWithPagedKVCacheWrapper:
         q_dt = q_data_type or data_type or torch.bfloat16
         kv_dt = kv_data_type or data_type or q_dt
         out_dt = out_data_type or q_dt
+        host_indptr = _host_i32(indptr)
+        n_indices = (indices.numel() if isinstance(indices, torch.Tensor)
+                     else int(np.asarray(indices).size))
+        if len(host_indptr) and n_indices < int(host_indptr[-1]):
+            # the kernels read page ids indices[indptr[r] .. indptr[r+1]) on the
+            # device; a shorter table would be read past its end
+            raise ValueError(f"indices holds {n_indices} page ids; indptr[-1] is "
+                             f"{int(host_indptr[-1])}")
         if self._plan is not None:
             self._plan.close()
+            self._plan = None
         dev = self._ws.device.index or 0
+        indptr = host_indptr
         self._plan = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
                           _dtype_code(q_dt), _dtype_code(kv_dt), _dtype_code(out_dt), sm_scale,
                           slots, balance, min_chunk_pages, dev, qo_indptr=qo_indptr,
@@ -272,6 +291,9 @@ class BatchDecodeWithPagedKVCacheWrapper:
         if p is None:
             raise RuntimeError("plan() must be called before run()")
         k, v = _split_kv(paged_kv_cache)
+        _same_device(self._ws.device, q=q, k=k, v=v, out=out, lse=lse, k_scale=k_scale,
+                     v_scale=v_scale, prior_v=None if prior is None else prior[0],
+                     prior_lse=None if prior is None else prior[1])
         if q.shape != (p.query_rows, p.num_qo_heads, p.head_dim) or not q.is_contiguous():
             raise ValueError(
                 f"q must be contiguous [{p.query_rows}, {p.num_qo_heads}, {p.head_dim}]")
@@ -378,6 +400,11 @@ def merge_state(v_a, s_a, v_b, s_b, v_out=None, s_out=None, out_dtype=None):
         raise ValueError("v_out has the wrong shape, dtype or layout")
     if s_out is None:
         s_out = torch.empty(v_a.shape[:2], dtype=torch.float32, device=v_a.device)
+    elif s_out.shape != v_a.shape[:2] or s_out.dtype != torch.float32 or not s_out.is_contiguous():
+        raise ValueError("s_out must be contiguous float32 [rows, heads]")
+    _same_device(v_a.device, v_b=v_b, s_a=s_a, s_b=s_b, v_out=v_out, s_out=s_out)
+    if not v_a.is_cuda:
+        raise ValueError("merge_state works on device tensors")
     a = _lib.MergeStatesArgs()
     a.rows, a.num_heads, a.head_dim = v_a.shape
     a.in_dtype = _dtype_code(v_a.dtype)

@@ -20,7 +20,7 @@ def _say(*a):
     print("[gpu-cascade]", *a, flush=True)
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 96, 128])
 @pytest.mark.parametrize("in_dt,out_dt", [(torch.float32, torch.float32),
                                           (torch.float32, torch.bfloat16),
                                           (torch.bfloat16, torch.float32)])
@@ -41,6 +41,40 @@ def test_merge_states_matches_oracle(d, in_dt, out_dt):
     got = v.double().cpu().numpy()
     bound = 1e-5 + (np.abs(ref_v) * 2.0 ** -8 if out_dt == torch.bfloat16 else 0.0)
     assert np.all(np.abs(got - ref_v) <= bound)
+    np.testing.assert_allclose(s.cpu().numpy(), ref_s, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 520])
+@pytest.mark.parametrize("alias", ["a", "b"])
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_merge_states_in_place(d, alias, dt):
+    """Output written over one of the inputs (rows and LSEs): the same bits as
+    the out-of-place merge, for head_dims whose (row, head) spans several
+    wavefronts (96, 192, 520) as well as 64 and 128."""
+    rng = np.random.default_rng(4000 + d)
+    rows, heads = 53, 6
+    va = torch.from_numpy(rng.standard_normal((rows, heads, d), dtype=np.float32)).to(dt).to(DEV)
+    vb = torch.from_numpy(rng.standard_normal((rows, heads, d), dtype=np.float32)).to(dt).to(DEV)
+    sa = torch.from_numpy((3 * rng.standard_normal((rows, heads))).astype(np.float32)).to(DEV)
+    sb = torch.from_numpy((3 * rng.standard_normal((rows, heads))).astype(np.float32)).to(DEV)
+    sa[0, :2] = -math.inf
+    sb[3, 1:4] = -math.inf
+    _say("merge_states in place", d, alias, dt)
+    want_v, want_s = pk.merge_state(va, sa, vb, sb)
+    torch.cuda.synchronize()
+    if alias == "a":
+        v, s = va.clone(), sa.clone()
+        pk.merge_state(v, s, vb, sb, v_out=v, s_out=s)
+    else:
+        v, s = vb.clone(), sb.clone()
+        pk.merge_state(va, sa, v, s, v_out=v, s_out=s)
+    torch.cuda.synchronize()
+    assert torch.equal(v, want_v)
+    assert torch.equal(s, want_s)
+    ref_v, ref_s = merge.merge_normalized(va.double().cpu().numpy(), sa.cpu().numpy(),
+                                          vb.double().cpu().numpy(), sb.cpu().numpy())
+    bound = 1e-5 + (np.abs(ref_v) * 2.0 ** -8 if dt == torch.bfloat16 else 0.0)
+    assert np.all(np.abs(v.double().cpu().numpy() - ref_v) <= bound)
     np.testing.assert_allclose(s.cpu().numpy(), ref_s, rtol=0, atol=1e-5)
 
 

@@ -1,5 +1,6 @@
 """Pins for the oracle's partition rule: hand-worked cases and invariants."""
 import json
+import math
 import os
 
 import numpy as np
@@ -45,27 +46,72 @@ def _random_table(rng, B, P, max_pages):
     return indptr, last
 
 
-@pytest.mark.parametrize("seed", range(25))
-def test_partition_invariants(seed):
+def _near_equal_table(rng, B, P, N):
+    """B requests of at most N pages, each at least N - N // 9 (so the longest is
+    within 1/8 of the mean), the first exactly N."""
+    n = rng.integers(N - N // 9, N + 1, size=B)
+    n[0] = N
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
+    last = rng.integers(1, P + 1, size=B).astype(np.int32)
+    return indptr, last
+
+
+def partition_case(seed):
+    """A seeded plan() input. Seeds cycle over three kinds so that a third of
+    them are near-equal batches, a third single requests (always near-equal),
+    and a third free random tables; slots_per_cu is drawn from 1-4."""
     rng = np.random.default_rng(seed)
-    B = int(rng.integers(1, 40))
     P = int(rng.choice([1, 4, 16, 64]))
-    indptr, last = _random_table(rng, B, P, int(rng.integers(1, 300)))
-    hkv = int(rng.choice([1, 2, 8]))
-    slots = int(rng.integers(1, 2048))
-    balance = int(rng.integers(1, 5))
-    cmin = int(rng.integers(1, 40))
-    p = oplan.plan(indptr, last, P, hkv, slots, balance, cmin)
+    kind = seed % 3
+    if kind == 0:
+        B = int(rng.integers(1, 40))
+        indptr, last = _random_table(rng, B, P, int(rng.integers(1, 300)))
+    elif kind == 1:
+        indptr, last = _near_equal_table(rng, int(rng.integers(2, 300)), P,
+                                         int(rng.integers(1, 400)))
+    else:
+        indptr, last = _near_equal_table(rng, 1, P, int(rng.integers(1, 5000)))
+    return dict(indptr=indptr, last=last, P=P, hkv=int(rng.choice([1, 2, 4, 8])),
+                slots=int(rng.integers(1, 2048)), balance=int(rng.integers(1, 5)),
+                cmin=int(rng.integers(1, 40)), per_cu=int(rng.integers(1, 5)))
+
+
+def expected_chunk_pages(c):
+    """The chunk length the rule asks for, found by enumeration.
+
+    Near-equal batches: every k from 1 to max(1, N // C_min) is priced as
+    (equal work units over the compute units, in whole waves) x (one unit's
+    pages + 2 C_min), and the cheapest k, the smallest on ties, gives
+    C = ceil(N / k). Other batches: the fair share of a slot, clamped to
+    [C_min, N]."""
+    n = np.diff(c["indptr"]).astype(np.int64)
+    B, S, N, H = len(n), int(n.sum()), int(n.max()), c["hkv"]
+    if 8 * N * B <= 9 * S:
+        cus = math.ceil(c["slots"] / c["per_cu"])
+        kmax = max(1, N // c["cmin"])
+        prices = {k: math.ceil(B * H * k / (cus * c["balance"])) * (math.ceil(N / k) + 2 * c["cmin"])
+                  for k in range(1, kmax + 1)}
+        cheapest = min(prices.values())
+        k = min(k for k, v in prices.items() if v == cheapest)
+        return math.ceil(N / k), True
+    share = math.ceil(S * H / (c["slots"] * c["balance"]))
+    return min(N, max(c["cmin"], share)), False
+
+
+def check_partition(seed):
+    """Every pin of one seeded partition: the chunk length against the
+    enumeration above, then coverage, token counts, partial slots, merge
+    index and order checked from their definitions."""
+    c = partition_case(seed)
+    indptr, last, P = c["indptr"], c["last"], c["P"]
+    B = len(last)
+    p = oplan.plan(indptr, last, P, c["hkv"], c["slots"], c["balance"], c["cmin"],
+                   slots_per_cu=c["per_cu"])
     C = p["chunk_pages"]
     n = np.diff(indptr)
     L = (n - 1) * P + last
-    S, N = int(n.sum()), int(n.max())
-    # chunk length: the closed form, and its bounds
-    if 8 * N * B <= 9 * S and 2 * B * hkv >= slots:
-        assert C == N
-    else:
-        assert C == min(N, max(cmin, -(-(S * hkv) // (slots * balance))))
-    assert 1 <= C <= N
+    assert C == expected_chunk_pages(c)[0]
+    assert 1 <= C <= int(n.max())
     items = p["items"]
     # coverage: per request, chunks tile its page range in order, tokens add up
     for r in range(B):
@@ -75,6 +121,9 @@ def test_partition_invariants(seed):
         assert np.all(mine[1:, 1] == mine[:-1, 2])
         assert np.all(mine[:, 2] - mine[:, 1] <= C) and np.all(mine[:, 2] > mine[:, 1])
         assert mine[:, 3].sum() == L[r]
+        # each chunk's tokens: whole pages, less the tail of the request's last page
+        tail = np.where(mine[:, 2] == indptr[r + 1], P - last[r], 0)
+        assert np.array_equal(mine[:, 3], (mine[:, 2] - mine[:, 1]) * P - tail)
         G = len(mine)
         assert G == -(-n[r] // C)
         if G > 1:
@@ -84,10 +133,32 @@ def test_partition_invariants(seed):
     # partial slots are a permutation of [0, num_partials)
     slots_used = np.sort(items[items[:, 4] >= 0, 4])
     assert np.array_equal(slots_used, np.arange(p["num_partials"]))
-    # longest first, ties by request
+    # longest first, ties by request, then chunk
     keys = list(zip(-items[:, 3], items[:, 0], items[:, 1]))
     assert keys == sorted(keys)
     assert p["split_requests"].tolist() == [r for r in range(B) if -(-n[r] // C) > 1]
+
+
+SEEDS = range(90)
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_partition_invariants(seed):
+    check_partition(seed)
+
+
+def test_partition_seeds_reach_both_branches():
+    """At least a third of the seeded cases take the near-equal branch, some
+    of them with several slots per compute unit and with one request, and the
+    enumeration there picks more than one distinct k."""
+    near = [s for s in SEEDS if expected_chunk_pages(partition_case(s))[1]]
+    assert 3 * len(near) >= len(SEEDS)
+    assert any(partition_case(s)["per_cu"] > 1 for s in near)
+    assert any(len(partition_case(s)["last"]) == 1 for s in near)
+    assert len(near) < len(SEEDS)
+    split = [s for s in near
+             if expected_chunk_pages(partition_case(s))[0] < np.diff(partition_case(s)["indptr"]).max()]
+    assert split and len(split) < len(near)
 
 
 @pytest.mark.parametrize("seed", range(25))
@@ -152,6 +223,21 @@ def test_uniform_batch_is_cut_to_fill_the_device():
     # C_min bounds k: with C_min=4 only k=1 is allowed
     p = oplan.plan(indptr, last, 16, 8, slots=2048, balance=1, min_chunk_pages=4)
     assert p["chunk_pages"] == 4 and p["num_partials"] == 0
+
+
+def test_cost_ties_take_the_fewest_chunks():
+    """Three requests of 4 pages, one KV head, 2 slots, C_min = 1, worked by
+    hand: k=1 costs ceil(3/2)*(4+2) = 12, k=2 ceil(6/2)*(2+2) = 12, k=3
+    ceil(9/2)*(2+2) = 20, k=4 ceil(12/2)*(1+2) = 18. k=1 and k=2 tie; the
+    smaller k wins, so the requests stay whole (C = 4) rather than C = 2."""
+    indptr = np.array([0, 4, 8, 12], np.int32)
+    last = np.array([16, 5, 16], np.int32)
+    p = oplan.plan(indptr, last, 16, 1, slots=2, balance=1, min_chunk_pages=1)
+    assert p["chunk_pages"] == 4 and p["num_partials"] == 0
+    # the same batch on 2 compute units with 2 slots each (4 slots) prices
+    # waves over compute units: identical choice
+    p = oplan.plan(indptr, last, 16, 1, slots=4, balance=1, min_chunk_pages=1, slots_per_cu=2)
+    assert p["chunk_pages"] == 4
 
 
 def test_waves_count_compute_units_not_slots():

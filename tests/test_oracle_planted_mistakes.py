@@ -109,27 +109,74 @@ def test_wrong_e4m3_bias_is_caught(monkeypatch):
     assert e4m3.value(0x38) != 1.0 and e4m3.value(0x7E) != 448.0
 
 
-def test_wrong_bf16_shift_is_caught():
-    bits = np.array([0x3F80], np.uint16)
-    wrong = (bits.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
-    assert wrong[0] != storage.widen(bits, "bf16")[0] == 1.0
+def test_wrong_bf16_shift_is_caught(monkeypatch):
+    """A widening that shifts the stored bits by 15 instead of 16 fails the
+    bf16 pins (torch's own bfloat16 conversion and the known patterns)."""
+    import test_oracle_e4m3_storage as pins
+    real = storage.widen
+
+    def wrong(x, dtype):
+        if dtype == "bf16":
+            bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(15)
+            return bits.view(np.float32).astype(np.float64)
+        return real(x, dtype)
+
+    monkeypatch.setattr(storage, "widen", wrong)
+    for pin in (pins.test_bf16_widening_matches_torch, pins.test_bf16_widening_known_patterns):
+        with pytest.raises(AssertionError):
+            pin()
 
 
-@pytest.mark.parametrize("mutant", ["off_by_one_kvlen", "no_last_page_trim"])
-def test_plan_mutants_are_caught(mutant, monkeypatch):
+# Plausible mistakes in the partition rule, each a one-place edit of the
+# oracle's own source: (text in oracle/plan.py, its replacement).
+PLAN_MUTANTS = {
+    "tie_break_to_largest_k": ("cost < best_cost", "cost <= best_cost"),
+    "cost_without_start_term": ("+ 2 * min_chunk_pages)", "+ 0 * min_chunk_pages)"),
+    "waves_over_slots_not_compute_units": ("_ceil_div(slots, max(1, slots_per_cu))", "slots"),
+    "near_equal_test_without_slack": ("8 * N * units <= 9 * S", "N * units <= S"),
+    "share_without_kv_heads": ("_ceil_div(S * num_kv_heads, slots * balance)",
+                               "_ceil_div(S, slots * balance)"),
+    "no_last_page_trim": ("kv_len -= page_size - last[r]", "kv_len -= 0"),
+    "shortest_first": ("rows.sort(key=lambda t: (-t[3],", "rows.sort(key=lambda t: (t[3],"),
+    "partial_slot_off_by_one": ("slot = merge_indptr[r] + c * nq[r]",
+                                "slot = merge_indptr[r] + 1 + c * nq[r]"),
+}
+
+
+def _mutant_plan(name):
+    import os
+    import types
+
     from oracle import plan as oplan
-    import json, os
-    with open(os.path.join(os.path.dirname(__file__), "golden", "plan_worked_example.json")) as f:
-        ex = json.load(f)
-    c = ex["cases"][1]
-    p = oplan.plan(c["indptr"], c["last_page_len"], ex["page_size"], 1, c["slots"],
-                   c["balance"], c["min_chunk_pages"])
-    items = p["items"].copy()
-    if mutant == "off_by_one_kvlen":
-        items[:, 3] -= 1
-    else:
-        items[items[:, 0] == 1, 3] = (items[items[:, 0] == 1, 2] - items[items[:, 0] == 1, 1]) * 16
-    assert items.tolist() != c["items"]
+    old, new = PLAN_MUTANTS[name]
+    with open(os.path.join(os.path.dirname(oplan.__file__), "plan.py")) as f:
+        src = f.read()
+    assert src.count(old) == 1, f"mutant {name}: the text to edit must occur once"
+    mod = types.ModuleType(f"plan_mutant_{name}")
+    exec(compile(src.replace(old, new), f"<oracle.plan mutant {name}>", "exec"), mod.__dict__)
+    return mod.plan
+
+
+@pytest.mark.parametrize("mutant", sorted(PLAN_MUTANTS))
+def test_plan_mutants_are_caught(mutant, monkeypatch):
+    """oracle.plan replaced by a mutated copy: the hand-worked partitions or the
+    seeded invariants (chunk length by enumeration, coverage, token counts,
+    partial slots, order) must then fail."""
+    from oracle import plan as oplan
+
+    import test_oracle_plan as pins
+    monkeypatch.setattr(oplan, "plan", _mutant_plan(mutant))
+    failed = 0
+    hand = [pins.test_hand_worked_partitions, pins.test_hand_worked_multi_query_partitions,
+            pins.test_cost_ties_take_the_fewest_chunks, pins.test_uniform_batch_is_cut_to_fill_the_device,
+            pins.test_waves_count_compute_units_not_slots,
+            pins.test_uniform_batch_just_over_the_device_is_cut_into_waves]
+    for pin in hand + [lambda s=s: pins.check_partition(s) for s in pins.SEEDS]:
+        try:
+            pin()
+        except AssertionError:
+            failed += 1
+    assert failed > 0, f"no pin caught the {mutant} mutant"
 
 
 def test_rowwise_scale_slot_mixup_is_caught():
