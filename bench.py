@@ -4,9 +4,10 @@
 One step is one run() over the whole batch: the split-KV decode kernel and,
 for a plan that splits requests, the merge of their partial states (folded
 into the decode kernel for a few short splits, else the merge kernel). The
-default workload is the
-Llama-3-8B-shaped decode batch (B=64, 32 query / 8 KV heads, head_dim 128,
-16-token pages, every context 2048, bf16). Inputs are synthetic (seeded
+default workload is the heterogeneous ragged batch, the largest that the
+measurements cover and the one the load balancing is for (B=256, 32 query /
+8 KV heads, head_dim 128, 16-token pages, bf16, context lengths log-uniform
+in [256, 65536]); ``--config`` selects another. Inputs are synthetic (seeded
 normal values, shuffled page table) and resident in HBM before timing.
 
 Timing: W untimed warmup steps, then K timed steps. Before each timed step a
@@ -23,8 +24,11 @@ pkd_run_timed); HBM traffic comes from the committed rocprofv3 counter
 summary when it was taken on the current kernel sources. ``cpu_baseline``
 times the float64 oracle on a bounded sample of the same batch (about 12 s
 of work) on one host core (and its ``parallel`` entry, the same sample over
-single-threaded worker processes);
-``calibration`` is a plain 1 GiB streaming read timed on the same device.
+single-threaded worker processes, one per core of this process's affinity
+mask up to 16, the CPU share of one GPU on the measurement hosts);
+``calibration`` times the library's plain streaming-read kernel
+(``pkd_stream_read``) over the 1 GiB flush buffer with 1, 2 and 4
+workgroups per compute unit on the same device.
 
 Prints one JSON line.
 """
@@ -230,16 +234,18 @@ def _oracle_pool(w, items, workers: int, passes: int = 1) -> float:
                 p.terminate()
 
 
-def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
+def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 2 << 30):
     """The oracle, as it stands, on whole requests of the same batch.
 
     Single thread: requests in batch order until about `budget_s` seconds of
     CPU work have been spent; a batch that takes less is run again, whole,
     until the budget is reached (so the rate rests on seconds of work).
     Parallel: the same requests (up to `keep_bytes` of host KV) again, spread
-    by KV bytes over worker processes, one per host core this process may use
-    (at most 16), each single-threaded, repeated so that the pool works for
-    about a quarter of the budget. Copying KV to the host and handing it to
+    by KV bytes over worker processes, one per core of this process's
+    affinity mask up to 16 (the CPU share of one GPU on the measurement
+    hosts; the mask's size and the host's core count are reported beside
+    it), each single-threaded, repeated so that the pool works for about a
+    quarter of the budget. Copying KV to the host and handing it to
     the workers is outside both timings.
     """
     from threadpoolctl import threadpool_limits
@@ -302,7 +308,8 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
                 passes += 1
     gbs = done_bytes / t_total / 1e9
 
-    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(kept)))
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(16, affinity, len(kept)))
     # one pass over `kept` takes about t_kept on one thread; aim for a quarter
     # of the budget of wall time on `workers` processes
     t_kept = t_total * kept_kv / max(1, done_bytes)
@@ -323,6 +330,8 @@ def cpu_baseline(dcase, w, budget_s: float = 12.0, keep_bytes: int = 8 << 30):
             "value": round(kept_kv * par_passes / t_par / 1e9, 4),
             "unit": "GB/s",
             "cores": workers,
+            "affinity_cores": affinity,
+            "host_cores": os.cpu_count(),
             "sample": (f"the first {len(kept)} of those requests"
                        + (f", {par_passes} passes" if par_passes > 1 else "")
                        + f", over {workers} single-threaded worker processes, {t_par:.2f} s"),
@@ -339,7 +348,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="llama3_8b_bf16")
+    ap.add_argument("--config", default="ragged_loguniform_bf16")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--warm", action="store_true", help="skip the cache flush between steps")
     ap.add_argument("--warm-ref", action="store_true",
@@ -585,16 +594,24 @@ def main(argv=None) -> int:
         dec_ms = bracket_ms
     print(f"[bench] timed {args.steps} steps in {wall_s:.2f} s", file=sys.stderr, flush=True)
 
-    # Calibration: the plain 1 GiB read used as the cache flush, timed alone.
-    cal_ms = []
-    for _ in range(10):
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record()
-        flush_i64.max()
-        c1.record()
-        torch.cuda.synchronize()
-        cal_ms.append(c0.elapsed_time(c1))
-    cal_gbs = flush.numel() / (statistics.median(cal_ms) * 1e-3) / 1e9
+    # Calibration: the library's plain streaming read over the 1 GiB flush
+    # buffer, at 1, 2 and 4 workgroups per compute unit (median of 10 each).
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    cal = {}
+    sink = torch.empty(4 * 4 * cus, dtype=torch.int32, device=dev)
+    for per_cu in (1, 2, 4):
+        pk.stream_read(flush, per_cu * cus, sink)  # warm the launch path
+        cal_ms = []
+        for _ in range(10):
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record()
+            pk.stream_read(flush, per_cu * cus, sink)
+            c1.record()
+            torch.cuda.synchronize()
+            cal_ms.append(c0.elapsed_time(c1))
+        cal[per_cu] = flush.numel() / (statistics.median(cal_ms) * 1e-3) / 1e9
+    best_cal = max(cal, key=cal.get)
+    cal_gbs = cal[best_cal]
 
     warm_ms = None
     if args.warm_ref:  # back-to-back steps, for reference
@@ -651,9 +668,13 @@ def main(argv=None) -> int:
                   "folded into the decode kernel" if info.get("merge_folded") else
                   "separate merge kernel inside the step"),
         "calibration": {
-            "kernel": "torch int64 max over a 1 GiB buffer (plain streaming read)",
+            "kernel": ("stream_read_kernel (pkd_stream_read): plain streaming read of a 1 GiB "
+                       "buffer, 16-byte loads, 8 KiB in flight per wavefront"),
             "read_gbs": round(cal_gbs, 1),
             "pct_of_peak_hbm": round(100.0 * cal_gbs / PEAK_HBM_GBS, 2),
+            "workgroups_per_cu": best_cal,
+            "read_gbs_by_workgroups_per_cu": {str(k): round(v, 1) for k, v in cal.items()},
+            "decode_kernel_over_calibration": round(dec_gbs / cal_gbs, 4),
         },
         "plan_us_host": round(plan_us, 1),
         "plan_us_host_first": round(first_plan_us, 1),

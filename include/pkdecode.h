@@ -408,6 +408,19 @@ int pkd_merge_states(const pkd_merge_states_args* args);
 int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t head_dim,
                      int32_t group, int32_t page_size, int32_t* wgs_per_cu, int32_t* num_cus);
 
+/* Calibration: enqueue one plain streaming read of `bytes` bytes at `buf`
+ * (device memory, 16-byte aligned, bytes a positive multiple of 16) by
+ * `workgroups` workgroups of four wavefronts, each keeping 8 KiB per
+ * wavefront in flight over consecutive 32 KiB blocks. `sink` (device,
+ * uint32[4 * workgroups]) receives an XOR of the data so that the reads are
+ * not optimised away. Timing it (events on `stream`) gives the HBM read rate
+ * one kernel reaches on the device, the ceiling the decode kernels' KV-read
+ * rate is set against: the pages measure decode kernels as a fraction of
+ * memory bandwidth ("Attention Kernel Comparison: FlashAttention vs
+ * FlashInfer vs xformers vs Triton", opening paragraphs). */
+int pkd_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                    void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -11,6 +11,7 @@ from .wrapper import (  # noqa: F401
     Plan,
     merge_state,
     plan_partition,
+    stream_read,
 )
 
 __all__ = [
@@ -20,6 +21,7 @@ __all__ = [
     "Plan",
     "PkdError",
     "plan_partition",
+    "stream_read",
     "load",
     "LIB_PATH",
     "DEFAULT_WORKSPACE_BYTES",

@@ -167,6 +167,9 @@ def load() -> ctypes.CDLL:
     lib.pkd_merge_states.restype = ctypes.c_int
     lib.pkd_device_slots.argtypes = [ctypes.c_int32] * 6 + [_c_i32p, _c_i32p]
     lib.pkd_device_slots.restype = ctypes.c_int
+    lib.pkd_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    lib.pkd_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib
 

@@ -714,6 +714,20 @@ int pkd_merge_states(const pkd_merge_states_args* m) {
   return ok();
 }
 
+int pkd_stream_read(const void* buf, size_t bytes, int32_t workgroups, uint32_t* sink,
+                    void* stream) {
+  if (!buf || !sink) return fail(PKD_ERR_INVALID_ARGUMENT, "buf and sink must not be NULL");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 || bytes % 16 || bytes == 0)
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "buf must be 16-byte aligned and bytes a positive multiple of 16");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "workgroups must lie in [1, 2^20]");
+  const hipError_t e = pkd::launch_stream_read(buf, int64_t(bytes), workgroups, sink,
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "stream_read launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 void pkd_plan_destroy(pkd_plan* p) {
   if (!p) return;
   pinned_release(p->staging);  // reused only after its copy has completed

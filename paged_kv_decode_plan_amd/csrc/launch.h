@@ -119,4 +119,10 @@ struct MergeStatesLaunch {
 };
 hipError_t launch_merge_states(const MergeStatesLaunch& a, hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 16) at `buf` (16-byte aligned) by
+// `workgroups` workgroups of four wavefronts; `sink` receives 4 words per
+// workgroup.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int workgroups, uint32_t* sink,
+                              hipStream_t stream);
+
 }  // namespace pkd

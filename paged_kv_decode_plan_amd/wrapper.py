@@ -475,3 +475,21 @@ class CascadeBatchDecodeWrapper:
     def close(self) -> None:
         for w in self._levels:
             w.close()
+
+
+def stream_read(buf, workgroups: int, sink=None):
+    """Enqueue the calibration read (``pkd_stream_read``) of the whole of the
+    contiguous device tensor ``buf`` by ``workgroups`` workgroups on the current
+    stream; returns the uint32 sink ``[4 * workgroups]`` it writes."""
+    import torch
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    if sink is None:
+        sink = torch.empty(4 * workgroups, dtype=torch.int32, device=buf.device)
+    elif sink.numel() < 4 * workgroups or sink.element_size() != 4 or sink.device != buf.device:
+        raise ValueError("sink must hold 4 * workgroups 32-bit words on buf's device")
+    stream = torch.cuda.current_stream(buf.device).cuda_stream
+    _lib.check(_lib.load().pkd_stream_read(
+        ctypes.c_void_p(buf.data_ptr()), ctypes.c_size_t(buf.numel() * buf.element_size()),
+        ctypes.c_int32(workgroups), ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream)))
+    return sink

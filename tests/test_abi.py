@@ -159,3 +159,16 @@ def test_check_page_ids_rejects_bad_arguments():
         _lib.PKD_ERR_INVALID_ARGUMENT
     assert lib.pkd_check_page_ids(None, 4, 8, None, ctypes.byref(cnt), None) == \
         _lib.PKD_ERR_INVALID_ARGUMENT  # null indices with a positive count
+
+
+def test_stream_read_rejects_bad_arguments():
+    """The calibration read checks its arguments on the host before launching."""
+    lib = pk.load()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.pkd_stream_read(None, 1 << 20, 256, fake, None) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_stream_read(fake, 1 << 20, 256, None, None) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_stream_read(ctypes.c_void_p(0x1008), 1 << 20, 256, fake,
+                               None) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_stream_read(fake, 100, 256, fake, None) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert lib.pkd_stream_read(fake, 1 << 20, 0, fake, None) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert b"workgroups" in lib.pkd_last_error()

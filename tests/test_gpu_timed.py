@@ -58,3 +58,18 @@ def test_timed_run_matches_run_and_stamps_the_kernel(split):
     wr.close()
     ref_out, ref_l = oracle_for(case)
     compare(out, lse, ref_out, ref_l, "bf16")
+
+
+@pytest.mark.parametrize("workgroups", [1, 256, 1024])
+def test_stream_read_reads_every_word(workgroups):
+    """The calibration read folds every 32-bit word of the buffer into its sink
+    (XOR over all sink words = XOR over the buffer), for a buffer that ends in
+    a ragged tail of its last 32 KiB block."""
+    rng = np.random.default_rng(workgroups)
+    words = rng.integers(-2**31, 2**31, size=(10 << 20) // 4 + 12, dtype=np.int64).astype(np.int32)
+    buf = torch.from_numpy(words).to("cuda:0")
+    print("[gpu] stream_read", workgroups, flush=True)
+    sink = pk.stream_read(buf, workgroups)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words.view(np.uint32))
