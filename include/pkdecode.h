@@ -342,6 +342,22 @@ int pkd_run_stages(const pkd_plan* plan, const pkd_run_args* args, int32_t stage
 int pkd_run_timed(const pkd_plan* plan, const pkd_run_args* args, int32_t stages,
                   void* decode_start, void* decode_stop);
 
+/* pkd_run for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops and harnesses that forbid allocation): the same
+ * kernels and results as pkd_run, but the plan's work list, merge records,
+ * fold counters and partial states live in a scratch array the library holds
+ * in each device's memory (16 MiB, a static device array, from the library's
+ * load until the process ends) instead of a caller-allocated workspace;
+ * args->workspace and args->workspace_bytes are ignored and the plan needs no
+ * pkd_plan_upload. The call enqueues on args->stream a copy of the plan's
+ * work list (from the plan's host image, which it has read when it returns)
+ * into the current device's scratch, then the run, and allocates nothing.
+ * A plan whose info.workspace_bytes exceeds the scratch is refused with
+ * PKD_ERR_WORKSPACE_TOO_SMALL. Every call on a device uses that device's one
+ * scratch array: calls that may overlap on one device (other streams, other
+ * threads) race and must be ordered by the caller. */
+int pkd_run_static(const pkd_plan* plan, const pkd_run_args* args);
+
 /* Count the page ids among indices[0 .. count) (device memory) that lie
  * outside [0, num_pages), the pool's page count, after the work already
  * queued on `stream`: the call copies the ids to the host and synchronises

@@ -152,6 +152,8 @@ def load() -> ctypes.CDLL:
     lib.pkd_plan_upload.restype = ctypes.c_int
     lib.pkd_run.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs)]
     lib.pkd_run.restype = ctypes.c_int
+    lib.pkd_run_static.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs)]
+    lib.pkd_run_static.restype = ctypes.c_int
     lib.pkd_run_stages.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs), ctypes.c_int32]
     lib.pkd_run_stages.restype = ctypes.c_int
     lib.pkd_run_timed.argtypes = [ctypes.c_void_p, ctypes.POINTER(RunArgs), ctypes.c_int32,

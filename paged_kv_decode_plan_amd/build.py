@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libpkdecode.so")
 ARCH = "gfx950"
 
 SOURCES = ["planner.cpp", "capi.cpp", "dispatch.hip", "decode_valu.hip", "decode_mfma.hip",
-           "merge.hip", "merge_states.hip", "calibrate.hip"]
+           "merge.hip", "merge_states.hip", "calibrate.hip", "scratch.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

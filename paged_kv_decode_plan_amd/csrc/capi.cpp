@@ -220,6 +220,109 @@ struct pkd_plan {
   int device = 0;
 };
 
+namespace {
+
+// Argument checks shared by pkd_run_timed and pkd_run_static (everything but
+// the workspace).
+int check_run_args(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
+  if (!p || !r) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
+  if (stages < 1 || stages > PKD_STAGE_ALL)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of PKD_STAGE_ALL");
+  const pkd_plan_args& a = p->args;
+  if (!r->q || !r->k || !r->v || !r->indices || !r->out)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "q, k, v, indices and out must not be NULL");
+  if ((a.kv_dtype == PKD_DTYPE_E4M3 || nibbles(a.kv_dtype)) &&
+      (!r->k_scale || !r->v_scale))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "e4m3, e2m1 and int4 KV need k_scale and v_scale");
+  if ((a.kv_scale_per_token || nibbles(a.kv_dtype)) &&
+      (reinterpret_cast<uintptr_t>(r->k_scale) % 16 || reinterpret_cast<uintptr_t>(r->v_scale) % 16))
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "row-wise and per-channel scale arrays must be 16-byte aligned");
+  const int vec_bytes = a.kv_dtype == PKD_DTYPE_E4M3 ? 8 : 16;
+  const uintptr_t kp = reinterpret_cast<uintptr_t>(r->k), vp = reinterpret_cast<uintptr_t>(r->v);
+  auto stride_ok = [&](int64_t st) {
+    return (!nibbles(a.kv_dtype) || st % 2 == 0) &&
+           kv_elems_bytes(a.kv_dtype, st) % vec_bytes == 0;
+  };
+  if (kp % vec_bytes || vp % vec_bytes || !stride_ok(r->page_stride) ||
+      !stride_ok(r->token_stride) || !stride_ok(r->head_stride))
+    return fail(PKD_ERR_INVALID_ARGUMENT,
+                "k, v and the strides must be %d-byte aligned for 128-bit row loads", vec_bytes);
+  if (reinterpret_cast<uintptr_t>(r->q) % 16)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
+  if (r->page_stride < 0 || r->token_stride < 0 || r->head_stride < 0)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
+  if (!r->prior_out != !r->prior_lse)
+    return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out and prior_lse go together");
+  if (r->prior_out && (reinterpret_cast<uintptr_t>(r->prior_out) % 16 ||
+                       reinterpret_cast<uintptr_t>(r->prior_lse) % 4))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out must be 16-byte aligned");
+  return PKD_OK;
+}
+
+// Enqueue the run's kernels with the plan's workspace image at `ws`.
+int launch_run(const pkd_plan* p, const pkd_run_args* r, int32_t stages, char* ws,
+               void* decode_start, void* decode_stop) {
+  const pkd_plan_args& a = p->args;
+  pkd::DecodeLaunch L;
+  L.kv_dtype = p->kv_impl;
+  L.head_dim = a.head_dim;
+  L.group = a.num_qo_heads / a.num_kv_heads;
+  L.rows = p->rows;
+  L.wgs_cap = p->wgs_cap;
+  L.heads_per_wg = p->heads_per_wg;
+  L.num_items = p->launch_items;
+  L.num_kv_heads = a.num_kv_heads;
+  L.num_qo_heads = a.num_qo_heads;
+  L.page_size_log2 = ilog2(a.page_size);
+  L.sm_scale_log2 = float(double(p->sm_scale) * 1.4426950408889634);
+  L.q_kind = kind_of(a.q_dtype);
+  L.out_kind = kind_of(a.out_dtype);
+  L.q = r->q;
+  L.k = r->k;
+  L.v = r->v;
+  L.page_stride = r->page_stride;
+  L.token_stride = r->token_stride;
+  L.head_stride = r->head_stride;
+  L.indices = r->indices;
+  L.k_scale = r->k_scale;
+  L.v_scale = r->v_scale;
+  L.out = r->out;
+  L.lse = r->lse;
+  L.prior_out = r->prior_out;
+  L.prior_lse = r->prior_lse;
+  L.items = reinterpret_cast<const pkd::DeviceItem*>(ws + p->off_items);
+  L.merge_tasks = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_split);
+  L.part_md = reinterpret_cast<float*>(ws + p->off_part_md);
+  L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
+  L.num_split = p->launch_tasks;
+  L.counts = p->fixed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+  L.block_merges = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_blocks);
+  L.counters = reinterpret_cast<int32_t*>(ws + p->off_counters);
+  // A whole run of an exact plan whose split requests have at most
+  // kFuseChunks chunks, over at most kFuseMaxWgs workgroups, folds the merge
+  // into the decode kernel (one launch instead of two: what matters when the
+  // batch is small). Longer folds run
+  // faster in the separate merge kernel, which spreads them over many more
+  // workgroups; fixed-capacity plans keep both launches so that one captured
+  // graph fits every plan; the stages alone always keep them apart.
+  L.fuse_merge = stages == PKD_STAGE_ALL && p->fuse_ok ? 1 : 0;
+  hipStream_t s = static_cast<hipStream_t>(r->stream);
+  hipError_t e;
+  if (stages & PKD_STAGE_DECODE) {
+    e = pkd::launch_decode(L, s, static_cast<hipEvent_t>(decode_start),
+                           static_cast<hipEvent_t>(decode_stop));
+    if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  }
+  if ((stages & PKD_STAGE_MERGE) && !L.fuse_merge) {
+    e = pkd::launch_merge(L, s);
+    if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* pkd_last_error(void) { return g_last_error.c_str(); }
@@ -556,100 +659,34 @@ int pkd_run_stages(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
 
 int pkd_run_timed(const pkd_plan* p, const pkd_run_args* r, int32_t stages, void* decode_start,
                   void* decode_stop) {
-  if (!p || !r) return fail(PKD_ERR_INVALID_ARGUMENT, "null argument");
-  if (stages < 1 || stages > PKD_STAGE_ALL)
-    return fail(PKD_ERR_INVALID_ARGUMENT, "stages must be a non-empty subset of PKD_STAGE_ALL");
-  const pkd_plan_args& a = p->args;
-  if (!r->q || !r->k || !r->v || !r->indices || !r->out || !r->workspace)
-    return fail(PKD_ERR_INVALID_ARGUMENT, "q, k, v, indices, out and workspace must not be NULL");
-  if ((a.kv_dtype == PKD_DTYPE_E4M3 || nibbles(a.kv_dtype)) &&
-      (!r->k_scale || !r->v_scale))
-    return fail(PKD_ERR_INVALID_ARGUMENT, "e4m3, e2m1 and int4 KV need k_scale and v_scale");
-  if ((a.kv_scale_per_token || nibbles(a.kv_dtype)) &&
-      (reinterpret_cast<uintptr_t>(r->k_scale) % 16 || reinterpret_cast<uintptr_t>(r->v_scale) % 16))
-    return fail(PKD_ERR_INVALID_ARGUMENT,
-                "row-wise and per-channel scale arrays must be 16-byte aligned");
+  if (int rc = check_run_args(p, r, stages); rc != PKD_OK) return rc;
+  if (!r->workspace) return fail(PKD_ERR_INVALID_ARGUMENT, "workspace must not be NULL");
   if (r->workspace != p->uploaded_to)
     return fail(PKD_ERR_PLAN_MISMATCH, "workspace differs from the one the plan was uploaded to");
   if (r->workspace_bytes < p->info.workspace_bytes)
     return fail(PKD_ERR_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, the plan needs %zu",
                 r->workspace_bytes, p->info.workspace_bytes);
-  const int vec_bytes = a.kv_dtype == PKD_DTYPE_E4M3 ? 8 : 16;
-  const uintptr_t kp = reinterpret_cast<uintptr_t>(r->k), vp = reinterpret_cast<uintptr_t>(r->v);
-  auto stride_ok = [&](int64_t st) {
-    return (!nibbles(a.kv_dtype) || st % 2 == 0) &&
-           kv_elems_bytes(a.kv_dtype, st) % vec_bytes == 0;
-  };
-  if (kp % vec_bytes || vp % vec_bytes || !stride_ok(r->page_stride) ||
-      !stride_ok(r->token_stride) || !stride_ok(r->head_stride))
-    return fail(PKD_ERR_INVALID_ARGUMENT,
-                "k, v and the strides must be %d-byte aligned for 128-bit row loads", vec_bytes);
-  if (reinterpret_cast<uintptr_t>(r->q) % 16)
-    return fail(PKD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
-  if (r->page_stride < 0 || r->token_stride < 0 || r->head_stride < 0)
-    return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
-  if (!r->prior_out != !r->prior_lse)
-    return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out and prior_lse go together");
-  if (r->prior_out && (reinterpret_cast<uintptr_t>(r->prior_out) % 16 ||
-                       reinterpret_cast<uintptr_t>(r->prior_lse) % 4))
-    return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out must be 16-byte aligned");
+  return launch_run(p, r, stages, static_cast<char*>(r->workspace), decode_start, decode_stop);
+}
 
-  pkd::DecodeLaunch L;
-  L.kv_dtype = p->kv_impl;
-  L.head_dim = a.head_dim;
-  L.group = a.num_qo_heads / a.num_kv_heads;
-  L.rows = p->rows;
-  L.wgs_cap = p->wgs_cap;
-  L.heads_per_wg = p->heads_per_wg;
-  L.num_items = p->launch_items;
-  L.num_kv_heads = a.num_kv_heads;
-  L.num_qo_heads = a.num_qo_heads;
-  L.page_size_log2 = ilog2(a.page_size);
-  L.sm_scale_log2 = float(double(p->sm_scale) * 1.4426950408889634);
-  L.q_kind = kind_of(a.q_dtype);
-  L.out_kind = kind_of(a.out_dtype);
-  L.q = r->q;
-  L.k = r->k;
-  L.v = r->v;
-  L.page_stride = r->page_stride;
-  L.token_stride = r->token_stride;
-  L.head_stride = r->head_stride;
-  L.indices = r->indices;
-  L.k_scale = r->k_scale;
-  L.v_scale = r->v_scale;
-  L.out = r->out;
-  L.lse = r->lse;
-  L.prior_out = r->prior_out;
-  L.prior_lse = r->prior_lse;
-  char* ws = static_cast<char*>(r->workspace);
-  L.items = reinterpret_cast<const pkd::DeviceItem*>(ws + p->off_items);
-  L.merge_tasks = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_split);
-  L.part_md = reinterpret_cast<float*>(ws + p->off_part_md);
-  L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
-  L.num_split = p->launch_tasks;
-  L.counts = p->fixed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
-  L.block_merges = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_blocks);
-  L.counters = reinterpret_cast<int32_t*>(ws + p->off_counters);
-  // A whole run of an exact plan whose split requests have at most
-  // kFuseChunks chunks, over at most kFuseMaxWgs workgroups, folds the merge
-  // into the decode kernel (one launch instead of two: what matters when the
-  // batch is small). Longer folds run
-  // faster in the separate merge kernel, which spreads them over many more
-  // workgroups; fixed-capacity plans keep both launches so that one captured
-  // graph fits every plan; the stages alone always keep them apart.
-  L.fuse_merge = stages == PKD_STAGE_ALL && p->fuse_ok ? 1 : 0;
-  hipStream_t s = static_cast<hipStream_t>(r->stream);
-  hipError_t e;
-  if (stages & PKD_STAGE_DECODE) {
-    e = pkd::launch_decode(L, s, static_cast<hipEvent_t>(decode_start),
-                           static_cast<hipEvent_t>(decode_stop));
-    if (e != hipSuccess) return fail(PKD_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-  }
-  if ((stages & PKD_STAGE_MERGE) && !L.fuse_merge) {
-    e = pkd::launch_merge(L, s);
-    if (e != hipSuccess) return fail(PKD_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
-  }
-  return ok();
+int pkd_run_static(const pkd_plan* p, const pkd_run_args* r) {
+  if (int rc = check_run_args(p, r, PKD_STAGE_ALL); rc != PKD_OK) return rc;
+  if (p->info.workspace_bytes > pkd::kStaticScratchBytes)
+    return fail(PKD_ERR_WORKSPACE_TOO_SMALL,
+                "the plan needs %zu bytes of scratch; the static scratch holds %zu (use pkd_run "
+                "with a caller-allocated workspace)",
+                p->info.workspace_bytes, pkd::kStaticScratchBytes);
+  void* ws = nullptr;
+  int dev = -1;
+  if (const hipError_t e = pkd::static_scratch_address(&ws, &dev); e != hipSuccess)
+    return fail(PKD_ERR_HIP, "static scratch of device %d: %s", dev, hipGetErrorString(e));
+  // The plan's work list, merge records and zeroed fold counters, copied from
+  // the plan's host image (pageable memory: the copy has read it when the
+  // call returns); the previous call's contents are overwritten.
+  const hipError_t e = hipMemcpyAsync(ws, p->header.data(), p->header_bytes,
+                                      hipMemcpyHostToDevice, static_cast<hipStream_t>(r->stream));
+  if (e != hipSuccess) return fail(PKD_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  return launch_run(p, r, PKD_STAGE_ALL, static_cast<char*>(ws), nullptr, nullptr);
 }
 
 int pkd_check_page_ids(const int32_t* indices, int64_t count, int32_t num_pages, void* stream,

@@ -125,4 +125,9 @@ hipError_t launch_merge_states(const MergeStatesLaunch& a, hipStream_t stream);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, int workgroups, uint32_t* sink,
                               hipStream_t stream);
 
+// Static device scratch of the entry point that allocates nothing: its size,
+// and its address on the current device (*device receives that device).
+constexpr size_t kStaticScratchBytes = size_t(16) << 20;
+hipError_t static_scratch_address(void** ptr, int* device);
+
 }  // namespace pkd

@@ -124,8 +124,13 @@ class Plan:
                                              ctypes.c_size_t(workspace_bytes),
                                              ctypes.c_void_p(stream_ptr)))
 
-    def run_raw(self, args: "_lib.RunArgs", stages: int = _lib.STAGE_ALL, events=None) -> None:
-        if events is not None:  # raw hipEvent_t handles stamped by the decode kernel's dispatch
+    def run_raw(self, args: "_lib.RunArgs", stages: int = _lib.STAGE_ALL, events=None,
+                static_scratch: bool = False) -> None:
+        if static_scratch:  # the library's static device scratch, no workspace
+            if stages != _lib.STAGE_ALL or events is not None:
+                raise ValueError("the static-scratch run takes whole runs without events")
+            _lib.check(self._lib.pkd_run_static(self._handle, ctypes.byref(args)))
+        elif events is not None:  # raw hipEvent_t handles stamped by the decode kernel's dispatch
             _lib.check(self._lib.pkd_run_timed(self._handle, ctypes.byref(args), stages,
                                                ctypes.c_void_p(events[0]),
                                                ctypes.c_void_p(events[1])))
@@ -275,7 +280,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
     # -- run -----------------------------------------------------------------
     def run(self, q, paged_kv_cache, out=None, lse=None, return_lse: bool = False,
             k_scale=None, v_scale=None, stages: int = _lib.STAGE_ALL, decode_events=None,
-            check_page_ids: bool = False, prior=None):
+            check_page_ids: bool = False, prior=None, static_scratch: bool = False):
         """``decode_events``: an optional pair of ``torch.cuda.Event(enable_timing=True)``
         that the decode kernel's own dispatch records as it starts and completes
         (``pkd_run_timed``); ``start.elapsed_time(stop)`` is then the kernel's time.
@@ -285,7 +290,11 @@ class BatchDecodeWithPagedKVCacheWrapper:
         ``PkdError`` (INVALID_ARGUMENT) instead of running on such a table.
         ``prior``: ``(v, lse)``, another normalised result of the same rows over a
         disjoint token set (float32 ``[rows, Hq, head_dim]`` and ``[rows, Hq]``),
-        merged into the output as it is written (cascade attention's levels)."""
+        merged into the output as it is written (cascade attention's levels).
+        ``static_scratch``: run through ``pkd_run_static``, which keeps the
+        plan's work list and partial states in the library's own device scratch
+        instead of the workspace (for callers that cannot allocate; the binding
+        itself still allocates ``out``/``lse`` when they are not given)."""
         import torch
         p = self._plan
         if p is None:
@@ -369,7 +378,7 @@ class BatchDecodeWithPagedKVCacheWrapper:
                 if not ev.cuda_event:  # torch creates the HIP event at its first record
                     ev.record()
             events = (decode_events[0].cuda_event, decode_events[1].cuda_event)
-        p.run_raw(a, stages, events)
+        p.run_raw(a, stages, events, static_scratch=static_scratch)
         return (out, lse) if (return_lse or lse is not None) else out
 
     forward = run

@@ -172,3 +172,24 @@ def test_stream_read_rejects_bad_arguments():
     assert lib.pkd_stream_read(fake, 100, 256, fake, None) == _lib.PKD_ERR_INVALID_ARGUMENT
     assert lib.pkd_stream_read(fake, 1 << 20, 0, fake, None) == _lib.PKD_ERR_INVALID_ARGUMENT
     assert b"workgroups" in lib.pkd_last_error()
+
+
+def test_static_scratch_run_refuses_large_plans_before_device_work():
+    """pkd_run_static checks its arguments and the plan's scratch need (16 MiB
+    at most) on the host before any HIP call."""
+    lib = pk.load()
+    indptr = list(range(0, 65 * 128, 128))
+    rc, h, msg = _create(indptr=indptr, last=[16] * 64, num_qo_heads=32, num_kv_heads=8,
+                         slots=16384, balance=1, min_chunk_pages=1)
+    assert rc == 0, msg
+    info = _lib.PlanInfo()
+    assert lib.pkd_plan_get_info(h, ctypes.byref(info)) == 0
+    assert info.workspace_bytes > 16 << 20
+    r = _lib.RunArgs()
+    assert lib.pkd_run_static(h, ctypes.byref(r)) == _lib.PKD_ERR_INVALID_ARGUMENT
+    fake = 1 << 20
+    r.q = r.k = r.v = r.indices = r.out = fake  # never dereferenced: refused first
+    assert lib.pkd_run_static(h, ctypes.byref(r)) == _lib.PKD_ERR_WORKSPACE_TOO_SMALL
+    assert b"static scratch" in lib.pkd_last_error()
+    assert lib.pkd_run_static(None, ctypes.byref(r)) == _lib.PKD_ERR_INVALID_ARGUMENT
+    lib.pkd_plan_destroy(h)

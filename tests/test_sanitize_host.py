@@ -29,8 +29,8 @@ from oracle import plan as oplan
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "paged_kv_decode_plan_amd", "csrc")
 BUILD = os.path.join(ROOT, "_build")
-KERNEL_TUS = ["dispatch.hip", "decode_valu.hip", "decode_mfma.hip", "merge.hip",
-              "merge_states.hip"]
+# every device-code translation unit of the library (all of csrc/*.hip)
+KERNEL_TUS = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
 SANITIZE = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined".split()
 ENV = {
     "ASAN_OPTIONS": "detect_leaks=1:abort_on_error=0:exitcode=86",
