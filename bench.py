@@ -78,13 +78,18 @@ def kv_bytes(w, table, logical: bool = False) -> int:
     return b
 
 
+# The sources the decode kernels are built and launched from: a change to any
+# of them makes committed counter readings of the decode kernel stale.
+DECODE_SOURCES = ("decode_mfma.hip", "decode_valu.hip", "dispatch.hip", "kernel_common.h",
+                  "launch.h")
+
+
 def kernel_source_sha() -> str:
-    """Hash of every device-code source (kernels, their shared header, dispatch)."""
+    """Hash of the decode kernels' sources (kernels, shared header, launch)."""
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith(".hip") or name == "kernel_common.h":
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in DECODE_SOURCES:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
@@ -129,6 +134,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: s
     fills = [v for n, g, v in wr if n.startswith("vectorized_elementwise") and v > 0.5 * gib_kib]
     f_scale = gib_kib / (sum(flush_reads) / len(flush_reads))
     w_scale = gib_kib / (sum(fills) / len(fills))
+    # cross-check: the library's calibration read of the same 1 GiB buffer
+    cal_reads = [v for n, g, v in fr if n.startswith("stream_read_kernel")]
+    cal_scale = gib_kib / (sum(cal_reads) / len(cal_reads)) if cal_reads else None
     dec_f = [v for n, g, v in fr if n.startswith("decode_")]
     dec_w = [v for n, g, v in wr if n.startswith("decode_")]
     fetch_b = sum(dec_f) / len(dec_f) * 1024 * f_scale
@@ -141,6 +149,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, workload: str, command: s
         "write_kib_raw_mean": sum(dec_w) / len(dec_w),
         "fetch_scale": f_scale,
         "write_scale": w_scale,
+        "fetch_scale_of_calibration_read": cal_scale,
         "scale_reference": "1 GiB cache-flush read (reduce_kernel) for FETCH_SIZE; 1 GiB zero "
                            "fill (vectorized_elementwise_kernel) for WRITE_SIZE, same runs",
         "fetch_bytes_per_launch": fetch_b,
@@ -669,7 +678,7 @@ def main(argv=None) -> int:
                   "separate merge kernel inside the step"),
         "calibration": {
             "kernel": ("stream_read_kernel (pkd_stream_read): plain streaming read of a 1 GiB "
-                       "buffer, 16-byte loads, 8 KiB in flight per wavefront"),
+                       "buffer, 16-byte non-temporal loads, 8 KiB in flight per wavefront"),
             "read_gbs": round(cal_gbs, 1),
             "pct_of_peak_hbm": round(100.0 * cal_gbs / PEAK_HBM_GBS, 2),
             "workgroups_per_cu": best_cal,

@@ -206,8 +206,11 @@ typedef struct {
   int32_t queries_per_item;    /* new tokens of one request a work item carries at most */
   int32_t max_qo_len;          /* most new tokens of one request */
   int32_t num_merge_tasks;     /* q rows of split requests (merge grid / num_qo_heads) */
-  int32_t units_per_item;      /* decode workgroups per work item (one per KV head) */
+  int32_t units_per_item;      /* decode workgroups per work item: one per KV head or
+                                  per pair of KV heads */
   int32_t merge_folded;        /* 1: pkd_run folds the merge into the decode kernel */
+  int32_t slots_per_cu;        /* resident workgroups per compute unit the rule took
+                                  (the device query's; 1 when slots was given) */
 } pkd_plan_info;
 
 /* Arguments of pkd_run. All pointers are device pointers.
@@ -427,7 +430,8 @@ int pkd_device_slots(int32_t device, int32_t q_dtype, int32_t kv_dtype, int32_t 
 /* Calibration: enqueue one plain streaming read of `bytes` bytes at `buf`
  * (device memory, 16-byte aligned, bytes a positive multiple of 16) by
  * `workgroups` workgroups of four wavefronts, each keeping 8 KiB per
- * wavefront in flight over consecutive 32 KiB blocks. `sink` (device,
+ * wavefront in flight over consecutive 32 KiB blocks, with non-temporal
+ * loads (the data is read once). `sink` (device,
  * uint32[4 * workgroups]) receives an XOR of the data so that the reads are
  * not optimised away. Timing it (events on `stream`) gives the HBM read rate
  * one kernel reaches on the device, the ceiling the decode kernels' KV-read

@@ -78,6 +78,7 @@ class PlanInfo(ctypes.Structure):
         ("num_merge_tasks", ctypes.c_int32),
         ("units_per_item", ctypes.c_int32),
         ("merge_folded", ctypes.c_int32),
+        ("slots_per_cu", ctypes.c_int32),
     ]
 
 

@@ -541,7 +541,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   constexpr size_t kFuseMaxWgs = 64;
   size_t split_wgs = 0;
   for (const auto& it : part.items)
-    if (it.partial_slot >= 0) split_wgs += size_t(a->num_kv_heads / heads_per_wg);
+    if (it.partial_slot >= 0) split_wgs += size_t(pin.units_per_item);
   p->fuse_ok = !fixed && max_chunks <= kFuseChunks && split_wgs <= kFuseMaxWgs;
   p->off_items = 256;
   p->off_split = align256(p->off_items + lay_items * sizeof(pkd::DeviceItem));
@@ -590,6 +590,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   inf.max_qo_len = max_q;
   inf.num_merge_tasks = int32_t(n_tasks);
   inf.units_per_item = pin.units_per_item;
+  inf.slots_per_cu = pin.slots_per_cu;
   inf.merge_folded = p->fuse_ok && n_split > 0 ? 1 : 0;
   *out = p;
   return ok();

@@ -164,7 +164,10 @@ def plan_partition(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, 
                    kv_dtype="bf16", q_dtype="bf16", out_dtype="f32", slots=1024, balance=0,
                    min_chunk_pages=0, qo_indptr=None, causal=True, capacity=None,
                    kv_scale="page"):
-    """Host-only: build a plan with an explicit slot count and return its decisions."""
+    """Build a plan and return its decisions (info, work list, merge index,
+    split requests). Host-only with an explicit slot count; ``slots=0`` asks
+    the device (device 0) for its resident-workgroup count, as run()'s
+    default plans do."""
     p = Plan(indptr, last_page_len, num_qo_heads, num_kv_heads, head_dim, page_size,
              _dtype_code(q_dtype), _dtype_code(kv_dtype), _dtype_code(out_dtype), None, slots,
              balance, min_chunk_pages, qo_indptr=qo_indptr, causal=causal, capacity=capacity,

@@ -56,7 +56,7 @@ def test_small_ragged_matches_oracle(kv, d, g, qd, split):
 
 
 @pytest.mark.parametrize("kv,qd", [("bf16", "bf16"), ("e4m3", "bf16"), ("f16", "f16")])
-@pytest.mark.parametrize("hkv", [3, 4])
+@pytest.mark.parametrize("hkv", [3, 4, 8, 16])
 @pytest.mark.parametrize("split", ["auto", "forced"])
 def test_one_or_two_kv_heads_per_workgroup(kv, qd, hkv, split):
     """An odd KV head count keeps one KV head per workgroup; an even one may
@@ -69,7 +69,7 @@ def test_one_or_two_kv_heads_per_workgroup(kv, qd, hkv, split):
     ref_out, ref_lse = oracle_for(case)
     kw = dict(slots=8, balance=1, min_chunk_pages=1) if split == "forced" else {}
     out, lse, info = run_hip(to_device(case), **kw)
-    assert info["units_per_item"] in (hkv, hkv // 2)
+    assert info["units_per_item"] in (hkv, hkv // 2, hkv // 8)
     compare(out, lse, ref_out, ref_lse, kv)
 
 
@@ -266,38 +266,111 @@ def test_shared_prefix_pages_are_legal():
         compare(out, lse, ref_out, ref_lse, "bf16")
 
 
-# ------------------------------------------------------------------ full-size workloads, sampled
+# ------------------------------------------------------------------ full-size workloads
 
 FULL = ["llama3_8b_bf16", "ragged_loguniform_bf16", "long_ctx_gqa8_bf16", "fp8_kv_e4m3"]
 
 
+def _run_full(dc, **plan_kw):
+    """run() of a full-size device case (default plan unless plan_kw), with the
+    plan's split requests."""
+    import paged_kv_decode_plan_amd as pk
+    from gpu_helpers import workspace
+    w = dc["workload"]
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+    wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], w.num_qo_heads, w.num_kv_heads,
+            w.head_dim, w.page_size, q_data_type=dc["q"].dtype,
+            kv_data_type=w.kv_dtype if w.kv_dtype == "e4m3" else dc["kv"].dtype,
+            out_data_type=torch.float32, sm_scale=w.scale(), **plan_kw)
+    out, lse = wr.run(dc["q"], dc["kv"], return_lse=True, k_scale=dc["k_scale"],
+                      v_scale=dc["v_scale"])
+    torch.cuda.synchronize()
+    info = wr.plan_info
+    split = wr._plan.worklist()[2].tolist()
+    wr.close()
+    return out, lse, info, split
+
+
+def _check_requests(dc, out, lse, rows, kv):
+    for n, r in enumerate(rows):
+        sub = sample_request_case(dc, r)
+        ref_out, ref_lse = oracle_for(sub)
+        if n % 8 == 0:
+            _say(f"  request {r} ({n + 1}/{len(rows)}), {int(dc['kv_lens'][r])} tokens")
+        compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, kv)
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_workload_sampled_rows(name):
-    """Full-size batch in the bench's launch configuration; the oracle checks
-    sampled requests (shortest, longest and a few random ones), all heads."""
+def test_full_size_workload(name):
+    """Full-size batch in the bench's launch configuration (the device-default
+    plan), compared element by element with the oracle: every request of the
+    Llama-shaped batch and of the long-context pair; every split request of
+    the ragged batch and 16 more; 24 requests of the fp8 batch (whose default
+    plan splits none), then every split request of a plan that splits (balance
+    4) over the same device data."""
     w = CONFIGS[name]
     seed = list(CONFIGS).index(name) + 1
     _say("full-size", name, "seed", seed)
     dc = device_case(w, seed, "cuda:0", poison=True)
-    out, lse, info = run_hip(dc)
+    out, lse, info, split = _run_full(dc)
     _say("plan", info)
+    assert np.all(np.isfinite(out_to_f64(out)))
     lens = dc["kv_lens"]
     rng = np.random.default_rng(seed)
-    rows = sorted({int(np.argmin(lens)), int(np.argmax(lens)),
-                   *rng.choice(len(lens), size=min(2, len(lens)), replace=False).tolist()})
-    if name == "long_ctx_gqa8_bf16":
-        rows = [1]
-    o = out_to_f64(out)
-    assert np.all(np.isfinite(o))
-    lv = lse.cpu().numpy().astype(np.float64)
-    for r in rows:
-        sub = sample_request_case(dc, r)
-        ref_out, ref_lse = oracle_for(sub)
-        _say("  row", r, "len", int(lens[r]))
-        compare(out[r:r + 1], lse[r:r + 1], ref_out, ref_lse, w.kv_dtype)
+    if name in ("llama3_8b_bf16", "long_ctx_gqa8_bf16"):
+        rows = list(range(w.batch))
+    else:
+        others = [r for r in range(w.batch) if r not in set(split)]
+        extra = 16 if name == "ragged_loguniform_bf16" else 24
+        rows = sorted(set(split) | {int(np.argmin(lens)), int(np.argmax(lens))}
+                      | set(rng.choice(others, size=extra, replace=False).tolist()))
+    if name == "ragged_loguniform_bf16":
+        assert len(split) > 0
+    _check_requests(dc, out, lse, rows, w.kv_dtype)
+    if name == "fp8_kv_e4m3":
+        out2, lse2, info2, split2 = _run_full(dc, balance=4)
+        _say("balance 4 plan", info2)
+        assert len(split2) > 0
+        _check_requests(dc, out2, lse2, split2, w.kv_dtype)
     del dc
     torch.cuda.empty_cache()
-    assert lv.shape == (w.batch, w.num_qo_heads)
+
+
+# Decode workgroups per compute unit that the library keeps by default for a
+# one-token plan on the MFMA kernel (an LDS reservation): one for 16-bit and
+# e4m3 KV, two for e2m1, three for int4.
+DEFAULT_RESIDENCY = {"bf16": 1, "f16": 1, "e4m3": 1, "e2m1": 2, "i4": 3}
+
+
+@pytest.mark.parametrize("name", [n for n in CONFIGS if CONFIGS[n].shared_prefix is None])
+def test_device_default_plan_matches_the_oracle_rule(name):
+    """The plan run() uses by default (slots = 0: the device's compute units
+    times the kernel's resident workgroups) against the oracle's rule with the
+    same slots, slots per compute unit, balance and shortest chunk, bit for
+    bit; the slot count is the compute units times that residency."""
+    import paged_kv_decode_plan_amd as pk
+    from oracle import plan as oplan
+    from workloads import page_table
+    w = CONFIGS[name]
+    t = page_table(w, seed=list(CONFIGS).index(name) + 1)
+    info, items, merge, split = pk.plan_partition(
+        t["indptr"], t["last_page_len"], w.num_qo_heads, w.num_kv_heads, w.head_dim,
+        w.page_size, kv_dtype=w.kv_dtype, q_dtype=w.q_dtype, slots=0,
+        qo_indptr=t["qo_indptr"], kv_scale=w.kv_scale)
+    _say("default plan", name, {k: info[k] for k in ("slots", "slots_per_cu", "num_items",
+                                                     "num_partials", "units_per_item")})
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert info["slots"] == info["slots_per_cu"] * cus
+    one_token = t["qo_indptr"] is None and w.head_dim == 128 and w.q_dtype != "f32"
+    if one_token and w.kv_dtype in DEFAULT_RESIDENCY:
+        assert info["slots_per_cu"] == DEFAULT_RESIDENCY[w.kv_dtype]
+    ref = oplan.plan(t["indptr"], t["last_page_len"], w.page_size, info["units_per_item"],
+                     info["slots"], info["balance"], info["min_chunk_pages"], t["qo_indptr"],
+                     info["queries_per_item"], slots_per_cu=info["slots_per_cu"])
+    assert info["chunk_pages"] == ref["chunk_pages"]
+    assert np.array_equal(items, ref["items"])
+    assert np.array_equal(merge, ref["merge_indptr"])
+    assert np.array_equal(split, ref["split_requests"])
 
 
 # ------------------------------------------------------------------ merge paths
