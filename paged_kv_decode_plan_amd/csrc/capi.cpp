@@ -42,6 +42,11 @@ int ok() { return PKD_OK; }
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// The workspace starts with a 256-byte block: the counts of a fixed-capacity
+// plan at byte 0 and, at this offset, the two work counters of persistent
+// decode launches (zero in every upload; the kernel leaves them at zero).
+constexpr size_t kWorkCountersOffset = 128;
+
 // 4-bit KV formats: two elements per byte.
 bool nibbles(int dtype) { return dtype == PKD_DTYPE_E2M1 || dtype == PKD_DTYPE_I4; }
 
@@ -297,6 +302,7 @@ int launch_run(const pkd_plan* p, const pkd_run_args* r, int32_t stages, char* w
   L.part_o = reinterpret_cast<float*>(ws + p->off_part_o);
   L.num_split = p->launch_tasks;
   L.counts = p->fixed ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+  L.work = reinterpret_cast<int32_t*>(ws + kWorkCountersOffset);
   L.block_merges = reinterpret_cast<const pkd::MergeTask*>(ws + p->off_blocks);
   L.counters = reinterpret_cast<int32_t*>(ws + p->off_counters);
   // A whole run of an exact plan whose split requests have at most
@@ -522,7 +528,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
                 "capacities are %d, %d and %d",
                 n_items, n_tasks, np, caps[0], caps[1], caps[2]);
   }
-  // Workspace: [counts (256 B) | items | merge tasks | fused-merge records |
+  // Workspace: [counts and work counters (256 B) | items | merge tasks | fused-merge records |
   // fused-merge counters | partial (m, d) | partial o], sized by the plan
   // itself or, for a fixed-capacity plan, by its capacities (records never
   // outnumber merge tasks). The uploaded header runs through the counters,

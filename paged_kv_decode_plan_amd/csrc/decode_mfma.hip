@@ -878,37 +878,36 @@ __device__ inline void load_pid_block(const Ctx& c, int wave, int first_tile, in
   }
 }
 
-// Register budget: 128 VGPRs (4 wavefronts per SIMD) when a tile is one
-// 16-token sub-tile of pages >= 16; larger tiles and per-lane page lookups need
-// up to 168 (3 wavefronts per SIMD); row-wise e4m3 scales ride along with the
-// loads and get up to 256 (2 per SIMD, still twice what one workgroup per CU
-// uses). e2m1 keeps four sub-tiles and the q hi/lo pair in flight and takes
-// the same 256, as do head pairs (two scales per page for e4m3).
-// int4 (the most VALU work per byte) gets 168 so that three workgroups fit a
-// CU (its 4 KiB tiles need 148-159).
+// Register budget: up to 168 VGPRs (3 wavefronts per SIMD) by default, as
+// one workgroup of four wavefronts per CU (the default residency) leaves
+// room for; row-wise e4m3 scales ride along with the loads and get up to 256
+// (2 per SIMD), as do e2m1 (four sub-tiles and the q hi/lo pair in flight),
+// head pairs (two scales per page for e4m3), two column groups and e4m3 or
+// int4 with pages under 16 tokens (per-lane page lookups). int4 (the
+// most VALU work per byte) gets 168 so that three workgroups fit a CU (its
+// 4 KiB tiles need 159-165 with the persistent unit loop).
 template <int KV, bool PAGE16, int HP, int G>
 constexpr int waves_per_simd() {
-  if constexpr (KV == kI4) return G <= 16 ? 3 : 2;
-  return KV == kE4M3T || nib4<KV>() || HP > 1 || G > 16 ? 2 : PAGE16 && nsub<KV>() == 1 ? 4 : 3;
+  if constexpr (KV == kI4) return G <= 16 && PAGE16 ? 3 : 2;
+  return KV == kE4M3T || nib4<KV>() || HP > 1 || G > 16 || (fp8<KV>() && !PAGE16) ? 2 : 3;
 }
 
-// G: S columns (query rows) per workgroup. HP = 2: the workgroup's "KV head"
-// kvh of the launch is a pair of KV heads 2*kvh, 2*kvh + 1 with G / 2 query
-// heads each (the launch passes num_kv_heads / 2 and group_log2 + 1, so the
-// epilogue and the merge address query heads as usual).
+// One work unit: work item `item` (a run of one request's pages for a block
+// of its query tokens) for KV head (pair) kvh, from its query rows to its
+// output rows or partial states. Called by every thread of the workgroup;
+// `st` is the workgroup's shared state image. Persistent launches: thread 0
+// takes the workgroup's next unit when this one's tiles are done (so units are
+// handed out in the order workgroups become free) and returns it.
 template <int KV, int G, bool PAGE16, int HP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16, HP, G>()))) void decode_mfma_kernel(KernelArgs a) {
-  static_assert(G >= 1 && G <= 32, "at most 32 query rows per KV head");
-  static_assert(HP == 1 || (G >= HP && PAGE16), "head pairs: pages >= 16");
+__device__ inline int decode_unit(const KernelArgs& a, WaveStates<G, kD>& st, int item, int kvh) {
   constexpr int NG = G > 16 ? 2 : 1;  // column groups of 16
-  __shared__ WaveStates<G, kD> st;
-
-  int item, kvh;
-  decode_block(a.num_kv_heads, a.xcd_group, &item, &kvh);
-  if (item >= launch_items(a)) return;  // grid padding; no barrier passed yet
   const DeviceItem it = a.items[item];
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The lane index is opaque (opaque_tid) so that nothing derived from it
+  // (lane offsets, masks) is computed once for all the units of a persistent
+  // workgroup and held in registers across them.
+  const int tid = opaque_tid();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   Ctx c;
   c.kbase = static_cast<const char*>(a.k);
@@ -1149,7 +1148,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_
     }
   }
   __syncthreads();
+  int next = 0;
+  if (a.persistent && tid == 0) next = int(gridDim.x) + atomicAdd(a.work, 1);
   finish_workgroup<G, kD>(st, a, it, kvh);
+  return next;
+}
+
+// G: S columns (query rows) per workgroup. HP = 2: the workgroup's "KV head"
+// kvh of the launch is a pair of KV heads 2*kvh, 2*kvh + 1 with G / 2 query
+// heads each (the launch passes num_kv_heads / 2 and group_log2 + 1, so the
+// epilogue and the merge address query heads as usual).
+//
+// Work units are (item, KV head (pair)) in plan order. A plain launch runs
+// one unit per workgroup (decode_block). A persistent launch runs the
+// device's resident workgroups, each taking units from a counter until none
+// is left: the longest units still start first, every compute unit takes the
+// next unit as soon as it is free (a plain launch hands workgroup ids to the
+// eight XCDs in turn, so a free compute unit can idle until an id for its XCD
+// comes up), and no workgroup waits for another (the counters are only ever
+// incremented), so every workgroup exits.
+template <int KV, int G, bool PAGE16, int HP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KV, PAGE16, HP, G>()))) void decode_mfma_kernel(KernelArgs a) {
+  static_assert(G >= 1 && G <= 32, "at most 32 query rows per KV head");
+  static_assert(HP == 1 || (G >= HP && PAGE16), "head pairs: pages >= 16");
+  __shared__ WaveStates<G, kD> st;
+  __shared__ int s_next;
+
+  if (!a.persistent) {
+    int item, kvh;
+    decode_block(a.num_kv_heads, a.xcd_group, &item, &kvh);
+    if (item >= launch_items(a)) return;  // grid padding; no barrier passed yet
+    decode_unit<KV, G, PAGE16, HP>(a, st, item, kvh);
+    return;
+  }
+  const int units = launch_items(a) * a.num_kv_heads;
+  for (int u = blockIdx.x; u < units;) {
+    const int item = u / a.num_kv_heads;
+    const int next = decode_unit<KV, G, PAGE16, HP>(a, st, item, u - item * a.num_kv_heads);
+    if (threadIdx.x == 0) s_next = next;
+    __syncthreads();  // also: the next unit writes st only after every read of this one
+    u = s_next;
+    __syncthreads();
+  }
+  // The last workgroup to finish resets the counters (by then every
+  // workgroup has made its last fetch).
+  if (threadIdx.x == 0 && atomicAdd(a.work + 1, 1) == int(gridDim.x) - 1) {
+    __hip_atomic_store(a.work, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.work + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int KV, bool P16>

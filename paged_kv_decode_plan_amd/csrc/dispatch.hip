@@ -12,6 +12,10 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "kernel_common.h"
 
 namespace pkd {
@@ -67,6 +71,48 @@ static hipError_t cap_lds(DecodeFn fn, int cap, size_t* bytes) {
       e != hipSuccess)
     return e;
   if (attr.sharedSizeBytes < kTotal[cap]) *bytes = kTotal[cap] - attr.sharedSizeBytes;
+  return hipSuccess;
+}
+
+// Persistent launches of the MFMA kernel (see decode_mfma_kernel) when a
+// plan has more work units than the device holds resident workgroups: for
+// 16-bit and e4m3 KV, which run one workgroup per compute unit (measured on
+// MI355X: the ragged batch 1602.6 -> 1586.6 us per decode launch, the fp8
+// batch 687.9 -> 661.3 us), not for e2m1 and int4 KV, which run two and three
+// (404.3 against 397.8 us and 451.2 against 428.3 us).
+#ifndef PKD_PERSISTENT
+#define PKD_PERSISTENT 1
+#endif
+#ifndef PKD_PERSISTENT_NIB4
+#define PKD_PERSISTENT_NIB4 0
+#endif
+
+// Workgroups of `fn` (with `lds` bytes of dynamic LDS) the current device
+// holds at once: resident per compute unit x compute units, cached per
+// (device, kernel, LDS).
+static hipError_t resident_workgroups(DecodeFn fn, size_t lds, int* out) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  const auto key = std::make_tuple(dev, reinterpret_cast<const void*>(fn), lds);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (auto it = cache.find(key); it != cache.end()) {
+      *out = it->second;
+      return hipSuccess;
+    }
+  }
+  int cus = 0, per_cu = 0;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      e != hipSuccess)
+    return e;
+  if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, lds);
+      e != hipSuccess)
+    return e;
+  *out = cus * per_cu;
+  std::lock_guard<std::mutex> lk(mu);
+  cache[key] = *out;
   return hipSuccess;
 }
 
@@ -133,6 +179,8 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream, hipEvent_t s
   a.fuse_merge = L.fuse_merge;
   a.part_o = L.part_o;
   a.part_md = L.part_md;
+  a.work = L.work;
+  a.persistent = 0;
   a.num_items = L.num_items;
   a.xcd_group = (L.kv_dtype == kE4M3 || L.kv_dtype == kE4M3T || L.kv_dtype == kE2M1 ||
                  L.kv_dtype == kI4)
@@ -146,9 +194,19 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream, hipEvent_t s
   a.sm_scale_log2 = L.sm_scale_log2;
   a.q_kind = L.q_kind;
   a.out_kind = L.out_kind;
-  const unsigned grid = decode_grid_size(L.num_items, a.num_kv_heads, a.xcd_group);
+  unsigned grid = decode_grid_size(L.num_items, a.num_kv_heads, a.xcd_group);
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, L.wgs_cap, &lds); e != hipSuccess) return e;
+  const bool nib4 = L.kv_dtype == kE2M1 || L.kv_dtype == kI4;
+  if (PKD_PERSISTENT && (PKD_PERSISTENT_NIB4 || !nib4) && L.work &&
+      decode_uses_mfma(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_kind, 1 << L.page_size_log2)) {
+    int resident = 0;
+    if (hipError_t e = resident_workgroups(fn, lds, &resident); e != hipSuccess) return e;
+    if (resident > 0 && int64_t(L.num_items) * a.num_kv_heads > resident) {
+      a.persistent = 1;
+      grid = unsigned(resident);
+    }
+  }
   if (start || stop)
     hipExtLaunchKernelGGL(fn, dim3(grid), dim3(kThreads), lds, stream, start, stop, 0, a);
   else

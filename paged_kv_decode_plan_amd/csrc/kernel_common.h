@@ -38,6 +38,12 @@ struct KernelArgs {
   int fuse_merge;
   float* part_o;
   float* part_md;
+  // Persistent launch (persistent = 1): the grid is the device's resident
+  // workgroups and each workgroup takes work units (item, KV head) in plan
+  // order from work[0]; work[1] counts finished workgroups, and the last one
+  // resets both to zero for the next launch.
+  int* work;
+  int persistent;
   int num_items;
   int xcd_group;  // workgroup-id grouping g (see decode_block)
   int num_kv_heads;
@@ -99,6 +105,15 @@ __device__ inline uint2 pack4_16(float x, float y, float z, float w, int kind) {
                uint32_t(float_to_bf16_rne(z)) | (uint32_t(float_to_bf16_rne(w)) << 16)};
 }
 
+// threadIdx.x through an empty asm statement: the epilogues below run once
+// per work unit of a persistent workgroup, and values derived from an opaque
+// index are not computed once for all units and held in registers.
+__device__ inline int opaque_tid() {
+  int t = int(threadIdx.x);
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // Fold another normalised result of the same row (output value v_p per dim,
 // natural-log LSE lse_p; the cascade's other level) into the state (M in
 // log2 units, d, o) about to be written: the prior is the state
@@ -137,9 +152,10 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
   __shared__ int s_last;
   const MergeTask mt = a.block_merges[it.block_merge];
   int32_t* counter = a.counters + int64_t(it.block_merge) * a.num_kv_heads + kvh;
+  const int tid = opaque_tid();
   __threadfence();  // this workgroup's partial states before its arrival
   __syncthreads();
-  if (threadIdx.x == 0) s_last = atomicAdd(counter, 1) == mt.count - 1;
+  if (tid == 0) s_last = atomicAdd(counter, 1) == mt.count - 1;
   __syncthreads();
   if (!s_last) return;
   __threadfence();  // every other chunk's partial states after the count
@@ -149,7 +165,7 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
   constexpr int kU = 8;  // chunks whose loads are in flight together
   const float2* md = reinterpret_cast<const float2*>(a.part_md);
   const float4* po = reinterpret_cast<const float4*>(a.part_o);
-  for (int idx = threadIdx.x; idx < rows * kQuads; idx += nthreads) {
+  for (int idx = tid; idx < rows * kQuads; idx += nthreads) {
     const int h = idx / kQuads;
     const int qd = idx % kQuads;
     const int i = h >> a.group_log2;
@@ -197,7 +213,7 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
     }
     if (a.lse && qd == 0) a.lse[row] = Dn > 0.f ? (M + log2f(Dn)) * kLn2 : -INFINITY;
   }
-  if (threadIdx.x == 0) *counter = 0;
+  if (tid == 0) *counter = 0;
 }
 
 // Shared-memory image of the wavefronts' states for the final merge.
@@ -218,7 +234,7 @@ template <int G, int D>
 __device__ inline void finish_workgroup(const WaveStates<G, D>& s, const KernelArgs& a,
                                         const DeviceItem& it, int kvh) {
   const int gmask = (1 << a.group_log2) - 1;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = opaque_tid(); idx < G * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx % D;
     const int i = h >> a.group_log2;

@@ -78,6 +78,9 @@ struct DecodeLaunch {
   // by the kernels (num_items / num_split are then the capacities). nullptr:
   // the launch is sized exactly.
   const int32_t* counts = nullptr;
+  // Two counters, zero between launches, for a persistent launch of the MFMA
+  // kernel (work units taken, workgroups finished); nullptr: plain launches.
+  int32_t* work = nullptr;
   // Merge folded into the decode kernel: one record per (split request, query
   // block) (out_row = its first q row, count = chunks, stride = q_r) and one
   // arrival counter per (record, KV head), zero between runs.

@@ -1,0 +1,78 @@
+"""Persistent decode launches: a plan with more work units (item x KV-head
+pair) than the device holds resident workgroups runs as that many
+workgroups, each taking units from a counter in the workspace, which the last
+one to finish resets. Checked on the GPU against the oracle, and run again
+(also after another plan used the same workspace) with identical bits, which
+needs the counters back at zero after every launch."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_decode_plan_amd as pk
+from gpu_helpers import compare, oracle_for, to_device, workspace
+from workloads import custom_workload, host_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print("[gpu-persistent]", *a, flush=True)
+
+
+def _plan(dc, w, **kw):
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+    wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], w.num_qo_heads, w.num_kv_heads,
+            w.head_dim, w.page_size, q_data_type=torch.bfloat16,
+            kv_data_type="e4m3" if w.kv_dtype == "e4m3" else torch.bfloat16,
+            out_data_type=torch.float32, sm_scale=w.scale(), **kw)
+    return wr
+
+
+def _run(wr, dc):
+    out, lse = wr.run(dc["q"], dc["kv"], return_lse=True, k_scale=dc["k_scale"],
+                      v_scale=dc["v_scale"])
+    torch.cuda.synchronize()
+    return out, lse
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("split", ["none", "some"])
+def test_many_units_match_the_oracle_and_repeat(kv, split):
+    rng = np.random.default_rng(77 if kv == "bf16" else 78)
+    lens = rng.integers(1, 400, size=320).tolist()
+    if split == "some":
+        lens[:6] = [6000, 5000, 4200, 3900, 3100, 2500]
+    w = custom_workload(len(lens), 32, 8, 128, 16, kv, "bf16", lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 9)
+    case = host_case(w, 2024, poison=True)
+    dc = to_device(case)
+    kw = dict(balance=4) if split == "some" else {}
+    wr = _plan(dc, w, **kw)
+    info = wr.plan_info
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _say(kv, split, {k: info[k] for k in ("num_items", "units_per_item", "num_split_requests")})
+    # more units than one workgroup per compute unit: the persistent launch
+    assert info["num_items"] * info["units_per_item"] > 2 * cus
+    if split == "some":
+        assert info["num_split_requests"] > 0
+    out, lse = _run(wr, dc)
+    ref, ref_lse = oracle_for(case)
+    compare(out, lse, ref, ref_lse, kv)
+    for _ in range(2):
+        again, again_lse = _run(wr, dc)
+        assert torch.equal(again, out) and torch.equal(again_lse, lse)
+    wr.close()
+
+    # another plan through the same workspace (its own upload), then this one again
+    small = custom_workload(3, 32, 8, 128, 16, kv, "bf16", [100, 900, 17], pool_pages=70)
+    scase = host_case(small, 5, poison=True)
+    sdc = to_device(scase)
+    swr = _plan(sdc, small, slots=8, balance=1, min_chunk_pages=1)
+    sout, slse = _run(swr, sdc)
+    sref, sref_lse = oracle_for(scase)
+    compare(sout, slse, sref, sref_lse, kv)
+    swr.close()
+    wr = _plan(dc, w, **kw)
+    again, again_lse = _run(wr, dc)
+    assert torch.equal(again, out) and torch.equal(again_lse, lse)
+    wr.close()
