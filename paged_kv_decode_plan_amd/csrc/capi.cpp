@@ -516,7 +516,7 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
     }
   }
   const size_t n_blocks = blocks.size();
-  constexpr int32_t kFuseChunks = 4;
+  constexpr int32_t kFuseChunks = 16;
   int32_t max_chunks = 0;
   for (const auto& b : blocks) max_chunks = std::max(max_chunks, b.count);
   if (fixed && (n_items > size_t(caps[0]) || n_tasks > size_t(caps[1]) ||
@@ -540,10 +540,12 @@ int pkd_plan_create(const pkd_plan_args* a, pkd_plan** out) {
   p->launch_items = int32_t(lay_items);
   p->launch_tasks = fixed ? caps[1] : int32_t(n_tasks);
   p->num_blocks = int32_t(n_blocks);
-  // Folding costs every split workgroup a device-scope release fence (and the
-  // last one an acquire), which on MI355X write back and invalidate its XCD's
-  // L2: cheap for a few workgroups (a lone long request: 25 -> 21.6 us), ruinous
-  // for hundreds (64 requests of 512 tokens split in two: 33 -> 109 us).
+  // Folding costs every split workgroup a device-scope release (and the last
+  // one an acquire), which on MI355X write back and invalidate its XCD's L2:
+  // cheaper than the merge launch for a few workgroups (the single-sequence
+  // step, 512 tokens in eight chunks over four KV heads: 12.7 -> 11.9 us),
+  // dearer for hundreds (64 requests split in two over eight KV heads: 94.0
+  // -> 99.4 us; 32-chunk requests: 166.6 -> 177.2 us).
   constexpr size_t kFuseMaxWgs = 64;
   size_t split_wgs = 0;
   for (const auto& it : part.items)

@@ -139,13 +139,17 @@ __device__ inline float4 fold_prior4(float4 O, float4 vp, const PriorWeights& w)
 }
 
 // The merge of a split request, folded into the decode kernel: every
-// workgroup of a chunk publishes its partial states (release fence), then
-// counts itself in with one atomic add on the (request, query block, KV head)
-// counter; the one that completes the count is the last, and after an acquire
-// fence it folds the chunks' partial states of its rows with the
-// online-softmax rule (chunks in order, so the result does not depend on
-// which workgroup finishes last), writes the output rows and LSE, and resets
-// the counter for the next run. Called by every thread of the workgroup.
+// workgroup of a chunk counts itself in with one atomic add on the (request,
+// query block, KV head) counter, made by one thread after a workgroup
+// barrier and with release ordering at device scope, which publishes every
+// wavefront's partial states; the one that completes the count is the last,
+// and after an acquire fence it folds the chunks' partial states of its rows
+// with the online-softmax rule (chunks in order, so the result does not
+// depend on which workgroup finishes last), writes the output rows and LSE,
+// and resets the counter for the next run. Called by every thread of the
+// workgroup. On gfx950 a device-scope release writes back the XCD's L2 and an
+// acquire invalidates it, each a few microseconds: one thread does each, once
+// per workgroup (a fence in every thread took four of each per workgroup).
 template <int D>
 __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, int kvh,
                                      int nthreads) {
@@ -153,12 +157,16 @@ __device__ inline void merge_if_last(const KernelArgs& a, const DeviceItem& it, 
   const MergeTask mt = a.block_merges[it.block_merge];
   int32_t* counter = a.counters + int64_t(it.block_merge) * a.num_kv_heads + kvh;
   const int tid = opaque_tid();
-  __threadfence();  // this workgroup's partial states before its arrival
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(counter, 1) == mt.count - 1;
+  __syncthreads();  // every wavefront's partial states before thread 0's arrival
+  if (tid == 0) {
+    const int prior = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = prior == mt.count - 1;
+    // the other chunks' partial states after their arrivals
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    s_last = last;
+  }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();  // every other chunk's partial states after the count
   const int gmask = (1 << a.group_log2) - 1;
   const int rows = it.q_len << a.group_log2;
   constexpr int kQuads = D / 4;

@@ -383,9 +383,10 @@ def _merge_case(lens, seed, kv="bf16"):
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 def test_folded_merge_matches_oracle_and_resets(kv):
-    """Short splits (at most four chunks per request): run() folds the merge
-    into the decode kernel; the result matches the oracle and repeating the
-    run (arrival counters back at zero) gives the same bits."""
+    """Short splits (at most sixteen chunks per request, few workgroups):
+    run() folds the merge into the decode kernel; the result matches the
+    oracle and repeating the run (arrival counters back at zero) gives the
+    same bits."""
     import paged_kv_decode_plan_amd as pk
     from gpu_helpers import workspace
     w, case = _merge_case([300, 64, 900, 17], 31, kv)

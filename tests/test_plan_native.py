@@ -292,6 +292,20 @@ def test_many_split_workgroups_keep_the_merge_kernel():
     assert many["num_split_requests"] == 64 and many["merge_folded"] == 0
 
 
+@pytest.mark.parametrize("chunks,folded", [(8, 1), (16, 1), (17, 0)])
+def test_fold_takes_up_to_sixteen_chunks(chunks, folded):
+    """A split request of up to sixteen chunks over few workgroups folds its
+    merge into the decode kernel; one more chunk keeps the merge kernel. The
+    single-sequence shape (512 tokens, four KV heads, 64-token chunks) is the
+    eight-chunk case."""
+    P = 16
+    hkv = 4 if chunks == 8 else 1
+    info = pk.plan_partition([0, 4 * chunks], [P], hkv, hkv, 64, P, kv_dtype="f32",
+                             q_dtype="f32", slots=1024)[0]
+    assert info["min_chunk_pages"] == 4 and info["chunk_pages"] == 4
+    assert info["num_split_requests"] == 1 and info["merge_folded"] == folded
+
+
 def test_plans_from_many_threads_match_sequential_plans():
     """pkd_plan_create / get_worklist / destroy from eight host threads at
     once (each with its own tables, and some calls failing on purpose so
