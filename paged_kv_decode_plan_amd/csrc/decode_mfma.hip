@@ -480,9 +480,13 @@ __device__ inline float token_scale(const float* sc, const Ctx& c, const KernelA
 }
 
 // S = K . q^T of one loaded sub-tile: lane l gets tokens 4*q4 + r of head j.
+// The accumulation starts from `init` (int4: minus what the +8 of the widened
+// K codes adds to every score of the column, so no per-score correction is
+// needed afterwards).
 template <int KV>
-__device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>()]) {
-  f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+__device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>()],
+                             float init = 0.f) {
+  f32x4_t s = {init, init, init, init};
   if constexpr (wide16<KV>()) {
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) s = mfma<KV>(ld.k[dc], qb[dc], s);
@@ -523,8 +527,7 @@ __device__ inline f32x4_t qk(const Loads<KV>& ld, const u32x4_t (&qb)[q_ops<KV>(
 template <int KV, bool PAGE16, bool FULL, int HP>
 __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const Ctx& c,
                                   const KernelArgs& a, int kvh, int t0, const TilePages& tp,
-                                  int lim, bool cross, float corr, float m_run, float (&sc)[4],
-                                  bool& grow) {
+                                  int lim, bool cross, float m_run, float (&sc)[4], bool& grow) {
   float ks = a.sm_scale_log2;
   if constexpr (KV == kE4M3 && PAGE16) ks *= tp.ks;
 #pragma unroll
@@ -534,8 +537,7 @@ __device__ inline void scale_mask(const f32x4_t& s, const Loads<KV>& ld, const C
     if constexpr (KV == kE4M3 && !PAGE16) kr = ks * token_scale(a.k_scale, c, a, kvh, t);
     if constexpr (KV == kE4M3T) kr = ks * ld.ks[r];
     const bool ok = (FULL || t < lim) && (HP == 1 || !cross);
-    // int4: remove the +8 of the widened K codes (corr = 8 * sum of q')
-    const float v = ok ? (KV == kI4 ? s[r] - corr : s[r]) * kr : -INFINITY;
+    const float v = ok ? s[r] * kr : -INFINITY;
     sc[r] = v;
     grow |= v > m_run + kSlack;
   }
@@ -584,7 +586,7 @@ __device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ct
     // masked scores give 0, also when m_run = -inf (head pairs mask the
     // other head's lanes in full tiles too, while m_run is already finite)
     if constexpr (!FULL) p[e] = sc[e] == -INFINITY ? 0.f : p[e];
-    if constexpr (KV != kI4) d_run += p[e];
+    d_run += p[e];
   }
   if constexpr (KV == kE4M3) {
 #pragma unroll
@@ -603,14 +605,6 @@ __device__ inline void probs(const float (&sc)[4], const Loads<KV>& ld, const Ct
   }
   split16<KV>(p[0], p[1], p_hi.x, p_lo.x);
   split16<KV>(p[2], p[3], p_hi.y, p_lo.y);
-  if constexpr (KV == kI4) {
-    // d is the sum of the weights P.V is given (hi + lo), so that the +8 of
-    // the int4 V operands cancels exactly against 8 d in the epilogue
-    auto lo16 = [](uint32_t w) { return __builtin_bit_cast(float, w << 16); };
-    auto hi16 = [](uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); };
-    d_run += (lo16(p_hi.x) + lo16(p_lo.x)) + (hi16(p_hi.x) + hi16(p_lo.x)) +
-             (lo16(p_hi.y) + lo16(p_lo.y)) + (hi16(p_hi.y) + hi16(p_lo.y));
-  }
 }
 
 // V as the B operand of P.V for output columns nc: four 16-bit values,
@@ -731,7 +725,7 @@ struct Groups {
   f32x4_t acc[NG][8];
   float m_run[NG];  // reference max (log2 units), uniform over quarters
   float d_run[NG];  // sum of p over this lane's tokens
-  float corr[NG];   // int4: what the +8 of the K codes adds to this column's scores
+  float s0[NG];     // start of the score accumulation (int4: minus what the +8 of the K codes adds)
   int lim[NG];      // tokens of the item seen by this lane's row (column j of S)
   bool cross[NG];   // head pairs: the lane's S rows are not its column's head (masked)
 };
@@ -744,11 +738,11 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
   uint2 p_hi[NG], p_lo[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const f32x4_t s = qk<KV>(ld, gs.qb[g]);
+    const f32x4_t s = qk<KV>(ld, gs.qb[g], gs.s0[g]);
     float sc[1][4];
     bool grow = false;
     scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, gs.lim[g], gs.cross[g],
-                                     gs.corr[g], gs.m_run[g], sc[0], grow);
+                                     gs.m_run[g], sc[0], grow);
     move_max<FULL, 1>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
     probs<KV, PAGE16, FULL, HP>(sc[0], ld, c, a, kvh, t0, tp, gs.m_run[g], gs.d_run[g], p_hi[g],
                                 p_lo[g]);
@@ -778,14 +772,14 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
   u32x4_t p_hi[NG], p_lo[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const f32x4_t sa = qk<KV>(la, gs.qb[g]);
-    const f32x4_t sb = qk<KV>(lb, gs.qb[g]);
+    const f32x4_t sa = qk<KV>(la, gs.qb[g], gs.s0[g]);
+    const f32x4_t sb = qk<KV>(lb, gs.qb[g], gs.s0[g]);
     float sc[2][4];
     bool grow = false;
     scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, gs.lim[g], gs.cross[g],
-                                     gs.corr[g], gs.m_run[g], sc[0], grow);
+                                     gs.m_run[g], sc[0], grow);
     scale_mask<KV, PAGE16, FULL, HP>(sb, lb, c, a, kvh, t0 + ST, tb, gs.lim[g], gs.cross[g],
-                                     gs.corr[g], gs.m_run[g], sc[1], grow);
+                                     gs.m_run[g], sc[1], grow);
     move_max<FULL, 2>(sc, c, grow, gs.acc[g], gs.m_run[g], gs.d_run[g]);
     uint2 pa_hi, pa_lo, pb_hi, pb_lo;
     probs<KV, PAGE16, FULL, HP>(sc[0], la, c, a, kvh, t0, ta, gs.m_run[g], gs.d_run[g], pa_hi,
@@ -1014,7 +1008,7 @@ __device__ inline int decode_unit(const KernelArgs& a, WaveStates<G, kD>& st, in
     // column hold 32 dims each
     qsum += __shfl_xor(qsum, 16, 64);
     qsum += __shfl_xor(qsum, 32, 64);
-    gs.corr[g] = qsum * (1.f / 64.f);
+    gs.s0[g] = KV == kI4 ? -qsum * (1.f / 64.f) : 0.f;
   }
 
 #pragma unroll
@@ -1124,7 +1118,10 @@ __device__ inline int decode_unit(const KernelArgs& a, WaveStates<G, kD>& st, in
         const float vsv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
         if constexpr (KV == kI4) {
           // O holds sum P * (code + 8) * 2^-9 for row 4*q4 + r, whose d
-          // (the sum of P, in column lane 4*q4 + r) removes the + 8
+          // (the sum of P, in column lane 4*q4 + r) removes the + 8. P.V
+          // takes P as hi + lo bf16 parts, within 2^-17 of P, so what is
+          // left of the + 8 after normalising is below 8 * 2^-17 of one
+          // code step (v_scale)
           const float dr = __shfl(d_run, 4 * q4 + r, 64) * (1.f / 64.f);
 #pragma unroll
           for (int nc = 0; nc < 8; ++nc) acc[nc][r] = (acc[nc][r] - dr) * (vsv[nc] * 512.f);
