@@ -228,7 +228,8 @@ typedef struct {
  *               Strides are in elements (e2m1 and int4: two per byte, so the
  *               combined pool's strides above hold with head_dim counted in
  *               elements); k, v and every stride must be 16-byte aligned for
- *               f32/bf16/f16/e2m1/int4 and 8-byte aligned for e4m3.
+ *               f32/bf16/f16/e2m1/int4 and 8-byte aligned for e4m3, and a
+ *               page (page_stride) must span less than 4 GiB.
  *  indices      int32 page ids of the page table (length indptr[B]); ids may
  *               repeat across requests (shared prefixes) and are not range
  *               checked (pkd_check_page_ids does that off the hot path)

@@ -257,6 +257,10 @@ int check_run_args(const pkd_plan* p, const pkd_run_args* r, int32_t stages) {
     return fail(PKD_ERR_INVALID_ARGUMENT, "q must be 16-byte aligned");
   if (r->page_stride < 0 || r->token_stride < 0 || r->head_stride < 0)
     return fail(PKD_ERR_INVALID_ARGUMENT, "strides must be non-negative");
+  // The decode kernels form a tile's address as 32-bit byte offsets within a
+  // page on top of the page's 64-bit base.
+  if (kv_elems_bytes(a.kv_dtype, r->page_stride) >= (int64_t(1) << 32))
+    return fail(PKD_ERR_INVALID_ARGUMENT, "a page (page_stride) must span less than 4 GiB");
   if (!r->prior_out != !r->prior_lse)
     return fail(PKD_ERR_INVALID_ARGUMENT, "prior_out and prior_lse go together");
   if (r->prior_out && (reinterpret_cast<uintptr_t>(r->prior_out) % 16 ||

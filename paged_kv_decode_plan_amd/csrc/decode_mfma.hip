@@ -324,6 +324,12 @@ struct TilePages {
 struct Ctx {
   const char* kbase;
   const char* vbase;
+  // The K and V rows of this workgroup's (first) KV head in page 0, slot 0,
+  // and the page and token strides in bytes (a page spans less than 4 GiB,
+  // which the library checks), for the wavefront-uniform tile bases.
+  const char* kbase_h;
+  const char* vbase_h;
+  uint32_t page_bytes, token_bytes;
   const int32_t* page_ids;  // the item's slice of the page table
   const float* k_scale;     // row-wise e4m3 scales (kE4M3T only)
   const float* v_scale;
@@ -357,10 +363,10 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
     // sub-tile past the end loads from the last sub-tile's rows (tp.page is
     // that sub-tile's page).
     const int tb = FULL ? t0 : min(t0, last & ~(sub_tokens<HP>() - 1));
-    const int64_t base =
-        kv_bytes<KV>(tp.page * c.page_stride + int64_t(tb & c.pmask) * c.token_stride + c.head_off);
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase + base);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase + base);
+    const uint64_t base = uint64_t(uint32_t(tp.page)) * c.page_bytes +
+                          uint32_t(tb & c.pmask) * c.token_bytes;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase_h + base);
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase_h + base);
     uint32_t koff = c.koff;
     if constexpr (!FULL) {
       if constexpr (HP > 1) {  // row j: token j % (16 / HP) of head j / (16 / HP)
@@ -915,6 +921,10 @@ __device__ inline int decode_unit(const KernelArgs& a, WaveStates<G, kD>& st, in
   c.token_stride = a.token_stride;
   c.head_stride = a.head_stride;
   c.head_off = int64_t(c.kvh) * a.head_stride;
+  c.kbase_h = c.kbase + kv_bytes<KV>(c.head_off);
+  c.vbase_h = c.vbase + kv_bytes<KV>(c.head_off);
+  c.page_bytes = uint32_t(kv_bytes<KV>(a.page_stride));
+  c.token_bytes = uint32_t(kv_bytes<KV>(a.token_stride));
   c.log2p = a.page_size_log2;
   c.pmask = (1 << a.page_size_log2) - 1;
   c.kv_len = it.kv_len;

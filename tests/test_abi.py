@@ -117,6 +117,25 @@ def test_run_rejects_before_any_device_work():
     lib.pkd_plan_destroy(None)
 
 
+def test_run_rejects_pages_of_4_gib_or_more():
+    """Tile addresses are 32-bit byte offsets within a page on top of the
+    page's base, so a page stride of 4 GiB or more is refused up front."""
+    lib = pk.load()
+    rc, h, msg = _create()
+    assert rc == 0, msg
+    r = _lib.RunArgs()
+    fake = 1 << 20
+    r.q = r.k = r.v = r.indices = r.out = r.workspace = fake
+    r.workspace_bytes = 1 << 30
+    r.token_stride, r.head_stride = 2 * 128, 128
+    r.page_stride = (1 << 32) // 2  # bf16: exactly 4 GiB
+    assert lib.pkd_run(h, ctypes.byref(r)) == _lib.PKD_ERR_INVALID_ARGUMENT
+    assert b"4 GiB" in lib.pkd_last_error()
+    r.page_stride = (1 << 32) // 2 - 8  # just under: the plan check comes next
+    assert lib.pkd_run(h, ctypes.byref(r)) == _lib.PKD_ERR_PLAN_MISMATCH
+    lib.pkd_plan_destroy(h)
+
+
 def test_upload_rejects_small_or_misaligned_workspace():
     lib = pk.load()
     rc, h, msg = _create()
