@@ -744,7 +744,7 @@ __device__ inline void process_sub(const Loads<KV>& ld, const Ctx& c, const Kern
   uint2 p_hi[NG], p_lo[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const f32x4_t s = qk<KV>(ld, gs.qb[g], gs.s0[g]);
+    const f32x4_t s = qk<KV>(ld, gs.qb[g], KV == kI4 ? gs.s0[g] : 0.f);
     float sc[1][4];
     bool grow = false;
     scale_mask<KV, PAGE16, FULL, HP>(s, ld, c, a, kvh, t0, tp, gs.lim[g], gs.cross[g],
@@ -778,8 +778,8 @@ __device__ inline void process_pair(const Loads<KV>& la, const Loads<KV>& lb, co
   u32x4_t p_hi[NG], p_lo[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
-    const f32x4_t sa = qk<KV>(la, gs.qb[g], gs.s0[g]);
-    const f32x4_t sb = qk<KV>(lb, gs.qb[g], gs.s0[g]);
+    const f32x4_t sa = qk<KV>(la, gs.qb[g], KV == kI4 ? gs.s0[g] : 0.f);
+    const f32x4_t sb = qk<KV>(lb, gs.qb[g], KV == kI4 ? gs.s0[g] : 0.f);
     float sc[2][4];
     bool grow = false;
     scale_mask<KV, PAGE16, FULL, HP>(sa, la, c, a, kvh, t0, ta, gs.lim[g], gs.cross[g],

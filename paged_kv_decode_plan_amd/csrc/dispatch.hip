@@ -76,10 +76,12 @@ static hipError_t cap_lds(DecodeFn fn, int cap, size_t* bytes) {
 
 // Persistent launches of the MFMA kernel (see decode_mfma_kernel) when a
 // plan has more work units than the device holds resident workgroups: for
-// 16-bit and e4m3 KV, which run one workgroup per compute unit (measured on
-// MI355X: the ragged batch 1602.6 -> 1586.6 us per decode launch, the fp8
-// batch 687.9 -> 661.3 us), not for e2m1 and int4 KV, which run two and three
-// (404.3 against 397.8 us and 451.2 against 428.3 us).
+// 16-bit and e4m3 KV with per-page scales, which run one workgroup per
+// compute unit (measured on MI355X: the ragged batch 1602.6 -> 1586.6 us per
+// decode launch, the fp8 batch 687.9 -> 661.3 us), not for e2m1 and int4 KV,
+// which run two and three (404.3 against 397.8 us and 451.2 against
+// 428.3 us), nor for e4m3 with row-wise scales, whose persistent launch was
+// slower (843 against 754 us on its fp8 batch).
 #ifndef PKD_PERSISTENT
 #define PKD_PERSISTENT 1
 #endif
@@ -198,7 +200,7 @@ hipError_t launch_decode(const DecodeLaunch& L, hipStream_t stream, hipEvent_t s
   size_t lds = 0;
   if (hipError_t e = cap_lds(fn, L.wgs_cap, &lds); e != hipSuccess) return e;
   const bool nib4 = L.kv_dtype == kE2M1 || L.kv_dtype == kI4;
-  if (PKD_PERSISTENT && (PKD_PERSISTENT_NIB4 || !nib4) && L.work &&
+  if (PKD_PERSISTENT && (PKD_PERSISTENT_NIB4 || !nib4) && L.kv_dtype != kE4M3T && L.work &&
       decode_uses_mfma(L.kv_dtype, L.head_dim, L.group, L.rows, L.q_kind, 1 << L.page_size_log2)) {
     int resident = 0;
     if (hipError_t e = resident_workgroups(fn, lds, &resident); e != hipSuccess) return e;
