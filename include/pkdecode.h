@@ -312,8 +312,8 @@ int pkd_plan_get_worklist(const pkd_plan* plan, int32_t* items_out, int32_t* mer
 int pkd_plan_upload(pkd_plan* plan, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Enqueue the run on args->stream: the decode kernel and, when a request was
- * split, the merge. For an exact plan whose split requests have at most four
- * chunks, with at most 64 workgroups working on split requests in all, the
+ * split, the merge. For an exact plan whose split requests have at most
+ * sixteen chunks, with at most 64 workgroups working on split requests in all, the
  * merge is folded into the decode kernel (one launch): the last
  * workgroup of each split request (per query block and KV head) folds its
  * partial states into the output rows, counting chunk arrivals with an
