@@ -382,6 +382,41 @@ def _merge_case(lens, seed, kv="bf16"):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("chunks", [8, 16, 17])
+def test_fold_takes_up_to_sixteen_chunks(kv, chunks):
+    """One request cut into exactly `chunks` chunks of four pages (a pair of
+    KV heads per workgroup, so at most 34 split workgroups): up to sixteen
+    chunks the merge is folded into the decode kernel, seventeen take the
+    merge kernel; either way the rows match the oracle, and a second run
+    (fold counters back at zero) gives the same bits."""
+    import paged_kv_decode_plan_amd as pk
+    from gpu_helpers import workspace
+    lens = [64 * chunks - 5, 40, 64, 3]
+    w, case = _merge_case(lens, 40 + chunks, kv)
+    ref_out, ref_lse = oracle_for(case)
+    dc = to_device(case)
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+    wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], 16, 4, 128, 16,
+            q_data_type=torch.bfloat16, kv_data_type="e4m3" if kv == "e4m3" else torch.bfloat16,
+            out_data_type=torch.float32, sm_scale=w.scale(), slots=1024, balance=1,
+            min_chunk_pages=4)
+    info = wr.plan_info
+    _say("fold limit", kv, chunks, {k: info[k] for k in ("num_items", "num_split_requests",
+                                                          "merge_folded", "chunk_pages")})
+    assert info["chunk_pages"] == 4 and info["num_split_requests"] == 1
+    assert info["merge_folded"] == (1 if chunks <= 16 else 0)
+    outs = []
+    for _ in range(2):
+        out, lse = wr.run(dc["q"], dc["kv"], return_lse=True, k_scale=dc["k_scale"],
+                          v_scale=dc["v_scale"])
+        torch.cuda.synchronize()
+        compare(out, lse, ref_out, ref_lse, kv)
+        outs.append((out.clone(), lse.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    wr.close()
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
 def test_folded_merge_matches_oracle_and_resets(kv):
     """Short splits (at most sixteen chunks per request, few workgroups):
     run() folds the merge into the decode kernel; the result matches the
