@@ -1,6 +1,6 @@
 // Plain streaming read of device memory, for gfx950: the calibration that
 // puts the decode kernels' KV-read rate beside what one kernel can pull from
-// HBM on the same device (the pages judge decode kernels by the fraction of
+// HBM on the same device (the pages rate decode kernels by the fraction of
 // memory bandwidth they reach: "Attention Kernel Comparison: FlashAttention
 // vs FlashInfer vs xformers vs Triton", opening paragraphs).
 //

@@ -1,4 +1,4 @@
-// Host-side driver for the sanitizer build of libpkdecode's host code
+// Host-side test program for the sanitizer build of libpkdecode's host code
 // (planner and C ABI), built with AddressSanitizer and UndefinedBehavior-
 // Sanitizer on the CPU only: no kernel is launched and no GPU is needed.
 //

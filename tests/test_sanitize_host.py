@@ -1,9 +1,10 @@
 """The library's host code under AddressSanitizer and UndefinedBehaviorSanitizer.
 
-The planner and the C ABI (``planner.cpp``, ``capi.cpp``) and a driver
+The planner and the C ABI (``planner.cpp``, ``capi.cpp``) and a test program
 (``tests/sanitize/host_paths.cpp``) are compiled for the host only with both
 sanitizers; the kernel translation units are linked from the regular build's
-objects (their device code is not run: no kernel is launched). The driver then
+objects (their device code is not run: no kernel is launched). The test
+program then
 
 * builds partitions of seeded tables through the C++ planner directly, which
   this test compares bit for bit with the float64 oracle's rule, including
@@ -57,7 +58,7 @@ def _kernel_object(name, tmp):
 
 
 @pytest.fixture(scope="module")
-def driver(tmp_path_factory):
+def sanitized_program(tmp_path_factory):
     if not os.path.exists(_hipcc()):
         pytest.skip("hipcc is not installed")
     tmp = str(tmp_path_factory.mktemp("sanitize"))
@@ -147,9 +148,9 @@ def _encode(cases):
     return "\n".join(lines) + "\n"
 
 
-def test_planner_under_sanitizers_matches_the_oracle(driver):
+def test_planner_under_sanitizers_matches_the_oracle(sanitized_program):
     cases = _cases()
-    out = _run(driver, "partition", _encode(cases)).splitlines()
+    out = _run(sanitized_program, "partition", _encode(cases)).splitlines()
     pos = 0
     per_cu_seen = set()
     for c in cases:
@@ -176,15 +177,15 @@ def test_planner_under_sanitizers_matches_the_oracle(driver):
     assert per_cu_seen == {1, 2, 3, 4}
 
 
-def test_planner_rejects_bad_tables_under_sanitizers(driver):
+def test_planner_rejects_bad_tables_under_sanitizers(sanitized_program):
     bad = [dict(indptr=[0, 0], last=[1]), dict(indptr=[0, 2], last=[0]),
            dict(indptr=[0, 2], last=[17]), dict(indptr=[1, 2], last=[1])]
     cases = [dict(indptr=np.array(b["indptr"]), last=np.array(b["last"]), P=16, units=1,
                   slots=8, per_cu=1, balance=1, cmin=1, causal=True, qpi=1, qo=None)
              for b in bad]
-    out = _run(driver, "partition", _encode(cases)).splitlines()
+    out = _run(sanitized_program, "partition", _encode(cases)).splitlines()
     assert len(out) == len(bad) and all(line.startswith("err ") for line in out)
 
 
-def test_c_abi_host_paths_under_sanitizers(driver):
-    assert "abi checks: 0 failures" in _run(driver, "abi")
+def test_c_abi_host_paths_under_sanitizers(sanitized_program):
+    assert "abi checks: 0 failures" in _run(sanitized_program, "abi")
