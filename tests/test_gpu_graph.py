@@ -170,3 +170,67 @@ def test_fixed_capacity_plan_merges_a_prior_result():
             compare(out, lse, want_v, want_s, "bf16")
             res.append((out, lse))
         assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_graph_replays_a_persistent_launch(kv):
+    """A fixed-capacity plan with more work units (item x KV-head pair) than
+    the device holds resident workgroups runs as a persistent launch, whose
+    workgroups take units from counters in the workspace that the last one
+    resets. Captured once, its replays (eager work between them) match the
+    oracle and each other bit for bit, also for a second plan uploaded to the
+    same workspace afterwards."""
+    rng = np.random.default_rng(31 if kv == "bf16" else 32)
+    P, Hq, Hkv, D, B, pool = 16, 32, 8, 128, 320, 8200
+    tabs = [_tables(rng, pool, P, B, 400, 1) for _ in range(2)]
+    cap = dict(items=1024, merge_tasks=512, partials=1024, qo_len=1)
+    w0 = custom_workload(1, Hq, Hkv, D, P, kv, "bf16", [1], pool_pages=pool)
+    base = host_case(w0, 7, poison=False, table=explicit_table([[0]], [1], P, pool))
+    kvd = to_device(base)
+    q_buf = torch.zeros((B, Hq, D), dtype=torch.bfloat16, device=DEV)
+    out_buf = torch.zeros((B, Hq, D), dtype=torch.float32, device=DEV)
+    lse_buf = torch.zeros((B, Hq), dtype=torch.float32, device=DEV)
+    idx_buf = torch.zeros(max(len(t["indices"]) for t in tabs), dtype=torch.int32, device=DEV)
+    wr = pk.BatchDecodeWithPagedKVCacheWrapper(workspace(), "NHD")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    qrng = np.random.default_rng(98)
+    graph = None
+    for step, t in enumerate(tabs):
+        q = torch.from_numpy(qrng.standard_normal((B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+        qbits = q.view(torch.int16).numpy().view(np.uint16)
+        q_buf.copy_(q.to(DEV))
+        idx_buf.zero_()
+        idx_buf[: len(t["indices"])].copy_(torch.from_numpy(t["indices"]))
+        wr.plan(t["indptr"], idx_buf, t["last_page_len"], Hq, Hkv, D, P,
+                q_data_type=torch.bfloat16,
+                kv_data_type="e4m3" if kv == "e4m3" else torch.bfloat16,
+                out_data_type=torch.float32, sm_scale=D ** -0.5, capacity=cap)
+        info = wr.plan_info
+        units = info["num_items"] * info["units_per_item"]
+        _say("persistent", kv, "step", step, "items", info["num_items"], "units", units)
+        assert units > 2 * cus  # more units than one workgroup per compute unit
+        args = dict(out=out_buf, lse=lse_buf, k_scale=kvd["k_scale"], v_scale=kvd["v_scale"])
+        if graph is None:
+            wr.run(q_buf, kvd["kv"], **args)  # eager once: code objects loaded
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                wr.run(q_buf, kvd["kv"], **args)
+        ref_out, ref_lse = attention.decode(qbits, base["kv"], t["indptr"], t["indices"],
+                                            t["last_page_len"], num_kv_heads=Hkv,
+                                            q_dtype="bf16", kv_dtype=kv, sm_scale=D ** -0.5,
+                                            k_scale=base["k_scale"], v_scale=base["v_scale"])
+        for rep in range(3):
+            out_buf.fill_(float("nan"))
+            lse_buf.fill_(float("nan"))
+            scratch = torch.randn(1 << 20, device=DEV).sum()  # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            compare(out_buf, lse_buf, ref_out, ref_lse, kv)
+            if rep == 0:
+                first = out_buf.clone()
+            else:
+                assert torch.equal(out_buf, first)
+            del scratch
+    wr.close()
