@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import paged_kv_decode_plan_amd as pk
-from gpu_helpers import compare, oracle_for, to_device, workspace
+from gpu_helpers import compare, oracle_for, run_hip, to_device, workspace
 from workloads import custom_workload, host_case
 
 pytestmark = pytest.mark.gpu
@@ -76,3 +76,30 @@ def test_many_units_match_the_oracle_and_repeat(kv, split):
     again, again_lse = _run(wr, dc)
     assert torch.equal(again, out) and torch.equal(again_lse, lse)
     wr.close()
+
+
+@pytest.mark.parametrize("kv,q_dtype,hq,qo", [
+    ("f16", "f16", 32, None),    # fp16 KV on the fp16 MFMA
+    ("bf16", "bf16", 32, 3),     # three new tokens per request (12 rows per KV head)
+    ("bf16", "bf16", 128, None),  # 16 query heads per KV head: a pair's 32 rows, two column groups
+    ("e4m3", "bf16", 32, 2),
+])
+def test_persistent_launch_other_forms(kv, q_dtype, hq, qo):
+    """Persistent launches of the other MFMA forms (fp16 KV, several new
+    tokens per request, two column groups per workgroup) against the oracle,
+    and bit-identical when run again."""
+    rng = np.random.default_rng(90 + hq + (qo or 0))
+    lens = rng.integers(4, 300, size=300).tolist()
+    qo_lens = None if qo is None else [min(qo, n) for n in lens]
+    w = custom_workload(len(lens), hq, 8, 128, 16, kv, q_dtype, lens,
+                        pool_pages=sum(-(-x // 16) for x in lens) + 9, qo_lens=qo_lens)
+    case = host_case(w, 2100 + hq, poison=True)
+    dc = to_device(case)
+    out, lse, info = run_hip(dc)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    _say(kv, q_dtype, hq, qo, {k: info[k] for k in ("num_items", "units_per_item", "slots")})
+    assert info["num_items"] * info["units_per_item"] > info["slots"] >= cus
+    ref, ref_lse = oracle_for(case)
+    compare(out, lse, ref, ref_lse, kv)
+    again, again_lse, _ = run_hip(dc)
+    assert torch.equal(again, out) and torch.equal(again_lse, lse)
