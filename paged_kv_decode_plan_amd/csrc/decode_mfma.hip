@@ -326,7 +326,7 @@ struct Ctx {
   const char* vbase;
   // The K and V rows of this workgroup's (first) KV head in page 0, slot 0,
   // and the page and token strides in bytes (a page spans less than 4 GiB,
-  // which the library checks), for the wavefront-uniform tile bases.
+  // which the library checks), for the 4-bit forms' tile bases.
   const char* kbase_h;
   const char* vbase_h;
   uint32_t page_bytes, token_bytes;
@@ -363,10 +363,23 @@ __device__ inline void issue_sub(Loads<KV>& ld, const Ctx& c, int t0, const Tile
     // sub-tile past the end loads from the last sub-tile's rows (tp.page is
     // that sub-tile's page).
     const int tb = FULL ? t0 : min(t0, last & ~(sub_tokens<HP>() - 1));
-    const uint64_t base = uint64_t(uint32_t(tp.page)) * c.page_bytes +
-                          uint32_t(tb & c.pmask) * c.token_bytes;
-    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(c.kbase_h + base);
-    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(c.vbase_h + base);
+    __amdgpu_buffer_rsrc_t kr, vr;
+    if constexpr (nib4<KV>()) {
+      // 32-bit byte offsets within the page on top of the KV head's row in
+      // page 0: fewer live scalar registers, which the 4-bit head-pair
+      // instances need (their tile loop otherwise reloads spilled ones)
+      const uint64_t base = uint64_t(uint32_t(tp.page)) * c.page_bytes +
+                            uint32_t(tb & c.pmask) * c.token_bytes;
+      kr = tile_rsrc(c.kbase_h + base);
+      vr = tile_rsrc(c.vbase_h + base);
+    } else {
+      // (the same addresses from 64-bit element offsets: with the form above
+      // the row-wise e4m3 kernel ran 10 % slower on MI355X, the others alike)
+      const int64_t base = kv_bytes<KV>(tp.page * c.page_stride +
+                                        int64_t(tb & c.pmask) * c.token_stride + c.head_off);
+      kr = tile_rsrc(c.kbase + base);
+      vr = tile_rsrc(c.vbase + base);
+    }
     uint32_t koff = c.koff;
     if constexpr (!FULL) {
       if constexpr (HP > 1) {  // row j: token j % (16 / HP) of head j / (16 / HP)
