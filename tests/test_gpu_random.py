@@ -72,3 +72,44 @@ def test_random_configuration(seed):
     kw = dict(slots=16, balance=1, min_chunk_pages=1) if c["split"] else {}
     out, lse, _ = run_hip(to_device(case), out_dtype=c["out"], **kw)
     compare(out, lse, ref_out, ref_lse, c["kv"], out_dtype=c["out"])
+
+
+N_LARGE = 12
+
+
+def draw_large_case(seed: int) -> dict:
+    """A batch of 150-1050 short requests on an MFMA form with the device's
+    default plan: mostly more work units than resident workgroups, so the
+    16-bit and per-page e4m3 forms run persistent launches and the others
+    grids of several rounds."""
+    rng = np.random.default_rng([seed, 77001])
+    kv = str(rng.choice(["bf16", "f16", "e4m3", "e4m3t", "e2m1", "i4"]))
+    kv_scale = "token" if kv == "e4m3t" else "page"
+    kv = "e4m3" if kv == "e4m3t" else kv
+    qd = "f16" if kv == "f16" else "bf16"
+    g = int(rng.choice([1, 2, 4, 8]))
+    hkv = int(rng.choice([2, 4, 8]))
+    P = int(rng.choice([16, 32]))
+    B = int(rng.integers(150, 351)) * (3 if hkv == 2 else 1)  # two heads: one unit per item
+    lens = [int(x) for x in rng.integers(1, 300, size=B)]
+    qo = None
+    if rng.random() < 0.3:
+        qo = [int(rng.integers(1, min(L, 4) + 1)) for L in lens]
+    return dict(kv=kv, kv_scale=kv_scale, qd=qd, d=128, g=g, hkv=hkv, P=P, lens=lens, qo=qo)
+
+
+@pytest.mark.parametrize("seed", range(N_LARGE))
+def test_random_large_batch(seed):
+    c = draw_large_case(seed)
+    pool = sum(-(-L // c["P"]) for L in c["lens"]) + 3
+    w = custom_workload(len(c["lens"]), c["g"] * c["hkv"], c["hkv"], c["d"], c["P"], c["kv"],
+                        c["qd"], c["lens"], pool_pages=pool, qo_lens=c["qo"],
+                        kv_scale=c["kv_scale"])
+    case = host_case(w, 9000 + seed, poison=True)
+    print("[gpu-random-large]", seed, {k: v for k, v in c.items() if k != "lens"},
+          "B", len(c["lens"]), flush=True)
+    ref_out, ref_lse = oracle_for(case)
+    out, lse, info = run_hip(to_device(case))
+    print("[gpu-random-large]", seed, "units", info["num_items"] * info["units_per_item"],
+          "slots", info["slots"], flush=True)
+    compare(out, lse, ref_out, ref_lse, c["kv"])
