@@ -3,7 +3,8 @@ pair) than the device holds resident workgroups runs as that many
 workgroups, each taking units from a counter in the workspace, which the last
 one to finish resets. Checked on the GPU against the oracle, and run again
 (also after another plan used the same workspace) with identical bits, which
-needs the counters back at zero after every launch."""
+needs the counters back at zero after every launch; one case also folds the
+merge of its split requests into the same persistent launch."""
 import numpy as np
 import pytest
 import torch
@@ -36,12 +37,14 @@ def _run(wr, dc):
 
 
 @pytest.mark.parametrize("kv", ["bf16", "e4m3"])
-@pytest.mark.parametrize("split", ["none", "some"])
+@pytest.mark.parametrize("split", ["none", "some", "folded"])
 def test_many_units_match_the_oracle_and_repeat(kv, split):
     rng = np.random.default_rng(77 if kv == "bf16" else 78)
     lens = rng.integers(1, 400, size=320).tolist()
     if split == "some":
         lens[:6] = [6000, 5000, 4200, 3900, 3100, 2500]
+    elif split == "folded":  # two requests split over few workgroups: the merge folds in
+        lens[:2] = [4000, 3500]
     w = custom_workload(len(lens), 32, 8, 128, 16, kv, "bf16", lens,
                         pool_pages=sum(-(-x // 16) for x in lens) + 9)
     case = host_case(w, 2024, poison=True)
@@ -53,8 +56,9 @@ def test_many_units_match_the_oracle_and_repeat(kv, split):
     _say(kv, split, {k: info[k] for k in ("num_items", "units_per_item", "num_split_requests")})
     # more units than one workgroup per compute unit: the persistent launch
     assert info["num_items"] * info["units_per_item"] > 2 * cus
-    if split == "some":
+    if split != "none":
         assert info["num_split_requests"] > 0
+    assert info["merge_folded"] == (1 if split == "folded" else 0)
     out, lse = _run(wr, dc)
     ref, ref_lse = oracle_for(case)
     compare(out, lse, ref, ref_lse, kv)

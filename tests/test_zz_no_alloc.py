@@ -4,8 +4,10 @@ Two calls in a row on one device, the second with a smaller batch (so the
 static scratch still holds the first call's larger work list and partial
 states), each compared bit for bit with pkd_run's result on a caller
 workspace (same kernels, same launch) and with the oracle. The first plan
-splits many requests (separate merge kernel), the second few (merge folded
-into the decode kernel, whose arrival counters live in the scratch).
+splits many requests (separate merge kernel) and has more work units than
+one workgroup per compute unit (a persistent launch, whose work counters
+live in the scratch), the second few (merge folded into the decode kernel,
+whose arrival counters live in the scratch too).
 """
 import numpy as np
 import pytest
@@ -41,6 +43,8 @@ def test_static_scratch_matches_the_workspace_run_twice():
     big = [4096] * 12 + [100, 3000, 17, 2500]
     case1, info1, s1, w1 = _run_both(big, 71, slots=256, balance=2, min_chunk_pages=4)
     assert info1["num_split_requests"] >= 12 and info1["merge_folded"] == 0
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert info1["num_items"] * info1["units_per_item"] > cus
     print("[gpu] no-alloc: second call (smaller batch, merge folded)", flush=True)
     small = [900, 33, 2048]
     case2, info2, s2, w2 = _run_both(small, 72, slots=8, balance=1, min_chunk_pages=1)
