@@ -107,3 +107,62 @@ def test_persistent_launch_other_forms(kv, q_dtype, hq, qo):
     compare(out, lse, ref, ref_lse, kv)
     again, again_lse, _ = run_hip(dc)
     assert torch.equal(again, out) and torch.equal(again_lse, lse)
+
+
+def test_two_persistent_launches_on_two_streams():
+    """Two plans with more work units than resident workgroups, each with its
+    own workspace and stream (default priority), launched interleaved so that
+    the two persistent grids share the device: neither has all its workgroups
+    resident, which is safe because no workgroup waits for another (units come
+    from a counter that only grows; the last arrival of a split request folds
+    its merge). The results equal the same runs made one after the other, bit
+    for bit, and the oracle."""
+    cases = []
+    for seed, (kv, extra) in enumerate([("bf16", None), ("e4m3", [4000, 3500])]):
+        rng = np.random.default_rng(90 + seed)
+        lens = rng.integers(1, 400, size=320).tolist()
+        if extra:
+            lens[:len(extra)] = extra
+        w = custom_workload(len(lens), 32, 8, 128, 16, kv, "bf16", lens,
+                            pool_pages=sum(-(-x // 16) for x in lens) + 5)
+        cases.append((w, host_case(w, 300 + seed, poison=True)))
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    dcs = [to_device(c) for _, c in cases]
+    seq = []
+    for (w, _), dc in zip(cases, dcs):
+        wr = _plan(dc, w)
+        info = wr.plan_info
+        _say("two streams", w.kv_dtype, {k: info[k] for k in ("num_items", "merge_folded")})
+        assert info["num_items"] * info["units_per_item"] > 2 * cus
+        seq.append(_run(wr, dc))
+        wr.close()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    wrappers = []
+    for (w, _), dc, st in zip(cases, dcs, streams):
+        wr = pk.BatchDecodeWithPagedKVCacheWrapper(
+            torch.empty(16 << 20, dtype=torch.uint8, device="cuda:0"), "NHD")
+        with torch.cuda.stream(st):
+            wr.plan(dc["indptr"], dc["indices"], dc["last_page_len"], w.num_qo_heads,
+                    w.num_kv_heads, w.head_dim, w.page_size, q_data_type=torch.bfloat16,
+                    kv_data_type="e4m3" if w.kv_dtype == "e4m3" else torch.bfloat16,
+                    out_data_type=torch.float32, sm_scale=w.scale())
+        wrappers.append(wr)
+    assert wrappers[1].plan_info["merge_folded"] == 1
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(3):
+        res = []
+        for wr, dc, st in zip(wrappers, dcs, streams):
+            with torch.cuda.stream(st):
+                res.append(wr.run(dc["q"], dc["kv"], return_lse=True, k_scale=dc["k_scale"],
+                                  v_scale=dc["v_scale"]))
+        outs.append(res)
+    torch.cuda.synchronize()
+    for res in outs:
+        for (o, l), (so, sl) in zip(res, seq):
+            assert torch.equal(o, so) and torch.equal(l, sl)
+    for (w, c), (o, l) in zip(cases, seq):
+        ref, ref_lse = oracle_for(c)
+        compare(o, l, ref, ref_lse, w.kv_dtype)
+    for wr in wrappers:
+        wr.close()
